@@ -1,0 +1,245 @@
+"""Python binding of ``libar.so``, the gfx950 custom all-reduce reduction kernels.
+
+Argument marshalling only: every step of the hot path runs in the HIP
+kernels behind the C ABI declared in ``include/ar.h``.  PyTorch supplies the
+device memory (tensors) and the stream.  There is no CPU fallback: if the
+library is missing, importing this package raises.
+
+Functions mirror the C entry points and take ``torch.Tensor`` arguments:
+
+    ar_oneshot(ins, out)                         one output = sum of ranks
+    ar_twoshot_rs(ins, segs, flags, step, r0=0, r1=None, outs=None)
+    ar_twoshot_ag(segs, outs, flags, step, r0=0, r1=None)
+    ar_ll_pack(srcs, wires, proto, step)
+    ar_ll_reduce_unpack(wires, out, step, flags)
+    ar_ll128_reduce_unpack(wires, out, step, flags)
+    ar_flag_barrier_reset(flags, n)
+
+Each call enqueues on ``stream`` (default: torch's current stream) and
+raises :class:`ArError` on a synchronous error.  Asynchronous timeouts are
+read with :func:`read_status` after synchronising.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+from . import accounting  # noqa: F401  (re-exported helper module)
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libar.so")
+
+AR_OK, AR_ERR_ARG, AR_ERR_ALIGN, AR_ERR_DIVISIBLE, AR_ERR_ALIAS, AR_ERR_TIMEOUT, AR_ERR_HIP = range(7)
+AR_F32, AR_BF16 = 0, 1
+AR_PROTO_LL, AR_PROTO_LL128 = 0, 1
+AR_MAX_RANKS = 16
+AR_SLOTS_PER_RANK = 1024
+PHASE_TWOSHOT_AG, PHASE_LL, PHASE_LL128 = 1, 2, 3
+
+_DTYPES = {torch.float32: AR_F32, torch.bfloat16: AR_BF16}
+_PROTOS = {"ll": AR_PROTO_LL, "ll128": AR_PROTO_LL128, AR_PROTO_LL: AR_PROTO_LL, AR_PROTO_LL128: AR_PROTO_LL128}
+
+
+class ArError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = code
+        msg = _lib.ar_status_string(code).decode() if _lib is not None else str(code)
+        super().__init__(f"{where}: {msg} (status {code})")
+
+
+def _load(path: str = LIB_PATH):
+    if not os.path.exists(path):
+        raise ImportError(
+            f"{path} is missing: build it with `python -m custom_all_reduce_amd.build` "
+            "(there is no CPU fallback)"
+        )
+    lib = ctypes.CDLL(path)
+    vp, sz, i32, u32, u64 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_uint32, ctypes.c_uint64
+    P = ctypes.POINTER(ctypes.c_void_p)
+    lib.ar_flag_bytes.argtypes, lib.ar_flag_bytes.restype = [i32], sz
+    lib.ar_ll_wire_bytes.argtypes, lib.ar_ll_wire_bytes.restype = [i32, sz], sz
+    lib.ar_set_poll_timeout_ns.argtypes, lib.ar_set_poll_timeout_ns.restype = [u64], None
+    lib.ar_get_poll_timeout_ns.argtypes, lib.ar_get_poll_timeout_ns.restype = [], u64
+    lib.ar_status_string.argtypes, lib.ar_status_string.restype = [i32], ctypes.c_char_p
+    lib.ar_oneshot.argtypes, lib.ar_oneshot.restype = [P, i32, vp, sz, i32, vp], i32
+    lib.ar_twoshot_rs.argtypes, lib.ar_twoshot_rs.restype = [P, i32, P, sz, i32, i32, i32, vp, u32, P, vp], i32
+    lib.ar_twoshot_ag.argtypes, lib.ar_twoshot_ag.restype = [P, i32, P, sz, i32, i32, i32, vp, u32, vp], i32
+    lib.ar_ll_pack.argtypes, lib.ar_ll_pack.restype = [P, P, i32, sz, i32, i32, u32, vp], i32
+    lib.ar_ll_reduce_unpack.argtypes, lib.ar_ll_reduce_unpack.restype = [P, i32, vp, sz, i32, u32, vp, vp], i32
+    lib.ar_ll128_reduce_unpack.argtypes = [P, i32, vp, sz, i32, u32, vp, vp]
+    lib.ar_ll128_reduce_unpack.restype = i32
+    lib.ar_flag_barrier_reset.argtypes, lib.ar_flag_barrier_reset.restype = [vp, i32, vp], i32
+    return lib
+
+
+_lib = None
+_lib = _load()
+lib = _lib
+
+
+# ------------------------------------------------------------------ helpers --
+def _ptr_array(ptrs):
+    return (ctypes.c_void_p * len(ptrs))(*ptrs)
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    try:
+        return _DTYPES[t.dtype]
+    except KeyError:
+        raise TypeError(f"unsupported dtype {t.dtype}: use float32 or bfloat16") from None
+
+
+def _dev_tensor(t: torch.Tensor, what: str):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{what} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{what} must be a device tensor, got {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{what} must be contiguous")
+    return t
+
+
+def _check(code: int, where: str):
+    if code != AR_OK:
+        raise ArError(code, where)
+
+
+def flag_bytes(n: int) -> int:
+    return int(_lib.ar_flag_bytes(n))
+
+
+def ll_wire_bytes(proto, nbytes: int) -> int:
+    return int(_lib.ar_ll_wire_bytes(_PROTOS[proto], int(nbytes)))
+
+
+def set_poll_timeout_ns(ns: int):
+    _lib.ar_set_poll_timeout_ns(int(ns))
+
+
+def get_poll_timeout_ns() -> int:
+    return int(_lib.ar_get_poll_timeout_ns())
+
+
+def new_flags(n: int, device=None) -> torch.Tensor:
+    """Allocate a flag region for n ranks (uint32 words) and reset it on the
+    current stream.  Set-up only; not part of the per-step path."""
+    words = flag_bytes(n) // 4
+    f = torch.empty(words, dtype=torch.int32, device=device or "cuda")
+    ar_flag_barrier_reset(f, n)
+    return f
+
+
+def read_status(flags: torch.Tensor):
+    """(status word, detail word) of a flag region; synchronises the device."""
+    s = flags[:2].cpu().numpy().view("uint32")
+    return int(s[0]), int(s[1])
+
+
+def decode_status(word: int):
+    """Split a status word into (code, phase, rank)."""
+    return word & 0xFF, (word >> 8) & 0xFF, (word >> 16) & 0xFFFF
+
+
+def raise_on_status(flags: torch.Tensor, where: str = "kernel"):
+    word, detail = read_status(flags)
+    if word != 0:
+        code, phase, rank = decode_status(word)
+        err = ArError(code, f"{where} (phase {phase}, rank {rank}, index {detail})")
+        err.phase, err.rank, err.detail = phase, rank, detail
+        raise err
+
+
+# ------------------------------------------------------------- entry points --
+def ar_oneshot(ins, out: torch.Tensor, stream=None):
+    """out = sum of ins (fp32 accumulation in rank order, one rounding)."""
+    ins = [_dev_tensor(t, "input") for t in ins]
+    out = _dev_tensor(out, "out")
+    dt = _dtype_code(out)
+    for t in ins:
+        if t.dtype != out.dtype or t.numel() != out.numel():
+            raise ValueError("inputs and output must share dtype and numel")
+    code = _lib.ar_oneshot(_ptr_array([t.data_ptr() for t in ins]), len(ins), out.data_ptr(), out.numel(), dt,
+                           _stream(stream))
+    _check(code, "ar_oneshot")
+    return out
+
+
+def ar_twoshot_rs(ins, segs, flags, step: int, r0: int = 0, r1=None, outs=None, stream=None):
+    """Reduce-scatter for ranks [r0, r1); with ``outs`` also the barrier and
+    the all-gather in the same (cooperative) launch."""
+    n = len(ins)
+    r1 = n if r1 is None else r1
+    ins = [_dev_tensor(t, "input") for t in ins]
+    segs = [_dev_tensor(t, "segment") for t in segs]
+    flags = _dev_tensor(flags, "flags")
+    dt = _dtype_code(ins[0])
+    numel = ins[0].numel()
+    if len(segs) != n:
+        raise ValueError("need one segment buffer per rank")
+    out_arr = None
+    if outs is not None:
+        if len(outs) != n:
+            raise ValueError("outs must hold n entries (None outside [r0, r1))")
+        out_arr = _ptr_array([(_dev_tensor(o, "out").data_ptr() if o is not None else 0) for o in outs])
+    code = _lib.ar_twoshot_rs(_ptr_array([t.data_ptr() for t in ins]), n, _ptr_array([t.data_ptr() for t in segs]),
+                              numel, dt, r0, r1, flags.data_ptr(), int(step), out_arr, _stream(stream))
+    _check(code, "ar_twoshot_rs")
+
+
+def ar_twoshot_ag(segs, outs, flags, step: int, r0: int = 0, r1=None, numel=None, stream=None):
+    """All-gather for ranks [r0, r1) after waiting on every segment's slots."""
+    n = len(segs)
+    r1 = n if r1 is None else r1
+    segs = [_dev_tensor(t, "segment") for t in segs]
+    flags = _dev_tensor(flags, "flags")
+    dt = _dtype_code(segs[0])
+    numel = segs[0].numel() * n if numel is None else numel
+    out_arr = _ptr_array([(_dev_tensor(o, "out").data_ptr() if o is not None else 0) for o in outs])
+    code = _lib.ar_twoshot_ag(_ptr_array([t.data_ptr() for t in segs]), n, out_arr, numel, dt, r0, r1,
+                              flags.data_ptr(), int(step), _stream(stream))
+    _check(code, "ar_twoshot_ag")
+
+
+def ar_ll_pack(srcs, wires, proto, step: int, stream=None):
+    """Pack every message of ``srcs`` into its wire buffer (uint8 tensors)."""
+    srcs = [_dev_tensor(t, "src") for t in srcs]
+    wires = [_dev_tensor(t, "wire") for t in wires]
+    dt = _dtype_code(srcs[0])
+    code = _lib.ar_ll_pack(_ptr_array([t.data_ptr() for t in srcs]), _ptr_array([t.data_ptr() for t in wires]),
+                           len(srcs), srcs[0].numel(), dt, _PROTOS[proto], int(step), _stream(stream))
+    _check(code, "ar_ll_pack")
+
+
+def ar_ll_reduce_unpack(wires, out, step: int, flags, stream=None):
+    wires = [_dev_tensor(t, "wire") for t in wires]
+    out = _dev_tensor(out, "out")
+    flags = _dev_tensor(flags, "flags")
+    code = _lib.ar_ll_reduce_unpack(_ptr_array([t.data_ptr() for t in wires]), len(wires), out.data_ptr(),
+                                    out.numel(), _dtype_code(out), int(step), flags.data_ptr(), _stream(stream))
+    _check(code, "ar_ll_reduce_unpack")
+    return out
+
+
+def ar_ll128_reduce_unpack(wires, out, step: int, flags, stream=None):
+    wires = [_dev_tensor(t, "wire") for t in wires]
+    out = _dev_tensor(out, "out")
+    flags = _dev_tensor(flags, "flags")
+    code = _lib.ar_ll128_reduce_unpack(_ptr_array([t.data_ptr() for t in wires]), len(wires), out.data_ptr(),
+                                       out.numel(), _dtype_code(out), int(step), flags.data_ptr(), _stream(stream))
+    _check(code, "ar_ll128_reduce_unpack")
+    return out
+
+
+def ar_flag_barrier_reset(flags, n: int, stream=None):
+    flags = _dev_tensor(flags, "flags")
+    if flags.numel() * flags.element_size() < flag_bytes(n):
+        raise ValueError("flag region too small for n ranks")
+    _check(_lib.ar_flag_barrier_reset(flags.data_ptr(), n, _stream(stream)), "ar_flag_barrier_reset")

@@ -1,0 +1,57 @@
+"""Algorithmic HBM bytes of each kernel, for throughput and roofline figures.
+
+Counts what the method must move on one GPU when the n ranks' buffers are n
+allocations on that GPU: every read of a rank buffer, segment or wire buffer
+and every write, each byte once.  S = numel * element size (bytes per rank).
+
+  oneshot                 reads n*S               writes S
+  twoshot, one rank       reads S (RS) + S (AG)   writes S/n (segment) + S (output)
+  twoshot, all n ranks    reads 2*n*S             writes S (segments) + n*S (outputs)
+  LL / LL128 pack, each   reads S                 writes W(S)
+  LL / LL128 reduce       reads n*W(S)            writes S
+
+W(S) = 8*ceil(S/4) for LL (4 data bytes per 8-byte line) and
+128*ceil(S/120) for LL128 (120 data bytes per 128-byte line) -- the line
+formats of the protocol table on "集合通信：NCCL 的算法、协议与推理框架的定制
+all-reduce".  The flag region (a few KiB) is left out.
+"""
+from __future__ import annotations
+
+HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, published peak
+
+
+def wire_bytes(proto: str, S: int) -> int:
+    if proto == "ll":
+        return 8 * ((S + 3) // 4)
+    if proto == "ll128":
+        return 128 * ((S + 119) // 120)
+    raise ValueError(proto)
+
+
+def oneshot(n: int, S: int):
+    return n * S, S
+
+
+def twoshot(n: int, S: int, ranks: int):
+    """ranks = how many emulated ranks the launch computes (1 or n)."""
+    return 2 * ranks * S, ranks * (S // n) + ranks * S
+
+
+def twoshot_rs(n: int, S: int, ranks: int):
+    return ranks * S, ranks * (S // n)
+
+
+def twoshot_ag(n: int, S: int, ranks: int):
+    return ranks * S, ranks * S
+
+
+def ll_pack(proto: str, S: int, count: int = 1):
+    return count * S, count * wire_bytes(proto, S)
+
+
+def ll_reduce(proto: str, n: int, S: int):
+    return n * wire_bytes(proto, S), S
+
+
+def total(rw) -> int:
+    return int(rw[0] + rw[1])

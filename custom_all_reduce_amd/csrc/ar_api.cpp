@@ -1,0 +1,259 @@
+// C ABI of the library (declared in include/ar.h): synchronous argument
+// checks, then the launch.  Every check happens before anything is enqueued,
+// so an error return means the stream is untouched.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <mutex>
+#include <vector>
+
+#include "../../include/ar.h"
+#include "ar_launch.hpp"
+
+namespace ar {
+
+namespace {
+
+constexpr uint64_t kDefaultTimeoutNs = 1000000000ull;  // 1 s
+std::atomic<uint64_t> g_timeout_ns{kDefaultTimeoutNs};
+
+constexpr int kMaxDevices = 64;
+std::mutex g_info_mu;
+DeviceInfo g_info[kMaxDevices];
+bool g_info_ok[kMaxDevices] = {};
+
+// Largest message accepted per rank: the kernels index 16-byte vectors with
+// 32-bit integers.
+constexpr size_t kMaxBytes = size_t(1) << 36;
+constexpr size_t kStatusBytes = size_t(kStatusWords) * 4;
+
+size_t elem_bytes(int dtype) { return dtype == AR_F32 ? 4 : 2; }
+bool dtype_ok(int dtype) { return dtype == AR_F32 || dtype == AR_BF16; }
+bool ranks_ok(int n) { return n >= 2 && n <= AR_MAX_RANKS; }
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+struct Span {
+    uintptr_t lo, hi;
+    bool written;
+};
+
+Span span(const void* p, size_t bytes, bool written) {
+    const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+    return Span{lo, lo + bytes, written};
+}
+
+// A written span may not overlap any other span; read spans may overlap each
+// other (one buffer may stand for several emulated ranks).
+bool spans_ok(const std::vector<Span>& v) {
+    for (size_t a = 0; a < v.size(); ++a) {
+        if (!v[a].written || v[a].lo == v[a].hi) continue;
+        for (size_t b = 0; b < v.size(); ++b) {
+            if (a == b || v[b].lo == v[b].hi) continue;
+            if (v[a].lo < v[b].hi && v[b].lo < v[a].hi) return false;
+        }
+    }
+    return true;
+}
+
+uint64_t timeout_ticks() {
+    DeviceInfo info;
+    if (device_info(&info) != hipSuccess || info.wallclock_khz <= 0) return 100000000ull;
+    const uint64_t ns = g_timeout_ns.load();
+    const uint64_t khz = uint64_t(info.wallclock_khz);
+    const uint64_t ticks = ns / 1000000ull * khz + (ns % 1000000ull) * khz / 1000000ull;
+    return ticks == 0 ? 1 : ticks;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? AR_OK : AR_ERR_HIP; }
+
+size_t wire_bytes(int proto, size_t nbytes) {
+    if (proto == AR_PROTO_LL) return 8 * ((nbytes + 3) / 4);
+    if (proto == AR_PROTO_LL128) return 128 * ((nbytes + 119) / 120);
+    return 0;
+}
+
+// Shared checks of the two-shot entry points.
+int twoshot_check(const void* const* in, const void* const* seg, const void* const* out, int n,
+                  size_t numel, int dtype, int r0, int r1, const uint32_t* flags, uint32_t step) {
+    if (!ranks_ok(n) || !dtype_ok(dtype) || numel == 0 || !seg || !flags || step == 0) return AR_ERR_ARG;
+    if (r0 < 0 || r1 > n || r0 >= r1) return AR_ERR_ARG;
+    const size_t es = elem_bytes(dtype);
+    if (numel > kMaxBytes / es) return AR_ERR_ARG;
+    for (int i = 0; i < n; ++i) {
+        if (!seg[i] || (in && !in[i])) return AR_ERR_ARG;
+        if (!aligned16(seg[i]) || (in && !aligned16(in[i]))) return AR_ERR_ALIGN;
+    }
+    if (out)
+        for (int r = r0; r < r1; ++r) {
+            if (!out[r]) return AR_ERR_ARG;
+            if (!aligned16(out[r])) return AR_ERR_ALIGN;
+        }
+    if (!aligned16(flags)) return AR_ERR_ALIGN;
+    if (numel % size_t(n) != 0 || (numel / size_t(n) * es) % 16 != 0) return AR_ERR_DIVISIBLE;
+
+    const size_t S = numel * es, m_bytes = S / size_t(n);
+    std::vector<Span> v;
+    v.push_back(span(flags, ar_flag_bytes(n), true));
+    if (in)
+        for (int i = 0; i < n; ++i) v.push_back(span(in[i], S, false));
+    for (int j = 0; j < n; ++j) {
+        // with an input present (reduce-scatter), seg[r0..r1) are written
+        const bool written = in && j >= r0 && j < r1;
+        v.push_back(span(seg[j], m_bytes, written));
+    }
+    if (out)
+        for (int r = r0; r < r1; ++r) v.push_back(span(out[r], S, true));
+    if (!spans_ok(v)) return AR_ERR_ALIAS;
+    return AR_OK;
+}
+
+int ll_reduce_common(const void* const* wire, int n, void* out, size_t numel, int dtype,
+                     uint32_t step, uint32_t* flags, int proto, void* stream) {
+    if (!ranks_ok(n) || !dtype_ok(dtype) || numel == 0 || !wire || !out || !flags || step == 0)
+        return AR_ERR_ARG;
+    const size_t es = elem_bytes(dtype);
+    if (numel > kMaxBytes / es) return AR_ERR_ARG;
+    for (int i = 0; i < n; ++i) {
+        if (!wire[i]) return AR_ERR_ARG;
+        if (!aligned16(wire[i])) return AR_ERR_ALIGN;
+    }
+    if (!aligned16(out) || !aligned16(flags)) return AR_ERR_ALIGN;
+    const size_t S = numel * es, W = wire_bytes(proto, S);
+    std::vector<Span> v;
+    v.push_back(span(out, S, true));
+    v.push_back(span(flags, kStatusBytes, true));
+    for (int i = 0; i < n; ++i) v.push_back(span(wire[i], W, false));
+    if (!spans_ok(v)) return AR_ERR_ALIAS;
+    return hip_status(launch_ll_reduce(wire, n, out, numel, dtype, proto, step, flags, timeout_ticks(),
+                                       static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+hipError_t device_info(DeviceInfo* out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_info_mu);
+    if (!g_info_ok[dev]) {
+        DeviceInfo d{};
+        if ((e = hipDeviceGetAttribute(&d.cu_count, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess)
+            return e;
+        if ((e = hipDeviceGetAttribute(&d.wallclock_khz, hipDeviceAttributeWallClockRate, dev)) != hipSuccess)
+            return e;
+        if ((e = hipDeviceGetAttribute(&d.coop_supported, hipDeviceAttributeCooperativeLaunch, dev)) !=
+            hipSuccess)
+            return e;
+        g_info[dev] = d;
+        g_info_ok[dev] = true;
+    }
+    *out = g_info[dev];
+    return hipSuccess;
+}
+
+}  // namespace ar
+
+using namespace ar;
+
+extern "C" {
+
+size_t ar_flag_bytes(int n) {
+    if (!ranks_ok(n)) return 0;
+    return (size_t(kStatusWords) + size_t(n) * kSlotsPerRank) * 4;
+}
+
+size_t ar_ll_wire_bytes(int proto, size_t nbytes) { return wire_bytes(proto, nbytes); }
+
+void ar_set_poll_timeout_ns(uint64_t ns) { g_timeout_ns.store(ns == 0 ? kDefaultTimeoutNs : ns); }
+
+uint64_t ar_get_poll_timeout_ns(void) { return g_timeout_ns.load(); }
+
+const char* ar_status_string(int status) {
+    switch (status & 0xFF) {
+        case AR_OK: return "ok";
+        case AR_ERR_ARG: return "invalid argument";
+        case AR_ERR_ALIGN: return "pointer not 16-byte aligned";
+        case AR_ERR_DIVISIBLE: return "two-shot size not divisible into 16-byte segments";
+        case AR_ERR_ALIAS: return "written buffer overlaps another buffer";
+        case AR_ERR_TIMEOUT: return "flag wait timed out";
+        case AR_ERR_HIP: return "HIP runtime error";
+        default: return "unknown status";
+    }
+}
+
+int ar_oneshot(const void* const* in, int n, void* out, size_t numel, int dtype, void* stream) {
+    if (!in || !out || !ranks_ok(n) || !dtype_ok(dtype) || numel == 0) return AR_ERR_ARG;
+    const size_t es = elem_bytes(dtype);
+    if (numel > kMaxBytes / es) return AR_ERR_ARG;
+    for (int i = 0; i < n; ++i) {
+        if (!in[i]) return AR_ERR_ARG;
+        if (!aligned16(in[i])) return AR_ERR_ALIGN;
+    }
+    if (!aligned16(out)) return AR_ERR_ALIGN;
+    const size_t S = numel * es;
+    std::vector<Span> v;
+    v.push_back(span(out, S, true));
+    for (int i = 0; i < n; ++i) v.push_back(span(in[i], S, false));
+    if (!spans_ok(v)) return AR_ERR_ALIAS;
+    return hip_status(launch_oneshot(in, n, out, numel, dtype, static_cast<hipStream_t>(stream)));
+}
+
+int ar_twoshot_rs(const void* const* in, int n, void* const* seg, size_t numel, int dtype, int r0, int r1,
+                  uint32_t* flags, uint32_t step, void* const* out, void* stream) {
+    if (!in) return AR_ERR_ARG;
+    const int st = twoshot_check(in, seg, out, n, numel, dtype, r0, r1, flags, step);
+    if (st != AR_OK) return st;
+    TwoShotRequest rq{in, seg, out, n, numel, dtype, r0, r1, flags, step, true, out != nullptr,
+                      timeout_ticks()};
+    return hip_status(launch_twoshot(rq, static_cast<hipStream_t>(stream)));
+}
+
+int ar_twoshot_ag(const void* const* seg, int n, void* const* out, size_t numel, int dtype, int r0, int r1,
+                  uint32_t* flags, uint32_t step, void* stream) {
+    if (!out) return AR_ERR_ARG;
+    const int st = twoshot_check(nullptr, seg, out, n, numel, dtype, r0, r1, flags, step);
+    if (st != AR_OK) return st;
+    TwoShotRequest rq{nullptr, const_cast<void* const*>(seg), out, n, numel, dtype, r0, r1, flags, step,
+                      false, true, timeout_ticks()};
+    return hip_status(launch_twoshot(rq, static_cast<hipStream_t>(stream)));
+}
+
+int ar_ll_pack(const void* const* src, void* const* wire, int count, size_t numel, int dtype, int proto,
+               uint32_t step, void* stream) {
+    if (!src || !wire || count < 1 || count > AR_MAX_RANKS || numel == 0 || !dtype_ok(dtype) || step == 0)
+        return AR_ERR_ARG;
+    if (proto != AR_PROTO_LL && proto != AR_PROTO_LL128) return AR_ERR_ARG;
+    const size_t es = elem_bytes(dtype);
+    if (numel > kMaxBytes / es) return AR_ERR_ARG;
+    for (int i = 0; i < count; ++i) {
+        if (!src[i] || !wire[i]) return AR_ERR_ARG;
+        if (!aligned16(src[i]) || !aligned16(wire[i])) return AR_ERR_ALIGN;
+    }
+    const size_t S = numel * es, W = wire_bytes(proto, S);
+    std::vector<Span> v;
+    for (int i = 0; i < count; ++i) {
+        v.push_back(span(src[i], S, false));
+        v.push_back(span(wire[i], W, true));
+    }
+    if (!spans_ok(v)) return AR_ERR_ALIAS;
+    return hip_status(launch_ll_pack(src, wire, count, S, proto, step, static_cast<hipStream_t>(stream)));
+}
+
+int ar_ll_reduce_unpack(const void* const* wire, int n, void* out, size_t numel, int dtype, uint32_t step,
+                        uint32_t* flags, void* stream) {
+    return ll_reduce_common(wire, n, out, numel, dtype, step, flags, AR_PROTO_LL, stream);
+}
+
+int ar_ll128_reduce_unpack(const void* const* wire, int n, void* out, size_t numel, int dtype, uint32_t step,
+                           uint32_t* flags, void* stream) {
+    return ll_reduce_common(wire, n, out, numel, dtype, step, flags, AR_PROTO_LL128, stream);
+}
+
+int ar_flag_barrier_reset(uint32_t* flags, int n, void* stream) {
+    if (!flags || !ranks_ok(n)) return AR_ERR_ARG;
+    if (!aligned16(flags)) return AR_ERR_ALIGN;
+    return hip_status(launch_flag_reset(flags, ar_flag_bytes(n) / 4, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

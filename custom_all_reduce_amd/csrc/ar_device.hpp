@@ -1,0 +1,145 @@
+// Device-side helpers shared by the gfx950 kernels: 128-bit vector access,
+// fp32 accumulation of packed inputs, round-to-nearest-even to bfloat16, and
+// the bounded flag polling used by the two-shot barrier and the LL receivers.
+//
+// Written for CDNA4 (gfx950) only: 64-lane wavefronts, global_load/store_dwordx4,
+// wall clock from s_memrealtime (wall_clock64), agent-scope fences.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "ar_launch.hpp"
+
+namespace ar {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+
+struct bf16_t {};  // tag type: bfloat16 elements stored as raw 16-bit patterns
+
+template <typename T> struct elem;
+template <> struct elem<float> { static constexpr int per_vec = 4; static constexpr int bytes = 4; };
+template <> struct elem<bf16_t> { static constexpr int per_vec = 8; static constexpr int bytes = 2; };
+
+// ---- memory access -------------------------------------------------------
+// Streaming loads/stores: each input byte is read once, so mark them
+// non-temporal (global_load_dwordx4 ... nt).
+__device__ __forceinline__ u32x4 ld_stream(const u32x4* p) { return __builtin_nontemporal_load(p); }
+__device__ __forceinline__ void st_stream(u32x4* p, u32x4 v) { __builtin_nontemporal_store(v, p); }
+__device__ __forceinline__ u32x4 ld_plain(const u32x4* p) { return *p; }
+
+// ---- rounding ---------------------------------------------------------------
+// float32 -> bfloat16 pattern, round to nearest, ties to even.  Adding
+// 0x7FFF plus the lowest kept bit to the pattern carries into the kept half
+// exactly when the dropped half is above one half, or exactly one half with
+// an odd kept half; a carry out of the mantissa lands in the exponent (so
+// overflow gives infinity).  NaN keeps its sign and top payload bits and is
+// made quiet.
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+    uint32_t u = __float_as_uint(f);
+    uint32_t rounded = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+    uint32_t quiet = (u >> 16) | 0x40u;
+    return ((u & 0x7FFFFFFFu) > 0x7F800000u) ? quiet : rounded;
+}
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    return f32_to_bf16_rne(lo) | (f32_to_bf16_rne(hi) << 16);
+}
+
+// ---- accumulation -----------------------------------------------------------
+// Accumulator for one 16-byte vector position: 4 fp32 or 8 bf16 elements,
+// widened to fp32.  Starts at +0.0 and adds ranks in the order add() is
+// called (callers go rank 0 first).  No fast-math: the adds are not
+// reassociated or contracted.
+template <typename T> struct Acc;
+
+template <> struct Acc<float> {
+    float a[4];
+    __device__ __forceinline__ Acc() { a[0] = a[1] = a[2] = a[3] = 0.0f; }
+    __device__ __forceinline__ void add(u32x4 v) {
+        a[0] = a[0] + __uint_as_float(v.x);
+        a[1] = a[1] + __uint_as_float(v.y);
+        a[2] = a[2] + __uint_as_float(v.z);
+        a[3] = a[3] + __uint_as_float(v.w);
+    }
+    // add only the low 2 words (8 data bytes)
+    __device__ __forceinline__ void add_half(u32x4 v) {
+        a[0] = a[0] + __uint_as_float(v.x);
+        a[1] = a[1] + __uint_as_float(v.y);
+    }
+    __device__ __forceinline__ u32x4 result() const {
+        return u32x4{__float_as_uint(a[0]), __float_as_uint(a[1]), __float_as_uint(a[2]),
+                     __float_as_uint(a[3])};
+    }
+};
+
+template <> struct Acc<bf16_t> {
+    float a[8];
+    __device__ __forceinline__ Acc() {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) a[i] = 0.0f;
+    }
+    __device__ __forceinline__ void add(u32x4 v) {
+        a[0] = a[0] + bf16_lo(v.x); a[1] = a[1] + bf16_hi(v.x);
+        a[2] = a[2] + bf16_lo(v.y); a[3] = a[3] + bf16_hi(v.y);
+        a[4] = a[4] + bf16_lo(v.z); a[5] = a[5] + bf16_hi(v.z);
+        a[6] = a[6] + bf16_lo(v.w); a[7] = a[7] + bf16_hi(v.w);
+    }
+    __device__ __forceinline__ void add_half(u32x4 v) {
+        a[0] = a[0] + bf16_lo(v.x); a[1] = a[1] + bf16_hi(v.x);
+        a[2] = a[2] + bf16_lo(v.y); a[3] = a[3] + bf16_hi(v.y);
+    }
+    __device__ __forceinline__ u32x4 result() const {
+        return u32x4{pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]), pack_bf16x2(a[4], a[5]),
+                     pack_bf16x2(a[6], a[7])};
+    }
+};
+
+// Scalar element access for the partial last vector.
+__device__ __forceinline__ float load_scalar(const void* base, size_t k, float*) {
+    return static_cast<const float*>(base)[k];
+}
+__device__ __forceinline__ float load_scalar(const void* base, size_t k, bf16_t*) {
+    return __uint_as_float(uint32_t(static_cast<const uint16_t*>(base)[k]) << 16);
+}
+__device__ __forceinline__ void store_scalar(void* base, size_t k, float v, float*) {
+    static_cast<float*>(base)[k] = v;
+}
+__device__ __forceinline__ void store_scalar(void* base, size_t k, float v, bf16_t*) {
+    static_cast<uint16_t*>(base)[k] = uint16_t(f32_to_bf16_rne(v));
+}
+
+// ---- wave utilities -----------------------------------------------------------
+__device__ __forceinline__ int lane_id() { return __lane_id(); }
+__device__ __forceinline__ uint64_t wave_ballot(bool p) { return __ballot(p); }
+__device__ __forceinline__ uint64_t wave_exec() { return __ballot(true); }
+
+// ---- flags ----------------------------------------------------------------------
+__device__ __forceinline__ uint32_t flag_load_relaxed(const uint32_t* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void flag_store_relaxed(uint32_t* p, uint32_t v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t line_load_relaxed(const uint64_t* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void fence_release_agent() { __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent"); }
+__device__ __forceinline__ void fence_acquire_agent() { __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent"); }
+
+// Record the first asynchronous error of a launch in the flag region's
+// status line: word 0 = code | phase << 8 | rank << 16, word 1 = detail.
+__device__ __forceinline__ void report_timeout(uint32_t* status, uint32_t phase, uint32_t rank,
+                                               uint32_t detail) {
+    uint32_t code = kTimeoutCode | (phase << 8) | (rank << 16);
+    if (atomicCAS(status, 0u, code) == 0u) flag_store_relaxed(status + 1, detail);
+}
+
+__device__ __forceinline__ uint64_t now_ticks() { return wall_clock64(); }
+
+}  // namespace ar

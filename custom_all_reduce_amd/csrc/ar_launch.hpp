@@ -1,0 +1,79 @@
+// Internal launch interface between the C ABI (ar_api.cpp) and the kernel
+// files.  Arguments here are already validated.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include <type_traits>
+#include <utility>
+
+namespace ar {
+
+// Flag region layout (32-bit words): word 0 status, word 1 detail, words
+// 2..31 unused (one 128-byte line), then kSlotsPerRank arrival slots per rank.
+constexpr int kMaxRanks = 16;
+constexpr int kSlotsPerRank = 1024;
+constexpr int kStatusWords = 32;
+constexpr uint32_t kTimeoutCode = 5;  // AR_ERR_TIMEOUT
+
+struct DeviceInfo {
+    int cu_count;
+    int wallclock_khz;
+    int coop_supported;
+};
+
+// Cached per-device properties (queried once per device).
+hipError_t device_info(DeviceInfo* out);
+
+hipError_t launch_oneshot(const void* const* in, int n, void* out, size_t numel, int dtype,
+                          hipStream_t s);
+
+struct TwoShotRequest {
+    const void* const* in;   // may be null when !do_rs
+    void* const* seg;
+    void* const* out;        // may be null when !do_ag
+    int n;
+    size_t numel;
+    int dtype;
+    int r0, r1;
+    uint32_t* flags;
+    uint32_t step;
+    bool do_rs, do_ag;
+    uint64_t timeout_ticks;
+};
+hipError_t launch_twoshot(const TwoShotRequest& rq, hipStream_t s);
+
+hipError_t launch_ll_pack(const void* const* src, void* const* wire, int count, size_t nbytes,
+                          int proto, uint32_t step, hipStream_t s);
+
+hipError_t launch_ll_reduce(const void* const* wire, int n, void* out, size_t numel, int dtype,
+                            int proto, uint32_t step, uint32_t* flags, uint64_t timeout_ticks,
+                            hipStream_t s);
+
+hipError_t launch_flag_reset(uint32_t* flags, size_t words, hipStream_t s);
+
+// Call f(std::integral_constant<int, N>{}) for the rank count n in [2, 16].
+template <typename F>
+auto dispatch_ranks(int n, F&& f) {
+    switch (n) {
+        case 2: return f(std::integral_constant<int, 2>{});
+        case 3: return f(std::integral_constant<int, 3>{});
+        case 4: return f(std::integral_constant<int, 4>{});
+        case 5: return f(std::integral_constant<int, 5>{});
+        case 6: return f(std::integral_constant<int, 6>{});
+        case 7: return f(std::integral_constant<int, 7>{});
+        case 8: return f(std::integral_constant<int, 8>{});
+        case 9: return f(std::integral_constant<int, 9>{});
+        case 10: return f(std::integral_constant<int, 10>{});
+        case 11: return f(std::integral_constant<int, 11>{});
+        case 12: return f(std::integral_constant<int, 12>{});
+        case 13: return f(std::integral_constant<int, 13>{});
+        case 14: return f(std::integral_constant<int, 14>{});
+        case 15: return f(std::integral_constant<int, 15>{});
+        default: return f(std::integral_constant<int, 16>{});
+    }
+}
+
+}  // namespace ar

@@ -1,0 +1,180 @@
+/*
+ * ar.h -- C ABI of the MI355X (gfx950) per-GPU reduction kernels of a custom
+ * all-reduce: one-shot, two-shot (reduce-scatter, flag barrier, all-gather)
+ * and the LL / LL128 flag-packed protocols.
+ *
+ * Sources (page titles as printed):
+ *  [CAR]  "0-custom-all-reduce" (obnotes, Inference/sglang/jit_kernel): the
+ *         one-shot pull kernel, 实现 steps 1-6 -- a pointer table with one
+ *         mapped buffer per GPU, 16-byte vectors, fp32 accumulation in GPU
+ *         index order, one round-to-nearest cast, 16-byte alignment, the
+ *         two-shot divisibility requirement, start/end synchronisation, and
+ *         the rule that the output must not be a buffer others still read.
+ *  [NCCL] "集合通信：NCCL 的算法、协议与推理框架的定制 all-reduce"
+ *         (anrans.github.io, serving/comm/nccl): 算法 (one-shot, two-shot),
+ *         协议 table (LL, LL128, Simple), 练习 3 (registered buffers).
+ *  [MGPU] "多 GPU 与 NCCL" (anrans.github.io, cuda/tools/multi-gpu): 集合通信
+ *         table, all-reduce = reduce-scatter + all-gather.
+ *
+ * Conventions shared by every entry point
+ *  - n emulated ranks, 2 <= n <= AR_MAX_RANKS ([CAR] supports up to 16 GPUs).
+ *    Rank i's buffer is the i-th pointer of a pointer table; on one GPU the
+ *    n "registered buffers" are n separate device allocations.  Pointer
+ *    tables are host arrays; they are copied by value into the kernel
+ *    arguments, so they may be freed as soon as the call returns.
+ *  - Every data pointer is device memory of the current HIP device, 16-byte
+ *    aligned ([CAR] step 1: 128-bit accesses).  All memory is caller-owned;
+ *    the library never allocates on these paths.
+ *  - numel counts elements per rank; dtype is an ar_dtype.  Sums are taken in
+ *    fp32, rank 0 first, starting from +0.0, and rounded once to the output
+ *    type with round-to-nearest-even ([CAR] step 4).  Results are therefore
+ *    identical bit for bit on every rank and on every call.
+ *  - stream is a hipStream_t (NULL = the null stream).  Every call validates
+ *    its arguments synchronously, then enqueues its kernels and returns.
+ *    A call that returns an error enqueued nothing.
+ *  - Written buffers (outputs, segments, wire buffers) must not overlap any
+ *    other buffer of the same call (AR_ERR_ALIAS): [CAR] step 5 -- without a
+ *    staging copy the output must be a fresh buffer, not one a peer reads.
+ *  - Waits on flags are bounded by a wall-clock budget (ar_set_poll_timeout_ns).
+ *    A wait that runs out does not hang: the kernel writes
+ *    AR_ERR_TIMEOUT | phase << 8 | rank << 16 into status word 0 of the flag
+ *    region (first error wins), the index of the tile or line it waited on
+ *    into word 1, skips the work that depended on it, and exits normally.
+ *    Read the status after synchronising the stream.
+ *  - Reuse: a producer may overwrite a segment or wire buffer for step s+1
+ *    only after every consumer has finished step s (the end synchronisation
+ *    of [CAR] step 6).  On one GPU, stream order gives this.
+ */
+#ifndef AR_H
+#define AR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define AR_MAX_RANKS 16
+/* Flag slots per rank in the two-shot barrier region (see ar_flag_bytes). */
+#define AR_SLOTS_PER_RANK 1024
+
+typedef enum {
+    AR_OK = 0,
+    AR_ERR_ARG = 1,       /* null pointer, n out of range, numel 0, step 0, bad dtype/proto/ranks */
+    AR_ERR_ALIGN = 2,     /* a data pointer is not 16-byte aligned */
+    AR_ERR_DIVISIBLE = 3, /* two-shot: numel % n != 0 or a segment is not a whole number of 16-byte vectors */
+    AR_ERR_ALIAS = 4,     /* a written buffer overlaps another buffer of the call */
+    AR_ERR_TIMEOUT = 5,   /* asynchronous only: a flag wait ran out (status word of the flag region) */
+    AR_ERR_HIP = 6        /* a HIP runtime call failed (launch, device query, cooperative launch) */
+} ar_status;
+
+typedef enum { AR_F32 = 0, AR_BF16 = 1 } ar_dtype;
+typedef enum { AR_PROTO_LL = 0, AR_PROTO_LL128 = 1 } ar_proto;
+
+/* Phases reported in bits 8..15 of a timeout status word. */
+#define AR_PHASE_TWOSHOT_AG 1
+#define AR_PHASE_LL 2
+#define AR_PHASE_LL128 3
+
+/* Bytes of the flag region used by the two-shot barrier and the LL status
+ * word for up to n ranks: a 128-byte status line (word 0 status, word 1
+ * detail) then AR_SLOTS_PER_RANK 32-bit arrival slots per rank.  Returns 0
+ * if n is out of range. */
+size_t ar_flag_bytes(int n);
+
+/* Wire bytes for one rank's message of nbytes bytes ([NCCL] 协议 table):
+ * LL    -- 8-byte lines, each 4 data bytes then a 32-bit flag: 8*ceil(nbytes/4);
+ * LL128 -- 128-byte lines, each 120 data bytes then a 64-bit flag:
+ *          128*ceil(nbytes/120).
+ * The last line's data bytes past the message are zero.  Returns 0 on a bad
+ * proto. */
+size_t ar_ll_wire_bytes(int proto, size_t nbytes);
+
+/* Budget for every device-side flag wait, in nanoseconds (default 1 s).
+ * Process-wide; read at launch time.  0 restores the default. */
+void ar_set_poll_timeout_ns(uint64_t ns);
+uint64_t ar_get_poll_timeout_ns(void);
+
+/* Short English name of a status code (static storage). */
+const char* ar_status_string(int status);
+
+/* One-shot all-reduce, one GPU's share ([CAR] 实现 steps 1-5; [NCCL] 算法,
+ * one-shot): out[k] = round(sum over i = 0..n-1 of in[i][k]) for k < numel.
+ *  in    : host array of n device pointers, each numel elements of dtype.
+ *  out   : device buffer of numel elements; must not overlap any in[i].
+ * Reads n*S bytes and writes S bytes (S = numel * element size).  Any numel
+ * >= 1 is accepted; a partial last vector is handled element by element and
+ * no byte past numel is read or written.
+ * Errors: AR_ERR_ARG, AR_ERR_ALIGN, AR_ERR_ALIAS, AR_ERR_HIP. */
+int ar_oneshot(const void* const* in, int n, void* out, size_t numel, int dtype, void* stream);
+
+/* Two-shot phase 1, reduce-scatter ([NCCL] 算法, two-shot; [MGPU] 集合通信),
+ * optionally fused with the flag barrier and phase 2 in the same launch.
+ * With m = numel / n, emulated rank r in [r0, r1) sums segment r of every
+ * rank -- elements [r*m, (r+1)*m) -- into seg[r] (m elements, rounded once),
+ * then publishes step in its arrival slots of the flag region.
+ *  in    : n device pointers, numel elements each.
+ *  seg   : n device pointers, m elements each (only seg[r0..r1) written;
+ *          with out != NULL all n are read).
+ *  r0,r1 : 0 <= r0 < r1 <= n.  [0, n) emulates every rank with groups of
+ *          workgroups; [me, me+1) is one GPU's share.
+ *  flags : flag region of ar_flag_bytes(n) bytes, zeroed once by
+ *          ar_flag_barrier_reset before first use.
+ *  step  : step id, 1..2^32-1, increasing from call to call.
+ *  out   : NULL for reduce-scatter only.  Otherwise n device pointers
+ *          (entries outside [r0, r1) ignored); the launch becomes one
+ *          persistent cooperative grid that, after the reduce-scatter, waits
+ *          for every rank's slot >= step and copies seg[0..n) into out[r]
+ *          for r in [r0, r1) -- the same as calling ar_twoshot_ag next.
+ *          Segments of ranks outside [r0, r1) must have been published
+ *          already by earlier calls at this step or later.
+ * Requires numel % n == 0 and m * element size % 16 == 0 ([CAR] step 2:
+ * the two-shot kernel needs divisible sizes) -- else AR_ERR_DIVISIBLE.
+ * Errors: AR_ERR_ARG, AR_ERR_ALIGN, AR_ERR_DIVISIBLE, AR_ERR_ALIAS,
+ * AR_ERR_HIP; asynchronously AR_ERR_TIMEOUT (phase AR_PHASE_TWOSHOT_AG). */
+int ar_twoshot_rs(const void* const* in, int n, void* const* seg, size_t numel, int dtype,
+                  int r0, int r1, uint32_t* flags, uint32_t step, void* const* out, void* stream);
+
+/* Two-shot phase 2, all-gather ([NCCL] 算法, two-shot; [MGPU] 集合通信):
+ * for every rank r in [r0, r1), wait until each segment's arrival slots are
+ * >= step, then copy seg[0], ..., seg[n-1] in order into out[r] (a bit copy,
+ * no rounding).  Arguments as for ar_twoshot_rs; seg entries are read-only
+ * here.  Errors as ar_twoshot_rs. */
+int ar_twoshot_ag(const void* const* seg, int n, void* const* out, size_t numel, int dtype,
+                  int r0, int r1, uint32_t* flags, uint32_t step, void* stream);
+
+/* Sender side of LL / LL128 ([NCCL] 协议 table): pack count messages, each
+ * numel elements of dtype taken as bytes, into their wire buffers
+ * (ar_ll_wire_bytes(proto, numel * element size) bytes each).  Every line
+ * carries step as its flag (32-bit for LL, 64-bit for LL128), after its data.
+ * count >= 1 (1 = this GPU's own message; n = every emulated rank at once).
+ * Errors: AR_ERR_ARG, AR_ERR_ALIGN, AR_ERR_ALIAS, AR_ERR_HIP. */
+int ar_ll_pack(const void* const* src, void* const* wire, int count, size_t numel, int dtype,
+               int proto, uint32_t step, void* stream);
+
+/* Receiver side of LL ([NCCL] 协议 table): for every line of every rank's
+ * wire buffer wait until its flag is >= step, take the 4 data bytes out,
+ * and reduce the n messages exactly as ar_oneshot into out (numel elements).
+ *  flags : flag region (only the status words are used).
+ * Errors: AR_ERR_ARG, AR_ERR_ALIGN, AR_ERR_ALIAS, AR_ERR_HIP; asynchronously
+ * AR_ERR_TIMEOUT (phase AR_PHASE_LL, rank and line of a missing line). */
+int ar_ll_reduce_unpack(const void* const* wire, int n, void* out, size_t numel, int dtype,
+                        uint32_t step, uint32_t* flags, void* stream);
+
+/* Receiver side of LL128: as ar_ll_reduce_unpack with 128-byte lines holding
+ * 120 data bytes and a 64-bit flag.  Phase AR_PHASE_LL128 on timeout. */
+int ar_ll128_reduce_unpack(const void* const* wire, int n, void* out, size_t numel, int dtype,
+                           uint32_t step, uint32_t* flags, void* stream);
+
+/* Zero the whole flag region of ar_flag_bytes(n) bytes (status words and
+ * every arrival slot) with a fill kernel, so that steps may start again at
+ * 1: at set-up, after a timeout, and before step ids would wrap.
+ * Errors: AR_ERR_ARG, AR_ERR_ALIGN, AR_ERR_HIP. */
+int ar_flag_barrier_reset(uint32_t* flags, int n, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* AR_H */

@@ -1,0 +1,132 @@
+"""GPU parity of the LL and LL128 protocols (pack on the sender, poll +
+unpack + reduce on the receiver) against the CPU oracle, bit for bit."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from devtensors import bits, filled, first_mismatch, oracle_bits, to_dev
+
+pytestmark = pytest.mark.gpu
+
+car = pytest.importorskip("custom_all_reduce_amd")
+DT = {"f32": torch.float32, "bf16": torch.bfloat16}
+ES = {"f32": 4, "bf16": 2}
+
+
+def wires_for(n, numel, dt, proto):
+    W = car.ll_wire_bytes(proto, numel * ES[dt])
+    # wire buffers padded to 16 bytes plus a guard band of 256 bytes
+    bufs = [torch.full((W + 256,), 0xA5, dtype=torch.uint8, device="cuda") for _ in range(n)]
+    return bufs, W
+
+
+@pytest.mark.parametrize("proto", ["ll", "ll128"])
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("numel", [1, 2, 3, 5, 29, 30, 31, 59, 60, 61, 240, 1000, 4096 + 7, 65536 + 3])
+def test_pack_layout_matches_oracle(proto, dt, numel):
+    n = 2
+    host = synth.rank_inputs(n, numel, dt, "normal", config=90)
+    srcs = [to_dev(a) for a in host]
+    bufs, W = wires_for(n, numel, dt, proto)
+    car.ar_ll_pack(srcs, [b[:W] for b in bufs], proto, step=123457)
+    torch.cuda.synchronize()
+    for r in range(n):
+        got = bits(bufs[r])
+        want = oracle.ll_pack(proto, host[r], 123457)
+        assert np.array_equal(got[:W], want), first_mismatch(got[:W], want)
+        assert np.all(got[W:] == 0xA5), "pack wrote past the wire buffer"
+
+
+@pytest.mark.parametrize("proto", ["ll", "ll128"])
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("n", [2, 3, 8, 16])
+@pytest.mark.parametrize("numel", [1, 7, 61, 1023, 30 * 64 * 3 + 11, 100000 + 1])
+def test_reduce_matches_oracle(proto, dt, n, numel):
+    host = synth.rank_inputs(n, numel, dt, "normal", config=91 + n)
+    srcs = [to_dev(a) for a in host]
+    bufs, W = wires_for(n, numel, dt, proto)
+    wires = [b[:W] for b in bufs]
+    flags = car.new_flags(n)
+    outbuf = filled(numel + 64, DT[dt])
+    out = outbuf[:numel]
+    car.ar_ll_pack(srcs, wires, proto, step=9)
+    fn = car.ar_ll_reduce_unpack if proto == "ll" else car.ar_ll128_reduce_unpack
+    fn(wires, out, 9, flags)
+    torch.cuda.synchronize()
+    assert car.read_status(flags)[0] == 0
+    got = bits(out)
+    want = oracle_bits(oracle.ll_reduce(proto, [oracle.ll_pack(proto, a, 9) for a in host], numel, dt, 9))
+    assert np.array_equal(got, want), first_mismatch(got, want)
+    assert np.array_equal(want, oracle_bits(oracle.oneshot(host, dt)))
+    assert np.array_equal(bits(outbuf[numel:]), bits(filled(64, DT[dt]))), "wrote past the output"
+
+
+@pytest.mark.parametrize("proto", ["ll", "ll128"])
+@pytest.mark.parametrize("kib, steps", [(64, 1000), (1024, 100)])
+def test_steps_without_reset(proto, kib, steps):
+    """n = 8 ranks, fp32 payload of 64 KiB (steps 1..1000) or 1 MiB (steps
+    1..100) per rank; the data alternates between three sets so a receiver
+    that reused an old line would produce a wrong sum."""
+    n, dt = 8, "f32"
+    numel = kib * 1024 // 4
+    sets = [synth.rank_inputs(n, numel, dt, "normal", config=95 + k) for k in range(3)]
+    wants = [oracle_bits(oracle.oneshot(h, dt)) for h in sets]
+    dsets = [[to_dev(a) for a in h] for h in sets]
+    bufs, W = wires_for(n, numel, dt, proto)
+    wires = [b[:W] for b in bufs]
+    flags = car.new_flags(n)
+    outs = torch.empty((steps, numel), device="cuda")
+    fn = car.ar_ll_reduce_unpack if proto == "ll" else car.ar_ll128_reduce_unpack
+    for step in range(1, steps + 1):
+        car.ar_ll_pack(dsets[step % 3], wires, proto, step=step)
+        fn(wires, outs[step - 1], step, flags)
+    torch.cuda.synchronize()
+    assert car.read_status(flags)[0] == 0
+    got_all = outs.cpu().numpy().view(np.uint32)
+    for step in range(1, steps + 1):
+        got = got_all[step - 1]
+        assert np.array_equal(got, wants[step % 3]), f"step {step}: " + first_mismatch(got, wants[step % 3])
+
+
+@pytest.mark.parametrize("proto, phase", [("ll", 2), ("ll128", 3)])
+def test_stale_rank_times_out_and_names_it(proto, phase):
+    """Rank 5 packed step s-1; the receiver of step s must report (timeout,
+    phase, rank 5) after its tiny budget and exit normally."""
+    n, numel, dt = 8, 4096, "f32"
+    host = synth.rank_inputs(n, numel, dt, "normal", config=99)
+    srcs = [to_dev(a) for a in host]
+    bufs, W = wires_for(n, numel, dt, proto)
+    wires = [b[:W] for b in bufs]
+    flags = car.new_flags(n)
+    car.ar_ll_pack([s for i, s in enumerate(srcs) if i != 5], [w for i, w in enumerate(wires) if i != 5], proto,
+                   step=11)
+    car.ar_ll_pack([srcs[5]], [wires[5]], proto, step=10)
+    out = torch.empty(numel, device="cuda")
+    fn = car.ar_ll_reduce_unpack if proto == "ll" else car.ar_ll128_reduce_unpack
+    old = car.get_poll_timeout_ns()
+    car.set_poll_timeout_ns(20_000)
+    try:
+        fn(wires, out, 11, flags)
+        torch.cuda.synchronize()
+    finally:
+        car.set_poll_timeout_ns(old)
+    word, detail = car.read_status(flags)
+    code, ph, rank = car.decode_status(word)
+    assert (code, ph, rank) == (car.AR_ERR_TIMEOUT, phase, 5)
+    assert detail < (numel * 4 + 3) // 4
+    # the same wires at step 10 are ready for every rank (>= 10)
+    car.ar_flag_barrier_reset(flags, n)
+    fn(wires, out, 10, flags)
+    torch.cuda.synchronize()
+    assert car.read_status(flags)[0] == 0
+    assert np.array_equal(bits(out), oracle_bits(oracle.oneshot(host, dt)))
+
+
+def test_wire_sizes_for_the_64KiB_and_1MiB_messages():
+    for S in (64 * 1024, 1024 * 1024):
+        assert car.ll_wire_bytes("ll", S) == 2 * S
+        assert car.ll_wire_bytes("ll128", S) == oracle.ll_wire_bytes("ll128", S)
