@@ -158,30 +158,47 @@ def raise_on_status(flags: torch.Tensor, where: str = "kernel"):
 
 
 # ------------------------------------------------------------- entry points --
-def ar_oneshot(ins, out: torch.Tensor, stream=None):
-    """out = sum of ins (fp32 accumulation in rank order, one rounding)."""
+class Prepared:
+    """One entry point with its pointer tables already marshalled.
+
+    ``call(step=None, stream=None)`` enqueues it; only the step id and the
+    stream are filled in per call.  Holds references to the tensors so their
+    memory outlives the prepared call."""
+
+    __slots__ = ("fn", "args", "step_pos", "name", "keep")
+
+    def __init__(self, fn, args, step_pos, name, keep):
+        self.fn, self.args, self.step_pos, self.name, self.keep = fn, list(args), step_pos, name, keep
+
+    def __call__(self, step=None, stream=None):
+        args = self.args
+        if self.step_pos is not None:
+            if step is None:
+                raise ValueError(f"{self.name} needs a step id")
+            args[self.step_pos] = int(step)
+        args[-1] = _stream(stream)
+        code = self.fn(*args)
+        if code != AR_OK:
+            raise ArError(code, self.name)
+
+
+def prepare_oneshot(ins, out: torch.Tensor) -> Prepared:
     ins = [_dev_tensor(t, "input") for t in ins]
     out = _dev_tensor(out, "out")
     dt = _dtype_code(out)
     for t in ins:
         if t.dtype != out.dtype or t.numel() != out.numel():
             raise ValueError("inputs and output must share dtype and numel")
-    code = _lib.ar_oneshot(_ptr_array([t.data_ptr() for t in ins]), len(ins), out.data_ptr(), out.numel(), dt,
-                           _stream(stream))
-    _check(code, "ar_oneshot")
-    return out
+    args = [_ptr_array([t.data_ptr() for t in ins]), len(ins), out.data_ptr(), out.numel(), dt, None]
+    return Prepared(_lib.ar_oneshot, args, None, "ar_oneshot", (ins, out))
 
 
-def ar_twoshot_rs(ins, segs, flags, step: int, r0: int = 0, r1=None, outs=None, stream=None):
-    """Reduce-scatter for ranks [r0, r1); with ``outs`` also the barrier and
-    the all-gather in the same (cooperative) launch."""
+def prepare_twoshot_rs(ins, segs, flags, r0: int = 0, r1=None, outs=None) -> Prepared:
     n = len(ins)
     r1 = n if r1 is None else r1
     ins = [_dev_tensor(t, "input") for t in ins]
     segs = [_dev_tensor(t, "segment") for t in segs]
     flags = _dev_tensor(flags, "flags")
-    dt = _dtype_code(ins[0])
-    numel = ins[0].numel()
     if len(segs) != n:
         raise ValueError("need one segment buffer per rank")
     out_arr = None
@@ -189,52 +206,71 @@ def ar_twoshot_rs(ins, segs, flags, step: int, r0: int = 0, r1=None, outs=None, 
         if len(outs) != n:
             raise ValueError("outs must hold n entries (None outside [r0, r1))")
         out_arr = _ptr_array([(_dev_tensor(o, "out").data_ptr() if o is not None else 0) for o in outs])
-    code = _lib.ar_twoshot_rs(_ptr_array([t.data_ptr() for t in ins]), n, _ptr_array([t.data_ptr() for t in segs]),
-                              numel, dt, r0, r1, flags.data_ptr(), int(step), out_arr, _stream(stream))
-    _check(code, "ar_twoshot_rs")
+    args = [_ptr_array([t.data_ptr() for t in ins]), n, _ptr_array([t.data_ptr() for t in segs]), ins[0].numel(),
+            _dtype_code(ins[0]), r0, r1, flags.data_ptr(), 0, out_arr, None]
+    return Prepared(_lib.ar_twoshot_rs, args, 8, "ar_twoshot_rs", (ins, segs, flags, outs))
 
 
-def ar_twoshot_ag(segs, outs, flags, step: int, r0: int = 0, r1=None, numel=None, stream=None):
-    """All-gather for ranks [r0, r1) after waiting on every segment's slots."""
+def prepare_twoshot_ag(segs, outs, flags, r0: int = 0, r1=None, numel=None) -> Prepared:
     n = len(segs)
     r1 = n if r1 is None else r1
     segs = [_dev_tensor(t, "segment") for t in segs]
     flags = _dev_tensor(flags, "flags")
-    dt = _dtype_code(segs[0])
     numel = segs[0].numel() * n if numel is None else numel
     out_arr = _ptr_array([(_dev_tensor(o, "out").data_ptr() if o is not None else 0) for o in outs])
-    code = _lib.ar_twoshot_ag(_ptr_array([t.data_ptr() for t in segs]), n, out_arr, numel, dt, r0, r1,
-                              flags.data_ptr(), int(step), _stream(stream))
-    _check(code, "ar_twoshot_ag")
+    args = [_ptr_array([t.data_ptr() for t in segs]), n, out_arr, numel, _dtype_code(segs[0]), r0, r1,
+            flags.data_ptr(), 0, None]
+    return Prepared(_lib.ar_twoshot_ag, args, 8, "ar_twoshot_ag", (segs, outs, flags))
+
+
+def prepare_ll_pack(srcs, wires, proto) -> Prepared:
+    srcs = [_dev_tensor(t, "src") for t in srcs]
+    wires = [_dev_tensor(t, "wire") for t in wires]
+    args = [_ptr_array([t.data_ptr() for t in srcs]), _ptr_array([t.data_ptr() for t in wires]), len(srcs),
+            srcs[0].numel(), _dtype_code(srcs[0]), _PROTOS[proto], 0, None]
+    return Prepared(_lib.ar_ll_pack, args, 6, "ar_ll_pack", (srcs, wires))
+
+
+def prepare_ll_reduce(wires, out, flags, proto) -> Prepared:
+    wires = [_dev_tensor(t, "wire") for t in wires]
+    out = _dev_tensor(out, "out")
+    flags = _dev_tensor(flags, "flags")
+    fn, name = ((_lib.ar_ll_reduce_unpack, "ar_ll_reduce_unpack") if _PROTOS[proto] == AR_PROTO_LL
+                else (_lib.ar_ll128_reduce_unpack, "ar_ll128_reduce_unpack"))
+    args = [_ptr_array([t.data_ptr() for t in wires]), len(wires), out.data_ptr(), out.numel(), _dtype_code(out), 0,
+            flags.data_ptr(), None]
+    return Prepared(fn, args, 5, name, (wires, out, flags))
+
+
+def ar_oneshot(ins, out: torch.Tensor, stream=None):
+    """out = sum of ins (fp32 accumulation in rank order, one rounding)."""
+    prepare_oneshot(ins, out)(stream=stream)
+    return out
+
+
+def ar_twoshot_rs(ins, segs, flags, step: int, r0: int = 0, r1=None, outs=None, stream=None):
+    """Reduce-scatter for ranks [r0, r1); with ``outs`` also the barrier and
+    the all-gather in the same persistent launch."""
+    prepare_twoshot_rs(ins, segs, flags, r0, r1, outs)(step, stream)
+
+
+def ar_twoshot_ag(segs, outs, flags, step: int, r0: int = 0, r1=None, numel=None, stream=None):
+    """All-gather for ranks [r0, r1) after waiting on every segment's slots."""
+    prepare_twoshot_ag(segs, outs, flags, r0, r1, numel)(step, stream)
 
 
 def ar_ll_pack(srcs, wires, proto, step: int, stream=None):
     """Pack every message of ``srcs`` into its wire buffer (uint8 tensors)."""
-    srcs = [_dev_tensor(t, "src") for t in srcs]
-    wires = [_dev_tensor(t, "wire") for t in wires]
-    dt = _dtype_code(srcs[0])
-    code = _lib.ar_ll_pack(_ptr_array([t.data_ptr() for t in srcs]), _ptr_array([t.data_ptr() for t in wires]),
-                           len(srcs), srcs[0].numel(), dt, _PROTOS[proto], int(step), _stream(stream))
-    _check(code, "ar_ll_pack")
+    prepare_ll_pack(srcs, wires, proto)(step, stream)
 
 
 def ar_ll_reduce_unpack(wires, out, step: int, flags, stream=None):
-    wires = [_dev_tensor(t, "wire") for t in wires]
-    out = _dev_tensor(out, "out")
-    flags = _dev_tensor(flags, "flags")
-    code = _lib.ar_ll_reduce_unpack(_ptr_array([t.data_ptr() for t in wires]), len(wires), out.data_ptr(),
-                                    out.numel(), _dtype_code(out), int(step), flags.data_ptr(), _stream(stream))
-    _check(code, "ar_ll_reduce_unpack")
+    prepare_ll_reduce(wires, out, flags, "ll")(step, stream)
     return out
 
 
 def ar_ll128_reduce_unpack(wires, out, step: int, flags, stream=None):
-    wires = [_dev_tensor(t, "wire") for t in wires]
-    out = _dev_tensor(out, "out")
-    flags = _dev_tensor(flags, "flags")
-    code = _lib.ar_ll128_reduce_unpack(_ptr_array([t.data_ptr() for t in wires]), len(wires), out.data_ptr(),
-                                       out.numel(), _dtype_code(out), int(step), flags.data_ptr(), _stream(stream))
-    _check(code, "ar_ll128_reduce_unpack")
+    prepare_ll_reduce(wires, out, flags, "ll128")(step, stream)
     return out
 
 

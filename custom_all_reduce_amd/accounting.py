@@ -5,12 +5,16 @@ allocations on that GPU: every read of a rank buffer, segment or wire buffer
 and every write, each byte once.  S = numel * element size (bytes per rank).
 
   oneshot                 reads n*S               writes S
-  twoshot, one rank       reads S (RS) + S (AG)   writes S/n (segment) + S (output)
-  twoshot, all n ranks    reads 2*n*S             writes S (segments) + n*S (outputs)
+  twoshot, one rank       reads S (RS) + (n-1)*S/n (AG of the peers' segments)
+                          writes S/n (segment) + S (output)
+  twoshot, all n ranks    n times the above
+  twoshot RS only / AG only, per rank: reads S / S, writes S/n / S
   LL / LL128 pack, each   reads S                 writes W(S)
   LL / LL128 reduce       reads n*W(S)            writes S
 
-W(S) = 8*ceil(S/4) for LL (4 data bytes per 8-byte line) and
+In the fused two-shot the reduce-scatter writes rank r's own segment of its
+output straight from registers, so the all-gather reads only the other n-1
+segments.  W(S) = 8*ceil(S/4) for LL (4 data bytes per 8-byte line) and
 128*ceil(S/120) for LL128 (120 data bytes per 128-byte line) -- the line
 formats of the protocol table on "集合通信：NCCL 的算法、协议与推理框架的定制
 all-reduce".  The flag region (a few KiB) is left out.
@@ -33,8 +37,8 @@ def oneshot(n: int, S: int):
 
 
 def twoshot(n: int, S: int, ranks: int):
-    """ranks = how many emulated ranks the launch computes (1 or n)."""
-    return 2 * ranks * S, ranks * (S // n) + ranks * S
+    """Fused two-shot; ranks = how many emulated ranks the launch computes (1 or n)."""
+    return ranks * (S + (n - 1) * (S // n)), ranks * (S // n) + ranks * S
 
 
 def twoshot_rs(n: int, S: int, ranks: int):

@@ -7,7 +7,7 @@
 #include <mutex>
 #include <vector>
 
-#include "../../include/ar.h"
+#include "ar.h"
 #include "ar_launch.hpp"
 
 namespace ar {

@@ -7,8 +7,8 @@
 // LL128 line: 128 bytes = 120 data bytes, then a 64-bit flag.
 // Data bytes past the message in the last line are zero.
 //
-// LL receiver: a lane owns 32 wire bytes of every rank (4 lines, two 16-byte
-// loads per rank) and produces 16 output bytes with one 16-byte store.
+// LL receiver: a lane owns 16 wire bytes of every rank (2 lines, one 16-byte
+// load per rank) and produces 8 output bytes.
 // LL128 receiver: a wavefront owns 1 KiB of wire per rank = 8 lines; lane l
 // holds 16 bytes at part l % 8 of line l / 8, and the lane at part 7 holds 8
 // data bytes plus the flag.  Readiness of the whole wavefront is one ballot.
@@ -31,25 +31,38 @@ struct PackParams {
     uint32_t step;
 };
 
-// LL pack: lane c takes message bytes [16c, 16c+16) and writes 2 x 16 wire
-// bytes = 4 lines.  blockIdx.y selects the message.  The lane whose 16 bytes
-// run past the end reads byte by byte and zero-fills.
+// LL pack: lane c takes message bytes [8c, 8c+8) and writes the 16 wire
+// bytes of lines 2c and 2c+1, so each load instruction of a wavefront reads
+// 512 contiguous bytes and each store writes 1 KiB of whole lines.  A lane
+// handles kPackUnroll chunks kBlock apart.  blockIdx.y selects the message.
+// The lane whose chunk runs past the end reads byte by byte, zero-fills,
+// and writes only the lines that exist.
+constexpr int kPackUnroll = 4;
+
 __global__ __launch_bounds__(kBlock) void ll_pack_kernel(PackParams p) {
     const uint8_t* src = p.src[blockIdx.y];
     u32x4* wire = reinterpret_cast<u32x4*>(p.wire[blockIdx.y]);
-    const size_t c = size_t(blockIdx.x) * kBlock + threadIdx.x;
-    const size_t full = p.nbytes / 16;
-    const size_t words = (p.nbytes + 3) / 4;  // = lines
-    if (c < full) {
-        const u32x4 v = ld_stream(reinterpret_cast<const u32x4*>(src) + c);
-        st_stream(wire + 2 * c, u32x4{v.x, p.step, v.y, p.step});
-        st_stream(wire + 2 * c + 1, u32x4{v.z, p.step, v.w, p.step});
-    } else if (c * 4 < words) {
-        // last, partial chunk: lines 4c .. words-1, one 8-byte line at a time
-        uint32_t w[4] = {0u, 0u, 0u, 0u};
-        for (size_t b = 16 * c; b < p.nbytes; ++b) w[(b >> 2) & 3] |= uint32_t(src[b]) << (8 * (b & 3));
-        u32x2* lines = reinterpret_cast<u32x2*>(p.wire[blockIdx.y]);
-        for (size_t l = 4 * c; l < words; ++l) lines[l] = u32x2{w[l - 4 * c], p.step};
+    const size_t full = p.nbytes / 8;          // whole 8-byte chunks
+    const size_t lines = (p.nbytes + 3) / 4;   // = words
+    const size_t c0 = size_t(blockIdx.x) * (kBlock * kPackUnroll) + threadIdx.x;
+    u32x2 v[kPackUnroll];
+#pragma unroll
+    for (int u = 0; u < kPackUnroll; ++u) {
+        const size_t c = c0 + size_t(u) * kBlock;
+        if (c < full) v[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(src) + c);
+    }
+#pragma unroll
+    for (int u = 0; u < kPackUnroll; ++u) {
+        const size_t c = c0 + size_t(u) * kBlock;
+        if (c < full) {
+            st_stream(wire + c, u32x4{v[u].x, p.step, v[u].y, p.step});
+        } else if (2 * c < lines) {
+            uint32_t w[2] = {0u, 0u};
+            for (size_t b = 8 * c; b < p.nbytes; ++b) w[(b >> 2) & 1] |= uint32_t(src[b]) << (8 * (b & 3));
+            u32x2* ln = reinterpret_cast<u32x2*>(p.wire[blockIdx.y]);
+            ln[2 * c] = u32x2{w[0], p.step};
+            if (2 * c + 1 < lines) ln[2 * c + 1] = u32x2{w[1], p.step};
+        }
     }
 }
 
@@ -91,12 +104,36 @@ struct ReduceParams {
     uint32_t step;
 };
 
-// Wait (bounded) until every LL line of this lane's chunk is ready in every
-// rank; reloads with agent-coherent atomic 64-bit loads.  Returns false on
-// timeout (after reporting it).
+// LL receiver.  Lane chunk c = lines 2c and 2c+1 of every rank (one 16-byte
+// load per rank; a wavefront's load instruction reads 1 KiB of whole lines)
+// and output bytes [8c, 8c+8) (one 8-byte store).  A lane handles U chunks
+// kBlock apart, so U * n loads are in flight before the first add.
+template <typename T> struct HalfAcc;  // accumulator for 8 data bytes
+template <> struct HalfAcc<float> {
+    float a[2] = {0.0f, 0.0f};
+    __device__ __forceinline__ void add(uint32_t w0, uint32_t w1) {
+        a[0] = a[0] + __uint_as_float(w0);
+        a[1] = a[1] + __uint_as_float(w1);
+    }
+    __device__ __forceinline__ u32x2 result() const { return u32x2{__float_as_uint(a[0]), __float_as_uint(a[1])}; }
+};
+template <> struct HalfAcc<bf16_t> {
+    float a[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    __device__ __forceinline__ void add(uint32_t w0, uint32_t w1) {
+        a[0] = a[0] + bf16_lo(w0); a[1] = a[1] + bf16_hi(w0);
+        a[2] = a[2] + bf16_lo(w1); a[3] = a[3] + bf16_hi(w1);
+    }
+    __device__ __forceinline__ u32x2 result() const {
+        return u32x2{pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3])};
+    }
+};
+
+// Bounded wait for the lines [2c, 2c + nl) of every rank (nl = 1 or 2), re-read
+// with agent-coherent atomic 64-bit loads into x (data in .x/.z, flags in
+// .y/.w).  Lanes with nl == 0 just take part in the ballots.  Returns false
+// on timeout (reported).
 template <int NR>
-__device__ bool ll_slow_wait(const ReduceParams& p, size_t line0, uint32_t nl, uint64_t (&ln)[NR][4],
-                             int lane) {
+__device__ bool ll_slow_wait(const ReduceParams& p, size_t c, uint32_t nl, u32x4 (&x)[NR], int lane) {
     const uint64_t t0 = now_ticks();
     while (true) {
         bool ok = true;
@@ -104,79 +141,136 @@ __device__ bool ll_slow_wait(const ReduceParams& p, size_t line0, uint32_t nl, u
         uint32_t bad_l = 0;
 #pragma unroll
         for (int r = 0; r < NR; ++r) {
-            const uint64_t* w = reinterpret_cast<const uint64_t*>(p.wire[r]) + line0;
-#pragma unroll
-            for (uint32_t l = 0; l < 4; ++l) {
-                if (l < nl && uint32_t(ln[r][l] >> 32) < p.step) {
-                    ln[r][l] = line_load_relaxed(w + l);
-                    if (uint32_t(ln[r][l] >> 32) < p.step && ok) { ok = false; bad_r = r; bad_l = l; }
-                }
+            const uint64_t* w = reinterpret_cast<const uint64_t*>(p.wire[r]) + 2 * c;
+            if (nl > 0 && x[r].y < p.step) {
+                const uint64_t a = line_load_relaxed(w);
+                x[r].x = uint32_t(a);
+                x[r].y = uint32_t(a >> 32);
+                if (x[r].y < p.step && ok) { ok = false; bad_r = r; bad_l = 0; }
+            }
+            if (nl > 1 && x[r].w < p.step) {
+                const uint64_t b = line_load_relaxed(w + 1);
+                x[r].z = uint32_t(b);
+                x[r].w = uint32_t(b >> 32);
+                if (x[r].w < p.step && ok) { ok = false; bad_r = r; bad_l = 1; }
             }
         }
         const uint64_t missing = ~wave_ballot(ok) & wave_exec();
         if (missing == 0) return true;
         if (now_ticks() - t0 > p.timeout_ticks) {
             const int bl = __ffsll((unsigned long long)missing) - 1;
-            const int rr = __shfl(bad_r, bl);
-            const uint32_t ll = uint32_t(__shfl(uint32_t(line0 + bad_l), bl));
-            if (lane == bl) report_timeout(p.flags, 2u, uint32_t(rr), ll);
+            if (lane == bl) report_timeout(p.flags, 2u, uint32_t(bad_r), uint32_t(2 * c + bad_l));
             return false;
         }
         __builtin_amdgcn_s_sleep(1);
     }
 }
 
-template <typename T, int NR>
+template <typename T>
+__device__ __forceinline__ void store_out_bytes(uint8_t* out, size_t off, size_t nbytes, const uint32_t* words) {
+    for (size_t b = off; b < nbytes; b += elem<T>::bytes) {
+        const uint32_t word = words[(b - off) >> 2];
+        if (elem<T>::bytes == 4) *reinterpret_cast<uint32_t*>(out + b) = word;
+        else *reinterpret_cast<uint16_t*>(out + b) = uint16_t(word >> (8 * (b & 2)));
+    }
+}
+
+// LL receiver.  Lane chunk c = lines 2c and 2c+1 of every rank (one 16-byte
+// load per rank; a wavefront's load instruction reads 1 KiB of whole lines)
+// and output bytes [8c, 8c+8).  A lane handles U chunks kBlock apart.  The
+// main path is branch-free: lanes past the last two-line chunk load a valid
+// clamped chunk and discard it, so all U * n loads issue back to back.  A
+// final single line (odd line count) is finished by one lane on its own.
+template <typename T, int NR, int U>
 __global__ __launch_bounds__(kBlock) void ll_reduce_kernel(ReduceParams p) {
     const int lane = threadIdx.x & (kWave - 1);
-    const size_t c = size_t(blockIdx.x) * kBlock + threadIdx.x;  // 16-byte output chunk
-    const size_t line0 = 4 * c;
-    const bool active = line0 < p.nlines;
-    const uint32_t nl = active ? uint32_t(min(size_t(4), p.nlines - line0)) : 0u;
-    uint64_t ln[NR][4];
-    if (nl == 4) {
+    const size_t nfull = p.nlines / 2;  // chunks that hold two lines
+    const size_t c0 = size_t(blockIdx.x) * (kBlock * U) + threadIdx.x;
+    const u32x4* w[NR];
 #pragma unroll
-        for (int r = 0; r < NR; ++r) {
-            const u32x4* w = reinterpret_cast<const u32x4*>(p.wire[r]) + 2 * c;
-            const u32x4 a = ld_stream(w), b = ld_stream(w + 1);
-            ln[r][0] = uint64_t(a.x) | (uint64_t(a.y) << 32);
-            ln[r][1] = uint64_t(a.z) | (uint64_t(a.w) << 32);
-            ln[r][2] = uint64_t(b.x) | (uint64_t(b.y) << 32);
-            ln[r][3] = uint64_t(b.z) | (uint64_t(b.w) << 32);
+    for (int r = 0; r < NR; ++r) w[r] = reinterpret_cast<const u32x4*>(p.wire[r]);
+
+    if (nfull > 0) {
+        u32x4 x[U][NR];
+        bool act[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const size_t c = c0 + size_t(u) * kBlock;
+            act[u] = c < nfull;
+            const size_t cc = act[u] ? c : nfull - 1;
+#pragma unroll
+            for (int r = 0; r < NR; ++r) x[u][r] = ld_stream(w[r] + cc);
         }
-    } else {
+        bool ok = true;
 #pragma unroll
-        for (int r = 0; r < NR; ++r) {
-            const uint64_t* w = reinterpret_cast<const uint64_t*>(p.wire[r]) + line0;
+        for (int u = 0; u < U; ++u)
 #pragma unroll
-            for (int l = 0; l < 4; ++l) ln[r][l] = uint64_t(l < int(nl) ? w[l] : ~0ull);
+            for (int r = 0; r < NR; ++r) ok = ok && (!act[u] || (x[u][r].y >= p.step && x[u][r].w >= p.step));
+        if (wave_ballot(!ok) != 0) {
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                if (!ll_slow_wait<NR>(p, c0 + size_t(u) * kBlock, act[u] ? 2u : 0u, x[u], lane)) return;
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const size_t c = c0 + size_t(u) * kBlock;
+            HalfAcc<T> acc;
+#pragma unroll
+            for (int r = 0; r < NR; ++r) acc.add(x[u][r].x, x[u][r].z);
+            const u32x2 res = acc.result();
+            if (act[u]) {
+                if (8 * c + 8 <= p.nbytes) {
+                    __builtin_nontemporal_store(res, reinterpret_cast<u32x2*>(p.out) + c);
+                } else {
+                    const uint32_t rw[2] = {res.x, res.y};
+                    store_out_bytes<T>(p.out, 8 * c, p.nbytes, rw);
+                }
+            }
         }
     }
-    bool ok = true;
+    // A last chunk with a single line (odd line count): chunk nfull, finished
+    // by the one lane of the grid that owns that chunk index.
+    const size_t rel = nfull - size_t(blockIdx.x) * (kBlock * U);
+    if ((p.nlines & 1) && nfull >= size_t(blockIdx.x) * (kBlock * U) && rel < size_t(kBlock) * U &&
+        rel % kBlock == threadIdx.x) {
+        u32x4 x[NR];
 #pragma unroll
-    for (int r = 0; r < NR; ++r)
-#pragma unroll
-        for (int l = 0; l < 4; ++l) ok = ok && (l >= int(nl) || uint32_t(ln[r][l] >> 32) >= p.step);
-    if (wave_ballot(!ok) != 0) {
-        if (!ll_slow_wait<NR>(p, line0, nl, ln, lane)) return;
-    }
-    if (!active) return;
-    Acc<T> acc;
-#pragma unroll
-    for (int r = 0; r < NR; ++r)
-        acc.add(u32x4{uint32_t(ln[r][0]), uint32_t(ln[r][1]), uint32_t(ln[r][2]), uint32_t(ln[r][3])});
-    const u32x4 res = acc.result();
-    const size_t off = 16 * c;
-    if (off + 16 <= p.nbytes) {
-        st_stream(reinterpret_cast<u32x4*>(p.out) + c, res);
-    } else {
-        // partial chunk at the end: write only the message's bytes
-        const uint32_t rw[4] = {res.x, res.y, res.z, res.w};
-        for (size_t b = off; b < p.nbytes; b += elem<T>::bytes) {
-            const uint32_t word = rw[(b - off) >> 2];
-            if (elem<T>::bytes == 4) *reinterpret_cast<uint32_t*>(p.out + b) = word;
-            else *reinterpret_cast<uint16_t*>(p.out + b) = uint16_t(word >> (8 * (b & 2)));
+        for (int r = 0; r < NR; ++r) {
+            const u32x2 a = reinterpret_cast<const u32x2*>(p.wire[r])[2 * nfull];
+            x[r] = u32x4{a.x, a.y, 0u, 0xFFFFFFFFu};
         }
+        bool ok = true;
+#pragma unroll
+        for (int r = 0; r < NR; ++r) ok = ok && x[r].y >= p.step;
+        if (!ok) {
+            // single lane: poll alone (its own wave's ballot sees only it)
+            const uint64_t t0 = now_ticks();
+            while (!ok) {
+                ok = true;
+                int bad_r = 0;
+#pragma unroll
+                for (int r = 0; r < NR; ++r) {
+                    if (x[r].y < p.step) {
+                        const uint64_t a =
+                            line_load_relaxed(reinterpret_cast<const uint64_t*>(p.wire[r]) + 2 * nfull);
+                        x[r].x = uint32_t(a);
+                        x[r].y = uint32_t(a >> 32);
+                        if (x[r].y < p.step && ok) { ok = false; bad_r = r; }
+                    }
+                }
+                if (!ok && now_ticks() - t0 > p.timeout_ticks) {
+                    report_timeout(p.flags, 2u, uint32_t(bad_r), uint32_t(2 * nfull));
+                    return;
+                }
+                if (!ok) __builtin_amdgcn_s_sleep(1);
+            }
+        }
+        HalfAcc<T> acc;
+#pragma unroll
+        for (int r = 0; r < NR; ++r) acc.add(x[r].x, 0u);
+        const u32x2 res = acc.result();
+        const uint32_t rw[2] = {res.x, res.y};
+        store_out_bytes<T>(p.out, 8 * nfull, p.nbytes, rw);
     }
 }
 
@@ -184,19 +278,22 @@ template <typename T, int NR, int U>
 __global__ __launch_bounds__(kBlock) void ll128_reduce_kernel(ReduceParams p) {
     const int lane = threadIdx.x & (kWave - 1);
     const uint32_t part = uint32_t(lane) & 7u;
-    const size_t wave = size_t(blockIdx.x) * kWavesPerBlock + threadIdx.x / kWave;
+    const size_t wave = __builtin_amdgcn_readfirstlane(blockIdx.x * kWavesPerBlock + threadIdx.x / kWave);
     u32x4 x[U][NR];
     size_t line[U];
     bool valid[U];
+    const u32x4* w[NR];
+#pragma unroll
+    for (int r = 0; r < NR; ++r) w[r] = reinterpret_cast<const u32x4*>(p.wire[r]);
+    // Branch-free loads: lines past the end read the last line instead and
+    // are discarded.
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         line[u] = (wave * U + u) * 8 + size_t(lane) / 8;
         valid[u] = line[u] < p.nlines;
-        if (valid[u]) {
+        const size_t ll = valid[u] ? line[u] : p.nlines - 1;
 #pragma unroll
-            for (int r = 0; r < NR; ++r)
-                x[u][r] = ld_stream(reinterpret_cast<const u32x4*>(p.wire[r]) + line[u] * 8 + part);
-        }
+        for (int r = 0; r < NR; ++r) x[u][r] = ld_stream(w[r] + ll * 8 + part);
     }
     bool ok = true;
 #pragma unroll
@@ -242,9 +339,15 @@ __global__ __launch_bounds__(kBlock) void ll128_reduce_kernel(ReduceParams p) {
                 for (int r = 0; r < NR; ++r)
                     x[u][r] = ld_plain(reinterpret_cast<const u32x4*>(p.wire[r]) + line[u] * 8 + part);
     }
+    // Reduce, then repack through LDS: the 8 lines of a wavefront unit hold
+    // 960 contiguous output bytes (16-byte aligned, as 960 = 60 * 16), but a
+    // lane's piece starts at 120 * line + 16 * part, only 8-byte aligned.
+    // Write the pieces to a wavefront-private LDS strip, then let lanes 0..59
+    // store 16 aligned bytes each.
+    __shared__ __attribute__((aligned(16))) uint8_t strip[kWavesPerBlock][U][960];
+    uint8_t* my = &strip[threadIdx.x / kWave][0][0];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-        if (!valid[u]) continue;
         Acc<T> acc;
         if (part != 7u) {
 #pragma unroll
@@ -254,18 +357,27 @@ __global__ __launch_bounds__(kBlock) void ll128_reduce_kernel(ReduceParams p) {
             for (int r = 0; r < NR; ++r) acc.add_half(x[u][r]);
         }
         const u32x4 res = acc.result();
-        const size_t off = line[u] * 120 + size_t(part) * 16;
-        const uint32_t nb = part == 7u ? 8u : 16u;
-        if (off + nb <= p.nbytes) {
-            u32x2* d = reinterpret_cast<u32x2*>(p.out + off);  // 8-byte aligned
-            d[0] = u32x2{res.x, res.y};
-            if (nb == 16u) d[1] = u32x2{res.z, res.w};
-        } else if (off < p.nbytes) {
-            const uint32_t rw[4] = {res.x, res.y, res.z, res.w};
-            for (size_t b = off; b < p.nbytes; b += elem<T>::bytes) {
-                const uint32_t word = rw[(b - off) >> 2];
-                if (elem<T>::bytes == 4) *reinterpret_cast<uint32_t*>(p.out + b) = word;
-                else *reinterpret_cast<uint16_t*>(p.out + b) = uint16_t(word >> (8 * (b & 2)));
+        u32x2* d = reinterpret_cast<u32x2*>(my + u * 960 + (lane / 8) * 120 + part * 16);
+        d[0] = u32x2{res.x, res.y};
+        if (part != 7u) d[1] = u32x2{res.z, res.w};
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    if (lane < 60) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const size_t off = (wave * U + u) * 960 + size_t(lane) * 16;
+            const u32x4 v = *reinterpret_cast<const u32x4*>(my + u * 960 + lane * 16);
+            if (off + 16 <= p.nbytes) {
+                st_stream(reinterpret_cast<u32x4*>(p.out + off), v);
+            } else if (off < p.nbytes) {
+                const uint32_t rw[4] = {v.x, v.y, v.z, v.w};
+                for (size_t b = off; b < p.nbytes; b += elem<T>::bytes) {
+                    const uint32_t word = rw[(b - off) >> 2];
+                    if (elem<T>::bytes == 4) *reinterpret_cast<uint32_t*>(p.out + b) = word;
+                    else *reinterpret_cast<uint16_t*>(p.out + b) = uint16_t(word >> (8 * (b & 2)));
+                }
             }
         }
     }
@@ -274,9 +386,10 @@ __global__ __launch_bounds__(kBlock) void ll128_reduce_kernel(ReduceParams p) {
 template <typename T, int NR>
 hipError_t launch_reduce_t(const ReduceParams& p, int proto, hipStream_t s) {
     if (proto == 0) {
-        const size_t chunks = (p.nlines + 3) / 4;
-        const size_t grid = (chunks + kBlock - 1) / kBlock;
-        hipLaunchKernelGGL((ll_reduce_kernel<T, NR>), dim3(uint32_t(grid)), dim3(kBlock), 0, s, p);
+        constexpr int U = NR <= 8 ? 2 : 1;
+        const size_t chunks = (p.nlines + 1) / 2;
+        const size_t grid = (chunks + kBlock * U - 1) / (kBlock * U);
+        hipLaunchKernelGGL((ll_reduce_kernel<T, NR, U>), dim3(uint32_t(grid)), dim3(kBlock), 0, s, p);
     } else {
         constexpr int U = NR <= 8 ? 2 : 1;
         const size_t wave_units = (p.nlines + 7) / 8;
@@ -299,8 +412,8 @@ hipError_t launch_ll_pack(const void* const* src, void* const* wire, int count, 
     p.nbytes = nbytes;
     p.step = step;
     if (proto == 0) {
-        const size_t chunks = (nbytes + 15) / 16;
-        const size_t grid = (chunks + kBlock - 1) / kBlock;
+        const size_t chunks = (nbytes + 7) / 8;
+        const size_t grid = (chunks + kBlock * kPackUnroll - 1) / (kBlock * kPackUnroll);
         hipLaunchKernelGGL(ll_pack_kernel, dim3(uint32_t(grid), uint32_t(count)), dim3(kBlock), 0, s, p);
     } else {
         const size_t nlines = (nbytes + 119) / 120;

@@ -8,23 +8,31 @@
 // is cut into ktiles tiles of `tile` vectors (a multiple of 64; only a
 // segment's last tile may be shorter).  The tiling depends on mvec only, so
 // launches with different grids or rank ranges agree on it.
-//   phase 1 item (r, t): sum tile t of segment r over every rank -> seg[r]
-//   phase 2 item (ro, j, t): copy tile t of seg[j] into out[ro] at j*mvec
+//   phase 1 item (r, t): sum tile t of segment r over every rank -> seg[r];
+//                        in the fused form also -> out[r] at r*mvec (rank r's
+//                        own segment of its all-gather, from registers)
+//   phase 2 item (ro, j, t): copy tile t of seg[j] into out[ro] at j*mvec, for
+//                        every j (split form) or every j != ro (fused form)
 // Items are dealt to wavefronts round-robin; a wavefront walks its items as a
 // flat list of 64-vector units (one vector per lane) and keeps U units of
 // loads in flight before it adds or stores.
 //
-// Barrier.  Each tile (r, t) has a 32-bit arrival slot.  After its last
-// phase-1 store a wavefront issues one agent-scope release fence (writes back
-// its XCD's L2) and then stores `step` into the slot of every tile it
-// produced.  In phase 2 a wavefront polls the slots of all its items, one
-// slot per lane, until a ballot shows every lane sees slot >= step, then
-// issues one agent-scope acquire fence (invalidates stale L2 lines) and
-// copies.  Waits are bounded by a wall-clock budget; on expiry the first
+// Barrier.  Each tile (r, t) has a 32-bit arrival slot.  Segments are
+// written and read with device-coherent (sc1) accesses, so after its last
+// phase-1 store a wavefront only waits for its stores to complete and then
+// stores `step` into the slot of every tile it produced.  In phase 2 a
+// wavefront polls the slots of all its items, one slot per lane, until a
+// ballot shows every lane sees slot >= step, then copies.  (An agent-scope
+// release/acquire fence pair per wavefront would write back and invalidate
+// a whole XCD L2 each time; measured, that costs several times the copy.)  Waits are bounded by a wall-clock budget; on expiry the first
 // missing (rank, tile) goes to the status words and the wavefront skips its
-// copies.  In the fused form the whole grid is co-resident (cooperative
-// launch) and every wavefront finishes phase 1 before it polls, so every
-// slot a poller needs is eventually written.
+// copies.  In the fused form the grid is no larger than what the device
+// holds at once (occupancy-checked, persistent), and every wavefront finishes
+// phase 1 before it polls, so every slot a poller needs is eventually written
+// while nothing else occupies the CUs; if something does, the bounded wait
+// turns the stall into a reported timeout instead of a hang.
+#include <mutex>
+
 #include "ar_device.hpp"
 #include "ar_launch.hpp"
 
@@ -58,41 +66,52 @@ __device__ __forceinline__ void reduce_scatter_phase(const TwoShotParams& p, uin
     const uint32_t my_items = (items - wave + nwaves - 1) / nwaves;
     const uint32_t upt = p.tile / kWave;
     const uint32_t my_units = my_items * upt;
+    const u32x4* in[NR];
+#pragma unroll
+    for (int i = 0; i < NR; ++i) in[i] = p.in[i];
     for (uint32_t q0 = 0; q0 < my_units; q0 += U) {
+        // Unit q = 64 consecutive vectors of one tile.  wave, q0 and hence the
+        // tile and rank of every unit are wavefront-uniform (scalar); only the
+        // vector index carries the lane.  Units past the end re-read unit q0's
+        // tile start and are discarded, so the U * NR loads issue unbroken.
         u32x4 x[U][NR];
         uint32_t dst_idx[U];
-        int dst_rank[U];
+        uint32_t dst_rank[U];
         bool valid[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const uint32_t q = q0 + u;
+            const bool unit_ok = q0 + u < my_units;
+            const uint32_t q = unit_ok ? q0 + u : q0;
             const uint32_t k = q / upt, sub = q - k * upt;
             const uint32_t it = wave + k * nwaves;
             const uint32_t r = uint32_t(p.r0) + it / p.ktiles;
-            const uint32_t t = it % p.ktiles;
+            const uint32_t t = it - (it / p.ktiles) * p.ktiles;
             const uint32_t idx = t * p.tile + sub * kWave + uint32_t(lane);
-            valid[u] = (q < my_units) && (idx < p.mvec);
+            valid[u] = unit_ok && idx < p.mvec;
             dst_idx[u] = idx;
-            dst_rank[u] = int(r);
-            if (valid[u]) {
-                const size_t src = size_t(r) * p.mvec + idx;
+            dst_rank[u] = r;
+            const size_t src = size_t(r) * p.mvec + (valid[u] ? idx : t * p.tile);
 #pragma unroll
-                for (int i = 0; i < NR; ++i) x[u][i] = ld_stream(p.in[i] + src);
-            }
+            for (int i = 0; i < NR; ++i) x[u][i] = ld_stream(in[i] + src);
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            if (valid[u]) {
-                Acc<T> acc;
+            Acc<T> acc;
 #pragma unroll
-                for (int i = 0; i < NR; ++i) acc.add(x[u][i]);
-                st_stream(p.seg[dst_rank[u]] + dst_idx[u], acc.result());
+            for (int i = 0; i < NR; ++i) acc.add(x[u][i]);
+            const u32x4 v = acc.result();
+            if (valid[u]) {
+                st_coherent(p.seg[dst_rank[u]] + dst_idx[u], v);
+                // fused form: rank r's own segment of its output comes straight
+                // from registers (the all-gather copy of seg[r] into out[r])
+                if (p.do_ag) st_stream(p.out[dst_rank[u]] + size_t(dst_rank[u]) * p.mvec + dst_idx[u], v);
             }
         }
     }
-    // Publish: one release for everything this wavefront stored, then one
-    // slot store per produced tile (lane k stores the slot of item k).
-    fence_release_agent();
+    // Publish: wait until this wavefront's coherent segment stores have
+    // completed, then one slot store per produced tile (lane k stores the
+    // slot of item k).
+    wait_stores();
     __builtin_amdgcn_wave_barrier();
     uint32_t* slots = p.flags + kStatusWords;
     for (uint32_t k = uint32_t(lane); k < my_items; k += kWave) {
@@ -103,10 +122,18 @@ __device__ __forceinline__ void reduce_scatter_phase(const TwoShotParams& p, uin
     }
 }
 
+// Source segment of the jj-th all-gather copy into out[ro]: every segment in
+// order, or, when the reduce-scatter of the same launch already wrote out[ro]'s
+// own segment, every segment but ro's.
+__device__ __forceinline__ uint32_t ag_source(uint32_t jj, uint32_t ro, bool skip_own) {
+    return (skip_own && jj >= ro) ? jj + 1 : jj;
+}
+
 __device__ __forceinline__ void all_gather_phase(const TwoShotParams& p, int n, uint32_t wave,
                                                  uint32_t nwaves, int lane) {
     const uint32_t R = uint32_t(p.r1 - p.r0);
-    const uint32_t per_out = uint32_t(n) * p.ktiles;
+    const bool skip_own = p.do_rs != 0;
+    const uint32_t per_out = uint32_t(skip_own ? n - 1 : n) * p.ktiles;
     const uint32_t items = R * per_out;
     if (wave >= items) return;
     const uint32_t my_items = (items - wave + nwaves - 1) / nwaves;
@@ -119,8 +146,9 @@ __device__ __forceinline__ void all_gather_phase(const TwoShotParams& p, int n, 
         uint32_t j = 0, t = 0;
         if (need) {
             const uint32_t it = wave + k * nwaves;
+            const uint32_t ro = uint32_t(p.r0) + it / per_out;
             const uint32_t rem = it % per_out;
-            j = rem / p.ktiles;
+            j = ag_source(rem / p.ktiles, ro, skip_own);
             t = rem % p.ktiles;
         }
         const uint32_t* slot = slots + j * kSlotsPerRank + t;
@@ -139,8 +167,6 @@ __device__ __forceinline__ void all_gather_phase(const TwoShotParams& p, int n, 
             __builtin_amdgcn_s_sleep(1);
         }
     }
-    fence_acquire_agent();
-
     const uint32_t upt = p.tile / kWave;
     const uint32_t my_units = my_items * upt;
     for (uint32_t q0 = 0; q0 < my_units; q0 += kCopyUnroll) {
@@ -149,19 +175,18 @@ __device__ __forceinline__ void all_gather_phase(const TwoShotParams& p, int n, 
         bool valid[kCopyUnroll];
 #pragma unroll
         for (int u = 0; u < kCopyUnroll; ++u) {
-            const uint32_t q = q0 + u;
+            const bool unit_ok = q0 + u < my_units;
+            const uint32_t q = unit_ok ? q0 + u : q0;
             const uint32_t k = q / upt, sub = q - k * upt;
             const uint32_t it = wave + k * nwaves;
             const uint32_t ro = uint32_t(p.r0) + it / per_out;
             const uint32_t rem = it % per_out;
-            const uint32_t j = rem / p.ktiles;
+            const uint32_t j = ag_source(rem / p.ktiles, ro, skip_own);
             const uint32_t t = rem % p.ktiles;
             const uint32_t idx = t * p.tile + sub * kWave + uint32_t(lane);
-            valid[u] = (q < my_units) && (idx < p.mvec);
-            if (valid[u]) {
-                x[u] = ld_plain(p.seg[j] + idx);
-                dst[u] = p.out[ro] + size_t(j) * p.mvec + idx;
-            }
+            valid[u] = unit_ok && idx < p.mvec;
+            x[u] = ld_coherent(p.seg[j] + (valid[u] ? idx : t * p.tile));
+            dst[u] = p.out[ro] + size_t(j) * p.mvec + idx;
         }
 #pragma unroll
         for (int u = 0; u < kCopyUnroll; ++u)
@@ -172,7 +197,8 @@ __device__ __forceinline__ void all_gather_phase(const TwoShotParams& p, int n, 
 template <typename T, int NR, int U>
 __global__ __launch_bounds__(kBlock) void twoshot_kernel(TwoShotParams p) {
     const int lane = threadIdx.x & (kWave - 1);
-    const uint32_t wave = blockIdx.x * kWavesPerBlock + threadIdx.x / kWave;
+    // the wavefront index, made explicitly uniform so item arithmetic is scalar
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(blockIdx.x * kWavesPerBlock + threadIdx.x / kWave);
     const uint32_t nwaves = gridDim.x * kWavesPerBlock;
     if (p.do_rs) reduce_scatter_phase<T, NR, U>(p, wave, nwaves, lane);
     if (p.do_ag) all_gather_phase(p, NR, wave, nwaves, lane);
@@ -206,18 +232,27 @@ hipError_t launch_t(const TwoShotRequest& rq, hipStream_t s) {
     p.do_ag = rq.do_ag;
 
     auto kern = twoshot_kernel<T, NR, U>;
+    const uint32_t R = uint32_t(rq.r1 - rq.r0);
     if (rq.do_rs && rq.do_ag) {
-        int per_cu = 0;
-        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, kBlock, 0);
-        if (e != hipSuccess) return e;
-        if (per_cu < 1) return hipErrorCooperativeLaunchTooLarge;
-        if (per_cu > 2) per_cu = 2;
-        const dim3 grid(uint32_t(info.cu_count * per_cu)), block(kBlock);
-        void* args[] = {&p};
-        return hipLaunchCooperativeKernel(reinterpret_cast<const void*>(kern), grid, block, args, 0, s);
+        // Persistent grid for the fused form: at most as many workgroups as
+        // the device holds at once (occupancy of this kernel, capped at two
+        // per CU), so every producer is resident while consumers poll.  The
+        // occupancy is a property of the compiled kernel: query it once.
+        static int per_cu = -1;
+        static hipError_t occ_err = hipSuccess;
+        static std::once_flag once;
+        std::call_once(once, [&] { occ_err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, kBlock, 0); });
+        if (occ_err != hipSuccess) return occ_err;
+        if (per_cu < 1) return hipErrorLaunchOutOfResources;
+        const uint32_t resident = uint32_t(info.cu_count) * uint32_t(per_cu < 2 ? per_cu : 2);
+        // one wavefront per item (phase 1 plus phase 2) if the device holds that many
+        uint32_t grid = (R * uint32_t(NR) * p.ktiles + kWavesPerBlock - 1) / kWavesPerBlock;
+        if (grid > resident) grid = resident;
+        if (grid < 1) grid = 1;
+        hipLaunchKernelGGL(kern, dim3(grid), dim3(kBlock), 0, s, p);
+        return hipGetLastError();
     }
     // Split launches: size the grid to the work, at most two blocks per CU.
-    const uint32_t R = uint32_t(rq.r1 - rq.r0);
     const uint32_t items = rq.do_rs ? R * p.ktiles : R * uint32_t(NR) * p.ktiles;
     uint32_t grid = (items + kWavesPerBlock - 1) / kWavesPerBlock;
     const uint32_t cap = uint32_t(info.cu_count) * 2u;

@@ -103,13 +103,19 @@ def ll_wire_bytes(proto, S):
 
 def hbm_bytes(op, S, n, proto=None):
     """HBM bytes (reads, writes) one GPU's kernel must move when the n ranks'
-    buffers are n allocations on that GPU (local reads and all writes count)."""
+    buffers are n allocations on that GPU (local reads and all writes count).
+
+    Two-shot, one rank's share: the reduce-scatter reads segment r of all n
+    inputs (S bytes) and writes the reduced segment (S/n); the all-gather
+    fills the output (S) -- rank r's own segment straight from the reduce,
+    the other n-1 segments read from the peers (S (n-1)/n).  All n ranks: n
+    times that."""
     if op == "oneshot":
         return n * S, S
     if op == "twoshot_share":
-        return 2 * S, S / n + S
+        return S + (n - 1) * S // n, S // n + S
     if op == "twoshot_full":
-        return 2 * n * S, (n + 1) * S
+        return n * S + (n - 1) * S, S + n * S
     if op == "ll_pack":
         return S, ll_wire_bytes(proto, S)
     if op == "ll_reduce":
