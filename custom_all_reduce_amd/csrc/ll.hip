@@ -37,8 +37,7 @@ struct PackParams {
 // handles kPackUnroll chunks kBlock apart.  blockIdx.y selects the message.
 // The lane whose chunk runs past the end reads byte by byte, zero-fills,
 // and writes only the lines that exist.
-constexpr int kPackUnroll = 4;
-
+template <int kPackUnroll>
 __global__ __launch_bounds__(kBlock) void ll_pack_kernel(PackParams p) {
     const uint8_t* src = p.src[blockIdx.y];
     u32x4* wire = reinterpret_cast<u32x4*>(p.wire[blockIdx.y]);
@@ -391,7 +390,9 @@ hipError_t launch_reduce_t(const ReduceParams& p, int proto, hipStream_t s) {
         const size_t grid = (chunks + kBlock * U - 1) / (kBlock * U);
         hipLaunchKernelGGL((ll_reduce_kernel<T, NR, U>), dim3(uint32_t(grid)), dim3(kBlock), 0, s, p);
     } else {
-        constexpr int U = NR <= 8 ? 2 : 1;
+        // One 8-line unit per wavefront: measured faster than two for every
+        // size, and the two-unit fp32 instantiation stalls badly.
+        constexpr int U = 1;
         const size_t wave_units = (p.nlines + 7) / 8;
         const size_t waves = (wave_units + U - 1) / U;
         const size_t grid = (waves + kWavesPerBlock - 1) / kWavesPerBlock;
@@ -412,9 +413,17 @@ hipError_t launch_ll_pack(const void* const* src, void* const* wire, int count, 
     p.nbytes = nbytes;
     p.step = step;
     if (proto == 0) {
+        // Four chunks per lane once the grid still spans every CU several
+        // times over; one per lane for small messages, which want many
+        // workgroups rather than deep ones.
         const size_t chunks = (nbytes + 7) / 8;
-        const size_t grid = (chunks + kBlock * kPackUnroll - 1) / (kBlock * kPackUnroll);
-        hipLaunchKernelGGL(ll_pack_kernel, dim3(uint32_t(grid), uint32_t(count)), dim3(kBlock), 0, s, p);
+        if (chunks >= size_t(kBlock) * 4 * 2048) {
+            const size_t grid = (chunks + kBlock * 4 - 1) / (kBlock * 4);
+            hipLaunchKernelGGL(ll_pack_kernel<4>, dim3(uint32_t(grid), uint32_t(count)), dim3(kBlock), 0, s, p);
+        } else {
+            const size_t grid = (chunks + kBlock - 1) / kBlock;
+            hipLaunchKernelGGL(ll_pack_kernel<1>, dim3(uint32_t(grid), uint32_t(count)), dim3(kBlock), 0, s, p);
+        }
     } else {
         const size_t nlines = (nbytes + 119) / 120;
         const size_t grid = (nlines * 8 + kBlock - 1) / kBlock;

@@ -2,9 +2,9 @@
 // buffers, rank 0 first, rounded once ("0-custom-all-reduce", 实现 steps 1-5;
 // "集合通信：NCCL 的算法、协议与推理框架的定制 all-reduce", 算法, one-shot).
 //
-// Layout: each lane owns 16-byte vectors; a workgroup of 256 lanes covers
-// U * 256 consecutive vectors, lane-consecutive within each of the U rows, so
-// every load and store instruction of a wave touches 1 KiB of contiguous
+// Layout: each lane owns 16-byte vectors; a workgroup of kBlock lanes covers
+// U * kBlock consecutive vectors, lane-consecutive within each of the U rows,
+// so every load and store instruction of a wave touches 1 KiB of contiguous
 // memory.  All U * n loads of a lane are issued before the first add, which
 // keeps U * n * 16 bytes per lane in flight.  The partial last vector (numel
 // not a multiple of 4 fp32 / 8 bf16) is summed element by element by the last
@@ -15,7 +15,7 @@
 namespace ar {
 namespace {
 
-constexpr int kBlock = 256;
+constexpr int kBlock = 128;
 
 template <int NR> struct RankVecs { const u32x4* p[NR]; };
 
@@ -53,7 +53,10 @@ __global__ __launch_bounds__(kBlock) void oneshot_kernel(RankVecs<NR> in, u32x4*
 
 template <typename T, int NR>
 hipError_t launch_t(const void* const* in, void* out, size_t numel, hipStream_t s) {
-    constexpr int U = NR <= 4 ? 4 : (NR <= 8 ? 2 : 1);
+    // One vector per lane per rank and small workgroups: measured fastest
+    // from 128 KiB to 64 MiB per rank (more workgroups in flight beat deeper
+    // per-lane unrolling on this part).
+    constexpr int U = 1;
     const uint32_t nvec = uint32_t(numel / elem<T>::per_vec);
     const uint32_t ntail = uint32_t(numel % elem<T>::per_vec);
     RankVecs<NR> p;

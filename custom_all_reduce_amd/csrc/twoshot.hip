@@ -41,7 +41,7 @@ namespace {
 
 constexpr int kBlock = 256;
 constexpr int kWavesPerBlock = kBlock / kWave;
-constexpr int kCopyUnroll = 8;
+constexpr int kCopyUnroll = 4;
 
 struct TwoShotParams {
     const u32x4* in[kMaxRanks];
@@ -206,7 +206,10 @@ __global__ __launch_bounds__(kBlock) void twoshot_kernel(TwoShotParams p) {
 
 template <typename T, int NR>
 hipError_t launch_t(const TwoShotRequest& rq, hipStream_t s) {
-    constexpr int U = NR <= 4 ? 4 : (NR <= 8 ? 2 : 1);
+    // one unit in flight per wavefront in phase 1 (NR loads per lane), four in
+    // phase 2: measured best for decode-sized messages, equal within noise
+    // at 64 MiB per rank
+    constexpr int U = 1;
     DeviceInfo info;
     hipError_t e = device_info(&info);
     if (e != hipSuccess) return e;
