@@ -314,6 +314,8 @@ def main(argv=None):
     ap.add_argument("--eager", action="store_true", help="time eager launches instead of one graph replay")
     ap.add_argument("--no-kernel-times", action="store_true", help="skip the per-kernel timing graphs")
     ap.add_argument("--sweep", metavar="OUT.jsonl", help="also run the size sweep (n = 8, 16; fp32, bf16) into a file")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run ten 256 MiB device-to-device copies (reference for HBM byte counters), then exit")
     args = ap.parse_args(argv)
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -324,6 +326,18 @@ def main(argv=None):
 
     import numpy as np
     import torch
+
+    if args.calibrate_copy:
+        # A plain copy of known size: FETCH_SIZE and WRITE_SIZE of its kernel
+        # should read 256 MiB each; their ratio to that scales the counters.
+        a = torch.empty(256 << 20, dtype=torch.uint8, device="cuda").fill_(1)
+        b = torch.empty_like(a)
+        torch.cuda.synchronize()
+        for _ in range(10):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes": 256 << 20, "launches": 10}), flush=True)
+        return 0
 
     import custom_all_reduce_amd as car
     import synth

@@ -33,24 +33,27 @@ __device__ __forceinline__ void st_stream(u32x4* p, u32x4 v) { __builtin_nontemp
 __device__ __forceinline__ u32x4 ld_plain(const u32x4* p) { return *p; }
 
 // Device-coherent 16-byte access for data that one wavefront writes and a
-// wavefront on another XCD reads inside the same launch: two relaxed
-// agent-scope 64-bit atomics, i.e. global_store/load_dwordx2 with sc1.  Such
-// stores are written through to the device's point of coherence and such
-// loads are served from it, so neither side needs the L2-wide writeback
-// (release) or invalidate (acquire) that an agent-scope fence costs; the
-// producer only waits for its stores to complete (wait_stores) before it
-// publishes the flag, and the consumer issues its loads after it has seen
-// the flag.
-__device__ __forceinline__ void st_coherent(u32x4* p, u32x4 v) {
-    uint64_t* q = reinterpret_cast<uint64_t*>(p);
-    __hip_atomic_store(q, uint64_t(v.x) | (uint64_t(v.y) << 32), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_store(q + 1, uint64_t(v.z) | (uint64_t(v.w) << 32), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+// wavefront on another XCD reads inside the same launch: raw buffer
+// load/store with the sc1 cache policy (device scope).  Such stores are
+// written through to the device's point of coherence and such loads are
+// served from it, so neither side needs the L2-wide writeback (release) or
+// invalidate (acquire) that an agent-scope fence costs; the producer only
+// waits for its stores to complete (wait_stores) before it publishes a flag,
+// and the consumer issues its loads after it has seen the flag.  The buffer
+// resource covers one wavefront-uniform range (base and size in scalar
+// registers); accesses past its size are dropped / read as zero by the
+// hardware, so a resource is also a bounds check.
+constexpr int kCachePolicySc1 = 16;  // the sc1 bit of the cache-policy operand
+constexpr int kBufferConfigWord = 0x00020000;  // gfx9-family raw-buffer resource word 3
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_range(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, int(bytes), kBufferConfigWord);
 }
-__device__ __forceinline__ u32x4 ld_coherent(const u32x4* p) {
-    const uint64_t* q = reinterpret_cast<const uint64_t*>(p);
-    const uint64_t a = __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const uint64_t b = __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    return u32x4{uint32_t(a), uint32_t(a >> 32), uint32_t(b), uint32_t(b >> 32)};
+__device__ __forceinline__ void st_coherent(__amdgpu_buffer_rsrc_t r, uint32_t byte_off, u32x4 v) {
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, int(byte_off), 0, kCachePolicySc1);
+}
+__device__ __forceinline__ u32x4 ld_coherent(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, int(byte_off), 0, kCachePolicySc1);
 }
 // Wait until every memory operation this wavefront issued has completed
 // (s_waitcnt with all counters at zero).

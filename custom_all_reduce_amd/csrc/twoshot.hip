@@ -77,6 +77,7 @@ __device__ __forceinline__ void reduce_scatter_phase(const TwoShotParams& p, uin
         u32x4 x[U][NR];
         uint32_t dst_idx[U];
         uint32_t dst_rank[U];
+        uint32_t dst_t0[U];  // first vector of the unit's tile (wavefront-uniform)
         bool valid[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
@@ -90,6 +91,7 @@ __device__ __forceinline__ void reduce_scatter_phase(const TwoShotParams& p, uin
             valid[u] = unit_ok && idx < p.mvec;
             dst_idx[u] = idx;
             dst_rank[u] = r;
+            dst_t0[u] = t * p.tile;
             const size_t src = size_t(r) * p.mvec + (valid[u] ? idx : t * p.tile);
 #pragma unroll
             for (int i = 0; i < NR; ++i) x[u][i] = ld_stream(in[i] + src);
@@ -101,7 +103,10 @@ __device__ __forceinline__ void reduce_scatter_phase(const TwoShotParams& p, uin
             for (int i = 0; i < NR; ++i) acc.add(x[u][i]);
             const u32x4 v = acc.result();
             if (valid[u]) {
-                st_coherent(p.seg[dst_rank[u]] + dst_idx[u], v);
+                // the tile of seg[r] as one wavefront-uniform buffer range
+                const uint32_t t0 = dst_t0[u];
+                const uint32_t tile_bytes = min(p.tile, p.mvec - t0) * 16u;
+                st_coherent(buffer_range(p.seg[dst_rank[u]] + t0, tile_bytes), (dst_idx[u] - t0) * 16u, v);
                 // fused form: rank r's own segment of its output comes straight
                 // from registers (the all-gather copy of seg[r] into out[r])
                 if (p.do_ag) st_stream(p.out[dst_rank[u]] + size_t(dst_rank[u]) * p.mvec + dst_idx[u], v);
@@ -185,7 +190,9 @@ __device__ __forceinline__ void all_gather_phase(const TwoShotParams& p, int n, 
             const uint32_t t = rem % p.ktiles;
             const uint32_t idx = t * p.tile + sub * kWave + uint32_t(lane);
             valid[u] = unit_ok && idx < p.mvec;
-            x[u] = ld_coherent(p.seg[j] + (valid[u] ? idx : t * p.tile));
+            const uint32_t t0 = t * p.tile;
+            const uint32_t tile_bytes = min(p.tile, p.mvec - t0) * 16u;
+            x[u] = ld_coherent(buffer_range(p.seg[j] + t0, tile_bytes), (sub * kWave + uint32_t(lane)) * 16u);
             dst[u] = p.out[ro] + size_t(j) * p.mvec + idx;
         }
 #pragma unroll
