@@ -1,0 +1,84 @@
+"""Receivers that start before their data exists.
+
+The LL / LL128 receiver is launched while every flag of its wire buffers is
+still 0; the wire buffers live in pinned host memory, and the host writes the
+lines (all data first, then the flags) after a delay while the kernel polls.
+This exercises the receivers' polling slow paths against a writer that is
+truly concurrent (two GPU streams may share one hardware queue, so a second
+stream would not guarantee that).  Only loads touch host memory; the status
+words stay in device memory.  Every wait is bounded, so a mistake shows up
+as a reported timeout, never as a hang.
+
+(The two-shot barrier's concurrent case -- consumers polling while producers
+of the same launch publish -- is the fused full-emulation launch exercised
+throughout test_gpu_twoshot.py.)"""
+from __future__ import annotations
+
+import ctypes
+import time
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from devtensors import bits, oracle_bits, to_dev
+
+pytestmark = pytest.mark.gpu
+
+car = pytest.importorskip("custom_all_reduce_amd")
+
+
+def pinned_device_view(nbytes: int):
+    """Zeroed pinned host buffer and its device address."""
+    t = torch.zeros(nbytes + 16, dtype=torch.uint8, pin_memory=True)
+    hip = ctypes.CDLL("libamdhip64.so.7")
+    dp = ctypes.c_void_p()
+    assert hip.hipHostGetDevicePointer(ctypes.byref(dp), ctypes.c_void_p(t.data_ptr()), 0) == 0
+    off = (-dp.value) % 16  # 16-byte alignment on the device side
+    return t, off, dp.value + off
+
+
+def write_lines(host_buf: np.ndarray, proto: str, msg: np.ndarray, step: int):
+    """Host-side sender: every line's data, then (after all data) every flag."""
+    raw = msg.view(np.uint8)
+    d, lb = (4, 8) if proto == "ll" else (120, 128)
+    lines = -(-raw.size // d)
+    view = host_buf[: lines * lb].reshape(lines, lb)
+    pad = np.zeros(lines * d, np.uint8)
+    pad[: raw.size] = raw
+    view[:, :d] = pad.reshape(lines, d)
+    flag = np.zeros(lb - d, np.uint8)
+    flag[:4] = np.frombuffer(np.uint32(step).tobytes(), np.uint8)
+    view[:, d:] = flag
+
+
+@pytest.mark.parametrize("proto", ["ll", "ll128"])
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_receiver_polls_until_the_host_writes_the_lines(proto, dt):
+    n, numel = 4, 1500 + (1 if dt == "bf16" else 0)
+    es = 4 if dt == "f32" else 2
+    host = synth.rank_inputs(n, numel, dt, "normal", config=310)
+    want = oracle_bits(oracle.oneshot(host, dt))
+    W = car.ll_wire_bytes(proto, numel * es)
+    bufs = [pinned_device_view(W) for _ in range(n)]
+    out = torch.empty(numel, dtype=torch.float32 if dt == "f32" else torch.bfloat16, device="cuda")
+    flags = car.new_flags(n)
+    torch.cuda.synchronize()
+    wires = (ctypes.c_void_p * n)(*[b[2] for b in bufs])
+    fn = car.lib.ar_ll_reduce_unpack if proto == "ll" else car.lib.ar_ll128_reduce_unpack
+    old = car.get_poll_timeout_ns()
+    car.set_poll_timeout_ns(3_000_000_000)
+    try:
+        st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        assert fn(wires, n, out.data_ptr(), numel, 0 if dt == "f32" else 1, 9, flags.data_ptr(), st) == 0
+        time.sleep(0.05)  # the receiver is polling now
+        for r in range(n):
+            t, off, _ = bufs[r]
+            write_lines(t.numpy()[off:], proto, host[r], 9)
+        torch.cuda.synchronize()
+    finally:
+        car.set_poll_timeout_ns(old)
+    assert car.read_status(flags)[0] == 0
+    assert np.array_equal(bits(out), want)
