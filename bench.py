@@ -302,6 +302,72 @@ def sweep(args, torch, car, np, out_path):
     return rows, cross
 
 
+SELECT_SIZES = [16 << 10, 32 << 10, 64 << 10, 128 << 10, 256 << 10, 512 << 10, 1 << 20, 3 << 19, 2 << 20,
+                3 << 20, 4 << 20, 6 << 20, 8 << 20, 12 << 20, 16 << 20, 32 << 20, 64 << 20]
+SELECT_ALGOS = ["oneshot", "twoshot", "ll", "ll128"]
+
+
+def select_table(args, torch, car, np, out_path):
+    """One GPU's share of an all-reduce by each algorithm, n = 2..16, bf16,
+    over SELECT_SIZES bytes per rank (cold: buffer sets rotated over >= 1 GiB;
+    graph-replayed).  The shares: one-shot; rank 0's fused two-shot after the
+    peers' reduce-scatter; rank 0's LL / LL128 pack plus the receiver over
+    every rank's wire buffer, the peers' wires packed beforehand.  Writes one
+    JSON object per (n, size)."""
+    rows = []
+    gen = torch.Generator(device="cuda")
+    with open(out_path, "w", encoding="utf-8") as f:
+        for n in range(2, 17):
+            for S in SELECT_SIZES:
+                numel = S // 2
+                numel -= numel % (8 * n)  # whole 16-byte vectors in every segment
+                Sb = numel * 2
+                W1, W2 = car.ll_wire_bytes("ll", Sb), car.ll_wire_bytes("ll128", Sb)
+                fp = n * Sb + 3 * Sb + n * (W1 + W2)
+                nsets = max(2, int(np.ceil((1 << 30) / fp)))
+                gen.manual_seed(1000 * n + S.bit_length())
+                src = [torch.randn(numel, generator=gen, device="cuda").to(torch.bfloat16) for _ in range(n)]
+                flags = car.new_flags(n)
+                calls = {a: [] for a in SELECT_ALGOS}
+                keep = []
+                for _ in range(nsets):
+                    ins = [t.clone() for t in src]
+                    segs = [torch.empty(numel // n, dtype=torch.bfloat16, device="cuda") for _ in range(n)]
+                    out = torch.empty(numel, dtype=torch.bfloat16, device="cuda")
+                    w1 = [torch.empty(W1, dtype=torch.uint8, device="cuda") for _ in range(n)]
+                    w2 = [torch.empty(W2, dtype=torch.uint8, device="cuda") for _ in range(n)]
+                    keep.append((ins, segs, out, w1, w2))
+                    for r in range(1, n):
+                        car.ar_twoshot_rs(ins, segs, flags, PEER_STEP, r0=r, r1=r + 1)
+                    car.ar_ll_pack(ins[1:], w1[1:], "ll", PEER_STEP)
+                    car.ar_ll_pack(ins[1:], w2[1:], "ll128", PEER_STEP)
+                    one = car.prepare_oneshot(ins, out)
+                    calls["oneshot"].append(lambda s, one=one: one())
+                    calls["twoshot"].append(car.prepare_twoshot_rs(ins, segs, flags, 0, 1, [out] + [None] * (n - 1)))
+                    for name, w in (("ll", w1), ("ll128", w2)):
+                        pk = car.prepare_ll_pack([ins[0]], [w[0]], name)
+                        rd = car.prepare_ll_reduce(w, out, flags, name)
+                        calls[name].append(lambda s, pk=pk, rd=rd: (pk(s), rd(s)))
+                del src
+                torch.cuda.synchronize()
+                row = {"n": n, "bytes_per_rank": Sb}
+                K = int(min(200, max(16, 0.004 * 4e12 / ((n + 1) * Sb))))
+                for a in SELECT_ALGOS:
+                    cs = calls[a]
+                    g = graph_of(torch, lambda cs=cs: [cs[i % nsets](1 + i) for i in range(K)])
+                    timed_replay(torch, g)
+                    row[a + "_us"] = round(timed_replay(torch, g) * 1e3 / K, 3)
+                    del g
+                car.raise_on_status(flags, f"select-table n={n} S={Sb}")
+                rows.append(row)
+                f.write(json.dumps(row) + "\n")
+                f.flush()
+                print("select-table " + " ".join(f"{k}={v}" for k, v in row.items()), file=sys.stderr, flush=True)
+                del calls, keep
+                torch.cuda.empty_cache()
+    return rows
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -314,6 +380,8 @@ def main(argv=None):
     ap.add_argument("--eager", action="store_true", help="time eager launches instead of one graph replay")
     ap.add_argument("--no-kernel-times", action="store_true", help="skip the per-kernel timing graphs")
     ap.add_argument("--sweep", metavar="OUT.jsonl", help="also run the size sweep (n = 8, 16; fp32, bf16) into a file")
+    ap.add_argument("--select-table", metavar="OUT.jsonl",
+                    help="only time one GPU's share by each algorithm for n = 2..16 over a size grid, then exit")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run ten 256 MiB device-to-device copies (reference for HBM byte counters), then exit")
     args = ap.parse_args(argv)
@@ -341,6 +409,13 @@ def main(argv=None):
 
     import custom_all_reduce_amd as car
     import synth
+
+    if args.select_table:
+        torch.cuda.set_device(0)
+        car.set_poll_timeout_ns(50_000_000)
+        rows = select_table(args, torch, car, np, args.select_table)
+        print(json.dumps({"select_table_rows": len(rows), "file": args.select_table}), flush=True)
+        return 0
 
     n, dt_name, numel, desc = WORKLOADS[args.workload]
     dt = torch.float32 if dt_name == "f32" else torch.bfloat16

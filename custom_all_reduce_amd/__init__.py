@@ -71,6 +71,8 @@ def _load(path: str = LIB_PATH):
     lib.ar_ll128_reduce_unpack.argtypes = [P, i32, vp, sz, i32, u32, vp, vp]
     lib.ar_ll128_reduce_unpack.restype = i32
     lib.ar_flag_barrier_reset.argtypes, lib.ar_flag_barrier_reset.restype = [vp, i32, vp], i32
+    lib.ar_select_algo.argtypes, lib.ar_select_algo.restype = [i32, sz, i32, ctypes.c_double], i32
+    lib.ar_algo_cost_us.argtypes, lib.ar_algo_cost_us.restype = [i32, i32, sz, i32, ctypes.c_double], ctypes.c_double
     return lib
 
 
@@ -126,6 +128,30 @@ def set_poll_timeout_ns(ns: int):
 
 def get_poll_timeout_ns() -> int:
     return int(_lib.ar_get_poll_timeout_ns())
+
+
+ALGOS = ("oneshot", "twoshot", "ll", "ll128")  # ar_algo values 0..3
+
+
+def _dtype_arg(dtype) -> int:
+    return _DTYPES[dtype] if isinstance(dtype, torch.dtype) else int(dtype)
+
+
+def algo_cost_us(algo: str, n: int, numel: int, dtype, sync_us: float = 0.0):
+    """Modelled time of one call (ar_algo_cost_us); None where the algorithm
+    does not apply (a two-shot the size cannot split)."""
+    t = float(_lib.ar_algo_cost_us(ALGOS.index(algo), int(n), int(numel), _dtype_arg(dtype), float(sync_us)))
+    return None if t < 0 else t
+
+
+def select_algo(n: int, numel: int, dtype, sync_us: float = 0.0) -> str:
+    """Algorithm of least modelled time for an all-reduce of numel elements of
+    dtype (torch dtype or AR_F32/AR_BF16) per rank over n ranks, with sync_us
+    per cross-GPU semaphore synchronisation."""
+    r = int(_lib.ar_select_algo(int(n), int(numel), _dtype_arg(dtype), float(sync_us)))
+    if r < 0:
+        raise ArError(-r, "ar_select_algo")
+    return ALGOS[r]
 
 
 def new_flags(n: int, device=None) -> torch.Tensor:

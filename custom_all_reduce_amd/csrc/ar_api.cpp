@@ -28,6 +28,25 @@ constexpr size_t kMaxBytes = size_t(1) << 36;
 constexpr size_t kStatusBytes = size_t(kStatusWords) * 4;
 
 size_t elem_bytes(int dtype) { return dtype == AR_F32 ? 4 : 2; }
+
+#include "select_table.inc"
+
+// Semaphore synchronisations per call charged by the cost model: start and
+// end for the one-shot, two more around the two-shot's barrier; none for
+// LL / LL128, whose receivers learn of arrival from the flags in the lines.
+constexpr double kSemaphoreSyncs[4] = {2.0, 4.0, 0.0, 0.0};
+
+// Measured one-GPU time of algo at `bytes` per rank: piecewise linear in the
+// size between grid points, flat below the first (launch-bound), and
+// extended with the last segment's slope above the last (bandwidth-bound).
+double share_us(int algo, int n, double bytes) {
+    const float* t = kSelUs[n - 2][algo];
+    if (bytes <= double(kSelSizes[0])) return t[0];
+    int k = 1;
+    while (k < kSelNumSizes - 1 && bytes > double(kSelSizes[k])) ++k;
+    const double x0 = double(kSelSizes[k - 1]), x1 = double(kSelSizes[k]);
+    return t[k - 1] + (double(t[k]) - double(t[k - 1])) * (bytes - x0) / (x1 - x0);
+}
 bool dtype_ok(int dtype) { return dtype == AR_F32 || dtype == AR_BF16; }
 bool ranks_ok(int n) { return n >= 2 && n <= AR_MAX_RANKS; }
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -248,6 +267,26 @@ int ar_ll_reduce_unpack(const void* const* wire, int n, void* out, size_t numel,
 int ar_ll128_reduce_unpack(const void* const* wire, int n, void* out, size_t numel, int dtype, uint32_t step,
                            uint32_t* flags, void* stream) {
     return ll_reduce_common(wire, n, out, numel, dtype, step, flags, AR_PROTO_LL128, stream);
+}
+
+double ar_algo_cost_us(int algo, int n, size_t numel, int dtype, double sync_us) {
+    if (algo < AR_ALGO_ONESHOT || algo > AR_ALGO_LL128 || !ranks_ok(n) || !dtype_ok(dtype) || numel == 0 ||
+        !(sync_us >= 0.0))
+        return -1.0;
+    const size_t es = elem_bytes(dtype);
+    if (algo == AR_ALGO_TWOSHOT && !(numel % size_t(n) == 0 && (numel / size_t(n) * es) % 16 == 0)) return -1.0;
+    return share_us(algo, n, double(numel) * double(es)) + kSemaphoreSyncs[algo] * sync_us;
+}
+
+int ar_select_algo(int n, size_t numel, int dtype, double sync_us) {
+    if (!ranks_ok(n) || !dtype_ok(dtype) || numel == 0 || !(sync_us >= 0.0)) return -AR_ERR_ARG;
+    int best = AR_ALGO_ONESHOT;
+    double best_us = ar_algo_cost_us(best, n, numel, dtype, sync_us);
+    for (int a = AR_ALGO_TWOSHOT; a <= AR_ALGO_LL128; ++a) {
+        const double t = ar_algo_cost_us(a, n, numel, dtype, sync_us);
+        if (t >= 0.0 && t < best_us) best = a, best_us = t;
+    }
+    return best;
 }
 
 int ar_flag_barrier_reset(uint32_t* flags, int n, void* stream) {

@@ -167,6 +167,30 @@ int ar_ll_reduce_unpack(const void* const* wire, int n, void* out, size_t numel,
 int ar_ll128_reduce_unpack(const void* const* wire, int n, void* out, size_t numel, int dtype,
                            uint32_t step, uint32_t* flags, void* stream);
 
+/* Algorithm selection from measured costs ([NCCL] 算法 and 协议: no
+ * algorithm or protocol is best at every size, so the choice goes by message
+ * size and rank count; [CAR] keeps such a per-rank-count threshold map).
+ * The modelled time of algo for numel elements of dtype per rank over n ranks
+ * is t_share + k * sync_us, where
+ *  - t_share is the time of one GPU's share measured on MI355X with this
+ *    library's kernels (cold HBM, graph-replayed; one-shot; one rank's fused
+ *    two-shot; one rank's LL / LL128 pack plus the receiver), tabulated for
+ *    n = 2..16 over 16 KiB..64 MiB per rank, interpolated linearly in the
+ *    size, flat below the grid and extended with the last slope above it;
+ *  - k is the number of cross-GPU semaphore synchronisations per call, the
+ *    alpha terms of the [NCCL] 算法 alpha-beta model (2 for the one-shot, 4
+ *    for the two-shot; 协议 names the semaphore as alpha's main source),
+ *    and 0 for LL / LL128, whose flags travel with the data ([NCCL] 协议);
+ *  - sync_us >= 0 is the cost of one such synchronisation on the caller's
+ *    interconnect (0 when the ranks share one GPU).
+ * ar_algo_cost_us returns that time in microseconds, or a negative value for
+ * bad arguments or a two-shot the size cannot split into n whole 16-byte
+ * segments.  ar_select_algo returns the ar_algo of least modelled time (the
+ * lower value on a tie), or -AR_ERR_ARG for bad arguments. */
+typedef enum { AR_ALGO_ONESHOT = 0, AR_ALGO_TWOSHOT = 1, AR_ALGO_LL = 2, AR_ALGO_LL128 = 3 } ar_algo;
+double ar_algo_cost_us(int algo, int n, size_t numel, int dtype, double sync_us);
+int ar_select_algo(int n, size_t numel, int dtype, double sync_us);
+
 /* Zero the whole flag region of ar_flag_bytes(n) bytes (status words and
  * every arrival slot) with a fill kernel, so that steps may start again at
  * 1: at set-up, after a timeout, and before step ids would wrap.

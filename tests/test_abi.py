@@ -165,3 +165,74 @@ def test_accounting_matches_oracle_model():
             for proto in ("ll", "ll128"):
                 assert accounting.ll_pack(proto, S) == model.hbm_bytes("ll_pack", S, n, proto)
                 assert accounting.ll_reduce(proto, n, S) == model.hbm_bytes("ll_reduce", S, n, proto)
+
+
+# ---- algorithm selector (host logic) ------------------------------------------
+def _sizes():
+    # grid points, points between them, below and above the measured range
+    return [1 << 10, 16 << 10, 24 << 10, 200 << 10, 1 << 20, 1_300_000, 3 << 20, 5 << 20, 64 << 20, 100 << 20,
+            1 << 30]
+
+
+@pytest.mark.parametrize("n", list(range(2, 17)))
+@pytest.mark.parametrize("sync_us", [0.0, 1.5, 25.0])
+def test_selector_picks_the_least_modelled_cost(n, sync_us):
+    import torch
+    for dt, es in ((torch.bfloat16, 2), (torch.float32, 4)):
+        for S in _sizes():
+            numel = max(1, S // es)
+            costs = {a: car.algo_cost_us(a, n, numel, dt, sync_us) for a in car.ALGOS}
+            ok = {a: c for a, c in costs.items() if c is not None}
+            want = min(ok, key=lambda a: (ok[a], car.ALGOS.index(a)))
+            assert car.select_algo(n, numel, dt, sync_us) == want, (n, S, dt, sync_us, costs)
+            assert all(c > 0 for c in ok.values())
+
+
+def test_selector_cost_model_terms():
+    import torch
+    bf = torch.bfloat16
+    # sync terms: 2 per call for the one-shot, 4 for the two-shot, none for LL / LL128
+    for a, k in zip(car.ALGOS, (2, 4, 0, 0)):
+        assert car.algo_cost_us(a, 8, 1 << 20, bf, 10.0) == pytest.approx(car.algo_cost_us(a, 8, 1 << 20, bf, 0.0) + 10 * k)
+    # flat below the grid, increasing in size above it, linear beyond the last point
+    for a in car.ALGOS:
+        assert car.algo_cost_us(a, 8, 64, bf) == car.algo_cost_us(a, 8, 8 << 10, bf)
+        c = [car.algo_cost_us(a, 8, (s << 20) // 2, bf) for s in (64, 128, 192)]
+        assert c[2] - c[1] == pytest.approx(c[1] - c[0], rel=1e-6) and c[2] > c[1] > c[0]
+    # bf16 and fp32 of the same byte count cost the same
+    assert car.algo_cost_us("twoshot", 8, 1 << 20, bf) == car.algo_cost_us("twoshot", 8, 1 << 19, torch.float32)
+
+
+def test_selector_regimes():
+    """What the measured table must show: one GPU with no cross-GPU sync cost
+    takes the one-shot for small messages and (n >= 4) the two-shot for large
+    ones; two ranks never take the two-shot ([NCCL] 练习 2: at n = 2 both move
+    S, and the one-shot saves a synchronisation); a large sync cost moves small
+    messages to a flag protocol."""
+    import torch
+    bf = torch.bfloat16
+    for n in range(2, 17):
+        assert car.select_algo(n, 8 << 10, bf) == "oneshot"
+        big = (64 << 20) // 2
+        big -= big % (8 * n)  # n whole 16-byte segments
+        if n != 3:  # at n = 3 the two sides move 4S and 3S bytes of HBM: close
+            assert car.select_algo(n, big, bf) == ("oneshot" if n == 2 else "twoshot"), n
+        assert car.select_algo(n, 8 << 10, bf, sync_us=20.0) in ("ll", "ll128"), n
+    for S in _sizes():
+        assert car.select_algo(2, S // 2, bf) != "twoshot"
+
+
+def test_selector_never_picks_an_inapplicable_two_shot():
+    import torch
+    bf = torch.bfloat16
+    assert car.algo_cost_us("twoshot", 8, (16 << 20) // 2 + 1, bf) is None
+    assert car.algo_cost_us("twoshot", 16, 16 * 4, bf) is None  # 8-byte segments
+    assert car.select_algo(8, (16 << 20) // 2 + 1, bf) == "oneshot"
+    assert car.select_algo(8, (16 << 20) // 2, bf) == "twoshot"
+    assert car.lib.ar_select_algo(1, 10, 0, 0.0) == -car.AR_ERR_ARG
+    assert car.lib.ar_select_algo(17, 10, 0, 0.0) == -car.AR_ERR_ARG
+    assert car.lib.ar_select_algo(8, 0, 0, 0.0) == -car.AR_ERR_ARG
+    assert car.lib.ar_select_algo(8, 10, 5, 0.0) == -car.AR_ERR_ARG
+    assert car.lib.ar_select_algo(8, 10, 0, -1.0) == -car.AR_ERR_ARG
+    assert car.lib.ar_select_algo(8, 10, 0, float("nan")) == -car.AR_ERR_ARG
+    assert car.lib.ar_algo_cost_us(4, 8, 10, 0, 0.0) < 0
