@@ -235,6 +235,9 @@ def sweep(args, torch, car, np, out_path):
                 flags = car.new_flags(n)
                 calls = [step_calls(car, b, flags) for b in sets]
                 full = [car.prepare_twoshot_rs(b.ins, b.segs, flags, outs=b.outs) for b in sets]
+                bc_one = [car.prepare_reduce_bcast(b.ins, b.outs, ME, ME + 1) for b in sets]
+                bc_all = [car.prepare_reduce_bcast(b.ins, b.outs) for b in sets]
+                push = [car.prepare_push([b.ins[ME]], [b.outs]) for b in sets]
                 for b in sets:
                     publish_peers(car, b, flags)
                 run_step(calls[0], 1)
@@ -248,7 +251,11 @@ def sweep(args, torch, car, np, out_path):
                          ("ll_pack", 2, acc.ll_pack("ll", S, 1)), ("ll_reduce", 3, acc.ll_reduce("ll", n, S)),
                          ("ll128_pack", 4, acc.ll_pack("ll128", S, 1)),
                          ("ll128_reduce", 5, acc.ll_reduce("ll128", n, S)),
+                         ("bcast", "bc_one", acc.reduce_bcast(n, S, 1)),
+                         ("bcast_full", "bc_all", acc.reduce_bcast(n, S, n)),
+                         ("push", "push", acc.push(S, n)),
                          ("twoshot_full", None, acc.twoshot(n, S, n))]
+                extra = {"bc_one": bc_one, "bc_all": bc_all, "push": push}
                 for name, ki, rw in kinds:
                     base = step
 
@@ -256,6 +263,8 @@ def sweep(args, torch, car, np, out_path):
                         for i in range(K):
                             if ki is None:
                                 full[i % nsets](base + i)
+                            elif isinstance(ki, str):
+                                extra[ki][i % nsets]()
                             elif name == "oneshot":
                                 calls[i % nsets][0]()
                             elif name.endswith("reduce"):
@@ -281,7 +290,7 @@ def sweep(args, torch, car, np, out_path):
                     elif name == "twoshot":
                         t_two[S] = us
                 car.raise_on_status(flags, "sweep")
-                del sets, calls, full, src
+                del sets, calls, full, src, extra, bc_one, bc_all, push
                 torch.cuda.empty_cache()
             # crossover: first size where two-shot (one rank's share) beats one-shot,
             # log-linear interpolation of the time difference between the bracketing sizes
@@ -304,7 +313,7 @@ def sweep(args, torch, car, np, out_path):
 
 SELECT_SIZES = [16 << 10, 32 << 10, 64 << 10, 128 << 10, 256 << 10, 512 << 10, 1 << 20, 3 << 19, 2 << 20,
                 3 << 20, 4 << 20, 6 << 20, 8 << 20, 12 << 20, 16 << 20, 32 << 20, 64 << 20]
-SELECT_ALGOS = ["oneshot", "twoshot", "ll", "ll128"]
+SELECT_ALGOS = ["oneshot", "twoshot", "ll", "ll128", "push", "bcast"]
 
 
 def select_table(args, torch, car, np, out_path):
@@ -323,7 +332,7 @@ def select_table(args, torch, car, np, out_path):
                 numel -= numel % (8 * n)  # whole 16-byte vectors in every segment
                 Sb = numel * 2
                 W1, W2 = car.ll_wire_bytes("ll", Sb), car.ll_wire_bytes("ll128", Sb)
-                fp = n * Sb + 3 * Sb + n * (W1 + W2)
+                fp = n * Sb + 3 * Sb + n * (W1 + W2) + (2 * n - 1) * Sb + n * Sb
                 nsets = max(2, int(np.ceil((1 << 30) / fp)))
                 gen.manual_seed(1000 * n + S.bit_length())
                 src = [torch.randn(numel, generator=gen, device="cuda").to(torch.bfloat16) for _ in range(n)]
@@ -336,7 +345,12 @@ def select_table(args, torch, car, np, out_path):
                     out = torch.empty(numel, dtype=torch.bfloat16, device="cuda")
                     w1 = [torch.empty(W1, dtype=torch.uint8, device="cuda") for _ in range(n)]
                     w2 = [torch.empty(W2, dtype=torch.uint8, device="cuda") for _ in range(n)]
-                    keep.append((ins, segs, out, w1, w2))
+                    # push: rank 0's slot in every rank's staging buffer, and rank 0's
+                    # staging buffer (slot 0 is its own push target)
+                    slots0 = [torch.empty(numel, dtype=torch.bfloat16, device="cuda") for _ in range(n)]
+                    mine = [slots0[0]] + [torch.empty(numel, dtype=torch.bfloat16, device="cuda") for _ in range(1, n)]
+                    bouts = [out] + [torch.empty(numel, dtype=torch.bfloat16, device="cuda") for _ in range(1, n)]
+                    keep.append((ins, segs, out, w1, w2, slots0, mine, bouts))
                     for r in range(1, n):
                         car.ar_twoshot_rs(ins, segs, flags, PEER_STEP, r0=r, r1=r + 1)
                     car.ar_ll_pack(ins[1:], w1[1:], "ll", PEER_STEP)
@@ -348,6 +362,10 @@ def select_table(args, torch, car, np, out_path):
                         pk = car.prepare_ll_pack([ins[0]], [w[0]], name)
                         rd = car.prepare_ll_reduce(w, out, flags, name)
                         calls[name].append(lambda s, pk=pk, rd=rd: (pk(s), rd(s)))
+                    ps, po = car.prepare_push([ins[0]], [slots0]), car.prepare_oneshot(mine, out)
+                    calls["push"].append(lambda s, ps=ps, po=po: (ps(), po()))
+                    bc = car.prepare_reduce_bcast(ins, bouts, 0, 1)
+                    calls["bcast"].append(lambda s, bc=bc: bc())
                 del src
                 torch.cuda.synchronize()
                 row = {"n": n, "bytes_per_rank": Sb}

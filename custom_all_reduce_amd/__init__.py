@@ -64,6 +64,8 @@ def _load(path: str = LIB_PATH):
     lib.ar_get_poll_timeout_ns.argtypes, lib.ar_get_poll_timeout_ns.restype = [], u64
     lib.ar_status_string.argtypes, lib.ar_status_string.restype = [i32], ctypes.c_char_p
     lib.ar_oneshot.argtypes, lib.ar_oneshot.restype = [P, i32, vp, sz, i32, vp], i32
+    lib.ar_reduce_bcast.argtypes, lib.ar_reduce_bcast.restype = [P, i32, P, sz, i32, i32, i32, vp], i32
+    lib.ar_push.argtypes, lib.ar_push.restype = [P, i32, P, i32, sz, i32, vp], i32
     lib.ar_twoshot_rs.argtypes, lib.ar_twoshot_rs.restype = [P, i32, P, sz, i32, i32, i32, vp, u32, P, vp], i32
     lib.ar_twoshot_ag.argtypes, lib.ar_twoshot_ag.restype = [P, i32, P, sz, i32, i32, i32, vp, u32, vp], i32
     lib.ar_ll_pack.argtypes, lib.ar_ll_pack.restype = [P, P, i32, sz, i32, i32, u32, vp], i32
@@ -130,7 +132,7 @@ def get_poll_timeout_ns() -> int:
     return int(_lib.ar_get_poll_timeout_ns())
 
 
-ALGOS = ("oneshot", "twoshot", "ll", "ll128")  # ar_algo values 0..3
+ALGOS = ("oneshot", "twoshot", "ll", "ll128", "push", "bcast")  # ar_algo values 0..5
 
 
 def _dtype_arg(dtype) -> int:
@@ -219,6 +221,37 @@ def prepare_oneshot(ins, out: torch.Tensor) -> Prepared:
     return Prepared(_lib.ar_oneshot, args, None, "ar_oneshot", (ins, out))
 
 
+def _same_shape(ts, ref, what):
+    for t in ts:
+        if t.dtype != ref.dtype or t.numel() != ref.numel():
+            raise ValueError(f"{what} must share dtype and numel")
+
+
+def prepare_reduce_bcast(ins, outs, r0: int = 0, r1=None) -> Prepared:
+    n = len(ins)
+    r1 = n if r1 is None else r1
+    ins = [_dev_tensor(t, "input") for t in ins]
+    outs = [_dev_tensor(t, "out") for t in outs]
+    if len(outs) != n:
+        raise ValueError("need one output per rank")
+    _same_shape(ins + outs, ins[0], "inputs and outputs")
+    args = [_ptr_array([t.data_ptr() for t in ins]), n, _ptr_array([t.data_ptr() for t in outs]), ins[0].numel(),
+            _dtype_code(ins[0]), r0, r1, None]
+    return Prepared(_lib.ar_reduce_bcast, args, None, "ar_reduce_bcast", (ins, outs))
+
+
+def prepare_push(srcs, dsts) -> Prepared:
+    """dsts[i] lists sender i's destinations (the same count for every sender)."""
+    srcs = [_dev_tensor(t, "src") for t in srcs]
+    if len(dsts) != len(srcs) or len({len(d) for d in dsts}) != 1:
+        raise ValueError("dsts must hold one equally long list per sender")
+    flat = [_dev_tensor(t, "dst") for row in dsts for t in row]
+    _same_shape(srcs + flat, srcs[0], "sources and destinations")
+    args = [_ptr_array([t.data_ptr() for t in srcs]), len(srcs), _ptr_array([t.data_ptr() for t in flat]),
+            len(dsts[0]), srcs[0].numel(), _dtype_code(srcs[0]), None]
+    return Prepared(_lib.ar_push, args, None, "ar_push", (srcs, flat))
+
+
 def prepare_twoshot_rs(ins, segs, flags, r0: int = 0, r1=None, outs=None) -> Prepared:
     n = len(ins)
     r1 = n if r1 is None else r1
@@ -272,6 +305,16 @@ def ar_oneshot(ins, out: torch.Tensor, stream=None):
     """out = sum of ins (fp32 accumulation in rank order, one rounding)."""
     prepare_oneshot(ins, out)(stream=stream)
     return out
+
+
+def ar_reduce_bcast(ins, outs, r0: int = 0, r1=None, stream=None):
+    """Ranks [r0, r1) reduce their 1/n of the vectors into every output."""
+    prepare_reduce_bcast(ins, outs, r0, r1)(None, stream)
+
+
+def ar_push(srcs, dsts, stream=None):
+    """Copy srcs[i] into every tensor of dsts[i]."""
+    prepare_push(srcs, dsts)(None, stream)
 
 
 def ar_twoshot_rs(ins, segs, flags, step: int, r0: int = 0, r1=None, outs=None, stream=None):

@@ -9,6 +9,9 @@ and every write, each byte once.  S = numel * element size (bytes per rank).
                           writes S/n (segment) + S (output)
   twoshot, all n ranks    n times the above
   twoshot RS only / AG only, per rank: reads S / S, writes S/n / S
+  reduce_bcast, one rank  reads S (its 1/n of n inputs)   writes S (1/n into n outputs)
+  reduce_bcast, all n     reads n*S               writes n*S
+  push, one sender        reads S                 writes ndst*S
   LL / LL128 pack, each   reads S                 writes W(S)
   LL / LL128 reduce       reads n*W(S)            writes S
 
@@ -47,6 +50,16 @@ def twoshot_rs(n: int, S: int, ranks: int):
 
 def twoshot_ag(n: int, S: int, ranks: int):
     return ranks * S, ranks * S
+
+
+def reduce_bcast(n: int, S: int, ranks: int):
+    """ranks = how many emulated ranks' shares the launch computes; each
+    share reads its 1/n of every input and writes it into every output."""
+    return ranks * S, ranks * S
+
+
+def push(S: int, ndst: int, count: int = 1):
+    return count * S, count * ndst * S
 
 
 def ll_pack(proto: str, S: int, count: int = 1):

@@ -22,19 +22,20 @@ std::mutex g_info_mu;
 DeviceInfo g_info[kMaxDevices];
 bool g_info_ok[kMaxDevices] = {};
 
-// Largest message accepted per rank: the kernels index 16-byte vectors with
-// 32-bit integers.
-constexpr size_t kMaxBytes = size_t(1) << 36;
+// Largest message accepted per rank (32 GiB): the kernels index 16-byte
+// vectors with 32-bit integers and keep headroom for a grid's last workgroup.
+constexpr size_t kMaxBytes = size_t(1) << 35;
 constexpr size_t kStatusBytes = size_t(kStatusWords) * 4;
 
 size_t elem_bytes(int dtype) { return dtype == AR_F32 ? 4 : 2; }
 
 #include "select_table.inc"
 
-// Semaphore synchronisations per call charged by the cost model: start and
-// end for the one-shot, two more around the two-shot's barrier; none for
-// LL / LL128, whose receivers learn of arrival from the flags in the lines.
-constexpr double kSemaphoreSyncs[4] = {2.0, 4.0, 0.0, 0.0};
+// Semaphore synchronisations per call charged by the cost model, in ar_algo
+// order: start and end for the one-shot, the push and the reduce-broadcast;
+// two more around the two-shot's barrier; none for LL / LL128, whose
+// receivers learn of arrival from the flags in the lines.
+constexpr double kSemaphoreSyncs[kSelNumAlgos] = {2.0, 4.0, 0.0, 0.0, 2.0, 2.0};
 
 // Measured one-GPU time of algo at `bytes` per rank: piecewise linear in the
 // size between grid points, flat below the first (launch-bound), and
@@ -218,6 +219,46 @@ int ar_oneshot(const void* const* in, int n, void* out, size_t numel, int dtype,
     return hip_status(launch_oneshot(in, n, out, numel, dtype, static_cast<hipStream_t>(stream)));
 }
 
+int ar_reduce_bcast(const void* const* in, int n, void* const* out, size_t numel, int dtype, int r0, int r1,
+                    void* stream) {
+    if (!in || !out || !ranks_ok(n) || !dtype_ok(dtype) || numel == 0) return AR_ERR_ARG;
+    if (r0 < 0 || r1 > n || r0 >= r1) return AR_ERR_ARG;
+    const size_t es = elem_bytes(dtype);
+    if (numel > kMaxBytes / es) return AR_ERR_ARG;
+    for (int i = 0; i < n; ++i) {
+        if (!in[i] || !out[i]) return AR_ERR_ARG;
+        if (!aligned16(in[i]) || !aligned16(out[i])) return AR_ERR_ALIGN;
+    }
+    const size_t S = numel * es;
+    std::vector<Span> v;
+    for (int i = 0; i < n; ++i) v.push_back(span(out[i], S, true));
+    for (int i = 0; i < n; ++i) v.push_back(span(in[i], S, false));
+    if (!spans_ok(v)) return AR_ERR_ALIAS;
+    return hip_status(launch_reduce_bcast(in, n, out, numel, dtype, r0, r1, static_cast<hipStream_t>(stream)));
+}
+
+int ar_push(const void* const* src, int nsrc, void* const* dst, int ndst, size_t numel, int dtype, void* stream) {
+    if (!src || !dst || nsrc < 1 || nsrc > AR_MAX_RANKS || !ranks_ok(ndst) || !dtype_ok(dtype) || numel == 0)
+        return AR_ERR_ARG;
+    const size_t es = elem_bytes(dtype);
+    if (numel > kMaxBytes / es) return AR_ERR_ARG;
+    const size_t nd = size_t(nsrc) * size_t(ndst);
+    for (int i = 0; i < nsrc; ++i) {
+        if (!src[i]) return AR_ERR_ARG;
+        if (!aligned16(src[i])) return AR_ERR_ALIGN;
+    }
+    for (size_t j = 0; j < nd; ++j) {
+        if (!dst[j]) return AR_ERR_ARG;
+        if (!aligned16(dst[j])) return AR_ERR_ALIGN;
+    }
+    const size_t S = numel * es;
+    std::vector<Span> v;
+    for (size_t j = 0; j < nd; ++j) v.push_back(span(dst[j], S, true));
+    for (int i = 0; i < nsrc; ++i) v.push_back(span(src[i], S, false));
+    if (!spans_ok(v)) return AR_ERR_ALIAS;
+    return hip_status(launch_push(src, nsrc, dst, ndst, S, static_cast<hipStream_t>(stream)));
+}
+
 int ar_twoshot_rs(const void* const* in, int n, void* const* seg, size_t numel, int dtype, int r0, int r1,
                   uint32_t* flags, uint32_t step, void* const* out, void* stream) {
     if (!in) return AR_ERR_ARG;
@@ -270,7 +311,7 @@ int ar_ll128_reduce_unpack(const void* const* wire, int n, void* out, size_t num
 }
 
 double ar_algo_cost_us(int algo, int n, size_t numel, int dtype, double sync_us) {
-    if (algo < AR_ALGO_ONESHOT || algo > AR_ALGO_LL128 || !ranks_ok(n) || !dtype_ok(dtype) || numel == 0 ||
+    if (algo < AR_ALGO_ONESHOT || algo >= kSelNumAlgos || !ranks_ok(n) || !dtype_ok(dtype) || numel == 0 ||
         !(sync_us >= 0.0))
         return -1.0;
     const size_t es = elem_bytes(dtype);
@@ -282,7 +323,7 @@ int ar_select_algo(int n, size_t numel, int dtype, double sync_us) {
     if (!ranks_ok(n) || !dtype_ok(dtype) || numel == 0 || !(sync_us >= 0.0)) return -AR_ERR_ARG;
     int best = AR_ALGO_ONESHOT;
     double best_us = ar_algo_cost_us(best, n, numel, dtype, sync_us);
-    for (int a = AR_ALGO_TWOSHOT; a <= AR_ALGO_LL128; ++a) {
+    for (int a = AR_ALGO_TWOSHOT; a < kSelNumAlgos; ++a) {
         const double t = ar_algo_cost_us(a, n, numel, dtype, sync_us);
         if (t >= 0.0 && t < best_us) best = a, best_us = t;
     }

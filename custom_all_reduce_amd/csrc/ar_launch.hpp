@@ -30,6 +30,12 @@ hipError_t device_info(DeviceInfo* out);
 hipError_t launch_oneshot(const void* const* in, int n, void* out, size_t numel, int dtype,
                           hipStream_t s);
 
+hipError_t launch_reduce_bcast(const void* const* in, int n, void* const* out, size_t numel, int dtype, int r0,
+                               int r1, hipStream_t s);
+
+hipError_t launch_push(const void* const* src, int nsrc, void* const* dst, int ndst, size_t nbytes,
+                       hipStream_t s);
+
 struct TwoShotRequest {
     const void* const* in;   // may be null when !do_rs
     void* const* seg;

@@ -25,7 +25,8 @@
  *  - Every data pointer is device memory of the current HIP device, 16-byte
  *    aligned ([CAR] step 1: 128-bit accesses).  All memory is caller-owned;
  *    the library never allocates on these paths.
- *  - numel counts elements per rank; dtype is an ar_dtype.  Sums are taken in
+ *  - numel counts elements per rank, at most 2^35 bytes (32 GiB) per rank
+ *    (else AR_ERR_ARG); dtype is an ar_dtype.  Sums are taken in
  *    fp32, rank 0 first, starting from +0.0, and rounded once to the output
  *    type with round-to-nearest-even ([CAR] step 4).  Results are therefore
  *    identical bit for bit on every rank and on every call.
@@ -109,6 +110,35 @@ const char* ar_status_string(int status);
  * Errors: AR_ERR_ARG, AR_ERR_ALIGN, AR_ERR_ALIAS, AR_ERR_HIP. */
 int ar_oneshot(const void* const* in, int n, void* out, size_t numel, int dtype, void* stream);
 
+/* Reduce with a broadcast store: the kBroadcast store path of [CAR] step 5
+ * -- each result written to every rank's output, not only the local one --
+ * applied to one rank's share of the elements, which makes a two-shot whose
+ * all-gather the producer pushes ([NCCL] 算法, two-shot), with no barrier
+ * between the phases.  With V = floor(numel / (16 / element size)) whole
+ * 16-byte vectors, emulated rank r owns vectors [floor(r*V/n),
+ * floor((r+1)*V/n)) and rank n-1 also the partial last vector.  Every rank r
+ * in [r0, r1) sums its vectors of all n inputs exactly as ar_oneshot and
+ * stores the results at the same offsets of out[0..n).  [0, n) is the whole
+ * all-reduce in one launch (every out[j] = ar_oneshot's result); [me, me+1)
+ * is one GPU's share: reads S, writes S, S = numel * element size.
+ *  in, out : n device pointers each, numel elements of dtype; outputs must
+ *            not overlap each other or any input.
+ * Any numel >= 1; bytes of out outside the owned range are not touched.
+ * Errors: AR_ERR_ARG, AR_ERR_ALIGN, AR_ERR_ALIAS, AR_ERR_HIP. */
+int ar_reduce_bcast(const void* const* in, int n, void* const* out, size_t numel, int dtype, int r0, int r1,
+                    void* stream);
+
+/* Push copy for the one-shot push of [CAR] 实现: sender i copies its message
+ * src[i] (numel elements of dtype) into dst[i*ndst + j] for j < ndst -- its
+ * slot in every rank's staging buffer -- after which each rank reduces its
+ * own staging slots with ar_oneshot, reading only local memory.
+ *  src : nsrc device pointers, 1 <= nsrc <= AR_MAX_RANKS;
+ *  dst : nsrc * ndst device pointers, 2 <= ndst <= AR_MAX_RANKS, none
+ *        overlapping another destination or a source.
+ * A sender reads S and writes ndst * S.  Any numel >= 1.
+ * Errors: AR_ERR_ARG, AR_ERR_ALIGN, AR_ERR_ALIAS, AR_ERR_HIP. */
+int ar_push(const void* const* src, int nsrc, void* const* dst, int ndst, size_t numel, int dtype, void* stream);
+
 /* Two-shot phase 1, reduce-scatter ([NCCL] 算法, two-shot; [MGPU] 集合通信),
  * optionally fused with the flag barrier and phase 2 in the same launch.
  * With m = numel / n, emulated rank r in [r0, r1) sums segment r of every
@@ -174,20 +204,31 @@ int ar_ll128_reduce_unpack(const void* const* wire, int n, void* out, size_t num
  * is t_share + k * sync_us, where
  *  - t_share is the time of one GPU's share measured on MI355X with this
  *    library's kernels (cold HBM, graph-replayed; one-shot; one rank's fused
- *    two-shot; one rank's LL / LL128 pack plus the receiver), tabulated for
+ *    two-shot; one rank's LL / LL128 pack plus the receiver; one rank's push
+ *    plus its one-shot over its staging slots; one rank's reduce-broadcast
+ *    share), tabulated for
  *    n = 2..16 over 16 KiB..64 MiB per rank, interpolated linearly in the
  *    size, flat below the grid and extended with the last slope above it;
  *  - k is the number of cross-GPU semaphore synchronisations per call, the
  *    alpha terms of the [NCCL] 算法 alpha-beta model (2 for the one-shot, 4
  *    for the two-shot; 协议 names the semaphore as alpha's main source),
- *    and 0 for LL / LL128, whose flags travel with the data ([NCCL] 协议);
+ *    2 for the push and the reduce-broadcast (start and end, as the one-shot;
+ *    the broadcast has no barrier between its phases), and 0 for LL / LL128,
+ *    whose flags travel with the data ([NCCL] 协议);
  *  - sync_us >= 0 is the cost of one such synchronisation on the caller's
  *    interconnect (0 when the ranks share one GPU).
  * ar_algo_cost_us returns that time in microseconds, or a negative value for
  * bad arguments or a two-shot the size cannot split into n whole 16-byte
  * segments.  ar_select_algo returns the ar_algo of least modelled time (the
  * lower value on a tie), or -AR_ERR_ARG for bad arguments. */
-typedef enum { AR_ALGO_ONESHOT = 0, AR_ALGO_TWOSHOT = 1, AR_ALGO_LL = 2, AR_ALGO_LL128 = 3 } ar_algo;
+typedef enum {
+    AR_ALGO_ONESHOT = 0, /* ar_oneshot */
+    AR_ALGO_TWOSHOT = 1, /* ar_twoshot_rs with out (fused) */
+    AR_ALGO_LL = 2,      /* ar_ll_pack + ar_ll_reduce_unpack */
+    AR_ALGO_LL128 = 3,   /* ar_ll_pack + ar_ll128_reduce_unpack */
+    AR_ALGO_PUSH = 4,    /* ar_push into the staging slots + ar_oneshot over them */
+    AR_ALGO_BCAST = 5    /* ar_reduce_bcast */
+} ar_algo;
 double ar_algo_cost_us(int algo, int n, size_t numel, int dtype, double sync_us);
 int ar_select_algo(int n, size_t numel, int dtype, double sync_us);
 

@@ -192,7 +192,8 @@ def test_selector_cost_model_terms():
     import torch
     bf = torch.bfloat16
     # sync terms: 2 per call for the one-shot, 4 for the two-shot, none for LL / LL128
-    for a, k in zip(car.ALGOS, (2, 4, 0, 0)):
+    assert len(car.ALGOS) == 6
+    for a, k in zip(car.ALGOS, (2, 4, 0, 0, 2, 2)):
         assert car.algo_cost_us(a, 8, 1 << 20, bf, 10.0) == pytest.approx(car.algo_cost_us(a, 8, 1 << 20, bf, 0.0) + 10 * k)
     # flat below the grid, increasing in size above it, linear beyond the last point
     for a in car.ALGOS:
@@ -204,20 +205,25 @@ def test_selector_cost_model_terms():
 
 
 def test_selector_regimes():
-    """What the measured table must show: one GPU with no cross-GPU sync cost
-    takes the one-shot for small messages and (n >= 4) the two-shot for large
-    ones; two ranks never take the two-shot ([NCCL] 练习 2: at n = 2 both move
-    S, and the one-shot saves a synchronisation); a large sync cost moves small
-    messages to a flag protocol."""
+    """What the measured table must show.  With no cross-GPU sync cost (one
+    GPU): small messages take the one-shot or the reduce-broadcast (both one
+    launch-bound pass), large ones the reduce-broadcast, which moves the
+    fewest bytes (S read, S written per rank) with no barrier; two ranks never
+    take the two-shot ([NCCL] 练习 2: at n = 2 both move S, and the one-shot
+    saves a synchronisation); the push never wins (it is a copy plus the
+    one-shot, with the one-shot's synchronisations).  A large sync cost moves
+    small messages to a flag protocol."""
     import torch
     bf = torch.bfloat16
     for n in range(2, 17):
-        assert car.select_algo(n, 8 << 10, bf) == "oneshot"
+        assert car.select_algo(n, 8 << 10, bf) in ("oneshot", "bcast"), n
         big = (64 << 20) // 2
-        big -= big % (8 * n)  # n whole 16-byte segments
-        if n != 3:  # at n = 3 the two sides move 4S and 3S bytes of HBM: close
-            assert car.select_algo(n, big, bf) == ("oneshot" if n == 2 else "twoshot"), n
+        big -= big % (8 * n)
+        assert car.select_algo(n, big, bf) == "bcast", n
         assert car.select_algo(n, 8 << 10, bf, sync_us=20.0) in ("ll", "ll128"), n
+        for S in _sizes():
+            for sync in (0.0, 1.5, 25.0):
+                assert car.select_algo(n, S // 2, bf, sync) != "push"
     for S in _sizes():
         assert car.select_algo(2, S // 2, bf) != "twoshot"
 
@@ -227,12 +233,14 @@ def test_selector_never_picks_an_inapplicable_two_shot():
     bf = torch.bfloat16
     assert car.algo_cost_us("twoshot", 8, (16 << 20) // 2 + 1, bf) is None
     assert car.algo_cost_us("twoshot", 16, 16 * 4, bf) is None  # 8-byte segments
-    assert car.select_algo(8, (16 << 20) // 2 + 1, bf) == "oneshot"
-    assert car.select_algo(8, (16 << 20) // 2, bf) == "twoshot"
+    assert car.algo_cost_us("twoshot", 8, (16 << 20) // 2, bf) is not None
+    for sync in (0.0, 0.5, 3.0):  # wherever the two-shot would be cheapest, it must not be chosen
+        assert car.select_algo(8, (16 << 20) // 2 + 1, bf, sync) != "twoshot"
     assert car.lib.ar_select_algo(1, 10, 0, 0.0) == -car.AR_ERR_ARG
     assert car.lib.ar_select_algo(17, 10, 0, 0.0) == -car.AR_ERR_ARG
     assert car.lib.ar_select_algo(8, 0, 0, 0.0) == -car.AR_ERR_ARG
     assert car.lib.ar_select_algo(8, 10, 5, 0.0) == -car.AR_ERR_ARG
     assert car.lib.ar_select_algo(8, 10, 0, -1.0) == -car.AR_ERR_ARG
     assert car.lib.ar_select_algo(8, 10, 0, float("nan")) == -car.AR_ERR_ARG
-    assert car.lib.ar_algo_cost_us(4, 8, 10, 0, 0.0) < 0
+    assert car.lib.ar_algo_cost_us(6, 8, 10, 0, 0.0) < 0
+    assert car.lib.ar_algo_cost_us(-1, 8, 10, 0, 0.0) < 0

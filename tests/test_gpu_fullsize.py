@@ -72,6 +72,21 @@ def test_n16_64MiB_per_rank_all_paths_sampled(dt):
             car.raise_on_status(flags)
             assert np.array_equal(bits(out)[idx], want), proto
             del wires
+
+        # reduce-broadcast, rank 0's share and then the remaining ranks
+        bouts = [torch.empty(numel, dtype=tdt, device="cuda") for _ in range(n)]
+        car.ar_reduce_bcast(ins, bouts, 0, 1)
+        car.ar_reduce_bcast(ins, bouts, 1, n)
+        torch.cuda.synchronize()
+        for j in (0, 7, n - 1):
+            assert np.array_equal(bits(bouts[j])[idx], want), f"reduce-broadcast out[{j}]"
+        # push of rank 5's message to every rank, sampled bytes equal
+        car.ar_push([ins[5]], [bouts])
+        torch.cuda.synchronize()
+        src5 = bits(ins[5])[idx]
+        for j in (0, n - 1):
+            assert np.array_equal(bits(bouts[j])[idx], src5), f"push dst {j}"
+        del bouts
     finally:
         car.set_poll_timeout_ns(0)
 

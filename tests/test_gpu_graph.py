@@ -32,6 +32,10 @@ def test_graph_replays_of_every_path():
     w_128 = [torch.empty(car.ll_wire_bytes("ll128", S), dtype=torch.uint8, device="cuda") for _ in range(n)]
     out_ll = torch.empty(numel, dtype=tdt, device="cuda")
     out_128 = torch.empty(numel, dtype=tdt, device="cuda")
+    bc_full = [torch.empty(numel, dtype=tdt, device="cuda") for _ in range(n)]
+    bc_share = [torch.empty(numel, dtype=tdt, device="cuda") for _ in range(n)]
+    staging = [[torch.empty(numel, dtype=tdt, device="cuda") for _ in range(n)] for _ in range(n)]
+    out_push = torch.empty(numel, dtype=tdt, device="cuda")
     torch.cuda.synchronize()
 
     g = torch.cuda.CUDAGraph()
@@ -49,6 +53,12 @@ def test_graph_replays_of_every_path():
         car.ar_ll_reduce_unpack(w_ll, out_ll, 2, flags)
         car.ar_ll_pack(ins, w_128, "ll128", 2)
         car.ar_ll128_reduce_unpack(w_128, out_128, 2, flags)
+        car.ar_reduce_bcast(ins, bc_full)
+        for r in range(n):  # every rank's share, one launch each
+            car.ar_reduce_bcast(ins, bc_share, r, r + 1)
+        # one-shot push: sender i into slot i of every rank's staging buffer
+        car.ar_push(ins, [[staging[j][i] for j in range(n)] for i in range(n)])
+        car.ar_oneshot(staging[3], out_push)
     torch.cuda.synchronize()
 
     for rep in range(6):
@@ -59,6 +69,7 @@ def test_graph_replays_of_every_path():
         g.replay()
         torch.cuda.synchronize()
         assert car.read_status(flags)[0] == 0, f"replay {rep}"
-        for name, t in [("oneshot", out_one), ("share", out_share), ("ll", out_ll), ("ll128", out_128)] + \
-                       [(f"full{r}", outs_full[r]) for r in range(n)]:
+        for name, t in [("oneshot", out_one), ("share", out_share), ("ll", out_ll), ("ll128", out_128),
+                        ("push", out_push)] + [(f"full{r}", outs_full[r]) for r in range(n)] + \
+                       [(f"bcast{r}", bc_full[r]) for r in range(n)] + [(f"bshare{r}", bc_share[r]) for r in range(n)]:
             assert np.array_equal(bits(t), wants[k]), f"replay {rep}: {name}"
