@@ -238,6 +238,10 @@ def sweep(args, torch, car, np, out_path):
                 bc_one = [car.prepare_reduce_bcast(b.ins, b.outs, ME, ME + 1) for b in sets]
                 bc_all = [car.prepare_reduce_bcast(b.ins, b.outs) for b in sets]
                 push = [car.prepare_push([b.ins[ME]], [b.outs]) for b in sets]
+                stage = [car.prepare_push([b.ins[ME]], [[b.out]]) for b in sets]
+                ts_auto = [car.prepare_twoshot_rs(b.ins, b.segs, flags, r0=ME, r1=ME + 1,
+                                                  outs=[b.outs[r] if r == ME else None for r in range(n)])
+                           for b in sets]
                 for b in sets:
                     publish_peers(car, b, flags)
                 run_step(calls[0], 1)
@@ -254,8 +258,10 @@ def sweep(args, torch, car, np, out_path):
                          ("bcast", "bc_one", acc.reduce_bcast(n, S, 1)),
                          ("bcast_full", "bc_all", acc.reduce_bcast(n, S, n)),
                          ("push", "push", acc.push(S, n)),
+                         ("stage", "stage", acc.push(S, 1)),
+                         ("twoshot_auto", "ts_auto", acc.twoshot(n, S, 1)),
                          ("twoshot_full", None, acc.twoshot(n, S, n))]
-                extra = {"bc_one": bc_one, "bc_all": bc_all, "push": push}
+                extra = {"bc_one": bc_one, "bc_all": bc_all, "push": push, "stage": stage, "ts_auto": ts_auto}
                 for name, ki, rw in kinds:
                     base = step
 
@@ -263,6 +269,8 @@ def sweep(args, torch, car, np, out_path):
                         for i in range(K):
                             if ki is None:
                                 full[i % nsets](base + i)
+                            elif ki == "ts_auto":
+                                extra[ki][i % nsets](0)  # step id from the flag region
                             elif isinstance(ki, str):
                                 extra[ki][i % nsets]()
                             elif name == "oneshot":
@@ -290,7 +298,7 @@ def sweep(args, torch, car, np, out_path):
                     elif name == "twoshot":
                         t_two[S] = us
                 car.raise_on_status(flags, "sweep")
-                del sets, calls, full, src, extra, bc_one, bc_all, push
+                del sets, calls, full, src, extra, bc_one, bc_all, push, stage, ts_auto
                 torch.cuda.empty_cache()
             # crossover: first size where two-shot (one rank's share) beats one-shot,
             # log-linear interpolation of the time difference between the bracketing sizes

@@ -36,6 +36,7 @@ AR_F32, AR_BF16 = 0, 1
 AR_PROTO_LL, AR_PROTO_LL128 = 0, 1
 AR_MAX_RANKS = 16
 AR_SLOTS_PER_RANK = 1024
+AR_EPOCH_COPIES = 4096
 PHASE_TWOSHOT_AG, PHASE_LL, PHASE_LL128 = 1, 2, 3
 
 _DTYPES = {torch.float32: AR_F32, torch.bfloat16: AR_BF16}

@@ -95,7 +95,8 @@ size_t wire_bytes(int proto, size_t nbytes) {
 // Shared checks of the two-shot entry points.
 int twoshot_check(const void* const* in, const void* const* seg, const void* const* out, int n,
                   size_t numel, int dtype, int r0, int r1, const uint32_t* flags, uint32_t step) {
-    if (!ranks_ok(n) || !dtype_ok(dtype) || numel == 0 || !seg || !flags || step == 0) return AR_ERR_ARG;
+    (void)step;  // 0 = the step id kept in the flag region (auto)
+    if (!ranks_ok(n) || !dtype_ok(dtype) || numel == 0 || !seg || !flags) return AR_ERR_ARG;
     if (r0 < 0 || r1 > n || r0 >= r1) return AR_ERR_ARG;
     const size_t es = elem_bytes(dtype);
     if (numel > kMaxBytes / es) return AR_ERR_ARG;
@@ -180,7 +181,7 @@ extern "C" {
 
 size_t ar_flag_bytes(int n) {
     if (!ranks_ok(n)) return 0;
-    return (size_t(kStatusWords) + size_t(n) * kSlotsPerRank) * 4;
+    return (size_t(kStatusWords) + size_t(n) * (kSlotsPerRank + kEpochCopies)) * 4;
 }
 
 size_t ar_ll_wire_bytes(int proto, size_t nbytes) { return wire_bytes(proto, nbytes); }
@@ -238,7 +239,8 @@ int ar_reduce_bcast(const void* const* in, int n, void* const* out, size_t numel
 }
 
 int ar_push(const void* const* src, int nsrc, void* const* dst, int ndst, size_t numel, int dtype, void* stream) {
-    if (!src || !dst || nsrc < 1 || nsrc > AR_MAX_RANKS || !ranks_ok(ndst) || !dtype_ok(dtype) || numel == 0)
+    if (!src || !dst || nsrc < 1 || nsrc > AR_MAX_RANKS || ndst < 1 || ndst > AR_MAX_RANKS || !dtype_ok(dtype) ||
+        numel == 0)
         return AR_ERR_ARG;
     const size_t es = elem_bytes(dtype);
     if (numel > kMaxBytes / es) return AR_ERR_ARG;

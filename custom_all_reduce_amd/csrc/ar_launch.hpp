@@ -11,10 +11,13 @@
 
 namespace ar {
 
-// Flag region layout (32-bit words): word 0 status, word 1 detail, words
-// 2..31 unused (one 128-byte line), then kSlotsPerRank arrival slots per rank.
+// Flag region layout for n ranks (32-bit words): word 0 status, word 1
+// detail, words 2..31 unused (one 128-byte line), then kSlotsPerRank arrival
+// slots per rank, then kEpochCopies epoch copies per rank (one per wavefront
+// of an auto-step two-shot launch).
 constexpr int kMaxRanks = 16;
 constexpr int kSlotsPerRank = 1024;
+constexpr int kEpochCopies = 4096;
 constexpr int kStatusWords = 32;
 constexpr uint32_t kTimeoutCode = 5;  // AR_ERR_TIMEOUT
 

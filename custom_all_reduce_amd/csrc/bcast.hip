@@ -11,7 +11,8 @@
 //
 // push: a rank's message copied into n destinations (one slot of every
 // rank's staging buffer); the receivers then reduce their staging slots with
-// the one-shot.  One sender reads S and writes n * S.
+// the one-shot.  One sender reads S and writes n * S.  With one destination
+// it is the staging copy of a caller's tensor into its registered buffer.
 //
 // Both kernels keep one 16-byte vector per lane (the shape measured fastest
 // for the one-shot) and stream every access past the caches.
@@ -123,10 +124,12 @@ hipError_t launch_reduce_bcast(const void* const* in, int n, void* const* out, s
 hipError_t launch_push(const void* const* src, int nsrc, void* const* dst, int ndst, size_t nbytes,
                        hipStream_t s) {
     for (int i = 0; i < nsrc; ++i) {
-        const hipError_t e = dispatch_ranks(ndst, [&](auto nd) {
-            constexpr int ND = decltype(nd)::value;
-            return launch_push_t<ND>(src[i], dst + size_t(i) * ndst, nbytes, s);
-        });
+        // one destination: the staging copy into a registered buffer
+        const hipError_t e = ndst == 1 ? launch_push_t<1>(src[i], dst + i, nbytes, s)
+                                       : dispatch_ranks(ndst, [&](auto nd) {
+                                             constexpr int ND = decltype(nd)::value;
+                                             return launch_push_t<ND>(src[i], dst + size_t(i) * ndst, nbytes, s);
+                                         });
         if (e != hipSuccess) return e;
     }
     return hipSuccess;

@@ -31,6 +31,17 @@
 // phase 1 before it polls, so every slot a poller needs is eventually written
 // while nothing else occupies the CUs; if something does, the bounded wait
 // turns the stall into a reported timeout instead of a hang.
+//
+// Step ids.  An explicit step id comes with the call.  With step 0 (auto) it
+// comes from the flag region instead, so a launch captured once into a graph
+// gets a fresh id on every replay.  Every wavefront keeps its own copy of
+// each rank's epoch (the id of the rank's last reduce-scatter) after the
+// arrival slots; auto launches always use the same grid, so all copies move
+// in step.  A wavefront loads its copies when it starts (the loads overlap
+// its first reduce-scatter loads) and, if the launch reduces, stores epoch +
+// 1 back as soon as its reduce-scatter is done.  No other wavefront touches
+// those copies, so there is no counter, atomic or barrier.  A split
+// all-gather uses the current epoch, the id of the reduce-scatter before it.
 #include <mutex>
 
 #include "ar_device.hpp"
@@ -53,13 +64,14 @@ struct TwoShotParams {
     uint32_t tile;
     uint32_t ktiles;
     uint32_t step;
+    int auto_step;
     int r0, r1;
     int do_rs, do_ag;
 };
 
 template <typename T, int NR, int U>
-__device__ __forceinline__ void reduce_scatter_phase(const TwoShotParams& p, uint32_t wave,
-                                                     uint32_t nwaves, int lane) {
+__device__ __forceinline__ void reduce_scatter_phase(const TwoShotParams& p, uint32_t step_lane,
+                                                     uint32_t wave, uint32_t nwaves, int lane) {
     const uint32_t R = uint32_t(p.r1 - p.r0);
     const uint32_t items = R * p.ktiles;
     if (wave >= items) return;
@@ -115,15 +127,18 @@ __device__ __forceinline__ void reduce_scatter_phase(const TwoShotParams& p, uin
     }
     // Publish: wait until this wavefront's coherent segment stores have
     // completed, then one slot store per produced tile (lane k stores the
-    // slot of item k).
+    // slot of item k; the loop runs with every lane active so the step id
+    // of the item's rank can be read from lane r - r0).
     wait_stores();
     __builtin_amdgcn_wave_barrier();
     uint32_t* slots = p.flags + kStatusWords;
-    for (uint32_t k = uint32_t(lane); k < my_items; k += kWave) {
-        const uint32_t it = wave + k * nwaves;
+    for (uint32_t kb = 0; kb < my_items; kb += kWave) {
+        const uint32_t k = kb + uint32_t(lane);
+        const uint32_t it = wave + (k < my_items ? k : 0u) * nwaves;
         const uint32_t r = uint32_t(p.r0) + it / p.ktiles;
         const uint32_t t = it % p.ktiles;
-        flag_store_relaxed(slots + r * kSlotsPerRank + t, p.step);
+        const uint32_t st = __shfl(step_lane, int(r) - p.r0);
+        if (k < my_items) flag_store_relaxed(slots + r * kSlotsPerRank + t, st);
     }
 }
 
@@ -134,8 +149,8 @@ __device__ __forceinline__ uint32_t ag_source(uint32_t jj, uint32_t ro, bool ski
     return (skip_own && jj >= ro) ? jj + 1 : jj;
 }
 
-__device__ __forceinline__ void all_gather_phase(const TwoShotParams& p, int n, uint32_t wave,
-                                                 uint32_t nwaves, int lane) {
+__device__ __forceinline__ void all_gather_phase(const TwoShotParams& p, uint32_t step_lane, int n,
+                                                 uint32_t wave, uint32_t nwaves, int lane) {
     const uint32_t R = uint32_t(p.r1 - p.r0);
     const bool skip_own = p.do_rs != 0;
     const uint32_t per_out = uint32_t(skip_own ? n - 1 : n) * p.ktiles;
@@ -148,10 +163,13 @@ __device__ __forceinline__ void all_gather_phase(const TwoShotParams& p, int n, 
     for (uint32_t kb = 0; kb < my_items; kb += kWave) {
         const uint32_t k = kb + uint32_t(lane);
         const bool need = k < my_items;
+        // every lane active here: the output rank's step id is read from
+        // lane ro - r0
+        const uint32_t it = wave + (need ? k : 0u) * nwaves;
+        const uint32_t ro = uint32_t(p.r0) + it / per_out;
+        const uint32_t want = __shfl(step_lane, int(ro) - p.r0);
         uint32_t j = 0, t = 0;
         if (need) {
-            const uint32_t it = wave + k * nwaves;
-            const uint32_t ro = uint32_t(p.r0) + it / per_out;
             const uint32_t rem = it % per_out;
             j = ag_source(rem / p.ktiles, ro, skip_own);
             t = rem % p.ktiles;
@@ -159,7 +177,7 @@ __device__ __forceinline__ void all_gather_phase(const TwoShotParams& p, int n, 
         const uint32_t* slot = slots + j * kSlotsPerRank + t;
         const uint64_t t0 = now_ticks();
         while (true) {
-            const bool ok = !need || flag_load_relaxed(slot) >= p.step;
+            const bool ok = !need || flag_load_relaxed(slot) >= want;
             const uint64_t missing = ~wave_ballot(ok) & wave_exec();
             if (missing == 0) break;
             if (now_ticks() - t0 > p.timeout_ticks) {
@@ -207,8 +225,18 @@ __global__ __launch_bounds__(kBlock) void twoshot_kernel(TwoShotParams p) {
     // the wavefront index, made explicitly uniform so item arithmetic is scalar
     const uint32_t wave = __builtin_amdgcn_readfirstlane(blockIdx.x * kWavesPerBlock + threadIdx.x / kWave);
     const uint32_t nwaves = gridDim.x * kWavesPerBlock;
-    if (p.do_rs) reduce_scatter_phase<T, NR, U>(p, wave, nwaves, lane);
-    if (p.do_ag) all_gather_phase(p, NR, wave, nwaves, lane);
+    // Lane l < r1 - r0 holds the step id of rank r0 + l (this wavefront's
+    // epoch copy in auto mode).
+    const uint32_t R = uint32_t(p.r1 - p.r0);
+    uint32_t* epoch = p.flags + kStatusWords + NR * kSlotsPerRank + size_t(p.r0) * kEpochCopies + wave;
+    uint32_t step_lane = p.step;
+    if (p.auto_step && uint32_t(lane) < R)
+        step_lane = flag_load_relaxed(epoch + size_t(lane) * kEpochCopies) + (p.do_rs ? 1u : 0u);
+    if (p.do_rs) {
+        reduce_scatter_phase<T, NR, U>(p, step_lane, wave, nwaves, lane);
+        if (p.auto_step && uint32_t(lane) < R) flag_store_relaxed(epoch + size_t(lane) * kEpochCopies, step_lane);
+    }
+    if (p.do_ag) all_gather_phase(p, step_lane, NR, wave, nwaves, lane);
 }
 
 template <typename T, int NR>
@@ -236,6 +264,7 @@ hipError_t launch_t(const TwoShotRequest& rq, hipStream_t s) {
     p.flags = rq.flags;
     p.timeout_ticks = rq.timeout_ticks;
     p.step = rq.step;
+    p.auto_step = rq.step == 0;
     p.r0 = rq.r0;
     p.r1 = rq.r1;
     p.do_rs = rq.do_rs;
@@ -243,6 +272,16 @@ hipError_t launch_t(const TwoShotRequest& rq, hipStream_t s) {
 
     auto kern = twoshot_kernel<T, NR, U>;
     const uint32_t R = uint32_t(rq.r1 - rq.r0);
+    if (p.auto_step) {
+        // every auto launch on a flag region uses the same grid, two
+        // workgroups per CU (resident at once: the occupancy of every
+        // instantiation is at least that), so that each wavefront's epoch
+        // copies see every call
+        const uint32_t grid = uint32_t(info.cu_count) * 2u;
+        if (grid * uint32_t(kWavesPerBlock) > uint32_t(kEpochCopies)) return hipErrorInvalidConfiguration;
+        hipLaunchKernelGGL(kern, dim3(grid), dim3(kBlock), 0, s, p);
+        return hipGetLastError();
+    }
     if (rq.do_rs && rq.do_ag) {
         // Persistent grid for the fused form: at most as many workgroups as
         // the device holds at once (occupancy of this kernel, capped at two

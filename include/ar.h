@@ -59,10 +59,14 @@ extern "C" {
 #define AR_MAX_RANKS 16
 /* Flag slots per rank in the two-shot barrier region (see ar_flag_bytes). */
 #define AR_SLOTS_PER_RANK 1024
+/* Epoch copies per rank for auto step ids: one per wavefront of an auto-step
+ * two-shot launch, whose grid is two 256-lane workgroups per CU (see
+ * ar_flag_bytes). */
+#define AR_EPOCH_COPIES 4096
 
 typedef enum {
     AR_OK = 0,
-    AR_ERR_ARG = 1,       /* null pointer, n out of range, numel 0, step 0, bad dtype/proto/ranks */
+    AR_ERR_ARG = 1,       /* null pointer, n out of range, numel 0, LL step 0, bad dtype/proto/ranks */
     AR_ERR_ALIGN = 2,     /* a data pointer is not 16-byte aligned */
     AR_ERR_DIVISIBLE = 3, /* two-shot: numel % n != 0 or a segment is not a whole number of 16-byte vectors */
     AR_ERR_ALIAS = 4,     /* a written buffer overlaps another buffer of the call */
@@ -80,7 +84,9 @@ typedef enum { AR_PROTO_LL = 0, AR_PROTO_LL128 = 1 } ar_proto;
 
 /* Bytes of the flag region used by the two-shot barrier and the LL status
  * word for up to n ranks: a 128-byte status line (word 0 status, word 1
- * detail) then AR_SLOTS_PER_RANK 32-bit arrival slots per rank.  Returns 0
+ * detail), then AR_SLOTS_PER_RANK 32-bit arrival slots per rank, then
+ * AR_EPOCH_COPIES 32-bit epoch copies per rank (auto step ids): in all
+ * 128 + n * (AR_SLOTS_PER_RANK + AR_EPOCH_COPIES) * 4 bytes.  Returns 0
  * if n is out of range. */
 size_t ar_flag_bytes(int n);
 
@@ -131,9 +137,12 @@ int ar_reduce_bcast(const void* const* in, int n, void* const* out, size_t numel
 /* Push copy for the one-shot push of [CAR] 实现: sender i copies its message
  * src[i] (numel elements of dtype) into dst[i*ndst + j] for j < ndst -- its
  * slot in every rank's staging buffer -- after which each rank reduces its
- * own staging slots with ar_oneshot, reading only local memory.
+ * own staging slots with ar_oneshot, reading only local memory.  With
+ * ndst = 1 it is the staging copy of the non-graph path ([CAR] step 5: the
+ * caller's tensor is copied into its registered buffer, the reduction reads
+ * the registered buffers and may then write the caller's tensor in place).
  *  src : nsrc device pointers, 1 <= nsrc <= AR_MAX_RANKS;
- *  dst : nsrc * ndst device pointers, 2 <= ndst <= AR_MAX_RANKS, none
+ *  dst : nsrc * ndst device pointers, 1 <= ndst <= AR_MAX_RANKS, none
  *        overlapping another destination or a source.
  * A sender reads S and writes ndst * S.  Any numel >= 1.
  * Errors: AR_ERR_ARG, AR_ERR_ALIGN, AR_ERR_ALIAS, AR_ERR_HIP. */
@@ -151,10 +160,18 @@ int ar_push(const void* const* src, int nsrc, void* const* dst, int ndst, size_t
  *          workgroups; [me, me+1) is one GPU's share.
  *  flags : flag region of ar_flag_bytes(n) bytes, zeroed once by
  *          ar_flag_barrier_reset before first use.
- *  step  : step id, 1..2^32-1, increasing from call to call.
+ *  step  : step id, 1..2^32-1, increasing from call to call; or 0 (auto):
+ *          rank r's step id is its epoch, kept in the flag region (a copy
+ *          per wavefront), plus one, and the launch advances the epoch.
+ *          Auto launches use a fixed grid of two workgroups per CU
+ *          (AR_ERR_HIP on a device with more than AR_EPOCH_COPIES / 8 CUs).  Auto steps let a call
+ *          captured once into a HIP graph take a new id on every replay
+ *          with nothing reset in between ([CAR] 实现: the graph path keeps
+ *          fixed registered addresses).  Do not mix explicit and auto ids on
+ *          one flag region between resets; reset before 2^32 - 1 calls.
  *  out   : NULL for reduce-scatter only.  Otherwise n device pointers
  *          (entries outside [r0, r1) ignored); the launch becomes one
- *          persistent cooperative grid that, after the reduce-scatter, waits
+ *          persistent grid (no larger than the device holds at once) that, after the reduce-scatter, waits
  *          for every rank's slot >= step and copies seg[0..n) into out[r]
  *          for r in [r0, r1) -- the same as calling ar_twoshot_ag next.
  *          Segments of ranks outside [r0, r1) must have been published
@@ -170,7 +187,9 @@ int ar_twoshot_rs(const void* const* in, int n, void* const* seg, size_t numel, 
  * for every rank r in [r0, r1), wait until each segment's arrival slots are
  * >= step, then copy seg[0], ..., seg[n-1] in order into out[r] (a bit copy,
  * no rounding).  Arguments as for ar_twoshot_rs; seg entries are read-only
- * here.  Errors as ar_twoshot_rs. */
+ * here.  With step 0 (auto) it waits for each rank's current epoch, the id of
+ * the auto reduce-scatter before it, and leaves the epoch as it is.
+ * Errors as ar_twoshot_rs. */
 int ar_twoshot_ag(const void* const* seg, int n, void* const* out, size_t numel, int dtype,
                   int r0, int r1, uint32_t* flags, uint32_t step, void* stream);
 

@@ -217,8 +217,5 @@ def test_synchronous_errors_on_device_buffers():
         car.ar_twoshot_rs(rb.ins, rb.segs, rb.flags, step=1, outs=rb.outs)
     assert e.value.code == car.AR_ERR_DIVISIBLE
     with pytest.raises(car.ArError) as e:
-        car.ar_twoshot_rs(rk.ins, rk.segs, rk.flags, step=0, outs=rk.outs)
-    assert e.value.code == car.AR_ERR_ARG
-    with pytest.raises(car.ArError) as e:
         car.ar_twoshot_rs(rk.ins, [rk.ins[0][:100]] + rk.segs[1:], rk.flags, step=1)
     assert e.value.code == car.AR_ERR_ALIAS
