@@ -239,6 +239,8 @@ def sweep(args, torch, car, np, out_path):
                 bc_all = [car.prepare_reduce_bcast(b.ins, b.outs) for b in sets]
                 push = [car.prepare_push([b.ins[ME]], [b.outs]) for b in sets]
                 stage = [car.prepare_push([b.ins[ME]], [[b.out]]) for b in sets]
+                ag_copy = [car.prepare_twoshot_ag_copy(b.segs, [b.outs[r] if r == ME else None for r in range(n)],
+                                                       flags, ME, ME + 1) for b in sets]
                 ts_auto = [car.prepare_twoshot_rs(b.ins, b.segs, flags, r0=ME, r1=ME + 1,
                                                   outs=[b.outs[r] if r == ME else None for r in range(n)])
                            for b in sets]
@@ -259,9 +261,11 @@ def sweep(args, torch, car, np, out_path):
                          ("bcast_full", "bc_all", acc.reduce_bcast(n, S, n)),
                          ("push", "push", acc.push(S, n)),
                          ("stage", "stage", acc.push(S, 1)),
+                         ("ag_copy", "ag_copy", acc.twoshot_ag(n, S, 1)),
                          ("twoshot_auto", "ts_auto", acc.twoshot(n, S, 1)),
                          ("twoshot_full", None, acc.twoshot(n, S, n))]
-                extra = {"bc_one": bc_one, "bc_all": bc_all, "push": push, "stage": stage, "ts_auto": ts_auto}
+                extra = {"bc_one": bc_one, "bc_all": bc_all, "push": push, "stage": stage, "ts_auto": ts_auto,
+                         "ag_copy": ag_copy}
                 for name, ki, rw in kinds:
                     base = step
 
@@ -271,6 +275,8 @@ def sweep(args, torch, car, np, out_path):
                                 full[i % nsets](base + i)
                             elif ki == "ts_auto":
                                 extra[ki][i % nsets](0)  # step id from the flag region
+                            elif ki == "ag_copy":
+                                extra[ki][i % nsets](1)  # every slot holds a later step by now
                             elif isinstance(ki, str):
                                 extra[ki][i % nsets]()
                             elif name == "oneshot":
@@ -298,7 +304,7 @@ def sweep(args, torch, car, np, out_path):
                     elif name == "twoshot":
                         t_two[S] = us
                 car.raise_on_status(flags, "sweep")
-                del sets, calls, full, src, extra, bc_one, bc_all, push, stage, ts_auto
+                del sets, calls, full, src, extra, bc_one, bc_all, push, stage, ts_auto, ag_copy
                 torch.cuda.empty_cache()
             # crossover: first size where two-shot (one rank's share) beats one-shot,
             # log-linear interpolation of the time difference between the bracketing sizes

@@ -69,6 +69,7 @@ def _load(path: str = LIB_PATH):
     lib.ar_push.argtypes, lib.ar_push.restype = [P, i32, P, i32, sz, i32, vp], i32
     lib.ar_twoshot_rs.argtypes, lib.ar_twoshot_rs.restype = [P, i32, P, sz, i32, i32, i32, vp, u32, P, vp], i32
     lib.ar_twoshot_ag.argtypes, lib.ar_twoshot_ag.restype = [P, i32, P, sz, i32, i32, i32, vp, u32, vp], i32
+    lib.ar_twoshot_ag_copy.argtypes, lib.ar_twoshot_ag_copy.restype = [P, i32, P, sz, i32, i32, i32, vp, u32, vp], i32
     lib.ar_ll_pack.argtypes, lib.ar_ll_pack.restype = [P, P, i32, sz, i32, i32, u32, vp], i32
     lib.ar_ll_reduce_unpack.argtypes, lib.ar_ll_reduce_unpack.restype = [P, i32, vp, sz, i32, u32, vp, vp], i32
     lib.ar_ll128_reduce_unpack.argtypes = [P, i32, vp, sz, i32, u32, vp, vp]
@@ -283,6 +284,18 @@ def prepare_twoshot_ag(segs, outs, flags, r0: int = 0, r1=None, numel=None) -> P
     return Prepared(_lib.ar_twoshot_ag, args, 8, "ar_twoshot_ag", (segs, outs, flags))
 
 
+def prepare_twoshot_ag_copy(segs, outs, flags, r0: int = 0, r1=None, numel=None) -> Prepared:
+    n = len(segs)
+    r1 = n if r1 is None else r1
+    segs = [_dev_tensor(t, "segment") for t in segs]
+    flags = _dev_tensor(flags, "flags")
+    numel = segs[0].numel() * n if numel is None else numel
+    out_arr = _ptr_array([(_dev_tensor(o, "out").data_ptr() if o is not None else 0) for o in outs])
+    args = [_ptr_array([t.data_ptr() for t in segs]), n, out_arr, numel, _dtype_code(segs[0]), r0, r1,
+            flags.data_ptr(), 0, None]
+    return Prepared(_lib.ar_twoshot_ag_copy, args, 8, "ar_twoshot_ag_copy", (segs, outs, flags))
+
+
 def prepare_ll_pack(srcs, wires, proto) -> Prepared:
     srcs = [_dev_tensor(t, "src") for t in srcs]
     wires = [_dev_tensor(t, "wire") for t in wires]
@@ -327,6 +340,11 @@ def ar_twoshot_rs(ins, segs, flags, step: int, r0: int = 0, r1=None, outs=None, 
 def ar_twoshot_ag(segs, outs, flags, step: int, r0: int = 0, r1=None, numel=None, stream=None):
     """All-gather for ranks [r0, r1) after waiting on every segment's slots."""
     prepare_twoshot_ag(segs, outs, flags, r0, r1, numel)(step, stream)
+
+
+def ar_twoshot_ag_copy(segs, outs, flags, step: int, r0: int = 0, r1=None, numel=None, stream=None):
+    """All-gather on the copy engines after a one-workgroup slot wait."""
+    prepare_twoshot_ag_copy(segs, outs, flags, r0, r1, numel)(step, stream)
 
 
 def ar_ll_pack(srcs, wires, proto, step: int, stream=None):

@@ -332,6 +332,16 @@ int ar_select_algo(int n, size_t numel, int dtype, double sync_us) {
     return best;
 }
 
+int ar_twoshot_ag_copy(const void* const* seg, int n, void* const* out, size_t numel, int dtype, int r0, int r1,
+                       uint32_t* flags, uint32_t step, void* stream) {
+    if (!out) return AR_ERR_ARG;
+    const int st = twoshot_check(nullptr, seg, out, n, numel, dtype, r0, r1, flags, step);
+    if (st != AR_OK) return st;
+    TwoShotRequest rq{nullptr, const_cast<void* const*>(seg), out, n, numel, dtype, r0, r1, flags, step,
+                      false, true, timeout_ticks()};
+    return hip_status(launch_twoshot_ag_copy(rq, static_cast<hipStream_t>(stream)));
+}
+
 int ar_flag_barrier_reset(uint32_t* flags, int n, void* stream) {
     if (!flags || !ranks_ok(n)) return AR_ERR_ARG;
     if (!aligned16(flags)) return AR_ERR_ALIGN;

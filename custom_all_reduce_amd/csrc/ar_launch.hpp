@@ -53,6 +53,9 @@ struct TwoShotRequest {
     uint64_t timeout_ticks;
 };
 hipError_t launch_twoshot(const TwoShotRequest& rq, hipStream_t s);
+// All-gather on the copy engines: a one-workgroup slot wait, then n
+// hipMemcpyAsync copies per output rank.
+hipError_t launch_twoshot_ag_copy(const TwoShotRequest& rq, hipStream_t s);
 
 hipError_t launch_ll_pack(const void* const* src, void* const* wire, int count, size_t nbytes,
                           int proto, uint32_t step, hipStream_t s);

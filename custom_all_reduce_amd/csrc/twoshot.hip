@@ -239,6 +239,56 @@ __global__ __launch_bounds__(kBlock) void twoshot_kernel(TwoShotParams p) {
     if (p.do_ag) all_gather_phase(p, step_lane, NR, wave, nwaves, lane);
 }
 
+// The barrier of a copy-engine all-gather: one workgroup waits until the
+// arrival slot of every tile of every segment is >= the step id (the
+// largest of the ranks' in [r0, r1) in auto mode, where wavefront 0's epoch
+// copies stand for all copies), or reports a timeout; the copies follow in
+// stream order and need no compute unit.
+template <int NR>
+__global__ __launch_bounds__(kBlock) void ag_wait_kernel(TwoShotParams p) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    uint32_t want = p.step;
+    if (p.auto_step) {
+        want = 0;
+        for (int r = p.r0; r < p.r1; ++r) {
+            const uint32_t e = flag_load_relaxed(p.flags + kStatusWords + NR * kSlotsPerRank + size_t(r) * kEpochCopies);
+            want = e > want ? e : want;
+        }
+    }
+    const uint32_t* slots = p.flags + kStatusWords;
+    const uint32_t items = uint32_t(NR) * p.ktiles;
+    for (uint32_t kb = wave * kWave; kb < items; kb += kWavesPerBlock * kWave) {
+        const uint32_t k = kb + uint32_t(lane);
+        const bool need = k < items;
+        const uint32_t j = need ? k / p.ktiles : 0u, t = need ? k % p.ktiles : 0u;
+        const uint32_t* slot = slots + j * kSlotsPerRank + t;
+        const uint64_t t0 = now_ticks();
+        while (true) {
+            const bool ok = !need || flag_load_relaxed(slot) >= want;
+            const uint64_t missing = ~wave_ballot(ok) & wave_exec();
+            if (missing == 0) break;
+            if (now_ticks() - t0 > p.timeout_ticks) {
+                const int bad_lane = __ffsll((unsigned long long)missing) - 1;
+                const uint32_t bj = __shfl(j, bad_lane);
+                const uint32_t bt = __shfl(t, bad_lane);
+                if (lane == 0) report_timeout(p.flags, 1u, bj, bt);
+                return;
+            }
+            __builtin_amdgcn_s_sleep(1);
+        }
+    }
+}
+
+// Segment tiling shared by every two-shot launch and the copy-engine wait.
+void tile_params(TwoShotParams& p, size_t seg_bytes) {
+    p.mvec = uint32_t(seg_bytes / 16);
+    const uint32_t per_slot = (p.mvec + kSlotsPerRank - 1) / kSlotsPerRank;  // vectors per slot at least
+    p.tile = ((per_slot + kWave - 1) / kWave) * kWave;
+    if (p.tile == 0) p.tile = kWave;
+    p.ktiles = (p.mvec + p.tile - 1) / p.tile;
+}
+
 template <typename T, int NR>
 hipError_t launch_t(const TwoShotRequest& rq, hipStream_t s) {
     // one unit in flight per wavefront in phase 1 (NR loads per lane), four in
@@ -255,12 +305,7 @@ hipError_t launch_t(const TwoShotRequest& rq, hipStream_t s) {
         p.seg[r] = static_cast<u32x4*>(rq.seg[r]);
         p.out[r] = (rq.out && r >= rq.r0 && r < rq.r1) ? static_cast<u32x4*>(rq.out[r]) : nullptr;
     }
-    const size_t seg_bytes = rq.numel / size_t(NR) * size_t(elem<T>::bytes);
-    p.mvec = uint32_t(seg_bytes / 16);
-    const uint32_t per_slot = (p.mvec + kSlotsPerRank - 1) / kSlotsPerRank;  // vectors per slot at least
-    p.tile = ((per_slot + kWave - 1) / kWave) * kWave;
-    if (p.tile == 0) p.tile = kWave;
-    p.ktiles = (p.mvec + p.tile - 1) / p.tile;
+    tile_params(p, rq.numel / size_t(NR) * size_t(elem<T>::bytes));
     p.flags = rq.flags;
     p.timeout_ticks = rq.timeout_ticks;
     p.step = rq.step;
@@ -312,6 +357,33 @@ hipError_t launch_t(const TwoShotRequest& rq, hipStream_t s) {
 }
 
 }  // namespace
+
+hipError_t launch_twoshot_ag_copy(const TwoShotRequest& rq, hipStream_t s) {
+    const size_t es = rq.dtype == 0 ? 4 : 2;
+    const size_t m_bytes = rq.numel / size_t(rq.n) * es;
+    TwoShotParams p{};
+    tile_params(p, m_bytes);
+    p.flags = rq.flags;
+    p.timeout_ticks = rq.timeout_ticks;
+    p.step = rq.step;
+    p.auto_step = rq.step == 0;
+    p.r0 = rq.r0;
+    p.r1 = rq.r1;
+    hipError_t e = dispatch_ranks(rq.n, [&](auto nr) {
+        constexpr int NR = decltype(nr)::value;
+        hipLaunchKernelGGL(ag_wait_kernel<NR>, dim3(1), dim3(kBlock), 0, s, p);
+        return hipGetLastError();
+    });
+    if (e != hipSuccess) return e;
+    // the all-gather proper: n segment copies per output on the copy engines
+    for (int r = rq.r0; r < rq.r1; ++r)
+        for (int j = 0; j < rq.n; ++j) {
+            e = hipMemcpyAsync(static_cast<char*>(rq.out[r]) + size_t(j) * m_bytes, rq.seg[j], m_bytes,
+                               hipMemcpyDeviceToDeviceNoCU, s);
+            if (e != hipSuccess) return e;
+        }
+    return hipSuccess;
+}
 
 hipError_t launch_twoshot(const TwoShotRequest& rq, hipStream_t s) {
     return dispatch_ranks(rq.n, [&](auto nr) {

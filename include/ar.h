@@ -15,6 +15,8 @@
  *         协议 table (LL, LL128, Simple), 练习 3 (registered buffers).
  *  [MGPU] "多 GPU 与 NCCL" (anrans.github.io, cuda/tools/multi-gpu): 集合通信
  *         table, all-reduce = reduce-scatter + all-gather.
+ *  [SMF]  "Sm-free Allreduce using sharp" (obnotes, Big-Feature): 0 前言 --
+ *         moving the data with asynchronous copies instead of SM kernels.
  *
  * Conventions shared by every entry point
  *  - n emulated ranks, 2 <= n <= AR_MAX_RANKS ([CAR] supports up to 16 GPUs).
@@ -192,6 +194,19 @@ int ar_twoshot_rs(const void* const* in, int n, void* const* seg, size_t numel, 
  * Errors as ar_twoshot_rs. */
 int ar_twoshot_ag(const void* const* seg, int n, void* const* out, size_t numel, int dtype,
                   int r0, int r1, uint32_t* flags, uint32_t step, void* stream);
+
+/* Two-shot phase 2 on the copy engines: the same result as ar_twoshot_ag,
+ * with the compute units left to other work ([NCCL] 协议: communication run
+ * as thread blocks competes with compute for the SMs; [SMF] 0 前言: move the
+ * data with asynchronous copies instead).  One workgroup waits until every arrival slot of
+ * every segment is >= step (for step 0, the largest current epoch of the
+ * ranks in [r0, r1)); then, for every r in [r0, r1), n hipMemcpyAsync copies
+ * of kind hipMemcpyDeviceToDeviceNoCU move seg[0..n) into out[r].  On a
+ * timeout the status is written as for ar_twoshot_ag, but the copies still
+ * run: their output is then not valid.  Arguments and errors as
+ * ar_twoshot_ag (AR_ERR_HIP also when the runtime refuses a copy). */
+int ar_twoshot_ag_copy(const void* const* seg, int n, void* const* out, size_t numel, int dtype,
+                       int r0, int r1, uint32_t* flags, uint32_t step, void* stream);
 
 /* Sender side of LL / LL128 ([NCCL] 协议 table): pack count messages, each
  * numel elements of dtype taken as bytes, into their wire buffers
