@@ -22,6 +22,11 @@ namespace {
 
 constexpr int kBlock = 256;
 constexpr int kWavesPerBlock = kBlock / kWave;
+// LL128 receiver: one wavefront per workgroup (measured faster than four at
+// every size from 128 KiB to 8 MiB per rank: more, smaller workgroups spread
+// the few waves of a small message over more CUs).
+constexpr int kBlock128 = kWave;
+constexpr int kWavesPerBlock128 = 1;
 
 // ------------------------------------------------------------------ pack --
 struct PackParams {
@@ -274,10 +279,10 @@ __global__ __launch_bounds__(kBlock) void ll_reduce_kernel(ReduceParams p) {
 }
 
 template <typename T, int NR, int U>
-__global__ __launch_bounds__(kBlock) void ll128_reduce_kernel(ReduceParams p) {
+__global__ __launch_bounds__(kBlock128) void ll128_reduce_kernel(ReduceParams p) {
     const int lane = threadIdx.x & (kWave - 1);
     const uint32_t part = uint32_t(lane) & 7u;
-    const size_t wave = __builtin_amdgcn_readfirstlane(blockIdx.x * kWavesPerBlock + threadIdx.x / kWave);
+    const size_t wave = __builtin_amdgcn_readfirstlane(blockIdx.x * kWavesPerBlock128 + threadIdx.x / kWave);
     u32x4 x[U][NR];
     size_t line[U];
     bool valid[U];
@@ -343,7 +348,7 @@ __global__ __launch_bounds__(kBlock) void ll128_reduce_kernel(ReduceParams p) {
     // lane's piece starts at 120 * line + 16 * part, only 8-byte aligned.
     // Write the pieces to a wavefront-private LDS strip, then let lanes 0..59
     // store 16 aligned bytes each.
-    __shared__ __attribute__((aligned(16))) uint8_t strip[kWavesPerBlock][U][960];
+    __shared__ __attribute__((aligned(16))) uint8_t strip[kWavesPerBlock128][U][960];
     uint8_t* my = &strip[threadIdx.x / kWave][0][0];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -385,7 +390,10 @@ __global__ __launch_bounds__(kBlock) void ll128_reduce_kernel(ReduceParams p) {
 template <typename T, int NR>
 hipError_t launch_reduce_t(const ReduceParams& p, int proto, hipStream_t s) {
     if (proto == 0) {
-        constexpr int U = NR <= 8 ? 2 : 1;
+        // One 16-byte load per lane per rank: measured faster than two from
+        // 128 KiB to 8 MiB per rank (more workgroups in flight) and equal
+        // within a few percent at 64 MiB.
+        constexpr int U = 1;
         const size_t chunks = (p.nlines + 1) / 2;
         const size_t grid = (chunks + kBlock * U - 1) / (kBlock * U);
         hipLaunchKernelGGL((ll_reduce_kernel<T, NR, U>), dim3(uint32_t(grid)), dim3(kBlock), 0, s, p);
@@ -395,8 +403,8 @@ hipError_t launch_reduce_t(const ReduceParams& p, int proto, hipStream_t s) {
         constexpr int U = 1;
         const size_t wave_units = (p.nlines + 7) / 8;
         const size_t waves = (wave_units + U - 1) / U;
-        const size_t grid = (waves + kWavesPerBlock - 1) / kWavesPerBlock;
-        hipLaunchKernelGGL((ll128_reduce_kernel<T, NR, U>), dim3(uint32_t(grid)), dim3(kBlock), 0, s, p);
+        const size_t grid = (waves + kWavesPerBlock128 - 1) / kWavesPerBlock128;
+        hipLaunchKernelGGL((ll128_reduce_kernel<T, NR, U>), dim3(uint32_t(grid)), dim3(kBlock128), 0, s, p);
     }
     return hipGetLastError();
 }

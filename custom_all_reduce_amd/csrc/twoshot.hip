@@ -13,9 +13,10 @@
 //                        own segment of its all-gather, from registers)
 //   phase 2 item (ro, j, t): copy tile t of seg[j] into out[ro] at j*mvec, for
 //                        every j (split form) or every j != ro (fused form)
-// Items are dealt to wavefronts round-robin; a wavefront walks its items as a
-// flat list of 64-vector units (one vector per lane) and keeps U units of
-// loads in flight before it adds or stores.
+// Items are dealt to wavefronts round-robin (phase 2 starting after the
+// wavefronts that have phase-1 items); a wavefront walks its items as a flat
+// list of 64-vector units (one vector per lane) and keeps U units of loads in
+// flight before it adds or stores.
 //
 // Barrier.  Each tile (r, t) has a 32-bit arrival slot.  Segments are
 // written and read with device-coherent (sc1) accesses, so after its last
@@ -236,7 +237,15 @@ __global__ __launch_bounds__(kBlock) void twoshot_kernel(TwoShotParams p) {
         reduce_scatter_phase<T, NR, U>(p, step_lane, wave, nwaves, lane);
         if (p.auto_step && uint32_t(lane) < R) flag_store_relaxed(epoch + size_t(lane) * kEpochCopies, step_lane);
     }
-    if (p.do_ag) all_gather_phase(p, step_lane, NR, wave, nwaves, lane);
+    if (p.do_ag) {
+        // In the fused form the all-gather items are dealt starting after the
+        // wavefronts that hold reduce-scatter items, so that when the grid has
+        // a wavefront per item the two phases run side by side instead of one
+        // after the other in the same wavefronts.
+        const uint32_t rs_busy = p.do_rs ? min(R * p.ktiles, nwaves) : 0u;
+        const uint32_t ag_wave = wave >= rs_busy ? wave - rs_busy : wave + (nwaves - rs_busy);
+        all_gather_phase(p, step_lane, NR, ag_wave, nwaves, lane);
+    }
 }
 
 // The barrier of a copy-engine all-gather: one workgroup waits until the
