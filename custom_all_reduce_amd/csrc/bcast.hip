@@ -15,7 +15,10 @@
 // it is the staging copy of a caller's tensor into its registered buffer.
 //
 // Both kernels keep one 16-byte vector per lane (the shape measured fastest
-// for the one-shot) and stream every access past the caches.
+// for the one-shot) and stream their stores past the caches.  Their loads
+// are plain: measured, that is 15-20% faster at 64 MiB per rank than
+// nontemporal loads for these store-heavy kernels (the read-heavy one-shot,
+// two-shot and LL kernels measure the other way round).
 #include "ar_device.hpp"
 #include "ar_launch.hpp"
 
@@ -37,7 +40,7 @@ __global__ __launch_bounds__(kBlock) void reduce_bcast_kernel(InVecs<NR> in, Out
     if (idx < ve) {
         u32x4 x[NR];
 #pragma unroll
-        for (int r = 0; r < NR; ++r) x[r] = ld_stream(in.p[r] + idx);
+        for (int r = 0; r < NR; ++r) x[r] = in.p[r][idx];
         Acc<T> acc;
 #pragma unroll
         for (int r = 0; r < NR; ++r) acc.add(x[r]);
@@ -66,7 +69,7 @@ template <int ND>
 __global__ __launch_bounds__(kBlock) void push_kernel(PushArgs<ND> a, uint32_t nvec, uint32_t ntail) {
     const uint32_t idx = blockIdx.x * kBlock + threadIdx.x;
     if (idx < nvec) {
-        const u32x4 x = ld_stream(a.src + idx);
+        const u32x4 x = a.src[idx];
 #pragma unroll
         for (int j = 0; j < ND; ++j) st_stream(a.dst[j] + idx, x);
     }
