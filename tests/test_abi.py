@@ -20,13 +20,20 @@ HEADER = os.path.join(ROOT, "include", "ar.h")
 
 def declared_functions():
     text = open(HEADER, encoding="utf-8").read()
-    return sorted(set(re.findall(r"^(?:int|size_t|void|uint64_t|const char\*)\s+(ar_\w+)\(", text, re.M)))
+    return sorted(set(re.findall(r"^(?:int|size_t|void|uint64_t|double|const char\*)\s+(ar_\w+)\(", text, re.M)))
 
 
 def test_header_declares_the_seven_path_calls():
     names = declared_functions()
     for required in ("ar_oneshot", "ar_twoshot_rs", "ar_twoshot_ag", "ar_ll_pack", "ar_ll_reduce_unpack",
                      "ar_ll128_reduce_unpack", "ar_flag_barrier_reset"):
+        assert required in names
+
+
+def test_header_declares_the_store_paths_copy_engine_and_selector():
+    names = declared_functions()
+    for required in ("ar_reduce_bcast", "ar_push", "ar_twoshot_ag_copy", "ar_select_algo", "ar_algo_cost_us",
+                     "ar_flag_bytes", "ar_ll_wire_bytes", "ar_status_string"):
         assert required in names
 
 
@@ -99,6 +106,60 @@ def test_oneshot_argument_errors():
     assert L.ar_oneshot(ins, 4, A + 16, 16, 0, NUL) == car.AR_ERR_ALIAS
     assert L.ar_oneshot(ins, 4, A - 16 * 4 + 16, 16, 0, NUL) == car.AR_ERR_ALIAS
     # touching but not overlapping is fine -> would launch; not called here
+
+
+def test_size_limit_is_32_GiB_per_rank():
+    ins = fake_ins(2, stride=1 << 40)
+    out = A + (8 << 40)
+    # 2^35 bytes + one element is refused before anything else happens
+    assert L.ar_oneshot(ins, 2, out, (1 << 35) // 4 + 1, 0, NUL) == car.AR_ERR_ARG
+    assert L.ar_oneshot(ins, 2, out, (1 << 35) // 2 + 1, 1, NUL) == car.AR_ERR_ARG
+
+
+def test_reduce_bcast_argument_errors():
+    n = 4
+    ins, outs = fake_ins(n), fake_ins(n, base=A + (64 << 30))
+    f = L.ar_reduce_bcast
+    assert f(ins, 1, outs, 64, 0, 0, 1, NUL) == car.AR_ERR_ARG  # n < 2
+    assert f(ins, n, outs, 0, 0, 0, n, NUL) == car.AR_ERR_ARG  # numel 0
+    assert f(ins, n, outs, 64, 2, 0, n, NUL) == car.AR_ERR_ARG  # dtype
+    assert f(ins, n, outs, 64, 0, 2, 2, NUL) == car.AR_ERR_ARG  # empty rank range
+    assert f(ins, n, outs, 64, 0, 0, n + 1, NUL) == car.AR_ERR_ARG
+    assert f(ins, n, None, 64, 0, 0, n, NUL) == car.AR_ERR_ARG
+    assert f(ins, n, arr(A + (64 << 30), 0, A + (66 << 30), A + (67 << 30)), 64, 0, 0, n, NUL) == car.AR_ERR_ARG
+    assert f(ins, n, arr(A + (64 << 30) + 8, A + (65 << 30), A + (66 << 30), A + (67 << 30)), 64, 0, 0, n, NUL) \
+        == car.AR_ERR_ALIGN
+    # an output overlapping an input, and two outputs overlapping each other
+    assert f(ins, n, arr(A + 16, A + (65 << 30), A + (66 << 30), A + (67 << 30)), 64, 0, 0, n, NUL) == car.AR_ERR_ALIAS
+    assert f(ins, n, arr(A + (64 << 30), A + (64 << 30) + 128, A + (66 << 30), A + (67 << 30)), 64, 0, 0, n, NUL) \
+        == car.AR_ERR_ALIAS
+
+
+def test_push_argument_errors():
+    src = fake_ins(2)
+    dst = fake_ins(4, base=A + (64 << 30))
+    f = L.ar_push
+    assert f(src, 0, dst, 2, 64, 0, NUL) == car.AR_ERR_ARG  # no sender
+    assert f(src, 2, dst, 0, 64, 0, NUL) == car.AR_ERR_ARG  # no destination
+    assert f(src, 2, dst, 17, 64, 0, NUL) == car.AR_ERR_ARG
+    assert f(src, 2, dst, 2, 0, 0, NUL) == car.AR_ERR_ARG
+    assert f(src, 2, None, 2, 64, 0, NUL) == car.AR_ERR_ARG
+    assert f(src, 2, arr(A + (64 << 30) + 4, A + (65 << 30), A + (66 << 30), A + (67 << 30)), 2, 64, 0, NUL) \
+        == car.AR_ERR_ALIGN
+    assert f(src, 2, arr(A + (64 << 30), A + (65 << 30), A + 64, A + (67 << 30)), 2, 64, 0, NUL) == car.AR_ERR_ALIAS
+    assert f(src, 2, arr(A + (64 << 30), A + (64 << 30) + 16, A + (66 << 30), A + (67 << 30)), 2, 64, 0, NUL) \
+        == car.AR_ERR_ALIAS
+
+
+def test_ag_copy_argument_errors():
+    n = 4
+    segs, outs = fake_ins(n), fake_ins(n, base=A + (64 << 30))
+    flags = A + (200 << 30)
+    g = L.ar_twoshot_ag_copy
+    assert g(segs, n, None, 64, 0, 0, n, flags, 1, NUL) == car.AR_ERR_ARG
+    assert g(segs, n, outs, 66, 0, 0, n, flags, 1, NUL) == car.AR_ERR_DIVISIBLE
+    assert g(segs, n, outs, 64, 0, 3, 3, flags, 1, NUL) == car.AR_ERR_ARG
+    assert g(segs, n, outs, 64, 0, 0, n, flags + 4, 1, NUL) == car.AR_ERR_ALIGN
 
 
 def test_twoshot_argument_errors():
