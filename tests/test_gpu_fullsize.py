@@ -107,3 +107,45 @@ def test_n16_8MiB_full_emulation_two_shot_sampled():
     car.raise_on_status(flags)
     for r in range(n):
         assert np.array_equal(bits(outs[r])[idx], want), f"rank {r}"
+
+
+def test_n16_64MiB_copy_engine_all_gather_and_auto_step_sampled():
+    """One rank's reduce-scatter with an auto step id, then the copy-engine
+    all-gather, at 64 MiB per rank; and the fused full emulation with auto
+    step ids at 8 MiB, replayed twice without a reset."""
+    n, dt = 16, "bf16"
+    numel = (64 << 20) // 2
+    host = synth.rank_inputs(n, numel, dt, "normal", config=8)
+    idx = sample_indices(numel, seed=9)
+    want = expect_at(host, idx, dt)
+    ins = [to_dev(a) for a in host]
+    del host
+    segs = [torch.empty(numel // n, dtype=ins[0].dtype, device="cuda") for _ in range(n)]
+    out = torch.zeros(numel, dtype=ins[0].dtype, device="cuda")
+    flags = car.new_flags(n)
+    car.set_poll_timeout_ns(200_000_000)
+    try:
+        for r in range(n):
+            car.ar_twoshot_rs(ins, segs, flags, 0, r0=r, r1=r + 1)
+        car.ar_twoshot_ag_copy(segs, [out] + [None] * (n - 1), flags, 0, r0=0, r1=1)
+        torch.cuda.synchronize()
+        car.raise_on_status(flags)
+        assert np.array_equal(bits(out)[idx], want), "copy-engine all-gather"
+    finally:
+        car.set_poll_timeout_ns(0)
+    del ins, segs, out
+
+    numel = (8 << 20) // 2
+    host = synth.rank_inputs(n, numel, dt, "normal", config=10)
+    idx = sample_indices(numel, seed=11)
+    want = expect_at(host, idx, dt)
+    ins = [to_dev(a) for a in host]
+    segs = [torch.empty(numel // n, dtype=ins[0].dtype, device="cuda") for _ in range(n)]
+    outs = [torch.zeros(numel, dtype=ins[0].dtype, device="cuda") for _ in range(n)]
+    flags = car.new_flags(n)
+    for rep in range(2):
+        car.ar_twoshot_rs(ins, segs, flags, 0, outs=outs)
+        torch.cuda.synchronize()
+        car.raise_on_status(flags, f"auto step {rep}")
+        for r in (0, 5, n - 1):
+            assert np.array_equal(bits(outs[r])[idx], want), f"auto step {rep} rank {r}"
