@@ -201,7 +201,9 @@ int ar_twoshot_ag(const void* const* seg, int n, void* const* out, size_t numel,
  * data with asynchronous copies instead).  One workgroup waits until every arrival slot of
  * every segment is >= step (for step 0, the largest current epoch of the
  * ranks in [r0, r1)); then, for every r in [r0, r1), n hipMemcpyAsync copies
- * of kind hipMemcpyDeviceToDeviceNoCU move seg[0..n) into out[r].  On a
+ * of kind hipMemcpyDeviceToDeviceNoCU move seg[0..n) into out[r].  Captured
+ * into a HIP graph, the runtime runs these copies on the copy engines; called
+ * eagerly on one device it may run them as copy kernels instead.  On a
  * timeout the status is written as for ar_twoshot_ag, but the copies still
  * run: their output is then not valid.  Arguments and errors as
  * ar_twoshot_ag (AR_ERR_HIP also when the runtime refuses a copy). */
