@@ -400,6 +400,13 @@ def select_table(args, torch, car, np, out_path):
     return rows
 
 
+def device_summary(torch):
+    """What the run ran on, as the runtime reports it."""
+    p = torch.cuda.get_device_properties(0)
+    return {"name": p.name, "arch": getattr(p, "gcnArchName", ""), "compute_units": p.multi_processor_count,
+            "l2_bytes": getattr(p, "L2_cache_size", None), "hbm_bytes": p.total_memory}
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -582,6 +589,7 @@ def main(argv=None):
             "wall_s": round(wall, 3),
         },
         "kernels": kernels,
+        "device": device_summary(torch),
     }
     if dominant:
         A = kernels[dominant]["GBps"]
