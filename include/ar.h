@@ -47,6 +47,10 @@
  *  - Reuse: a producer may overwrite a segment or wire buffer for step s+1
  *    only after every consumer has finished step s (the end synchronisation
  *    of [CAR] step 6).  On one GPU, stream order gives this.
+ *  - Calls that share a flag region must be ordered, for example by issuing
+ *    them on one stream; auto step ids in particular rely on each call seeing
+ *    the epochs the previous one left.  Calls on one flag region that overlap
+ *    in time race.
  */
 #ifndef AR_H
 #define AR_H
