@@ -21,7 +21,6 @@ namespace ar {
 namespace {
 
 constexpr int kBlock = 256;
-constexpr int kWavesPerBlock = kBlock / kWave;
 // LL128 receiver: one wavefront per workgroup (measured faster than four at
 // every size from 128 KiB to 8 MiB per rank: more, smaller workgroups spread
 // the few waves of a small message over more CUs).
