@@ -1,0 +1,51 @@
+"""bench.py's host-side contract, on the CPU: more than one GPU is refused
+with a message, the per-step byte accounting matches the method's algorithmic
+bytes, and the workloads are the pages' tensor-parallel message shapes."""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+
+import bench
+from custom_all_reduce_amd import accounting as acc
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_more_than_one_gpu_is_refused_with_a_message():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, cwd=ROOT, timeout=120)
+    assert r.returncode == 2
+    assert "--gpus 1" in r.stderr and r.stdout == ""
+
+
+def test_step_bytes_are_one_gpus_algorithmic_bytes():
+    n, S = 8, 128 << 10
+    per = bench.step_bytes(n, S)
+    assert per["oneshot"] == n * S + S
+    # one rank's fused two-shot: S read for its segment, (n-1)/n S of peers' segments; S/n + S written
+    assert per["twoshot"] == S + (n - 1) * (S // n) + S // n + S
+    W1, W2 = acc.wire_bytes("ll", S), acc.wire_bytes("ll128", S)
+    assert W1 == 2 * S and W2 == 128 * -(-S // 120)
+    assert per["ll_pack"] == S + W1 and per["ll_reduce"] == n * W1 + S
+    assert per["ll128_pack"] == S + W2 and per["ll128_reduce"] == n * W2 + S
+    assert set(per) == set(bench.KERNELS)
+
+
+def test_workloads_are_the_pages_message_shapes():
+    n, dt, numel, _ = bench.WORKLOADS["decode"]
+    assert (n, dt, numel) == (8, "bf16", 8 * 8192)  # [8 tokens x hidden 8192]
+    n, dt, numel, _ = bench.WORKLOADS["prefill"]
+    assert (n, dt, numel) == (8, "bf16", 512 * 8192)
+    for w, bytes_per_rank in (("ll64k", 64 << 10), ("ll1m", 1 << 20)):
+        n, dt, numel, _ = bench.WORKLOADS[w]
+        assert dt == "f32" and numel * 4 == bytes_per_rank
+
+
+def test_store_path_accounting():
+    S, n = 1 << 20, 8
+    assert acc.reduce_bcast(n, S, 1) == (S, S)
+    assert acc.reduce_bcast(n, S, n) == (n * S, n * S)
+    assert acc.push(S, n) == (S, n * S)
+    assert acc.push(S, 1) == (S, S)
