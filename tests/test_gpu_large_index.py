@@ -1,0 +1,93 @@
+"""Index arithmetic at large sizes: n = 2 ranks of 2^30 + 5 bf16 elements
+(2 GiB and a ragged tail per rank; 2^27 16-byte vectors, LL wires of 4 GiB,
+byte offsets past 2^32).  Small-integer inputs keep every sum exact, so a
+wrong index anywhere shows as a wrong value.  Outputs are checked on samples
+around the power-of-two boundaries against the oracle run on the sampled
+columns."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from devtensors import bits, oracle_bits, to_dev
+
+pytestmark = pytest.mark.gpu
+
+car = pytest.importorskip("custom_all_reduce_amd")
+
+N = 2
+NUMEL = (1 << 30) + 5
+
+
+def sample(numel, seed=21):
+    rng = np.random.default_rng(seed)
+    pick = [np.arange(0, 4096), np.arange(numel - 4096, numel), rng.integers(0, numel, 20000)]
+    for e in range(20, 31):
+        b = 1 << e
+        if b < numel:
+            pick.append(np.arange(max(0, b - 40), min(numel, b + 40)))
+    return np.unique(np.concatenate(pick))
+
+
+@pytest.fixture(scope="module")
+def data():
+    host = synth.rank_inputs(N, NUMEL, "bf16", "int", config=30)
+    idx = sample(NUMEL)
+    want = oracle_bits(oracle.oneshot([np.ascontiguousarray(a[idx]) for a in host], "bf16"))
+    ins = [to_dev(a) for a in host]
+    del host
+    return ins, idx, want
+
+
+def check(t, idx, want, what):
+    got = bits(t)[idx]
+    bad = np.nonzero(got != want)[0]
+    assert bad.size == 0, f"{what}: {bad.size} sampled mismatches, first at element {idx[bad[0]]}"
+
+
+def test_oneshot_and_reduce_broadcast(data):
+    ins, idx, want = data
+    out = torch.empty(NUMEL, dtype=torch.bfloat16, device="cuda")
+    car.ar_oneshot(ins, out)
+    torch.cuda.synchronize()
+    check(out, idx, want, "one-shot")
+    outs = [out, torch.empty_like(out)]
+    car.ar_reduce_bcast(ins, outs)
+    torch.cuda.synchronize()
+    for j in range(N):
+        check(outs[j], idx, want, f"reduce-broadcast out[{j}]")
+
+
+def test_ll_and_ll128(data):
+    ins, idx, want = data
+    out = torch.empty(NUMEL, dtype=torch.bfloat16, device="cuda")
+    flags = car.new_flags(N)
+    for proto in ("ll", "ll128"):
+        W = car.ll_wire_bytes(proto, NUMEL * 2)
+        wires = [torch.empty(W, dtype=torch.uint8, device="cuda") for _ in range(N)]
+        car.ar_ll_pack(ins, wires, proto, 1)
+        (car.ar_ll_reduce_unpack if proto == "ll" else car.ar_ll128_reduce_unpack)(wires, out, 1, flags)
+        torch.cuda.synchronize()
+        car.raise_on_status(flags, proto)
+        check(out, idx, want, proto)
+        del wires
+        torch.cuda.empty_cache()
+
+
+def test_two_shot_divisible_prefix(data):
+    """The two-shot needs n whole 16-byte segments: the first 2^30 elements."""
+    ins, idx, want = data
+    m = 1 << 30
+    keep = idx < m
+    heads = [t[:m] for t in ins]
+    segs = [torch.empty(m // N, dtype=torch.bfloat16, device="cuda") for _ in range(N)]
+    outs = [torch.empty(m, dtype=torch.bfloat16, device="cuda") for _ in range(N)]
+    flags = car.new_flags(N)
+    car.ar_twoshot_rs(heads, segs, flags, 0, outs=outs)
+    torch.cuda.synchronize()
+    car.raise_on_status(flags)
+    for r in range(N):
+        check(outs[r], idx[keep], want[keep], f"two-shot rank {r}")
