@@ -1,0 +1,167 @@
+/*
+ * The C ABI from plain C: device buffers from the HIP runtime, calls through
+ * include/ar.h only, results compared bit for bit with the C oracle.
+ *
+ * Test infrastructure: it links the oracle (liboracle.so) to check the
+ * library (libar.so).  Exit status 0 when every case matches.
+ */
+#include <stdint.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <hip/hip_runtime_api.h>
+
+#include "ar.h"
+
+/* the oracle's entry points (oracle/ar_oracle.c) */
+void oracle_oneshot(const void* const* in, int n, void* out, size_t numel, int dtype);
+size_t oracle_ll_wire_bytes(int proto, size_t nbytes);
+
+#define CHECK_HIP(x)                                                              \
+    do {                                                                          \
+        hipError_t e_ = (x);                                                      \
+        if (e_ != hipSuccess) {                                                   \
+            fprintf(stderr, "%s:%d: %s\n", __FILE__, __LINE__, hipGetErrorString(e_)); \
+            exit(2);                                                              \
+        }                                                                         \
+    } while (0)
+
+static uint64_t lcg = 0x9E3779B97F4A7C15ull;
+static uint32_t next32(void) {
+    lcg = lcg * 6364136223846793005ull + 1442695040888963407ull;
+    return (uint32_t)(lcg >> 32);
+}
+
+/* float32 in [-4, 4) with a random 23-bit mantissa; bf16 = its top half */
+static void fill(void* dst, size_t numel, int dtype) {
+    for (size_t i = 0; i < numel; ++i) {
+        uint32_t u = 0x3F800000u | (next32() >> 9);  /* [1, 2) */
+        float f;
+        memcpy(&f, &u, 4);
+        f = (f - 1.5f) * 8.0f;
+        if (dtype == AR_F32) ((float*)dst)[i] = f;
+        else { memcpy(&u, &f, 4); ((uint16_t*)dst)[i] = (uint16_t)(u >> 16); }
+    }
+}
+
+typedef struct {
+    int n;
+    size_t numel, bytes;
+    int dtype;
+    void* host[AR_MAX_RANKS];
+    void* dev[AR_MAX_RANKS];
+    void* want;
+} Case;
+
+static void setup(Case* c, int n, size_t numel, int dtype) {
+    c->n = n;
+    c->numel = numel;
+    c->dtype = dtype;
+    c->bytes = numel * (dtype == AR_F32 ? 4 : 2);
+    for (int i = 0; i < n; ++i) {
+        c->host[i] = malloc(c->bytes);
+        fill(c->host[i], numel, dtype);
+        CHECK_HIP(hipMalloc(&c->dev[i], c->bytes));
+        CHECK_HIP(hipMemcpy(c->dev[i], c->host[i], c->bytes, hipMemcpyHostToDevice));
+    }
+    c->want = malloc(c->bytes);
+    oracle_oneshot((const void* const*)c->host, n, c->want, numel, dtype);
+}
+
+static int same(const Case* c, const void* dev_out, const char* what) {
+    void* got = malloc(c->bytes);
+    CHECK_HIP(hipMemcpy(got, dev_out, c->bytes, hipMemcpyDeviceToHost));
+    const int ok = memcmp(got, c->want, c->bytes) == 0;
+    printf("%-40s n=%2d numel=%8zu %s: %s\n", what, c->n, c->numel, c->dtype == AR_F32 ? "f32 " : "bf16",
+           ok ? "match" : "MISMATCH");
+    free(got);
+    return ok;
+}
+
+static void teardown(Case* c) {
+    for (int i = 0; i < c->n; ++i) {
+        free(c->host[i]);
+        CHECK_HIP(hipFree(c->dev[i]));
+    }
+    free(c->want);
+}
+
+int main(void) {
+    int ok = 1;
+    void* out;
+    uint32_t* flags;
+    Case c;
+
+    /* one-shot and reduce-broadcast, ragged size */
+    setup(&c, 8, 8 * 8192 + 3, AR_BF16);
+    CHECK_HIP(hipMalloc(&out, c.bytes));
+    ok &= ar_oneshot((const void* const*)c.dev, c.n, out, c.numel, c.dtype, NULL) == AR_OK;
+    CHECK_HIP(hipDeviceSynchronize());
+    ok &= same(&c, out, "ar_oneshot");
+    void* outs[AR_MAX_RANKS];
+    for (int i = 0; i < c.n; ++i) CHECK_HIP(hipMalloc(&outs[i], c.bytes));
+    ok &= ar_reduce_bcast((const void* const*)c.dev, c.n, outs, c.numel, c.dtype, 0, c.n, NULL) == AR_OK;
+    CHECK_HIP(hipDeviceSynchronize());
+    for (int i = 0; i < c.n; ++i) ok &= same(&c, outs[i], "ar_reduce_bcast");
+    /* a written buffer overlapping an input is refused before anything runs */
+    ok &= ar_oneshot((const void* const*)c.dev, c.n, c.dev[3], c.numel, c.dtype, NULL) == AR_ERR_ALIAS;
+    for (int i = 0; i < c.n; ++i) CHECK_HIP(hipFree(outs[i]));
+    CHECK_HIP(hipFree(out));
+    teardown(&c);
+
+    /* fused two-shot, every rank, explicit then device-kept step ids */
+    setup(&c, 8, 8 * 8192, AR_BF16);
+    void* segs[AR_MAX_RANKS];
+    for (int i = 0; i < c.n; ++i) {
+        CHECK_HIP(hipMalloc(&segs[i], c.bytes / c.n));
+        CHECK_HIP(hipMalloc(&outs[i], c.bytes));
+    }
+    CHECK_HIP(hipMalloc((void**)&flags, ar_flag_bytes(c.n)));
+    ok &= ar_flag_barrier_reset(flags, c.n, NULL) == AR_OK;
+    ok &= ar_twoshot_rs((const void* const*)c.dev, c.n, segs, c.numel, c.dtype, 0, c.n, flags, 1, outs, NULL) == AR_OK;
+    CHECK_HIP(hipDeviceSynchronize());
+    for (int i = 0; i < c.n; ++i) ok &= same(&c, outs[i], "ar_twoshot_rs (fused, step 1)");
+    ok &= ar_flag_barrier_reset(flags, c.n, NULL) == AR_OK;
+    for (int rep = 0; rep < 3; ++rep)
+        ok &= ar_twoshot_rs((const void* const*)c.dev, c.n, segs, c.numel, c.dtype, 0, c.n, flags, 0, outs, NULL) ==
+              AR_OK;
+    CHECK_HIP(hipDeviceSynchronize());
+    uint32_t status = 1;
+    CHECK_HIP(hipMemcpy(&status, flags, 4, hipMemcpyDeviceToHost));
+    ok &= status == 0;
+    for (int i = 0; i < c.n; ++i) ok &= same(&c, outs[i], "ar_twoshot_rs (fused, auto step x3)");
+    for (int i = 0; i < c.n; ++i) {
+        CHECK_HIP(hipFree(segs[i]));
+        CHECK_HIP(hipFree(outs[i]));
+    }
+    teardown(&c);
+
+    /* LL and LL128, fp32, ragged */
+    setup(&c, 4, 16384 + 1, AR_F32);
+    CHECK_HIP(hipMalloc(&out, c.bytes));
+    for (int proto = AR_PROTO_LL; proto <= AR_PROTO_LL128; ++proto) {
+        const size_t W = ar_ll_wire_bytes(proto, c.bytes);
+        ok &= W == oracle_ll_wire_bytes(proto, c.bytes);
+        void* wires[AR_MAX_RANKS];
+        for (int i = 0; i < c.n; ++i) CHECK_HIP(hipMalloc(&wires[i], W));
+        ok &= ar_ll_pack((const void* const*)c.dev, wires, c.n, c.numel, c.dtype, proto, 7, NULL) == AR_OK;
+        const int st = proto == AR_PROTO_LL
+                           ? ar_ll_reduce_unpack((const void* const*)wires, c.n, out, c.numel, c.dtype, 7, flags, NULL)
+                           : ar_ll128_reduce_unpack((const void* const*)wires, c.n, out, c.numel, c.dtype, 7, flags,
+                                                    NULL);
+        ok &= st == AR_OK;
+        CHECK_HIP(hipDeviceSynchronize());
+        ok &= same(&c, out, proto == AR_PROTO_LL ? "ar_ll_pack + ar_ll_reduce_unpack"
+                                                 : "ar_ll_pack + ar_ll128_reduce_unpack");
+        for (int i = 0; i < c.n; ++i) CHECK_HIP(hipFree(wires[i]));
+    }
+    CHECK_HIP(hipMemcpy(&status, flags, 4, hipMemcpyDeviceToHost));
+    ok &= status == 0;
+    CHECK_HIP(hipFree(out));
+    CHECK_HIP(hipFree(flags));
+    teardown(&c);
+
+    printf(ok ? "c abi ok\n" : "c abi FAILED\n");
+    return ok ? 0 : 1;
+}
