@@ -53,8 +53,8 @@ class ArError(RuntimeError):
 def _load(path: str = LIB_PATH):
     if not os.path.exists(path):
         raise ImportError(
-            f"{path} is missing: build it with `python -m custom_all_reduce_amd.build` "
-            "(there is no CPU fallback)"
+            f"{path} is missing: build it with `python custom_all_reduce_amd/build.py` from the repository "
+            "root (there is no CPU fallback)"
         )
     lib = ctypes.CDLL(path)
     vp, sz, i32, u32, u64 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_uint32, ctypes.c_uint64

@@ -1,6 +1,7 @@
 """Build the gfx950 C-ABI library ``libar.so`` in-tree with hipcc.
 
-Usage: ``python -m custom_all_reduce_amd.build`` (or call :func:`build`).
+Usage: ``python custom_all_reduce_amd/build.py`` from the repository root (a
+plain script: it imports nothing from the package), or call :func:`build`.
 Each source compiles to an object with hipcc (parallel), then hipcc links
 the shared library.  The library holds the kernels for gfx950 only.
 """

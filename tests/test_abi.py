@@ -305,3 +305,19 @@ def test_selector_never_picks_an_inapplicable_two_shot():
     assert car.lib.ar_select_algo(8, 10, 0, float("nan")) == -car.AR_ERR_ARG
     assert car.lib.ar_algo_cost_us(6, 8, 10, 0, 0.0) < 0
     assert car.lib.ar_algo_cost_us(-1, 8, 10, 0, 0.0) < 0
+
+
+def test_import_fails_loudly_without_the_library(tmp_path):
+    """No CPU fallback: a copy of the package without libar.so refuses to import."""
+    import shutil
+    import sys as _sys
+    pkg = tmp_path / "custom_all_reduce_amd"
+    pkg.mkdir()
+    src = os.path.join(ROOT, "custom_all_reduce_amd")
+    for f in os.listdir(src):
+        if f.endswith(".py"):
+            shutil.copy(os.path.join(src, f), pkg / f)
+    r = subprocess.run([_sys.executable, "-c", "import custom_all_reduce_amd"], cwd=tmp_path, capture_output=True,
+                       text=True, timeout=120, env={**os.environ, "PYTHONPATH": str(tmp_path)})
+    assert r.returncode != 0
+    assert "libar.so is missing" in r.stderr and "no CPU fallback" in r.stderr
