@@ -108,6 +108,9 @@ def _dev_tensor(t: torch.Tensor, what: str):
         raise TypeError(f"{what} must be a torch.Tensor")
     if t.device.type != "cuda":
         raise ValueError(f"{what} must be a device tensor, got {t.device}")
+    if t.device.index is not None and t.device.index != torch.cuda.current_device():
+        # every call runs on the current device; another device's memory is not its to touch
+        raise ValueError(f"{what} is on {t.device}, but the current device is cuda:{torch.cuda.current_device()}")
     if not t.is_contiguous():
         raise ValueError(f"{what} must be contiguous")
     return t
@@ -138,7 +141,11 @@ ALGOS = ("oneshot", "twoshot", "ll", "ll128", "push", "bcast")  # ar_algo values
 
 
 def _dtype_arg(dtype) -> int:
-    return _DTYPES[dtype] if isinstance(dtype, torch.dtype) else int(dtype)
+    if isinstance(dtype, torch.dtype):
+        if dtype not in _DTYPES:
+            raise TypeError(f"unsupported dtype {dtype}: use float32 or bfloat16")
+        return _DTYPES[dtype]
+    return int(dtype)
 
 
 def algo_cost_us(algo: str, n: int, numel: int, dtype, sync_us: float = 0.0):
