@@ -3,6 +3,7 @@
 // so an error return means the stream is untouched.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
 #include <mutex>
 #include <vector>
@@ -63,14 +64,14 @@ Span span(const void* p, size_t bytes, bool written) {
 }
 
 // A written span may not overlap any other span; read spans may overlap each
-// other (one buffer may stand for several emulated ranks).
-bool spans_ok(const std::vector<Span>& v) {
+// other (one buffer may stand for several emulated ranks).  Sorted by start,
+// a span can only overlap the spans that start before it ends.
+bool spans_ok(std::vector<Span> v) {
+    std::sort(v.begin(), v.end(), [](const Span& x, const Span& y) { return x.lo < y.lo; });
     for (size_t a = 0; a < v.size(); ++a) {
-        if (!v[a].written || v[a].lo == v[a].hi) continue;
-        for (size_t b = 0; b < v.size(); ++b) {
-            if (a == b || v[b].lo == v[b].hi) continue;
-            if (v[a].lo < v[b].hi && v[b].lo < v[a].hi) return false;
-        }
+        if (v[a].lo == v[a].hi) continue;
+        for (size_t b = a + 1; b < v.size() && v[b].lo < v[a].hi; ++b)
+            if (v[b].lo != v[b].hi && (v[a].written || v[b].written)) return false;
     }
     return true;
 }

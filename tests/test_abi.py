@@ -321,3 +321,25 @@ def test_import_fails_loudly_without_the_library(tmp_path):
                        text=True, timeout=120, env={**os.environ, "PYTHONPATH": str(tmp_path)})
     assert r.returncode != 0
     assert "libar.so is missing" in r.stderr and "no CPU fallback" in r.stderr
+
+
+def test_overlap_check_finds_one_planted_overlap_anywhere():
+    """Random layouts of 2..16 senders x destinations with exactly one planted
+    overlap (a destination inside a source, or two destinations sharing bytes)
+    are refused wherever the overlap sits in address order.  Every layout
+    holds an overlap, so no call here gets past validation."""
+    import random
+    rnd = random.Random(5)
+    S = 4096
+    for trial in range(300):
+        nsrc, ndst = rnd.randint(1, 16), rnd.randint(2, 16)
+        slots = rnd.sample(range(1, 100000), nsrc + nsrc * ndst)  # distinct, far apart (S-byte units * 4)
+        addrs = [A + s * 4 * S for s in slots]
+        src, dst = addrs[:nsrc], addrs[nsrc:]
+        k = rnd.randrange(len(dst))
+        if rnd.random() < 0.5:
+            dst[k] = rnd.choice(src) + 16 * rnd.randint(0, S // 16 - 1)  # inside a source
+        else:
+            other = rnd.choice([d for i, d in enumerate(dst) if i != k])
+            dst[k] = other + 16 * rnd.randint(0, S // 16 - 1)  # sharing bytes with another destination
+        assert L.ar_push(arr(*src), nsrc, arr(*dst), ndst, S // 2, 1, NUL) == car.AR_ERR_ALIAS, trial
