@@ -580,6 +580,7 @@ def main(argv=None):
             "workload": desc,
             "n_ranks": n,
             "bytes_per_rank": S,
+            "arithmetic": f"{dt_name} data, fp32 accumulation in rank order, one rounding to {dt_name}",
             "step": "rank 0's share: oneshot + twoshot(RS seg 0 -> barrier -> AG out 0, fused) + "
                     "LL pack(own)/reduce(n) + LL128 pack(own)/reduce(n); peers' shares published before timing",
             "algorithmic_bytes_per_step": bytes_per_step,
