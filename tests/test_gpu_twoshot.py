@@ -219,3 +219,36 @@ def test_synchronous_errors_on_device_buffers():
     with pytest.raises(car.ArError) as e:
         car.ar_twoshot_rs(rk.ins, [rk.ins[0][:100]] + rk.segs[1:], rk.flags, step=1)
     assert e.value.code == car.AR_ERR_ALIAS
+
+
+def test_largest_step_id_then_reset_and_restart():
+    """Step ids run up to 2^32 - 1; a reset lets them start again at 1
+    (every wait passes at >= step, so without the reset step 1 would see the
+    old slots as arrived)."""
+    n = 4
+    host = synth.rank_inputs(n, n * 8 * 300, "bf16", "normal", config=95)
+    want = oracle_bits(oracle.oneshot(host, "bf16"))
+    rk = Ranks(host, "bf16")
+    last = (1 << 32) - 1
+    car.ar_twoshot_rs(rk.ins, rk.segs, rk.flags, last, outs=rk.outs)
+    torch.cuda.synchronize()
+    car.raise_on_status(rk.flags)
+    for r in range(n):
+        assert np.array_equal(bits(rk.outs[r]), want)
+    for proto in ("ll", "ll128"):
+        W = car.ll_wire_bytes(proto, host[0].size * 2)
+        wires = [torch.empty(W, dtype=torch.uint8, device="cuda") for _ in range(n)]
+        out = torch.empty(host[0].size, dtype=rk.ins[0].dtype, device="cuda")
+        car.ar_ll_pack(rk.ins, wires, proto, last)
+        (car.ar_ll_reduce_unpack if proto == "ll" else car.ar_ll128_reduce_unpack)(wires, out, last, rk.flags)
+        torch.cuda.synchronize()
+        car.raise_on_status(rk.flags, proto)
+        assert np.array_equal(bits(out), want), proto
+    car.ar_flag_barrier_reset(rk.flags, n)
+    for o in rk.outs:
+        o.zero_()
+    car.ar_twoshot_rs(rk.ins, rk.segs, rk.flags, 1, outs=rk.outs)
+    torch.cuda.synchronize()
+    car.raise_on_status(rk.flags)
+    for r in range(n):
+        assert np.array_equal(bits(rk.outs[r]), want)
