@@ -157,6 +157,15 @@ def timed_replay(torch, g):
     return a.elapsed_time(b)
 
 
+def launch_floor_us(torch, K):
+    """Average time of one graph-replayed launch that does almost nothing (a
+    one-element fill), timed like the kernels: the floor under every launch."""
+    t = torch.zeros(1, device="cuda")
+    g = graph_of(torch, lambda: [t.fill_(float(i)) for i in range(K)])
+    timed_replay(torch, g)
+    return round(timed_replay(torch, g) * 1e3 / K, 3)
+
+
 def read_traffic(kernel: str, workload: str):
     """HBM bytes per launch from a committed counter summary, if it was taken
     on the current kernel source; else None."""
@@ -559,6 +568,7 @@ def main(argv=None):
             }
         car.raise_on_status(flags, "per-kernel timing")
     dominant = max(kernels, key=lambda k: kernels[k]["avg_us"]) if kernels else None
+    floor_us = launch_floor_us(torch, K) if kernels else None
     print(f"bench: timed {K} steps, {ms_per_step * 1e3:.2f} us per step; kernels {kernels}", file=sys.stderr,
           flush=True)
 
@@ -604,6 +614,8 @@ def main(argv=None):
             "frac": round(A / HBM_PEAK, 4),
             "traffic": tb,
             "algorithmic_bytes_per_launch": per_bytes[dominant],
+            "avg_us": kernels[dominant]["avg_us"],
+            "launch_floor_us": floor_us,
         }
     if args.cpu_seconds > 0:
         line["cpu_baseline"] = cpu_baseline(host, dt_name, n, numel, per_bytes, args.cpu_seconds)
