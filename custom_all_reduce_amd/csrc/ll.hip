@@ -21,6 +21,9 @@ namespace ar {
 namespace {
 
 constexpr int kBlock = 256;
+// LL receiver: one wavefront per workgroup (measured 5% faster than four at
+// 128 KiB, 8 MiB and 64 MiB per rank, 5% slower at 1 MiB).
+constexpr int kBlockLL = kWave;
 // LL128 receiver: one wavefront per workgroup (measured faster than four at
 // every size from 128 KiB to 8 MiB per rank: more, smaller workgroups spread
 // the few waves of a small message over more CUs).
@@ -110,7 +113,7 @@ struct ReduceParams {
 // LL receiver.  Lane chunk c = lines 2c and 2c+1 of every rank (one 16-byte
 // load per rank; a wavefront's load instruction reads 1 KiB of whole lines)
 // and output bytes [8c, 8c+8) (one 8-byte store).  A lane handles U chunks
-// kBlock apart, so U * n loads are in flight before the first add.
+// kBlockLL apart, so U * n loads are in flight before the first add.
 template <typename T> struct HalfAcc;  // accumulator for 8 data bytes
 template <> struct HalfAcc<float> {
     float a[2] = {0.0f, 0.0f};
@@ -180,15 +183,15 @@ __device__ __forceinline__ void store_out_bytes(uint8_t* out, size_t off, size_t
 
 // LL receiver.  Lane chunk c = lines 2c and 2c+1 of every rank (one 16-byte
 // load per rank; a wavefront's load instruction reads 1 KiB of whole lines)
-// and output bytes [8c, 8c+8).  A lane handles U chunks kBlock apart.  The
+// and output bytes [8c, 8c+8).  A lane handles U chunks kBlockLL apart.  The
 // main path is branch-free: lanes past the last two-line chunk load a valid
 // clamped chunk and discard it, so all U * n loads issue back to back.  A
 // final single line (odd line count) is finished by one lane on its own.
 template <typename T, int NR, int U>
-__global__ __launch_bounds__(kBlock) void ll_reduce_kernel(ReduceParams p) {
+__global__ __launch_bounds__(kBlockLL) void ll_reduce_kernel(ReduceParams p) {
     const int lane = threadIdx.x & (kWave - 1);
     const size_t nfull = p.nlines / 2;  // chunks that hold two lines
-    const size_t c0 = size_t(blockIdx.x) * (kBlock * U) + threadIdx.x;
+    const size_t c0 = size_t(blockIdx.x) * (kBlockLL * U) + threadIdx.x;
     const u32x4* w[NR];
 #pragma unroll
     for (int r = 0; r < NR; ++r) w[r] = reinterpret_cast<const u32x4*>(p.wire[r]);
@@ -198,7 +201,7 @@ __global__ __launch_bounds__(kBlock) void ll_reduce_kernel(ReduceParams p) {
         bool act[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const size_t c = c0 + size_t(u) * kBlock;
+            const size_t c = c0 + size_t(u) * kBlockLL;
             act[u] = c < nfull;
             const size_t cc = act[u] ? c : nfull - 1;
 #pragma unroll
@@ -212,11 +215,11 @@ __global__ __launch_bounds__(kBlock) void ll_reduce_kernel(ReduceParams p) {
         if (wave_ballot(!ok) != 0) {
 #pragma unroll
             for (int u = 0; u < U; ++u)
-                if (!ll_slow_wait<NR>(p, c0 + size_t(u) * kBlock, act[u] ? 2u : 0u, x[u], lane)) return;
+                if (!ll_slow_wait<NR>(p, c0 + size_t(u) * kBlockLL, act[u] ? 2u : 0u, x[u], lane)) return;
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const size_t c = c0 + size_t(u) * kBlock;
+            const size_t c = c0 + size_t(u) * kBlockLL;
             HalfAcc<T> acc;
 #pragma unroll
             for (int r = 0; r < NR; ++r) acc.add(x[u][r].x, x[u][r].z);
@@ -233,9 +236,9 @@ __global__ __launch_bounds__(kBlock) void ll_reduce_kernel(ReduceParams p) {
     }
     // A last chunk with a single line (odd line count): chunk nfull, finished
     // by the one lane of the grid that owns that chunk index.
-    const size_t rel = nfull - size_t(blockIdx.x) * (kBlock * U);
-    if ((p.nlines & 1) && nfull >= size_t(blockIdx.x) * (kBlock * U) && rel < size_t(kBlock) * U &&
-        rel % kBlock == threadIdx.x) {
+    const size_t rel = nfull - size_t(blockIdx.x) * (kBlockLL * U);
+    if ((p.nlines & 1) && nfull >= size_t(blockIdx.x) * (kBlockLL * U) && rel < size_t(kBlockLL) * U &&
+        rel % kBlockLL == threadIdx.x) {
         u32x4 x[NR];
 #pragma unroll
         for (int r = 0; r < NR; ++r) {
@@ -394,8 +397,8 @@ hipError_t launch_reduce_t(const ReduceParams& p, int proto, hipStream_t s) {
         // within a few percent at 64 MiB.
         constexpr int U = 1;
         const size_t chunks = (p.nlines + 1) / 2;
-        const size_t grid = (chunks + kBlock * U - 1) / (kBlock * U);
-        hipLaunchKernelGGL((ll_reduce_kernel<T, NR, U>), dim3(uint32_t(grid)), dim3(kBlock), 0, s, p);
+        const size_t grid = (chunks + kBlockLL * U - 1) / (kBlockLL * U);
+        hipLaunchKernelGGL((ll_reduce_kernel<T, NR, U>), dim3(uint32_t(grid)), dim3(kBlockLL), 0, s, p);
     } else {
         // One 8-line unit per wavefront: measured faster than two for every
         // size, and the two-unit fp32 instantiation stalls badly.
