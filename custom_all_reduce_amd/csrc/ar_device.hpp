@@ -60,23 +60,25 @@ __device__ __forceinline__ u32x4 ld_coherent(__amdgpu_buffer_rsrc_t r, uint32_t 
 __device__ __forceinline__ void wait_stores() { __builtin_amdgcn_s_waitcnt(0); }
 
 // ---- rounding ---------------------------------------------------------------
-// float32 -> bfloat16 pattern, round to nearest, ties to even.  Adding
-// 0x7FFF plus the lowest kept bit to the pattern carries into the kept half
-// exactly when the dropped half is above one half, or exactly one half with
-// an odd kept half; a carry out of the mantissa lands in the exponent (so
-// overflow gives infinity).  NaN keeps its sign and top payload bits and is
-// made quiet.
-__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
-    uint32_t u = __float_as_uint(f);
-    uint32_t rounded = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
-    uint32_t quiet = (u >> 16) | 0x40u;
-    return ((u & 0x7FFFFFFFu) > 0x7F800000u) ? quiet : rounded;
+// float32 -> bfloat16 pattern, round to nearest, ties to even; NaN keeps its
+// sign and top payload bits and is made quiet.  gfx950 has this conversion
+// in hardware for a pair of values (v_cvt_pk_bf16_f32, reached through a
+// vector conversion to __bf16): one instruction per two results in place of
+// the seven of an integer rounding sequence.  Checked on the device against
+// the integer definition (add 0x7FFF plus the lowest kept bit, keep the high
+// half; NaN -> pattern >> 16 | 0x40) for all 2^32 fp32 patterns: identical,
+// NaN included, under the default rounding and denormal modes that these
+// kernels run with.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    const f32x2 f = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));
 }
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) { return pack_bf16x2(f, 0.0f) & 0xFFFFu; }
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-    return f32_to_bf16_rne(lo) | (f32_to_bf16_rne(hi) << 16);
-}
 
 // ---- accumulation -----------------------------------------------------------
 // Accumulator for one 16-byte vector position: 4 fp32 or 8 bf16 elements,
@@ -124,6 +126,30 @@ template <> struct Acc<bf16_t> {
     __device__ __forceinline__ u32x4 result() const {
         return u32x4{pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]), pack_bf16x2(a[4], a[5]),
                      pack_bf16x2(a[6], a[7])};
+    }
+};
+
+// Accumulator for one 8-byte position: 2 fp32 or 4 bf16 elements, given as
+// two 32-bit words per rank; same order and rounding as Acc.
+template <typename T> struct Acc8;
+template <> struct Acc8<float> {
+    float a[2] = {0.0f, 0.0f};
+    __device__ __forceinline__ void add(uint32_t w0, uint32_t w1) {
+        a[0] = a[0] + __uint_as_float(w0);
+        a[1] = a[1] + __uint_as_float(w1);
+    }
+    __device__ __forceinline__ void add(u32x2 v) { add(v.x, v.y); }
+    __device__ __forceinline__ u32x2 result() const { return u32x2{__float_as_uint(a[0]), __float_as_uint(a[1])}; }
+};
+template <> struct Acc8<bf16_t> {
+    float a[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    __device__ __forceinline__ void add(uint32_t w0, uint32_t w1) {
+        a[0] = a[0] + bf16_lo(w0); a[1] = a[1] + bf16_hi(w0);
+        a[2] = a[2] + bf16_lo(w1); a[3] = a[3] + bf16_hi(w1);
+    }
+    __device__ __forceinline__ void add(u32x2 v) { add(v.x, v.y); }
+    __device__ __forceinline__ u32x2 result() const {
+        return u32x2{pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3])};
     }
 };
 

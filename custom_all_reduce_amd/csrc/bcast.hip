@@ -41,6 +41,7 @@ __global__ __launch_bounds__(kBlock) void reduce_bcast_kernel(InVecs<NR> in, Out
         u32x4 x[NR];
 #pragma unroll
         for (int r = 0; r < NR; ++r) x[r] = in.p[r][idx];
+        __builtin_amdgcn_sched_barrier(0);  // every load ahead of the first add
         Acc<T> acc;
 #pragma unroll
         for (int r = 0; r < NR; ++r) acc.add(x[r]);

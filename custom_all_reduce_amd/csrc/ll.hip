@@ -110,30 +110,6 @@ struct ReduceParams {
     uint32_t step;
 };
 
-// LL receiver.  Lane chunk c = lines 2c and 2c+1 of every rank (one 16-byte
-// load per rank; a wavefront's load instruction reads 1 KiB of whole lines)
-// and output bytes [8c, 8c+8) (one 8-byte store).  A lane handles U chunks
-// kBlockLL apart, so U * n loads are in flight before the first add.
-template <typename T> struct HalfAcc;  // accumulator for 8 data bytes
-template <> struct HalfAcc<float> {
-    float a[2] = {0.0f, 0.0f};
-    __device__ __forceinline__ void add(uint32_t w0, uint32_t w1) {
-        a[0] = a[0] + __uint_as_float(w0);
-        a[1] = a[1] + __uint_as_float(w1);
-    }
-    __device__ __forceinline__ u32x2 result() const { return u32x2{__float_as_uint(a[0]), __float_as_uint(a[1])}; }
-};
-template <> struct HalfAcc<bf16_t> {
-    float a[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-    __device__ __forceinline__ void add(uint32_t w0, uint32_t w1) {
-        a[0] = a[0] + bf16_lo(w0); a[1] = a[1] + bf16_hi(w0);
-        a[2] = a[2] + bf16_lo(w1); a[3] = a[3] + bf16_hi(w1);
-    }
-    __device__ __forceinline__ u32x2 result() const {
-        return u32x2{pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3])};
-    }
-};
-
 // Bounded wait for the lines [2c, 2c + nl) of every rank (nl = 1 or 2), re-read
 // with agent-coherent atomic 64-bit loads into x (data in .x/.z, flags in
 // .y/.w).  Lanes with nl == 0 just take part in the ballots.  Returns false
@@ -207,11 +183,20 @@ __global__ __launch_bounds__(kBlockLL) void ll_reduce_kernel(ReduceParams p) {
 #pragma unroll
             for (int r = 0; r < NR; ++r) x[u][r] = ld_stream(w[r] + cc);
         }
+        // Keep every load ahead of the first use: left alone, the scheduler
+        // sometimes hoists a flag compare between the loads, and the wait it
+        // needs then serialises two memory round trips.
+        __builtin_amdgcn_sched_barrier(0);
+        // Readiness without short-circuit branches: the smallest flag a lane
+        // holds, folded with min as the loads land.
         bool ok = true;
 #pragma unroll
-        for (int u = 0; u < U; ++u)
+        for (int u = 0; u < U; ++u) {
+            uint32_t fmin = 0xFFFFFFFFu;
 #pragma unroll
-            for (int r = 0; r < NR; ++r) ok = ok && (!act[u] || (x[u][r].y >= p.step && x[u][r].w >= p.step));
+            for (int r = 0; r < NR; ++r) fmin = min(fmin, min(x[u][r].y, x[u][r].w));
+            ok &= !act[u] | (fmin >= p.step);
+        }
         if (wave_ballot(!ok) != 0) {
 #pragma unroll
             for (int u = 0; u < U; ++u)
@@ -220,7 +205,7 @@ __global__ __launch_bounds__(kBlockLL) void ll_reduce_kernel(ReduceParams p) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const size_t c = c0 + size_t(u) * kBlockLL;
-            HalfAcc<T> acc;
+            Acc8<T> acc;
 #pragma unroll
             for (int r = 0; r < NR; ++r) acc.add(x[u][r].x, x[u][r].z);
             const u32x2 res = acc.result();
@@ -271,7 +256,7 @@ __global__ __launch_bounds__(kBlockLL) void ll_reduce_kernel(ReduceParams p) {
                 if (!ok) __builtin_amdgcn_s_sleep(1);
             }
         }
-        HalfAcc<T> acc;
+        Acc8<T> acc;
 #pragma unroll
         for (int r = 0; r < NR; ++r) acc.add(x[r].x, 0u);
         const u32x2 res = acc.result();
@@ -301,12 +286,17 @@ __global__ __launch_bounds__(kBlock128) void ll128_reduce_kernel(ReduceParams p)
 #pragma unroll
         for (int r = 0; r < NR; ++r) x[u][r] = ld_stream(w[r] + ll * 8 + part);
     }
+    __builtin_amdgcn_sched_barrier(0);  // every load ahead of the first use
+    // Readiness without short-circuit branches: the lane at part 7 folds the
+    // low flag words with min, a nonzero high word counting as ready.
     bool ok = true;
 #pragma unroll
-    for (int u = 0; u < U; ++u)
+    for (int u = 0; u < U; ++u) {
+        uint32_t fmin = 0xFFFFFFFFu;
 #pragma unroll
-        for (int r = 0; r < NR; ++r)
-            ok = ok && (!valid[u] || part != 7u || x[u][r].z >= p.step || x[u][r].w != 0u);
+        for (int r = 0; r < NR; ++r) fmin = min(fmin, x[u][r].w != 0u ? 0xFFFFFFFFu : x[u][r].z);
+        ok &= !valid[u] | (part != 7u) | (fmin >= p.step);
+    }
     if (wave_ballot(!ok) != 0) {
         // Slow path: poll the flags with coherent 64-bit loads, then re-read
         // the data of every line after an acquire fence.

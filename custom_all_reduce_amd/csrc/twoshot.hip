@@ -38,9 +38,9 @@
 // gets a fresh id on every replay.  Every wavefront keeps its own copy of
 // each rank's epoch (the id of the rank's last reduce-scatter) after the
 // arrival slots; auto launches always use the same grid, so all copies move
-// in step.  A wavefront loads its copies when it starts (the loads overlap
-// its first reduce-scatter loads) and, if the launch reduces, stores epoch +
-// 1 back as soon as its reduce-scatter is done.  No other wavefront touches
+// in step.  A wavefront loads its copies right behind its first
+// reduce-scatter loads (at the start if it has none to do) and, if the
+// launch reduces, stores epoch + 1 back as soon as its reduce-scatter is done.  No other wavefront touches
 // those copies, so there is no counter, atomic or barrier.  A split
 // all-gather uses the current epoch, the id of the reduce-scatter before it.
 #include <mutex>
@@ -71,11 +71,19 @@ struct TwoShotParams {
 };
 
 template <typename T, int NR, int U>
-__device__ __forceinline__ void reduce_scatter_phase(const TwoShotParams& p, uint32_t step_lane,
-                                                     uint32_t wave, uint32_t nwaves, int lane) {
+__device__ __forceinline__ void reduce_scatter_phase(const TwoShotParams& p, const uint32_t* epoch,
+                                                     uint32_t& epoch_lane, uint32_t wave, uint32_t nwaves,
+                                                     int lane) {
     const uint32_t R = uint32_t(p.r1 - p.r0);
     const uint32_t items = R * p.ktiles;
-    if (wave >= items) return;
+    // Auto step ids: lane l < R loads this wavefront's epoch copy of rank
+    // r0 + l right behind the first unit's loads, so that it travels with
+    // them instead of costing a round trip of its own before them.
+    const bool load_epoch = p.auto_step && uint32_t(lane) < R;
+    if (wave >= items) {
+        if (load_epoch) epoch_lane = flag_load_relaxed(epoch + size_t(lane) * kEpochCopies);
+        return;
+    }
     const uint32_t my_items = (items - wave + nwaves - 1) / nwaves;
     const uint32_t upt = p.tile / kWave;
     const uint32_t my_units = my_items * upt;
@@ -109,6 +117,8 @@ __device__ __forceinline__ void reduce_scatter_phase(const TwoShotParams& p, uin
 #pragma unroll
             for (int i = 0; i < NR; ++i) x[u][i] = ld_stream(in[i] + src);
         }
+        if (q0 == 0 && load_epoch) epoch_lane = flag_load_relaxed(epoch + size_t(lane) * kEpochCopies);
+        __builtin_amdgcn_sched_barrier(0);  // every load ahead of the first add
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             Acc<T> acc;
@@ -138,7 +148,7 @@ __device__ __forceinline__ void reduce_scatter_phase(const TwoShotParams& p, uin
         const uint32_t it = wave + (k < my_items ? k : 0u) * nwaves;
         const uint32_t r = uint32_t(p.r0) + it / p.ktiles;
         const uint32_t t = it % p.ktiles;
-        const uint32_t st = __shfl(step_lane, int(r) - p.r0);
+        const uint32_t st = __shfl(p.auto_step ? epoch_lane + 1u : p.step, int(r) - p.r0);
         if (k < my_items) flag_store_relaxed(slots + r * kSlotsPerRank + t, st);
     }
 }
@@ -230,13 +240,15 @@ __global__ __launch_bounds__(kBlock) void twoshot_kernel(TwoShotParams p) {
     // epoch copy in auto mode).
     const uint32_t R = uint32_t(p.r1 - p.r0);
     uint32_t* epoch = p.flags + kStatusWords + NR * kSlotsPerRank + size_t(p.r0) * kEpochCopies + wave;
-    uint32_t step_lane = p.step;
-    if (p.auto_step && uint32_t(lane) < R)
-        step_lane = flag_load_relaxed(epoch + size_t(lane) * kEpochCopies) + (p.do_rs ? 1u : 0u);
+    uint32_t epoch_lane = 0;
     if (p.do_rs) {
-        reduce_scatter_phase<T, NR, U>(p, step_lane, wave, nwaves, lane);
-        if (p.auto_step && uint32_t(lane) < R) flag_store_relaxed(epoch + size_t(lane) * kEpochCopies, step_lane);
+        reduce_scatter_phase<T, NR, U>(p, epoch, epoch_lane, wave, nwaves, lane);
+        if (p.auto_step && uint32_t(lane) < R) flag_store_relaxed(epoch + size_t(lane) * kEpochCopies, epoch_lane + 1u);
     }
+    else if (p.auto_step && uint32_t(lane) < R) {
+        epoch_lane = flag_load_relaxed(epoch + size_t(lane) * kEpochCopies);
+    }
+    const uint32_t step_lane = p.auto_step ? epoch_lane + (p.do_rs ? 1u : 0u) : p.step;
     if (p.do_ag) {
         // In the fused form the all-gather items are dealt starting after the
         // wavefronts that hold reduce-scatter items, so that when the grid has
