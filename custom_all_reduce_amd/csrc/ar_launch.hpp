@@ -13,8 +13,9 @@ namespace ar {
 
 // Flag region layout for n ranks (32-bit words): word 0 status, word 1
 // detail, words 2..31 unused (one 128-byte line), then kSlotsPerRank arrival
-// slots per rank, then kEpochCopies epoch copies per rank (one per wavefront
-// of an auto-step two-shot launch).
+// slots per rank, then kEpochCopies x n epoch copies: wavefront w of an
+// auto-step two-shot launch keeps rank r's copy at word w * n + r of that
+// area, so one wavefront's copies share a cache line.
 constexpr int kMaxRanks = 16;
 constexpr int kSlotsPerRank = 1024;
 constexpr int kEpochCopies = 4096;

@@ -38,9 +38,10 @@
 // gets a fresh id on every replay.  Every wavefront keeps its own copy of
 // each rank's epoch (the id of the rank's last reduce-scatter) after the
 // arrival slots; auto launches always use the same grid, so all copies move
-// in step.  A wavefront loads its copies right behind its first
-// reduce-scatter loads (at the start if it has none to do) and, if the
-// launch reduces, stores epoch + 1 back as soon as its reduce-scatter is done.  No other wavefront touches
+// in step.  A wavefront loads its copies right behind the first loads of
+// its first phase (reduce-scatter data or all-gather slot polls; on their
+// own if it has no work) and, if the launch reduces, stores epoch + 1 back
+// at its end.  No other wavefront touches
 // those copies, so there is no counter, atomic or barrier.  A split
 // all-gather uses the current epoch, the id of the reduce-scatter before it.
 #include <mutex>
@@ -71,19 +72,16 @@ struct TwoShotParams {
 };
 
 template <typename T, int NR, int U>
-__device__ __forceinline__ void reduce_scatter_phase(const TwoShotParams& p, const uint32_t* epoch,
+__device__ __forceinline__ bool reduce_scatter_phase(const TwoShotParams& p, const uint32_t* epoch,
                                                      uint32_t& epoch_lane, uint32_t wave, uint32_t nwaves,
                                                      int lane) {
     const uint32_t R = uint32_t(p.r1 - p.r0);
     const uint32_t items = R * p.ktiles;
+    if (wave >= items) return false;
     // Auto step ids: lane l < R loads this wavefront's epoch copy of rank
     // r0 + l right behind the first unit's loads, so that it travels with
     // them instead of costing a round trip of its own before them.
     const bool load_epoch = p.auto_step && uint32_t(lane) < R;
-    if (wave >= items) {
-        if (load_epoch) epoch_lane = flag_load_relaxed(epoch + size_t(lane) * kEpochCopies);
-        return;
-    }
     const uint32_t my_items = (items - wave + nwaves - 1) / nwaves;
     const uint32_t upt = p.tile / kWave;
     const uint32_t my_units = my_items * upt;
@@ -117,7 +115,7 @@ __device__ __forceinline__ void reduce_scatter_phase(const TwoShotParams& p, con
 #pragma unroll
             for (int i = 0; i < NR; ++i) x[u][i] = ld_stream(in[i] + src);
         }
-        if (q0 == 0 && load_epoch) epoch_lane = flag_load_relaxed(epoch + size_t(lane) * kEpochCopies);
+        if (q0 == 0 && load_epoch) epoch_lane = flag_load_relaxed(epoch + lane);
         __builtin_amdgcn_sched_barrier(0);  // every load ahead of the first add
 #pragma unroll
         for (int u = 0; u < U; ++u) {
@@ -151,6 +149,7 @@ __device__ __forceinline__ void reduce_scatter_phase(const TwoShotParams& p, con
         const uint32_t st = __shfl(p.auto_step ? epoch_lane + 1u : p.step, int(r) - p.r0);
         if (k < my_items) flag_store_relaxed(slots + r * kSlotsPerRank + t, st);
     }
+    return true;
 }
 
 // Source segment of the jj-th all-gather copy into out[ro]: every segment in
@@ -160,8 +159,13 @@ __device__ __forceinline__ uint32_t ag_source(uint32_t jj, uint32_t ro, bool ski
     return (skip_own && jj >= ro) ? jj + 1 : jj;
 }
 
-__device__ __forceinline__ void all_gather_phase(const TwoShotParams& p, uint32_t step_lane, int n,
-                                                 uint32_t wave, uint32_t nwaves, int lane) {
+// With auto step ids and no epoch loaded yet (have_epoch false), the
+// wavefront loads its epoch copies right behind its first slot poll, so the
+// two loads share one round trip; the step id a slot must reach is epoch +
+// step_inc.
+__device__ __forceinline__ void all_gather_phase(const TwoShotParams& p, const uint32_t* epoch,
+                                                 uint32_t& epoch_lane, bool& have_epoch, uint32_t step_inc,
+                                                 int n, uint32_t wave, uint32_t nwaves, int lane) {
     const uint32_t R = uint32_t(p.r1 - p.r0);
     const bool skip_own = p.do_rs != 0;
     const uint32_t per_out = uint32_t(skip_own ? n - 1 : n) * p.ktiles;
@@ -178,7 +182,6 @@ __device__ __forceinline__ void all_gather_phase(const TwoShotParams& p, uint32_
         // lane ro - r0
         const uint32_t it = wave + (need ? k : 0u) * nwaves;
         const uint32_t ro = uint32_t(p.r0) + it / per_out;
-        const uint32_t want = __shfl(step_lane, int(ro) - p.r0);
         uint32_t j = 0, t = 0;
         if (need) {
             const uint32_t rem = it % per_out;
@@ -186,9 +189,15 @@ __device__ __forceinline__ void all_gather_phase(const TwoShotParams& p, uint32_
             t = rem % p.ktiles;
         }
         const uint32_t* slot = slots + j * kSlotsPerRank + t;
+        uint32_t seen = need ? flag_load_relaxed(slot) : 0u;
+        if (!have_epoch) {
+            if (uint32_t(lane) < R) epoch_lane = flag_load_relaxed(epoch + lane);
+            have_epoch = true;
+        }
+        const uint32_t want = __shfl(p.auto_step ? epoch_lane + step_inc : p.step, int(ro) - p.r0);
         const uint64_t t0 = now_ticks();
         while (true) {
-            const bool ok = !need || flag_load_relaxed(slot) >= want;
+            const bool ok = !need || seen >= want;
             const uint64_t missing = ~wave_ballot(ok) & wave_exec();
             if (missing == 0) break;
             if (now_ticks() - t0 > p.timeout_ticks) {
@@ -199,6 +208,7 @@ __device__ __forceinline__ void all_gather_phase(const TwoShotParams& p, uint32_
                 return;  // skip every copy of this wavefront
             }
             __builtin_amdgcn_s_sleep(1);
+            if (need) seen = flag_load_relaxed(slot);
         }
     }
     const uint32_t upt = p.tile / kWave;
@@ -239,16 +249,15 @@ __global__ __launch_bounds__(kBlock) void twoshot_kernel(TwoShotParams p) {
     // Lane l < r1 - r0 holds the step id of rank r0 + l (this wavefront's
     // epoch copy in auto mode).
     const uint32_t R = uint32_t(p.r1 - p.r0);
-    uint32_t* epoch = p.flags + kStatusWords + NR * kSlotsPerRank + size_t(p.r0) * kEpochCopies + wave;
+    // this wavefront's epoch copies, one word per rank (lane l: rank r0 + l)
+    uint32_t* epoch = p.flags + kStatusWords + NR * kSlotsPerRank + size_t(wave) * NR + p.r0;
+    // Auto step ids: the epoch copies are loaded by whichever phase runs
+    // first in this wavefront, together with that phase's first loads (or
+    // on their own at the end if the wavefront has no work), and epoch + 1
+    // is stored back at the end if the launch reduces.
     uint32_t epoch_lane = 0;
-    if (p.do_rs) {
-        reduce_scatter_phase<T, NR, U>(p, epoch, epoch_lane, wave, nwaves, lane);
-        if (p.auto_step && uint32_t(lane) < R) flag_store_relaxed(epoch + size_t(lane) * kEpochCopies, epoch_lane + 1u);
-    }
-    else if (p.auto_step && uint32_t(lane) < R) {
-        epoch_lane = flag_load_relaxed(epoch + size_t(lane) * kEpochCopies);
-    }
-    const uint32_t step_lane = p.auto_step ? epoch_lane + (p.do_rs ? 1u : 0u) : p.step;
+    bool have_epoch = !p.auto_step;
+    if (p.do_rs && reduce_scatter_phase<T, NR, U>(p, epoch, epoch_lane, wave, nwaves, lane)) have_epoch = true;
     if (p.do_ag) {
         // In the fused form the all-gather items are dealt starting after the
         // wavefronts that hold reduce-scatter items, so that when the grid has
@@ -256,7 +265,11 @@ __global__ __launch_bounds__(kBlock) void twoshot_kernel(TwoShotParams p) {
         // after the other in the same wavefronts.
         const uint32_t rs_busy = p.do_rs ? min(R * p.ktiles, nwaves) : 0u;
         const uint32_t ag_wave = wave >= rs_busy ? wave - rs_busy : wave + (nwaves - rs_busy);
-        all_gather_phase(p, step_lane, NR, ag_wave, nwaves, lane);
+        all_gather_phase(p, epoch, epoch_lane, have_epoch, p.do_rs ? 1u : 0u, NR, ag_wave, nwaves, lane);
+    }
+    if (p.auto_step && p.do_rs) {
+        if (!have_epoch && uint32_t(lane) < R) epoch_lane = flag_load_relaxed(epoch + lane);
+        if (uint32_t(lane) < R) flag_store_relaxed(epoch + lane, epoch_lane + 1u);
     }
 }
 
@@ -273,7 +286,7 @@ __global__ __launch_bounds__(kBlock) void ag_wait_kernel(TwoShotParams p) {
     if (p.auto_step) {
         want = 0;
         for (int r = p.r0; r < p.r1; ++r) {
-            const uint32_t e = flag_load_relaxed(p.flags + kStatusWords + NR * kSlotsPerRank + size_t(r) * kEpochCopies);
+            const uint32_t e = flag_load_relaxed(p.flags + kStatusWords + NR * kSlotsPerRank + r);
             want = e > want ? e : want;
         }
     }

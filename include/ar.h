@@ -91,7 +91,8 @@ typedef enum { AR_PROTO_LL = 0, AR_PROTO_LL128 = 1 } ar_proto;
 /* Bytes of the flag region used by the two-shot barrier and the LL status
  * word for up to n ranks: a 128-byte status line (word 0 status, word 1
  * detail), then AR_SLOTS_PER_RANK 32-bit arrival slots per rank, then
- * AR_EPOCH_COPIES 32-bit epoch copies per rank (auto step ids): in all
+ * AR_EPOCH_COPIES groups of n 32-bit epoch copies (auto step ids; group w
+ * belongs to wavefront w of an auto launch, word r of it to rank r): in all
  * 128 + n * (AR_SLOTS_PER_RANK + AR_EPOCH_COPIES) * 4 bytes.  Returns 0
  * if n is out of range. */
 size_t ar_flag_bytes(int n);

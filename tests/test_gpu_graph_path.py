@@ -29,11 +29,12 @@ def epochs(flags, n):
     workgroups per CU take part in an auto launch; the other copies stay 0)."""
     grid = 8 * torch.cuda.get_device_properties(0).multi_processor_count
     base = 32 + n * car.AR_SLOTS_PER_RANK
-    w = flags[base:base + n * car.AR_EPOCH_COPIES].cpu().numpy().astype(np.int64).reshape(n, -1)
-    assert (w[:, grid:] == 0).all()
+    # group w (n words) belongs to wavefront w; word r of it to rank r
+    w = flags[base:base + n * car.AR_EPOCH_COPIES].cpu().numpy().astype(np.int64).reshape(-1, n)
+    assert (w[grid:, :] == 0).all()
     for r in range(n):
-        assert (w[r, :grid] == w[r, 0]).all(), f"rank {r}: epoch copies differ"
-    return w[:, 0].tolist()
+        assert (w[:grid, r] == w[0, r]).all(), f"rank {r}: epoch copies differ"
+    return w[0, :].tolist()
 
 
 class Set:

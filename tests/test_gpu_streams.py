@@ -66,5 +66,6 @@ def test_two_streams_from_two_threads():
             assert np.array_equal(bits(j.outs[r]), j.want), f"job {k} two-shot rank {r}"
             assert np.array_equal(bits(j.bc[r]), j.want), f"job {k} reduce-broadcast out[{r}]"
         base = 32 + j.n * car.AR_SLOTS_PER_RANK
-        ep = j.flags[base:base + j.n * car.AR_EPOCH_COPIES].cpu().numpy().reshape(j.n, -1)[:, 0]
+        # wavefront 0's group of epoch copies, one word per rank
+        ep = j.flags[base:base + j.n * car.AR_EPOCH_COPIES].cpu().numpy().reshape(-1, j.n)[0, :]
         assert (ep == STEPS).all(), f"job {k} epochs {ep}"
