@@ -344,8 +344,8 @@ def select_table(args, torch, car, np, out_path):
     over SELECT_SIZES bytes per rank (cold: buffer sets rotated over >= 1 GiB;
     graph-replayed).  The shares: one-shot; rank 0's fused two-shot after the
     peers' reduce-scatter; rank 0's LL / LL128 pack plus the receiver over
-    every rank's wire buffer, the peers' wires packed beforehand.  Writes one
-    JSON object per (n, size)."""
+    every rank's wire buffer, the peers' wires packed beforehand.  Each time
+    is the median of three replays.  Writes one JSON object per (n, size)."""
     rows = []
     gen = torch.Generator(device="cuda")
     with open(out_path, "w", encoding="utf-8") as f:
@@ -397,7 +397,9 @@ def select_table(args, torch, car, np, out_path):
                     cs = calls[a]
                     g = graph_of(torch, lambda cs=cs: [cs[i % nsets](1 + i) for i in range(K)])
                     timed_replay(torch, g)
-                    row[a + "_us"] = round(timed_replay(torch, g) * 1e3 / K, 3)
+                    # median of three replays: one disturbed replay does not move the table
+                    reps = sorted(timed_replay(torch, g) for _ in range(3))
+                    row[a + "_us"] = round(reps[1] * 1e3 / K, 3)
                     del g
                 car.raise_on_status(flags, f"select-table n={n} S={Sb}")
                 rows.append(row)

@@ -56,6 +56,27 @@ constexpr int kBlock = 256;
 constexpr int kWavesPerBlock = kBlock / kWave;
 constexpr int kCopyUnroll = 4;
 
+// Division by a launch-invariant divisor d for numerators below 2^31, as a
+// multiply-high, an add and a shift (Granlund and Montgomery, "Division by
+// invariant integers using multiplication", 1994, the round-up multiplier):
+// with s = ceil(log2 d) and m = ceil(2^(32+s) / d) = 2^32 + mlo,
+// n / d = (mulhi(n, mlo) + n) >> s.  The error of m is below d <= 2^s, so
+// the quotient is exact for every n < 2^32; n < 2^31 keeps the sum in 32
+// bits.  The item and unit indices divided here stay far below 2^31.
+struct FastDiv {
+    uint32_t d, mlo, s;
+};
+__device__ __forceinline__ uint32_t fdiv(uint32_t n, const FastDiv& f) { return (__umulhi(n, f.mlo) + n) >> f.s; }
+
+FastDiv make_fastdiv(uint32_t d) {
+    if (d == 0) return FastDiv{0, 0, 0};  // no items: never divided by
+    uint32_t s = 0;
+    while ((uint64_t(1) << s) < d) ++s;
+    const uint64_t two32s = uint64_t(1) << (32 + s);  // s <= 31 here
+    const uint64_t m = (two32s + d - 1) / d;            // in [2^32, 2^33)
+    return FastDiv{d, uint32_t(m - (uint64_t(1) << 32)), s};
+}
+
 struct TwoShotParams {
     const u32x4* in[kMaxRanks];
     u32x4* seg[kMaxRanks];
@@ -69,6 +90,9 @@ struct TwoShotParams {
     int auto_step;
     int r0, r1;
     int do_rs, do_ag;
+    FastDiv div_upt;      // units per tile
+    FastDiv div_ktiles;   // tiles per segment
+    FastDiv div_per_out;  // all-gather items per output rank
 };
 
 template <typename T, int NR, int U>
@@ -102,10 +126,11 @@ __device__ __forceinline__ bool reduce_scatter_phase(const TwoShotParams& p, con
         for (int u = 0; u < U; ++u) {
             const bool unit_ok = q0 + u < my_units;
             const uint32_t q = unit_ok ? q0 + u : q0;
-            const uint32_t k = q / upt, sub = q - k * upt;
+            const uint32_t k = fdiv(q, p.div_upt), sub = q - k * upt;
             const uint32_t it = wave + k * nwaves;
-            const uint32_t r = uint32_t(p.r0) + it / p.ktiles;
-            const uint32_t t = it - (it / p.ktiles) * p.ktiles;
+            const uint32_t rr = fdiv(it, p.div_ktiles);
+            const uint32_t r = uint32_t(p.r0) + rr;
+            const uint32_t t = it - rr * p.ktiles;
             const uint32_t idx = t * p.tile + sub * kWave + uint32_t(lane);
             valid[u] = unit_ok && idx < p.mvec;
             dst_idx[u] = idx;
@@ -144,8 +169,9 @@ __device__ __forceinline__ bool reduce_scatter_phase(const TwoShotParams& p, con
     for (uint32_t kb = 0; kb < my_items; kb += kWave) {
         const uint32_t k = kb + uint32_t(lane);
         const uint32_t it = wave + (k < my_items ? k : 0u) * nwaves;
-        const uint32_t r = uint32_t(p.r0) + it / p.ktiles;
-        const uint32_t t = it % p.ktiles;
+        const uint32_t rr = fdiv(it, p.div_ktiles);
+        const uint32_t r = uint32_t(p.r0) + rr;
+        const uint32_t t = it - rr * p.ktiles;
         const uint32_t st = __shfl(p.auto_step ? epoch_lane + 1u : p.step, int(r) - p.r0);
         if (k < my_items) flag_store_relaxed(slots + r * kSlotsPerRank + t, st);
     }
@@ -155,8 +181,10 @@ __device__ __forceinline__ bool reduce_scatter_phase(const TwoShotParams& p, con
 // Source segment of the jj-th all-gather copy into out[ro]: every segment in
 // order, or, when the reduce-scatter of the same launch already wrote out[ro]'s
 // own segment, every segment but ro's.
+// Integer arithmetic only (jj, ro < 2^31: the sign bit of ro - jj - 1 is
+// jj >= ro), so that wavefront-uniform operands stay in scalar registers.
 __device__ __forceinline__ uint32_t ag_source(uint32_t jj, uint32_t ro, bool skip_own) {
-    return (skip_own && jj >= ro) ? jj + 1 : jj;
+    return jj + (((ro - jj - 1u) >> 31) & uint32_t(skip_own));
 }
 
 // With auto step ids and no epoch loaded yet (have_epoch false), the
@@ -181,12 +209,14 @@ __device__ __forceinline__ void all_gather_phase(const TwoShotParams& p, const u
         // every lane active here: the output rank's step id is read from
         // lane ro - r0
         const uint32_t it = wave + (need ? k : 0u) * nwaves;
-        const uint32_t ro = uint32_t(p.r0) + it / per_out;
+        const uint32_t oo = fdiv(it, p.div_per_out);
+        const uint32_t ro = uint32_t(p.r0) + oo;
         uint32_t j = 0, t = 0;
         if (need) {
-            const uint32_t rem = it % per_out;
-            j = ag_source(rem / p.ktiles, ro, skip_own);
-            t = rem % p.ktiles;
+            const uint32_t rem = it - oo * per_out;
+            const uint32_t jj = fdiv(rem, p.div_ktiles);
+            j = ag_source(jj, ro, skip_own);
+            t = rem - jj * p.ktiles;
         }
         const uint32_t* slot = slots + j * kSlotsPerRank + t;
         uint32_t seen = need ? flag_load_relaxed(slot) : 0u;
@@ -221,12 +251,14 @@ __device__ __forceinline__ void all_gather_phase(const TwoShotParams& p, const u
         for (int u = 0; u < kCopyUnroll; ++u) {
             const bool unit_ok = q0 + u < my_units;
             const uint32_t q = unit_ok ? q0 + u : q0;
-            const uint32_t k = q / upt, sub = q - k * upt;
+            const uint32_t k = fdiv(q, p.div_upt), sub = q - k * upt;
             const uint32_t it = wave + k * nwaves;
-            const uint32_t ro = uint32_t(p.r0) + it / per_out;
-            const uint32_t rem = it % per_out;
-            const uint32_t j = ag_source(rem / p.ktiles, ro, skip_own);
-            const uint32_t t = rem % p.ktiles;
+            const uint32_t oo = fdiv(it, p.div_per_out);
+            const uint32_t ro = uint32_t(p.r0) + oo;
+            const uint32_t rem = it - oo * per_out;
+            const uint32_t jj = fdiv(rem, p.div_ktiles);
+            const uint32_t j = ag_source(jj, ro, skip_own);
+            const uint32_t t = rem - jj * p.ktiles;
             const uint32_t idx = t * p.tile + sub * kWave + uint32_t(lane);
             valid[u] = unit_ok && idx < p.mvec;
             const uint32_t t0 = t * p.tile;
@@ -321,6 +353,8 @@ void tile_params(TwoShotParams& p, size_t seg_bytes) {
     p.tile = ((per_slot + kWave - 1) / kWave) * kWave;
     if (p.tile == 0) p.tile = kWave;
     p.ktiles = (p.mvec + p.tile - 1) / p.tile;
+    p.div_upt = make_fastdiv(p.tile / kWave);
+    p.div_ktiles = make_fastdiv(p.ktiles);
 }
 
 template <typename T, int NR>
@@ -348,6 +382,7 @@ hipError_t launch_t(const TwoShotRequest& rq, hipStream_t s) {
     p.r1 = rq.r1;
     p.do_rs = rq.do_rs;
     p.do_ag = rq.do_ag;
+    p.div_per_out = make_fastdiv(uint32_t(rq.do_rs ? NR - 1 : NR) * p.ktiles);
 
     auto kern = twoshot_kernel<T, NR, U>;
     const uint32_t R = uint32_t(rq.r1 - rq.r0);
