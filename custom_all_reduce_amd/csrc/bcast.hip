@@ -14,11 +14,14 @@
 // the one-shot.  One sender reads S and writes n * S.  With one destination
 // it is the staging copy of a caller's tensor into its registered buffer.
 //
-// Both kernels keep one 16-byte vector per lane (the shape measured fastest
-// for the one-shot) and stream their stores past the caches.  Their loads
-// are plain: measured, that is 15-20% faster at 64 MiB per rank than
-// nontemporal loads for these store-heavy kernels (the read-heavy one-shot,
-// two-shot and LL kernels measure the other way round).
+// The reduce-broadcast takes one 8-byte half of a 16-byte vector per lane
+// (half the arithmetic per lane and twice the wavefronts, as in the
+// one-shot: measured equal or up to 8% faster, 3-4% for every rank's share
+// at 64 MiB); the push, which has no arithmetic, one 16-byte vector.  Both
+// stream their stores past the caches.  Their loads are plain: measured,
+// that is 15-20% faster at 64 MiB per rank than nontemporal loads for these
+// store-heavy kernels (the read-heavy one-shot, two-shot and LL kernels
+// measure the other way round).
 #include "ar_device.hpp"
 #include "ar_launch.hpp"
 
@@ -30,24 +33,25 @@ constexpr int kBlock = 128;
 template <int NR> struct InVecs { const u32x4* p[NR]; };
 template <int NR> struct OutVecs { u32x4* p[NR]; };
 
-// Vectors [vb, ve) of every input reduced and stored into all NR outputs.
-// With ntail != 0 (the launch owns the end of the message, ve = all full
+// Vectors [vb, ve) (16-byte units, the ownership unit) of every input
+// reduced and stored into all NR outputs, one 8-byte half per lane.  With
+// ntail != 0 (the launch owns the end of the message, ve = all full
 // vectors) the last workgroup also sums the ntail trailing elements.
 template <typename T, int NR>
 __global__ __launch_bounds__(kBlock) void reduce_bcast_kernel(InVecs<NR> in, OutVecs<NR> out, uint32_t vb,
                                                               uint32_t ve, uint32_t ntail) {
-    const uint32_t idx = vb + blockIdx.x * kBlock + threadIdx.x;
-    if (idx < ve) {
-        u32x4 x[NR];
+    const size_t h = size_t(vb) * 2 + size_t(blockIdx.x) * kBlock + threadIdx.x;
+    if (h < size_t(ve) * 2) {
+        u32x2 x[NR];
 #pragma unroll
-        for (int r = 0; r < NR; ++r) x[r] = in.p[r][idx];
+        for (int r = 0; r < NR; ++r) x[r] = reinterpret_cast<const u32x2*>(in.p[r])[h];
         __builtin_amdgcn_sched_barrier(0);  // every load ahead of the first add
-        Acc<T> acc;
+        Acc8<T> acc;
 #pragma unroll
         for (int r = 0; r < NR; ++r) acc.add(x[r]);
-        const u32x4 y = acc.result();
+        const u32x2 y = acc.result();
 #pragma unroll
-        for (int r = 0; r < NR; ++r) st_stream(out.p[r] + idx, y);
+        for (int r = 0; r < NR; ++r) __builtin_nontemporal_store(y, reinterpret_cast<u32x2*>(out.p[r]) + h);
     }
     if (ntail != 0 && blockIdx.x == gridDim.x - 1 && threadIdx.x < ntail) {
         const size_t k = size_t(ve) * elem<T>::per_vec + threadIdx.x;
@@ -95,7 +99,7 @@ hipError_t launch_bcast_t(const void* const* in, void* const* out, size_t numel,
         pi.p[r] = static_cast<const u32x4*>(in[r]);
         po.p[r] = static_cast<u32x4*>(out[r]);
     }
-    uint32_t grid = (ve - vb + kBlock - 1) / kBlock;
+    uint32_t grid = uint32_t((size_t(ve - vb) * 2 + kBlock - 1) / kBlock);
     if (grid == 0) grid = 1;
     hipLaunchKernelGGL((reduce_bcast_kernel<T, NR>), dim3(grid), dim3(kBlock), 0, s, pi, po, vb, ve, ntail);
     return hipGetLastError();
