@@ -53,7 +53,7 @@ WORKLOADS = {
 KERNELS = ["oneshot", "twoshot", "ll_pack", "ll_reduce", "ll128_pack", "ll128_reduce"]
 KERNEL_SOURCES = {
     "oneshot": ["oneshot.hip"],
-    "twoshot": ["twoshot.hip"],
+    "twoshot": ["twoshot.hip", "fastdiv.hpp"],
     "ll_pack": ["ll.hip"],
     "ll_reduce": ["ll.hip"],
     "ll128_pack": ["ll.hip"],

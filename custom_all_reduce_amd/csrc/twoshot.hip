@@ -48,6 +48,7 @@
 
 #include "ar_device.hpp"
 #include "ar_launch.hpp"
+#include "fastdiv.hpp"
 
 namespace ar {
 namespace {
@@ -56,26 +57,9 @@ constexpr int kBlock = 256;
 constexpr int kWavesPerBlock = kBlock / kWave;
 constexpr int kCopyUnroll = 4;
 
-// Division by a launch-invariant divisor d for numerators below 2^31, as a
-// multiply-high, an add and a shift (Granlund and Montgomery, "Division by
-// invariant integers using multiplication", 1994, the round-up multiplier):
-// with s = ceil(log2 d) and m = ceil(2^(32+s) / d) = 2^32 + mlo,
-// n / d = (mulhi(n, mlo) + n) >> s.  The error of m is below d <= 2^s, so
-// the quotient is exact for every n < 2^32; n < 2^31 keeps the sum in 32
-// bits.  The item and unit indices divided here stay far below 2^31.
-struct FastDiv {
-    uint32_t d, mlo, s;
-};
+// n / d for the launch-invariant divisors of the tiling (FastDiv, built on
+// the host by make_fastdiv): a multiply-high, an add and a shift.
 __device__ __forceinline__ uint32_t fdiv(uint32_t n, const FastDiv& f) { return (__umulhi(n, f.mlo) + n) >> f.s; }
-
-FastDiv make_fastdiv(uint32_t d) {
-    if (d == 0) return FastDiv{0, 0, 0};  // no items: never divided by
-    uint32_t s = 0;
-    while ((uint64_t(1) << s) < d) ++s;
-    const uint64_t two32s = uint64_t(1) << (32 + s);  // s <= 31 here
-    const uint64_t m = (two32s + d - 1) / d;            // in [2^32, 2^33)
-    return FastDiv{d, uint32_t(m - (uint64_t(1) << 32)), s};
-}
 
 struct TwoShotParams {
     const u32x4* in[kMaxRanks];
