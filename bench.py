@@ -61,11 +61,22 @@ KERNEL_SOURCES = {
 }
 
 
+def code_text(src: str) -> str:
+    """C++ source with comments removed and whitespace collapsed: what the
+    compiler sees, so that a comment edit does not count as a kernel change.
+    (The kernel sources hold no string literal that contains // or /*.)"""
+    src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", " ", src)
+    return " ".join(src.split())
+
+
 def kernel_src_sha(kernel: str) -> str:
+    """Hash of the code (comments excluded) of a kernel's sources, recorded
+    beside its HBM counters: the counters count only while it matches."""
     h = hashlib.sha256()
     for f in KERNEL_SOURCES[kernel] + ["ar_device.hpp"]:
-        with open(os.path.join(ROOT, "custom_all_reduce_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "custom_all_reduce_amd", "csrc", f), encoding="utf-8") as fh:
+            h.update(code_text(fh.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -16,7 +16,9 @@
 // Items are dealt to wavefronts round-robin (phase 2 starting after the
 // wavefronts that have phase-1 items); a wavefront walks its items as a flat
 // list of 64-vector units (one vector per lane) and keeps U units of loads in
-// flight before it adds or stores.
+// flight before it adds or stores.  A unit's item, rank and tile come from
+// divisions by launch-invariant values, done as multiply-high and shift with
+// multipliers computed on the host (fastdiv.hpp).
 //
 // Barrier.  Each tile (r, t) has a 32-bit arrival slot.  Segments are
 // written and read with device-coherent (sc1) accesses, so after its last
@@ -25,9 +27,9 @@
 // wavefront polls the slots of all its items, one slot per lane, until a
 // ballot shows every lane sees slot >= step, then copies.  (An agent-scope
 // release/acquire fence pair per wavefront would write back and invalidate
-// a whole XCD L2 each time; measured, that costs several times the copy.)  Waits are bounded by a wall-clock budget; on expiry the first
-// missing (rank, tile) goes to the status words and the wavefront skips its
-// copies.  In the fused form the grid is no larger than what the device
+// a whole XCD L2 each time; measured, that costs several times the copy.)
+// Waits are bounded by a wall-clock budget; on expiry the first missing
+// (rank, tile) goes to the status words and the wavefront skips its copies.  In the fused form the grid is no larger than what the device
 // holds at once (occupancy-checked, persistent), and every wavefront finishes
 // phase 1 before it polls, so every slot a poller needs is eventually written
 // while nothing else occupies the CUs; if something does, the bounded wait
@@ -41,9 +43,9 @@
 // in step.  A wavefront loads its copies right behind the first loads of
 // its first phase (reduce-scatter data or all-gather slot polls; on their
 // own if it has no work) and, if the launch reduces, stores epoch + 1 back
-// at its end.  No other wavefront touches
-// those copies, so there is no counter, atomic or barrier.  A split
-// all-gather uses the current epoch, the id of the reduce-scatter before it.
+// at its end.  No other wavefront touches those copies, so there is no
+// counter, atomic or barrier.  A split all-gather uses the current epoch,
+// the id of the reduce-scatter before it.
 #include <mutex>
 
 #include "ar_device.hpp"

@@ -49,3 +49,13 @@ def test_store_path_accounting():
     assert acc.reduce_bcast(n, S, n) == (n * S, n * S)
     assert acc.push(S, n) == (S, n * S)
     assert acc.push(S, 1) == (S, S)
+
+
+def test_kernel_hash_ignores_comments_but_not_code():
+    """The hash that keeps a kernel's HBM counters valid changes with its
+    code, not with its comments."""
+    src = 'int f(int a) {  // add one\n    /* block\n comment */ return a + 1;\n}\n'
+    assert bench.code_text(src) == bench.code_text(src.replace("add one", "increment"))
+    assert bench.code_text(src) == bench.code_text(src.replace("    ", "\t"))
+    assert bench.code_text(src) != bench.code_text(src.replace("a + 1", "a + 2"))
+    assert "//" not in bench.code_text(src) and "/*" not in bench.code_text(src)
