@@ -7,8 +7,9 @@
 // LL128 line: 128 bytes = 120 data bytes, then a 64-bit flag.
 // Data bytes past the message in the last line are zero.
 //
-// LL receiver: a lane owns 16 wire bytes of every rank (2 lines, one 16-byte
-// load per rank) and produces 8 output bytes.
+// LL receiver: up to 16 MiB per rank a lane owns one line of every rank (one
+// 8-byte load per rank) and produces 4 output bytes; above, 16 wire bytes of
+// every rank (2 lines, one 16-byte load per rank) and 8 output bytes.
 // LL128 receiver: a wavefront owns 1 KiB of wire per rank = 8 lines; lane l
 // holds 16 bytes at part l % 8 of line l / 8, and the lane at part 7 holds 8
 // data bytes plus the flag.  Readiness of the whole wavefront is one ballot.
@@ -24,6 +25,8 @@ constexpr int kBlock = 256;
 // LL receiver: one wavefront per workgroup (measured 5% faster than four at
 // 128 KiB, 8 MiB and 64 MiB per rank, 5% slower at 1 MiB).
 constexpr int kBlockLL = kWave;
+// Messages up to this many bytes per rank take the one-line LL receiver.
+constexpr size_t kOneLineMaxBytes = size_t(16) << 20;
 // LL128 receiver: one wavefront per workgroup (measured faster than four at
 // every size from 128 KiB to 8 MiB per rank: more, smaller workgroups spread
 // the few waves of a small message over more CUs).
@@ -265,6 +268,71 @@ __global__ __launch_bounds__(kBlockLL) void ll_reduce_kernel(ReduceParams p) {
     }
 }
 
+// LL receiver, one line per lane: lane c owns line c of every rank (one
+// 8-byte load per rank: 4 data bytes and the flag) and output bytes
+// [4c, 4c+4).  Half the elements per lane of the two-line kernel and twice
+// the wavefronts; measured faster up to 16 MiB per rank (n = 16 at 1 MiB:
+// 8.6 -> 7.4 us; n = 8 at 1-8 MiB: 3-4%), slower above (n = 16 at 64 MiB:
+// 342 -> 363 us), where the two-line kernel runs.
+template <typename T, int NR>
+__global__ __launch_bounds__(kBlockLL) void ll_reduce1_kernel(ReduceParams p) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const size_t c = size_t(blockIdx.x) * kBlockLL + threadIdx.x;
+    const bool act = c < p.nlines;
+    const size_t cc = act ? c : p.nlines - 1;
+    u32x2 x[NR];
+#pragma unroll
+    for (int r = 0; r < NR; ++r) x[r] = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p.wire[r]) + cc);
+    __builtin_amdgcn_sched_barrier(0);  // every load ahead of the first use
+    uint32_t fmin = 0xFFFFFFFFu;
+#pragma unroll
+    for (int r = 0; r < NR; ++r) fmin = min(fmin, x[r].y);
+    bool ok = !act | (fmin >= p.step);
+    if (wave_ballot(!ok) != 0) {
+        const uint64_t t0 = now_ticks();
+        while (true) {
+            bool good = true;
+            int bad_r = 0;
+#pragma unroll
+            for (int r = 0; r < NR; ++r) {
+                if (act && x[r].y < p.step) {
+                    const uint64_t a = line_load_relaxed(reinterpret_cast<const uint64_t*>(p.wire[r]) + c);
+                    x[r].x = uint32_t(a);
+                    x[r].y = uint32_t(a >> 32);
+                    if (x[r].y < p.step && good) { good = false; bad_r = r; }
+                }
+            }
+            const uint64_t missing = ~wave_ballot(good) & wave_exec();
+            if (missing == 0) break;
+            if (now_ticks() - t0 > p.timeout_ticks) {
+                const int bl = __ffsll((unsigned long long)missing) - 1;
+                if (lane == bl) report_timeout(p.flags, 2u, uint32_t(bad_r), uint32_t(c));
+                return;
+            }
+            __builtin_amdgcn_s_sleep(1);
+        }
+    }
+    if (!act) return;
+    uint32_t word;
+    if (elem<T>::bytes == 4) {
+        float a = 0.0f;
+#pragma unroll
+        for (int r = 0; r < NR; ++r) a = a + __uint_as_float(x[r].x);
+        word = __float_as_uint(a);
+    } else {
+        float a0 = 0.0f, a1 = 0.0f;
+#pragma unroll
+        for (int r = 0; r < NR; ++r) { a0 = a0 + bf16_lo(x[r].x); a1 = a1 + bf16_hi(x[r].x); }
+        word = pack_bf16x2(a0, a1);
+    }
+    if (4 * c + 4 <= p.nbytes) {
+        __builtin_nontemporal_store(word, reinterpret_cast<uint32_t*>(p.out) + c);
+    } else {
+        const uint32_t rw[1] = {word};
+        store_out_bytes<T>(p.out, 4 * c, p.nbytes, rw);
+    }
+}
+
 template <typename T, int NR, int U>
 __global__ __launch_bounds__(kBlock128) void ll128_reduce_kernel(ReduceParams p) {
     const int lane = threadIdx.x & (kWave - 1);
@@ -381,10 +449,13 @@ __global__ __launch_bounds__(kBlock128) void ll128_reduce_kernel(ReduceParams p)
 
 template <typename T, int NR>
 hipError_t launch_reduce_t(const ReduceParams& p, int proto, hipStream_t s) {
-    if (proto == 0) {
-        // One 16-byte load per lane per rank: measured faster than two from
-        // 128 KiB to 8 MiB per rank (more workgroups in flight) and equal
-        // within a few percent at 64 MiB.
+    if (proto == 0 && p.nbytes <= kOneLineMaxBytes) {
+        const size_t grid = (p.nlines + kBlockLL - 1) / kBlockLL;
+        hipLaunchKernelGGL((ll_reduce1_kernel<T, NR>), dim3(uint32_t(grid)), dim3(kBlockLL), 0, s, p);
+    } else if (proto == 0) {
+        // One 16-byte load (two lines) per lane per rank: measured faster
+        // than two from 128 KiB to 8 MiB per rank (more workgroups in flight)
+        // and equal within a few percent at 64 MiB.
         constexpr int U = 1;
         const size_t chunks = (p.nlines + 1) / 2;
         const size_t grid = (chunks + kBlockLL * U - 1) / (kBlockLL * U);

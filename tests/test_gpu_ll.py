@@ -130,3 +130,58 @@ def test_wire_sizes_for_the_64KiB_and_1MiB_messages():
     for S in (64 * 1024, 1024 * 1024):
         assert car.ll_wire_bytes("ll", S) == 2 * S
         assert car.ll_wire_bytes("ll128", S) == oracle.ll_wire_bytes("ll128", S)
+
+
+# The LL receiver has two kernels: one line per lane up to 16 MiB per rank,
+# two lines per lane above (whose odd last line is finished by one lane).
+# These cases sit on both sides of that boundary, with partial last lines.
+ONE_LINE_MAX = 16 << 20
+
+
+@pytest.mark.parametrize("dt, numel", [("f32", ONE_LINE_MAX // 4), ("f32", ONE_LINE_MAX // 4 + 3),
+                                       ("bf16", ONE_LINE_MAX // 2), ("bf16", ONE_LINE_MAX // 2 + 5)])
+@pytest.mark.parametrize("n", [2, 3])
+def test_ll_reduce_either_side_of_the_kernel_switch(dt, numel, n):
+    host = synth.rank_inputs(n, numel, dt, "normal", config=120 + n)
+    srcs = [to_dev(a) for a in host]
+    bufs, W = wires_for(n, numel, dt, "ll")
+    wires = [b[:W] for b in bufs]
+    flags = car.new_flags(n)
+    outbuf = filled(numel + 64, DT[dt])
+    out = outbuf[:numel]
+    car.ar_ll_pack(srcs, wires, "ll", step=4)
+    car.ar_ll_reduce_unpack(wires, out, 4, flags)
+    torch.cuda.synchronize()
+    assert car.read_status(flags)[0] == 0
+    got = bits(out)
+    want = oracle_bits(oracle.oneshot(host, dt))
+    assert np.array_equal(got, want), first_mismatch(got, want)
+    assert np.array_equal(bits(outbuf[numel:]), bits(filled(64, DT[dt]))), "wrote past the output"
+
+
+def test_stale_rank_above_the_kernel_switch_times_out():
+    """The two-line receiver's bounded wait: rank 1 packed the previous step."""
+    n, numel, dt = 2, ONE_LINE_MAX // 4 + 3, "f32"
+    host = synth.rank_inputs(n, numel, dt, "normal", config=130)
+    srcs = [to_dev(a) for a in host]
+    bufs, W = wires_for(n, numel, dt, "ll")
+    wires = [b[:W] for b in bufs]
+    flags = car.new_flags(n)
+    car.ar_ll_pack([srcs[0]], [wires[0]], "ll", step=21)
+    car.ar_ll_pack([srcs[1]], [wires[1]], "ll", step=20)
+    out = torch.empty(numel, device="cuda")
+    old = car.get_poll_timeout_ns()
+    car.set_poll_timeout_ns(20_000)
+    try:
+        car.ar_ll_reduce_unpack(wires, out, 21, flags)
+        torch.cuda.synchronize()
+    finally:
+        car.set_poll_timeout_ns(old)
+    word, detail = car.read_status(flags)
+    assert car.decode_status(word) == (car.AR_ERR_TIMEOUT, car.PHASE_LL, 1)
+    assert detail < numel
+    car.ar_flag_barrier_reset(flags, n)
+    car.ar_ll_reduce_unpack(wires, out, 20, flags)
+    torch.cuda.synchronize()
+    assert car.read_status(flags)[0] == 0
+    assert np.array_equal(bits(out), oracle_bits(oracle.oneshot(host, dt)))
