@@ -174,3 +174,20 @@ def test_device_errors_raise():
     with pytest.raises(car.ArError) as e:
         car.ar_oneshot([a[:1024], b[:1024]], a[4:1028])  # output inside an input
     assert e.value.code == car.AR_ERR_ALIAS
+
+
+# The one-shot takes 4-byte lanes below 512 KiB per rank and 8-byte lanes
+# from there on; these sizes sit on both sides of that switch, with and
+# without a partial last vector.
+NARROW_MAX = 512 << 10
+
+
+@pytest.mark.parametrize("dt, numel", [("f32", NARROW_MAX // 4 - 1), ("f32", NARROW_MAX // 4),
+                                       ("f32", NARROW_MAX // 4 + 1), ("bf16", NARROW_MAX // 2 - 1),
+                                       ("bf16", NARROW_MAX // 2), ("bf16", NARROW_MAX // 2 + 3)])
+@pytest.mark.parametrize("n", [3, 16])
+def test_either_side_of_the_lane_width_switch(dt, numel, n):
+    ins = synth.rank_inputs(n, numel, dt, "normal", config=140 + n)
+    got = run_oneshot(ins, dt)
+    want = oracle_bits(oracle.oneshot(ins, dt))
+    assert np.array_equal(got, want), first_mismatch(got, want)
