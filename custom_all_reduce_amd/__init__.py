@@ -13,6 +13,7 @@ Functions mirror the C entry points and take ``torch.Tensor`` arguments:
     ar_ll_pack(srcs, wires, proto, step)
     ar_ll_reduce_unpack(wires, out, step, flags)
     ar_ll128_reduce_unpack(wires, out, step, flags)
+    ar_ll_allreduce(src, wires, out, flags, proto, me, step)   pack + reduce, one launch
     ar_flag_barrier_reset(flags, n)
 
 Each call enqueues on ``stream`` (default: torch's current stream) and
@@ -74,6 +75,8 @@ def _load(path: str = LIB_PATH):
     lib.ar_ll_reduce_unpack.argtypes, lib.ar_ll_reduce_unpack.restype = [P, i32, vp, sz, i32, u32, vp, vp], i32
     lib.ar_ll128_reduce_unpack.argtypes = [P, i32, vp, sz, i32, u32, vp, vp]
     lib.ar_ll128_reduce_unpack.restype = i32
+    lib.ar_ll_allreduce.argtypes = [vp, P, i32, i32, vp, sz, i32, i32, u32, vp, vp]
+    lib.ar_ll_allreduce.restype = i32
     lib.ar_flag_barrier_reset.argtypes, lib.ar_flag_barrier_reset.restype = [vp, i32, vp], i32
     lib.ar_select_algo.argtypes, lib.ar_select_algo.restype = [i32, sz, i32, ctypes.c_double], i32
     lib.ar_algo_cost_us.argtypes, lib.ar_algo_cost_us.restype = [i32, i32, sz, i32, ctypes.c_double], ctypes.c_double
@@ -322,6 +325,20 @@ def prepare_ll_reduce(wires, out, flags, proto) -> Prepared:
     return Prepared(fn, args, 5, name, (wires, out, flags))
 
 
+def prepare_ll_allreduce(src, wires, out, flags, proto, me: int) -> Prepared:
+    """One GPU's LL / LL128 step in one launch: pack rank ``me``'s message
+    ``src`` into ``wires[me]`` and reduce every rank's message into ``out``."""
+    src = _dev_tensor(src, "src")
+    wires = [_dev_tensor(t, "wire") for t in wires]
+    out = _dev_tensor(out, "out")
+    flags = _dev_tensor(flags, "flags")
+    if src.dtype != out.dtype or src.numel() != out.numel():
+        raise ValueError("src and out must share dtype and numel")
+    args = [src.data_ptr(), _ptr_array([t.data_ptr() for t in wires]), len(wires), int(me), out.data_ptr(),
+            out.numel(), _dtype_code(out), _PROTOS[proto], 0, flags.data_ptr(), None]
+    return Prepared(_lib.ar_ll_allreduce, args, 8, "ar_ll_allreduce", (src, wires, out, flags))
+
+
 def ar_oneshot(ins, out: torch.Tensor, stream=None):
     """out = sum of ins (fp32 accumulation in rank order, one rounding)."""
     prepare_oneshot(ins, out)(stream=stream)
@@ -366,6 +383,11 @@ def ar_ll_reduce_unpack(wires, out, step: int, flags, stream=None):
 
 def ar_ll128_reduce_unpack(wires, out, step: int, flags, stream=None):
     prepare_ll_reduce(wires, out, flags, "ll128")(step, stream)
+    return out
+
+
+def ar_ll_allreduce(src, wires, out, flags, proto, me: int, step: int, stream=None):
+    prepare_ll_allreduce(src, wires, out, flags, proto, me)(step, stream)
     return out
 
 

@@ -313,6 +313,30 @@ int ar_ll128_reduce_unpack(const void* const* wire, int n, void* out, size_t num
     return ll_reduce_common(wire, n, out, numel, dtype, step, flags, AR_PROTO_LL128, stream);
 }
 
+int ar_ll_allreduce(const void* src, void* const* wire, int n, int me, void* out, size_t numel, int dtype,
+                    int proto, uint32_t step, uint32_t* flags, void* stream) {
+    if (!ranks_ok(n) || me < 0 || me >= n || !dtype_ok(dtype) || numel == 0 || !src || !wire || !out || !flags ||
+        step == 0)
+        return AR_ERR_ARG;
+    if (proto != AR_PROTO_LL && proto != AR_PROTO_LL128) return AR_ERR_ARG;
+    const size_t es = elem_bytes(dtype);
+    if (numel > kMaxBytes / es) return AR_ERR_ARG;
+    for (int i = 0; i < n; ++i) {
+        if (!wire[i]) return AR_ERR_ARG;
+        if (!aligned16(wire[i])) return AR_ERR_ALIGN;
+    }
+    if (!aligned16(src) || !aligned16(out) || !aligned16(flags)) return AR_ERR_ALIGN;
+    const size_t S = numel * es, W = wire_bytes(proto, S);
+    std::vector<Span> v;
+    v.push_back(span(src, S, false));
+    v.push_back(span(out, S, true));
+    v.push_back(span(flags, kStatusBytes, true));
+    for (int i = 0; i < n; ++i) v.push_back(span(wire[i], W, i == me));
+    if (!spans_ok(v)) return AR_ERR_ALIAS;
+    return hip_status(launch_ll_allreduce(src, wire, n, me, out, numel, dtype, proto, step, flags, timeout_ticks(),
+                                          static_cast<hipStream_t>(stream)));
+}
+
 double ar_algo_cost_us(int algo, int n, size_t numel, int dtype, double sync_us) {
     if (algo < AR_ALGO_ONESHOT || algo >= kSelNumAlgos || !ranks_ok(n) || !dtype_ok(dtype) || numel == 0 ||
         !(sync_us >= 0.0))

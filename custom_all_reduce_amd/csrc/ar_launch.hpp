@@ -65,6 +65,12 @@ hipError_t launch_ll_reduce(const void* const* wire, int n, void* out, size_t nu
                             int proto, uint32_t step, uint32_t* flags, uint64_t timeout_ticks,
                             hipStream_t s);
 
+// One GPU's LL / LL128 step in one launch: pack rank me's message src into
+// wire[me] and reduce all n messages into out (rank me's term from src).
+hipError_t launch_ll_allreduce(const void* src, const void* const* wire, int n, int me, void* out, size_t numel,
+                               int dtype, int proto, uint32_t step, uint32_t* flags, uint64_t timeout_ticks,
+                               hipStream_t s);
+
 hipError_t launch_flag_reset(uint32_t* flags, size_t words, hipStream_t s);
 
 // Call f(std::integral_constant<int, N>{}) for the rank count n in [2, 16].

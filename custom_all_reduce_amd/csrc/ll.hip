@@ -15,6 +15,12 @@
 // data bytes plus the flag.  Readiness of the whole wavefront is one ballot.
 // If a line is behind, the slow path re-reads with agent-coherent 64-bit
 // atomic loads until every flag is >= step or the wall-clock budget runs out.
+//
+// Send and receive in one launch (one GPU's LL step): the one-line LL
+// receiver and the LL128 receiver also take rank me's message.  Each lane
+// reads the message bytes its line position carries, writes rank me's line
+// (data and flag) to rank me's wire for the peers, and uses those bytes as
+// rank me's term of the fold, in rank order; rank me's wire is not read.
 #include "ar_device.hpp"
 #include "ar_launch.hpp"
 
@@ -111,6 +117,10 @@ struct ReduceParams {
     size_t nbytes;
     size_t nlines;  // lines per rank
     uint32_t step;
+    // send and receive in one launch: rank me's message and wire
+    int me;
+    const uint8_t* src;
+    uint8_t* own_wire;
 };
 
 // Bounded wait for the lines [2c, 2c + nl) of every rank (nl = 1 or 2), re-read
@@ -274,21 +284,47 @@ __global__ __launch_bounds__(kBlockLL) void ll_reduce_kernel(ReduceParams p) {
 // the wavefronts; measured faster up to 16 MiB per rank (n = 16 at 1 MiB:
 // 8.6 -> 7.4 us; n = 8 at 1-8 MiB: 3-4%), slower above (n = 16 at 64 MiB:
 // 342 -> 363 us), where the two-line kernel runs.
-template <typename T, int NR>
+//
+// kFused: rank me's term is word c of its message (message bytes [4c, 4c+4);
+// a final lone bf16 is zero-extended), loaded with the peers' lines by every
+// wavefront whose 64 words all exist and one by one in the last wavefront;
+// line c of rank me's wire is written from it, with the flag, before the
+// wavefront waits on any peer.
+template <typename T, int NR, bool kFused>
 __global__ __launch_bounds__(kBlockLL) void ll_reduce1_kernel(ReduceParams p) {
     const int lane = threadIdx.x & (kWave - 1);
     const size_t c = size_t(blockIdx.x) * kBlockLL + threadIdx.x;
     const bool act = c < p.nlines;
     const size_t cc = act ? c : p.nlines - 1;
+    const size_t words = p.nbytes / 4;  // whole 4-byte words of the message
+    const bool own_whole = kFused && (size_t(blockIdx.x) + 1) * kBlockLL <= words;  // wavefront-uniform
+    uint32_t own = 0;
+    bool own_late = false;
+    if (kFused && own_whole) own = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p.src) + c);
     u32x2 x[NR];
 #pragma unroll
-    for (int r = 0; r < NR; ++r) x[r] = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p.wire[r]) + cc);
+    for (int r = 0; r < NR; ++r)
+        if (!kFused || r != p.me) x[r] = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p.wire[r]) + cc);
     __builtin_amdgcn_sched_barrier(0);  // every load ahead of the first use
+    if constexpr (kFused) {
+        if (!own_whole && act)
+            own = c < words ? reinterpret_cast<const uint32_t*>(p.src)[c]
+                            : uint32_t(reinterpret_cast<const uint16_t*>(p.src)[2 * c]);
+        // rank me's line carries the step: the readiness checks pass it
+#pragma unroll
+        for (int r = 0; r < NR; ++r)
+            if (r == p.me) x[r] = u32x2{own, p.step};
+    }
     uint32_t fmin = 0xFFFFFFFFu;
 #pragma unroll
     for (int r = 0; r < NR; ++r) fmin = min(fmin, x[r].y);
     bool ok = !act | (fmin >= p.step);
+    // kFused: rank me's line for its peers goes out before any wait on a peer
+    // (slow path) or, when every line is already there, last, after the
+    // output (a store issued earlier is waited for by the compiler's later
+    // waits: stores and loads count in one counter).
     if (wave_ballot(!ok) != 0) {
+        if (kFused && act) __builtin_nontemporal_store(u32x2{own, p.step}, reinterpret_cast<u32x2*>(p.own_wire) + c);
         const uint64_t t0 = now_ticks();
         while (true) {
             bool good = true;
@@ -311,6 +347,9 @@ __global__ __launch_bounds__(kBlockLL) void ll_reduce1_kernel(ReduceParams p) {
             }
             __builtin_amdgcn_s_sleep(1);
         }
+        wait_stores();  // nothing of this path left to wait for where the paths join
+    } else if (kFused && act) {
+        own_late = true;
     }
     if (!act) return;
     uint32_t word;
@@ -331,9 +370,18 @@ __global__ __launch_bounds__(kBlockLL) void ll_reduce1_kernel(ReduceParams p) {
         const uint32_t rw[1] = {word};
         store_out_bytes<T>(p.out, 4 * c, p.nbytes, rw);
     }
+    if (kFused && own_late) __builtin_nontemporal_store(u32x2{own, p.step}, reinterpret_cast<u32x2*>(p.own_wire) + c);
 }
 
-template <typename T, int NR, int U>
+// kFused: rank me's term at a lane is the message bytes its line position
+// carries ([120 line + 16 part, +16), 8 bytes at part 7, zero past the
+// message), loaded with the peers' lines by every wavefront whose 8 lines
+// are whole and word by word in the last one; rank me's wire gets the line
+// (part 7 adds the flag) from it.  Rank me's slot of the wire table holds a
+// peer's wire: every slot is loaded unconditionally (a branch around one
+// load left that register undefined on one path, and the copies merging the
+// paths waited for every load), and the fold takes rank me's term instead.
+template <typename T, int NR, int U, bool kFused>
 __global__ __launch_bounds__(kBlock128) void ll128_reduce_kernel(ReduceParams p) {
     const int lane = threadIdx.x & (kWave - 1);
     const uint32_t part = uint32_t(lane) & 7u;
@@ -354,7 +402,46 @@ __global__ __launch_bounds__(kBlock128) void ll128_reduce_kernel(ReduceParams p)
 #pragma unroll
         for (int r = 0; r < NR; ++r) x[u][r] = ld_stream(w[r] + ll * 8 + part);
     }
+    uint32_t own[U][4] = {};
+    u32x4 mine[U];
+    bool own_whole[U];
+    if constexpr (kFused) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            // wavefront-uniform: every data byte of the unit's 8 lines exists
+            own_whole[u] = ((wave * U + u) * 8 + 8) * 120 <= p.nbytes;
+            if (own_whole[u]) {
+                // 8-byte aligned (120 line + 16 part); part 7 reads its 8 bytes twice
+                const u32x2* sp = reinterpret_cast<const u32x2*>(p.src + line[u] * 120 + size_t(part) * 16);
+                const u32x2 a = __builtin_nontemporal_load(sp);
+                const u32x2 b = __builtin_nontemporal_load(sp + (part != 7u ? 1 : 0));
+                own[u][0] = a.x; own[u][1] = a.y; own[u][2] = b.x; own[u][3] = b.y;
+            }
+        }
+    }
     __builtin_amdgcn_sched_barrier(0);  // every load ahead of the first use
+    if constexpr (kFused) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if (!own_whole[u] && valid[u]) {
+                // the last wavefront: each word on its own, independent loads
+                // (4-byte aligned: 120 line + 16 part is a multiple of 8); a
+                // final lone bf16 is zero-extended, bytes past it stay zero
+                const size_t off = line[u] * 120 + size_t(part) * 16;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const size_t b = off + 4 * size_t(i);
+                    if (i < (part == 7u ? 2 : 4)) {
+                        if (b + 4 <= p.nbytes) own[u][i] = *reinterpret_cast<const uint32_t*>(p.src + b);
+                        else if (b + 2 <= p.nbytes) own[u][i] = *reinterpret_cast<const uint16_t*>(p.src + b);
+                    }
+                }
+            }
+            if (part == 7u) { own[u][2] = p.step; own[u][3] = 0u; }  // 64-bit flag = step
+            mine[u] = u32x4{own[u][0], own[u][1], own[u][2], own[u][3]};
+            if (valid[u]) st_stream(reinterpret_cast<u32x4*>(p.own_wire) + line[u] * 8 + part, mine[u]);
+        }
+    }
     // Readiness without short-circuit branches: the lane at part 7 folds the
     // low flag words with min, a nonzero high word counting as ready.
     bool ok = true;
@@ -402,6 +489,11 @@ __global__ __launch_bounds__(kBlock128) void ll128_reduce_kernel(ReduceParams p)
 #pragma unroll
                 for (int r = 0; r < NR; ++r)
                     x[u][r] = ld_plain(reinterpret_cast<const u32x4*>(p.wire[r]) + line[u] * 8 + part);
+        // Wait for the re-reads here, so that where the two paths join the
+        // compiler has no load of this path to wait for; its wait would also
+        // cover rank me's line store of the fast path (stores count in the same
+        // counter), a memory round trip.
+        wait_stores();
     }
     // Reduce, then repack through LDS: the 8 lines of a wavefront unit hold
     // 960 contiguous output bytes (16-byte aligned, as 960 = 60 * 16), but a
@@ -415,19 +507,22 @@ __global__ __launch_bounds__(kBlock128) void ll128_reduce_kernel(ReduceParams p)
         Acc<T> acc;
         if (part != 7u) {
 #pragma unroll
-            for (int r = 0; r < NR; ++r) acc.add(x[u][r]);
+            for (int r = 0; r < NR; ++r) acc.add(kFused && r == p.me ? mine[u] : x[u][r]);
         } else {
 #pragma unroll
-            for (int r = 0; r < NR; ++r) acc.add_half(x[u][r]);
+            for (int r = 0; r < NR; ++r) acc.add_half(kFused && r == p.me ? mine[u] : x[u][r]);
         }
         const u32x4 res = acc.result();
         u32x2* d = reinterpret_cast<u32x2*>(my + u * 960 + (lane / 8) * 120 + part * 16);
         d[0] = u32x2{res.x, res.y};
         if (part != 7u) d[1] = u32x2{res.z, res.w};
     }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    // LDS-only fences: a workgroup fence over every address space would also
+    // wait for this wavefront's outstanding global stores (rank me's line in
+    // the send-and-receive form), a memory round trip the strip does not need.
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
     __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
     if (lane < 60) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
@@ -451,7 +546,7 @@ template <typename T, int NR>
 hipError_t launch_reduce_t(const ReduceParams& p, int proto, hipStream_t s) {
     if (proto == 0 && p.nbytes <= kOneLineMaxBytes) {
         const size_t grid = (p.nlines + kBlockLL - 1) / kBlockLL;
-        hipLaunchKernelGGL((ll_reduce1_kernel<T, NR>), dim3(uint32_t(grid)), dim3(kBlockLL), 0, s, p);
+        hipLaunchKernelGGL((ll_reduce1_kernel<T, NR, false>), dim3(uint32_t(grid)), dim3(kBlockLL), 0, s, p);
     } else if (proto == 0) {
         // One 16-byte load (two lines) per lane per rank: measured faster
         // than two from 128 KiB to 8 MiB per rank (more workgroups in flight)
@@ -467,7 +562,21 @@ hipError_t launch_reduce_t(const ReduceParams& p, int proto, hipStream_t s) {
         const size_t wave_units = (p.nlines + 7) / 8;
         const size_t waves = (wave_units + U - 1) / U;
         const size_t grid = (waves + kWavesPerBlock128 - 1) / kWavesPerBlock128;
-        hipLaunchKernelGGL((ll128_reduce_kernel<T, NR, U>), dim3(uint32_t(grid)), dim3(kBlock128), 0, s, p);
+        hipLaunchKernelGGL((ll128_reduce_kernel<T, NR, U, false>), dim3(uint32_t(grid)), dim3(kBlock128), 0, s, p);
+    }
+    return hipGetLastError();
+}
+
+// Send and receive in one launch.  LL takes the one-line receiver at every
+// size (the two-line one is 6% faster only above 16 MiB per rank).
+template <typename T, int NR>
+hipError_t launch_fused_t(const ReduceParams& p, int proto, hipStream_t s) {
+    if (proto == 0) {
+        const size_t grid = (p.nlines + kBlockLL - 1) / kBlockLL;
+        hipLaunchKernelGGL((ll_reduce1_kernel<T, NR, true>), dim3(uint32_t(grid)), dim3(kBlockLL), 0, s, p);
+    } else {
+        const size_t grid = (p.nlines + 7) / 8;
+        hipLaunchKernelGGL((ll128_reduce_kernel<T, NR, 1, true>), dim3(uint32_t(grid)), dim3(kBlock128), 0, s, p);
     }
     return hipGetLastError();
 }
@@ -518,6 +627,33 @@ hipError_t launch_ll_reduce(const void* const* wire, int n, void* out, size_t nu
     return dispatch_ranks(n, [&](auto nr) {
         constexpr int NR = decltype(nr)::value;
         return dtype == 0 ? launch_reduce_t<float, NR>(p, proto, s) : launch_reduce_t<bf16_t, NR>(p, proto, s);
+    });
+}
+
+}  // namespace ar
+
+namespace ar {
+
+hipError_t launch_ll_allreduce(const void* src, const void* const* wire, int n, int me, void* out, size_t numel,
+                               int dtype, int proto, uint32_t step, uint32_t* flags, uint64_t timeout_ticks,
+                               hipStream_t s) {
+    ReduceParams p{};
+    for (int i = 0; i < n; ++i) p.wire[i] = static_cast<const uint8_t*>(wire[i]);
+    p.out = static_cast<uint8_t*>(out);
+    p.flags = flags;
+    p.timeout_ticks = timeout_ticks;
+    p.nbytes = numel * (dtype == 0 ? 4 : 2);
+    p.nlines = proto == 0 ? (p.nbytes + 3) / 4 : (p.nbytes + 119) / 120;
+    p.step = step;
+    p.me = me;
+    p.src = static_cast<const uint8_t*>(src);
+    p.own_wire = const_cast<uint8_t*>(static_cast<const uint8_t*>(wire[me]));
+    // rank me's wire is written, not read: its slot loads a peer's line,
+    // which the fold does not use (the LL kernel skips the slot)
+    p.wire[me] = static_cast<const uint8_t*>(wire[(me + 1) % n]);
+    return dispatch_ranks(n, [&](auto nr) {
+        constexpr int NR = decltype(nr)::value;
+        return dtype == 0 ? launch_fused_t<float, NR>(p, proto, s) : launch_fused_t<bf16_t, NR>(p, proto, s);
     });
 }
 

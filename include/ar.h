@@ -238,6 +238,27 @@ int ar_ll_reduce_unpack(const void* const* wire, int n, void* out, size_t numel,
 int ar_ll128_reduce_unpack(const void* const* wire, int n, void* out, size_t numel, int dtype,
                            uint32_t step, uint32_t* flags, void* stream);
 
+/* One GPU's LL or LL128 step in one launch ([NCCL] 协议 table; the sender
+ * and the receiver of the protocol run in the same kernel, as a rank both
+ * sends its message and receives the others'):
+ *  - pack rank me's message src (numel elements) into wire[me] with flag
+ *    step, exactly as ar_ll_pack;
+ *  - wait for every line of every other rank's wire[r] to carry a flag >=
+ *    step and reduce the n messages into out exactly as ar_oneshot, rank
+ *    me's term taken from src (wire[me] is written, not read back).
+ *  wire  : n wire buffers of ar_ll_wire_bytes(proto, numel * elem) bytes, in
+ *          rank order; wire[me] is rank me's own (written), the others are
+ *          read.
+ *  me    : 0 <= me < n.
+ *  flags : flag region (only the status words are used).
+ * out, src and wire[me] may not overlap one another or any wire buffer;
+ * all pointers 16-byte aligned.  LL uses one line per lane at every size.
+ * Errors: AR_ERR_ARG, AR_ERR_ALIGN, AR_ERR_ALIAS, AR_ERR_HIP; asynchronously
+ * AR_ERR_TIMEOUT (phase AR_PHASE_LL or AR_PHASE_LL128, rank and line of a
+ * missing line). */
+int ar_ll_allreduce(const void* src, void* const* wire, int n, int me, void* out, size_t numel, int dtype,
+                    int proto, uint32_t step, uint32_t* flags, void* stream);
+
 /* Algorithm selection from measured costs ([NCCL] 算法 and 协议: no
  * algorithm or protocol is best at every size, so the choice goes by message
  * size and rank count; [CAR] keeps such a per-rank-count threshold map).

@@ -210,6 +210,33 @@ def test_ll_argument_errors():
     assert L.ar_flag_barrier_reset(flags + 8, 4, NUL) == car.AR_ERR_ALIGN
 
 
+def test_ll_allreduce_argument_errors():
+    n = 3
+    src = A + (90 << 30)
+    wires = fake_ins(n, base=A + (64 << 30))  # 1 GiB apart
+    out, flags = A + (100 << 30), A + (101 << 30)
+    f = L.ar_ll_allreduce
+    for proto in (0, 1):
+        assert f(src, wires, 1, 0, out, 10, 0, proto, 1, flags, NUL) == car.AR_ERR_ARG  # n
+        assert f(src, wires, n, -1, out, 10, 0, proto, 1, flags, NUL) == car.AR_ERR_ARG  # me
+        assert f(src, wires, n, n, out, 10, 0, proto, 1, flags, NUL) == car.AR_ERR_ARG
+        assert f(src, wires, n, 1, out, 10, 0, proto, 0, flags, NUL) == car.AR_ERR_ARG  # step 0
+        assert f(src, wires, n, 1, out, 0, 0, proto, 1, flags, NUL) == car.AR_ERR_ARG  # numel 0
+        assert f(None, wires, n, 1, out, 10, 0, proto, 1, flags, NUL) == car.AR_ERR_ARG
+        assert f(src, wires, n, 1, out, 10, 0, proto, 1, None, NUL) == car.AR_ERR_ARG
+        assert f(src, wires, n, 1, out, 10, 2, proto, 1, flags, NUL) == car.AR_ERR_ARG  # dtype
+        assert f(src + 4, wires, n, 1, out, 10, 0, proto, 1, flags, NUL) == car.AR_ERR_ALIGN
+        assert f(src, wires, n, 1, out + 8, 10, 0, proto, 1, flags, NUL) == car.AR_ERR_ALIGN
+        assert f(src, arr(A + (64 << 30), A + (65 << 30) + 4, A + (66 << 30)), n, 1, out, 10, 0, proto, 1, flags,
+                 NUL) == car.AR_ERR_ALIGN
+        # out (40 bytes) over the source; the source over rank me's (written) wire
+        assert f(src, wires, n, 1, src + 16, 10, 0, proto, 1, flags, NUL) == car.AR_ERR_ALIAS
+        assert f(A + (65 << 30) + 16, wires, n, 1, out, 10, 0, proto, 1, flags, NUL) == car.AR_ERR_ALIAS
+        # out over a peer's (read) wire
+        assert f(src, wires, n, 1, A + (66 << 30) + 16, 10, 0, proto, 1, flags, NUL) == car.AR_ERR_ALIAS
+    assert f(src, wires, n, 1, out, 10, 0, 2, 1, flags, NUL) == car.AR_ERR_ARG  # proto
+
+
 def test_status_strings():
     for code in range(7):
         assert L.ar_status_string(code).decode()

@@ -78,10 +78,12 @@ def test_fused_full_emulation_replays_without_reset(n, numel, dt):
             assert np.array_equal(bits(s.outs[r]), s.want[rep % 3]), f"replay {rep} rank {r}"
 
 
-def test_one_rank_shares_in_a_graph():
+@pytest.mark.parametrize("numel", [8 * 8192, 8 * 8 * 64 * 1024])
+def test_one_rank_shares_in_a_graph(numel):
     """Peers' reduce-scatters and rank 0's fused share as separate launches,
-    all with auto step ids, in one graph; eager auto calls in between."""
-    n, numel, dt = 8, 8 * 8192, "bf16"
+    all with auto step ids, in one graph; eager auto calls in between.  At
+    decode size (128 KiB per rank) and at 8 MiB per rank."""
+    n, dt = 8, "bf16"
     s = Set(n, numel, dt, [610, 611])
     out0 = [s.outs[0]] + [None] * (n - 1)
 

@@ -185,3 +185,105 @@ def test_stale_rank_above_the_kernel_switch_times_out():
     torch.cuda.synchronize()
     assert car.read_status(flags)[0] == 0
     assert np.array_equal(bits(out), oracle_bits(oracle.oneshot(host, dt)))
+
+
+# ------------------------------------------------- send + receive, one launch --
+def allreduce_case(proto, dt, n, me, numel, step, config):
+    """Peers' wires packed beforehand at `step`; rank me's message and the
+    reduction in one ar_ll_allreduce launch."""
+    host = synth.rank_inputs(n, numel, dt, "normal", config=config)
+    srcs = [to_dev(a) for a in host]
+    bufs, W = wires_for(n, numel, dt, proto)
+    wires = [b[:W] for b in bufs]
+    peers = [r for r in range(n) if r != me]
+    car.ar_ll_pack([srcs[r] for r in peers], [wires[r] for r in peers], proto, step=step)
+    flags = car.new_flags(n)
+    outbuf = filled(numel + 64, DT[dt])
+    out = outbuf[:numel]
+    car.ar_ll_allreduce(srcs[me], wires, out, flags, proto, me, step)
+    torch.cuda.synchronize()
+    return host, bufs, W, flags, outbuf, out
+
+
+@pytest.mark.parametrize("proto", ["ll", "ll128"])
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("n", [2, 3, 8, 16])
+@pytest.mark.parametrize("where", ["first", "middle", "last"])
+@pytest.mark.parametrize("numel", [1, 61, 30 * 64 * 3 + 11, 64 * 64 * 4, 100000 + 1])
+def test_allreduce_matches_oracle(proto, dt, n, where, numel):
+    """Output = the oracle's sum of all n messages; rank me's wire = the
+    oracle's packing of its message; nothing written past either."""
+    me = {"first": 0, "middle": n // 2, "last": n - 1}[where]
+    host, bufs, W, flags, outbuf, out = allreduce_case(proto, dt, n, me, numel, 77, 140 + n)
+    assert car.read_status(flags)[0] == 0
+    got = bits(out)
+    want = oracle_bits(oracle.oneshot(host, dt))
+    assert np.array_equal(got, want), first_mismatch(got, want)
+    assert np.array_equal(bits(outbuf[numel:]), bits(filled(64, DT[dt]))), "wrote past the output"
+    wire = bits(bufs[me])
+    want_wire = oracle.ll_pack(proto, host[me], 77)
+    assert np.array_equal(wire[:W], want_wire), "own wire: " + first_mismatch(wire[:W], want_wire)
+    assert np.all(wire[W:] == 0xA5), "wrote past rank me's wire"
+
+
+@pytest.mark.parametrize("proto", ["ll", "ll128"])
+@pytest.mark.parametrize("kib, steps", [(64, 300), (1024, 40)])
+def test_allreduce_steps_without_reset(proto, kib, steps):
+    """n = 8, fp32, rank 3's step: every step the peers pack new data, then
+    one launch packs rank 3's and reduces; data alternates between three sets."""
+    n, dt, me = 8, "f32", 3
+    numel = kib * 1024 // 4
+    sets = [synth.rank_inputs(n, numel, dt, "normal", config=150 + k) for k in range(3)]
+    wants = [oracle_bits(oracle.oneshot(h, dt)) for h in sets]
+    dsets = [[to_dev(a) for a in h] for h in sets]
+    bufs, W = wires_for(n, numel, dt, proto)
+    wires = [b[:W] for b in bufs]
+    flags = car.new_flags(n)
+    outs = torch.empty((steps, numel), device="cuda")
+    peers = [r for r in range(n) if r != me]
+    for step in range(1, steps + 1):
+        d = dsets[step % 3]
+        car.ar_ll_pack([d[r] for r in peers], [wires[r] for r in peers], proto, step=step)
+        car.ar_ll_allreduce(d[me], wires, outs[step - 1], flags, proto, me, step)
+    torch.cuda.synchronize()
+    assert car.read_status(flags)[0] == 0
+    got_all = outs.cpu().numpy().view(np.uint32)
+    for step in range(1, steps + 1):
+        got = got_all[step - 1]
+        assert np.array_equal(got, wants[step % 3]), f"step {step}: " + first_mismatch(got, wants[step % 3])
+
+
+@pytest.mark.parametrize("proto, phase", [("ll", 2), ("ll128", 3)])
+def test_allreduce_stale_peer_times_out_after_packing(proto, phase):
+    """Rank 5 packed the previous step: the launch still writes rank 2's
+    wire for step s, then reports (timeout, phase, rank 5) and exits."""
+    n, numel, dt, me = 8, 4096, "f32", 2
+    host = synth.rank_inputs(n, numel, dt, "normal", config=160)
+    srcs = [to_dev(a) for a in host]
+    bufs, W = wires_for(n, numel, dt, proto)
+    wires = [b[:W] for b in bufs]
+    flags = car.new_flags(n)
+    car.ar_ll_pack([srcs[r] for r in range(n) if r not in (me, 5)], [wires[r] for r in range(n) if r not in (me, 5)],
+                   proto, step=11)
+    car.ar_ll_pack([srcs[5]], [wires[5]], proto, step=10)
+    out = torch.empty(numel, device="cuda")
+    old = car.get_poll_timeout_ns()
+    car.set_poll_timeout_ns(20_000)
+    try:
+        car.ar_ll_allreduce(srcs[me], wires, out, flags, proto, me, 11)
+        torch.cuda.synchronize()
+    finally:
+        car.set_poll_timeout_ns(old)
+    code, ph, rank = car.decode_status(car.read_status(flags)[0])
+    assert (code, ph, rank) == (car.AR_ERR_TIMEOUT, phase, 5)
+    assert np.array_equal(bits(bufs[me])[:W], oracle.ll_pack(proto, host[me], 11))
+
+
+@pytest.mark.parametrize("dt, numel", [("f32", ONE_LINE_MAX // 4 + 3), ("bf16", ONE_LINE_MAX // 2 + 5)])
+def test_allreduce_ll_above_16MiB(dt, numel):
+    """The send-and-receive LL launch uses one line per lane at every size."""
+    host, bufs, W, flags, outbuf, out = allreduce_case("ll", dt, 2, 1, numel, 5, 170)
+    assert car.read_status(flags)[0] == 0
+    got, want = bits(out), oracle_bits(oracle.oneshot(host, dt))
+    assert np.array_equal(got, want), first_mismatch(got, want)
+    assert np.array_equal(bits(bufs[1])[:W], oracle.ll_pack("ll", host[1], 5))

@@ -123,6 +123,64 @@ def test_one_gpu_share_with_peers_published_earlier(dt):
     check_outputs(rk, host, ranks=[me])
 
 
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("n,seg_vectors", [(2, 64 * 1024), (8, 64 * 1024), (16, 32 * 1024), (8, 40017)])
+def test_share_at_prefill_sizes(n, dt, seg_vectors):
+    """One rank's share at 1024 tiles per segment (4-8 MiB per rank), where
+    the persistent grid has fewer wavefronts than items and each wavefront
+    holds a reduce-scatter tile and several all-gather tiles.  A short last
+    tile (40017 vectors) included; three steps with changing data on the same
+    buffers."""
+    es = 4 if dt == "f32" else 2
+    m = seg_vectors * (16 // es)
+    datasets = [synth.rank_inputs(n, n * m, dt, "normal", config=70 + k) for k in range(2)]
+    rk = Ranks(datasets[0], dt)
+    me = n - 1
+    outs = [rk.outs[r] if r == me else None for r in range(n)]
+    for step in (1, 2, 3):
+        host = datasets[step % 2]
+        rk.load(host)
+        for r in range(n):
+            if r != me:
+                car.ar_twoshot_rs(rk.ins, rk.segs, rk.flags, step=step, r0=r, r1=r + 1)
+        car.ar_twoshot_rs(rk.ins, rk.segs, rk.flags, step=step, r0=me, r1=me + 1, outs=outs)
+        torch.cuda.synchronize()
+        assert_ok(rk.flags)
+        check_outputs(rk, host, ranks=[me])
+
+
+def test_share_missing_peer_times_out_at_prefill_size():
+    """8 MiB per rank, a peer that never reduces: the share still publishes
+    its own tiles, then waits, runs out of time and names the missing
+    segment.  A reset then starts clean."""
+    n, dt, m = 8, "bf16", 8 * 64 * 1024
+    host = synth.rank_inputs(n, n * m, dt, "normal", config=75)
+    rk = Ranks(host, dt)
+    out0 = [rk.outs[0]] + [None] * (n - 1)
+    for r in range(1, n):
+        if r != 5:
+            car.ar_twoshot_rs(rk.ins, rk.segs, rk.flags, step=1, r0=r, r1=r + 1)
+    old = car.get_poll_timeout_ns()
+    car.set_poll_timeout_ns(2_000_000)
+    try:
+        car.ar_twoshot_rs(rk.ins, rk.segs, rk.flags, step=1, r0=0, r1=1, outs=out0)
+        torch.cuda.synchronize()
+    finally:
+        car.set_poll_timeout_ns(old)
+    code, phase, rank = car.decode_status(car.read_status(rk.flags)[0])
+    assert (code, phase, rank) == (car.AR_ERR_TIMEOUT, car.PHASE_TWOSHOT_AG, 5)
+    # rank 0 published every tile of its segment before it waited
+    ktiles = 1024  # 64 Ki vectors per segment: 1024 tiles of 64
+    slots0 = rk.flags[32:32 + ktiles].cpu().numpy().view("uint32")
+    assert (slots0 == 1).all()
+    # recovery
+    car.ar_flag_barrier_reset(rk.flags, n)
+    car.ar_twoshot_rs(rk.ins, rk.segs, rk.flags, step=1, outs=rk.outs)
+    torch.cuda.synchronize()
+    assert_ok(rk.flags)
+    check_outputs(rk, host)
+
+
 def test_many_steps_with_changing_data():
     """Steps 1..40 on the same buffers with new data every step: catches a
     consumer that reads a stale segment after the barrier."""
