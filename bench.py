@@ -7,7 +7,9 @@ HBM allocations on this GPU; this GPU plays rank `me` = 0:
   1. one-shot: the full output of rank me            (ar_oneshot)
   2. two-shot: reduce-scatter of segment me, flag barrier, all-gather into
      rank me's output, in one persistent launch      (ar_twoshot_rs, fused, [me, me+1))
-  3. LL: pack rank me's message, then poll/unpack/reduce all n wire buffers
+  3. LL: pack rank me's message into its wire buffer and poll/unpack/reduce
+     the peers' wire buffers, rank me's term from its message, in one launch
+     (ar_ll_allreduce)
   4. LL128: the same with 128-byte lines
 
 The peers' shares (their segments and slots, their packed wire buffers) are
@@ -50,14 +52,12 @@ WORKLOADS = {
     "ll64k": (8, "f32", 16384, "LL-sized message: n=8 ranks, fp32 64 KiB per rank"),
     "ll1m": (8, "f32", 262144, "n=8 ranks, fp32 1 MiB per rank"),
 }
-KERNELS = ["oneshot", "twoshot", "ll_pack", "ll_reduce", "ll128_pack", "ll128_reduce"]
+KERNELS = ["oneshot", "twoshot", "ll", "ll128"]
 KERNEL_SOURCES = {
     "oneshot": ["oneshot.hip"],
     "twoshot": ["twoshot.hip", "fastdiv.hpp"],
-    "ll_pack": ["ll.hip"],
-    "ll_reduce": ["ll.hip"],
-    "ll128_pack": ["ll.hip"],
-    "ll128_reduce": ["ll.hip"],
+    "ll": ["ll.hip"],
+    "ll128": ["ll.hip"],
 }
 
 
@@ -86,10 +86,8 @@ def step_bytes(n, S):
     per = {
         "oneshot": acc.total(acc.oneshot(n, S)),
         "twoshot": acc.total(acc.twoshot(n, S, 1)),
-        "ll_pack": acc.total(acc.ll_pack("ll", S, 1)),
-        "ll_reduce": acc.total(acc.ll_reduce("ll", n, S)),
-        "ll128_pack": acc.total(acc.ll_pack("ll128", S, 1)),
-        "ll128_reduce": acc.total(acc.ll_reduce("ll128", n, S)),
+        "ll": acc.total(acc.ll_allreduce("ll", n, S)),
+        "ll128": acc.total(acc.ll_allreduce("ll128", n, S)),
     }
     return per
 
@@ -119,17 +117,26 @@ PEER_STEP = 1 << 31  # step id of the peers' published shares, above every timed
 
 
 def step_calls(car, b, flags):
-    """The six launches of one step on buffer set b (rank ME's share)."""
+    """The four launches of one step on buffer set b (rank ME's share)."""
     n = len(b.ins)
     outs = [b.outs[r] if r == ME else None for r in range(n)]
     return [
         car.prepare_oneshot(b.ins, b.out),
         car.prepare_twoshot_rs(b.ins, b.segs, flags, r0=ME, r1=ME + 1, outs=outs),
-        car.prepare_ll_pack([b.ins[ME]], [b.w_ll[ME]], "ll"),
-        car.prepare_ll_reduce(b.w_ll, b.out_ll, flags, "ll"),
-        car.prepare_ll_pack([b.ins[ME]], [b.w_128[ME]], "ll128"),
-        car.prepare_ll_reduce(b.w_128, b.out_128, flags, "ll128"),
+        car.prepare_ll_allreduce(b.ins[ME], b.w_ll, b.out_ll, flags, "ll", ME),
+        car.prepare_ll_allreduce(b.ins[ME], b.w_128, b.out_128, flags, "ll128", ME),
     ]
+
+
+def split_ll_calls(car, b, flags):
+    """The LL / LL128 step as two launches each (pack, then receive), for
+    the sweep."""
+    return {
+        "ll_pack": car.prepare_ll_pack([b.ins[ME]], [b.w_ll[ME]], "ll"),
+        "ll_reduce": car.prepare_ll_reduce(b.w_ll, b.out_ll, flags, "ll"),
+        "ll128_pack": car.prepare_ll_pack([b.ins[ME]], [b.w_128[ME]], "ll128"),
+        "ll128_reduce": car.prepare_ll_reduce(b.w_128, b.out_128, flags, "ll128"),
+    }
 
 
 def publish_peers(car, b, flags):
@@ -264,6 +271,7 @@ def sweep(args, torch, car, np, out_path):
                 ts_auto = [car.prepare_twoshot_rs(b.ins, b.segs, flags, r0=ME, r1=ME + 1,
                                                   outs=[b.outs[r] if r == ME else None for r in range(n)])
                            for b in sets]
+                split = [split_ll_calls(car, b, flags) for b in sets]
                 for b in sets:
                     publish_peers(car, b, flags)
                 run_step(calls[0], 1)
@@ -274,9 +282,11 @@ def sweep(args, torch, car, np, out_path):
                 step = 3
                 # the full emulation rewrites every rank's slots, so it goes last
                 kinds = [("oneshot", 0, acc.oneshot(n, S)), ("twoshot", 1, acc.twoshot(n, S, 1)),
-                         ("ll_pack", 2, acc.ll_pack("ll", S, 1)), ("ll_reduce", 3, acc.ll_reduce("ll", n, S)),
-                         ("ll128_pack", 4, acc.ll_pack("ll128", S, 1)),
-                         ("ll128_reduce", 5, acc.ll_reduce("ll128", n, S)),
+                         ("ll", 2, acc.ll_allreduce("ll", n, S)), ("ll128", 3, acc.ll_allreduce("ll128", n, S)),
+                         ("ll_pack", "split", acc.ll_pack("ll", S, 1)),
+                         ("ll_reduce", "split", acc.ll_reduce("ll", n, S)),
+                         ("ll128_pack", "split", acc.ll_pack("ll128", S, 1)),
+                         ("ll128_reduce", "split", acc.ll_reduce("ll128", n, S)),
                          ("bcast", "bc_one", acc.reduce_bcast(n, S, 1)),
                          ("bcast_full", "bc_all", acc.reduce_bcast(n, S, n)),
                          ("push", "push", acc.push(S, n)),
@@ -297,12 +307,14 @@ def sweep(args, torch, car, np, out_path):
                                 extra[ki][i % nsets](0)  # step id from the flag region
                             elif ki == "ag_copy":
                                 extra[ki][i % nsets](1)  # every slot holds a later step by now
+                            elif ki == "split" and name.endswith("reduce"):
+                                split[i % nsets][name](1)  # every wire carries flags >= 1 by now
+                            elif ki == "split":
+                                split[i % nsets][name](base + i)
                             elif isinstance(ki, str):
                                 extra[ki][i % nsets]()
                             elif name == "oneshot":
                                 calls[i % nsets][0]()
-                            elif name.endswith("reduce"):
-                                calls[i % nsets][ki](1)
                             else:
                                 calls[i % nsets][ki](base + i)
 
@@ -324,7 +336,7 @@ def sweep(args, torch, car, np, out_path):
                     elif name == "twoshot":
                         t_two[S] = us
                 car.raise_on_status(flags, "sweep")
-                del sets, calls, full, src, extra, bc_one, bc_all, push, stage, ts_auto, ag_copy
+                del sets, calls, full, src, extra, bc_one, bc_all, push, stage, ts_auto, ag_copy, split
                 torch.cuda.empty_cache()
             # crossover: first size where two-shot (one rank's share) beats one-shot,
             # log-linear interpolation of the time difference between the bracketing sizes
@@ -354,8 +366,8 @@ def select_table(args, torch, car, np, out_path):
     """One GPU's share of an all-reduce by each algorithm, n = 2..16, bf16,
     over SELECT_SIZES bytes per rank (cold: buffer sets rotated over >= 1 GiB;
     graph-replayed).  The shares: one-shot; rank 0's fused two-shot after the
-    peers' reduce-scatter; rank 0's LL / LL128 pack plus the receiver over
-    every rank's wire buffer, the peers' wires packed beforehand.  Each time
+    peers' reduce-scatter; rank 0's LL / LL128 send and receive in one launch
+    (ar_ll_allreduce), the peers' wires packed beforehand.  Each time
     is the median of three replays.  Writes one JSON object per (n, size)."""
     rows = []
     gen = torch.Generator(device="cuda")
@@ -393,9 +405,7 @@ def select_table(args, torch, car, np, out_path):
                     calls["oneshot"].append(lambda s, one=one: one())
                     calls["twoshot"].append(car.prepare_twoshot_rs(ins, segs, flags, 0, 1, [out] + [None] * (n - 1)))
                     for name, w in (("ll", w1), ("ll128", w2)):
-                        pk = car.prepare_ll_pack([ins[0]], [w[0]], name)
-                        rd = car.prepare_ll_reduce(w, out, flags, name)
-                        calls[name].append(lambda s, pk=pk, rd=rd: (pk(s), rd(s)))
+                        calls[name].append(car.prepare_ll_allreduce(ins[0], w, out, flags, name, 0))
                     ps, po = car.prepare_push([ins[0]], [slots0]), car.prepare_oneshot(mine, out)
                     calls["push"].append(lambda s, ps=ps, po=po: (ps(), po()))
                     bc = car.prepare_reduce_bcast(ins, bouts, 0, 1)
@@ -563,15 +573,13 @@ def main(argv=None):
                     c = calls[i % nsets][ki]
                     if name == "oneshot":
                         c()
-                    elif name.endswith("reduce"):
-                        c(1)  # wires already carry flags >= 1 from the timed steps
                     else:
                         c(base + i)
 
             g = graph_of(torch, k_launches)
             ms = timed_replay(torch, g)
             del g
-            if name in ("twoshot", "ll_pack", "ll128_pack"):
+            if name != "oneshot":
                 step = base + K
             us = ms * 1e3 / K
             kernels[name] = {
@@ -605,7 +613,7 @@ def main(argv=None):
             "bytes_per_rank": S,
             "arithmetic": f"{dt_name} data, fp32 accumulation in rank order, one rounding to {dt_name}",
             "step": "rank 0's share: oneshot + twoshot(RS seg 0 -> barrier -> AG out 0, fused) + "
-                    "LL pack(own)/reduce(n) + LL128 pack(own)/reduce(n); peers' shares published before timing",
+                    "LL(pack own, reduce n; one launch) + LL128(same); peers' shares published before timing",
             "algorithmic_bytes_per_step": bytes_per_step,
             "cache": "warm (one buffer set)" if args.warm else
                      f"cold: {nsets} rotated buffer sets, {nsets * fp / 2**30:.2f} GiB",

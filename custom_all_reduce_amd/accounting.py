@@ -14,6 +14,8 @@ and every write, each byte once.  S = numel * element size (bytes per rank).
   push, one sender        reads S                 writes ndst*S
   LL / LL128 pack, each   reads S                 writes W(S)
   LL / LL128 reduce       reads n*W(S)            writes S
+  LL / LL128 send and     reads S (own message) + (n-1)*W(S) (the peers' wires)
+    receive, one launch   writes W(S) (own wire) + S
 
 In the fused two-shot the reduce-scatter writes rank r's own segment of its
 output straight from registers, so the all-gather reads only the other n-1
@@ -68,6 +70,13 @@ def ll_pack(proto: str, S: int, count: int = 1):
 
 def ll_reduce(proto: str, n: int, S: int):
     return n * wire_bytes(proto, S), S
+
+
+def ll_allreduce(proto: str, n: int, S: int):
+    """One GPU's LL / LL128 step in one launch: its own term comes from its
+    message, not from its wire buffer."""
+    W = wire_bytes(proto, S)
+    return S + (n - 1) * W, W + S
 
 
 def total(rw) -> int:

@@ -266,7 +266,8 @@ int ar_ll_allreduce(const void* src, void* const* wire, int n, int me, void* out
  * is t_share + k * sync_us, where
  *  - t_share is the time of one GPU's share measured on MI355X with this
  *    library's kernels (cold HBM, graph-replayed; one-shot; one rank's fused
- *    two-shot; one rank's LL / LL128 pack plus the receiver; one rank's push
+ *    two-shot; one rank's LL / LL128 send and receive in one launch
+ *    (ar_ll_allreduce); one rank's push
  *    plus its one-shot over its staging slots; one rank's reduce-broadcast
  *    share), tabulated for
  *    n = 2..16 over 16 KiB..64 MiB per rank, interpolated linearly in the
@@ -286,8 +287,8 @@ int ar_ll_allreduce(const void* src, void* const* wire, int n, int me, void* out
 typedef enum {
     AR_ALGO_ONESHOT = 0, /* ar_oneshot */
     AR_ALGO_TWOSHOT = 1, /* ar_twoshot_rs with out (fused) */
-    AR_ALGO_LL = 2,      /* ar_ll_pack + ar_ll_reduce_unpack */
-    AR_ALGO_LL128 = 3,   /* ar_ll_pack + ar_ll128_reduce_unpack */
+    AR_ALGO_LL = 2,      /* ar_ll_allreduce, LL (or ar_ll_pack + ar_ll_reduce_unpack) */
+    AR_ALGO_LL128 = 3,   /* ar_ll_allreduce, LL128 (or ar_ll_pack + ar_ll128_reduce_unpack) */
     AR_ALGO_PUSH = 4,    /* ar_push into the staging slots + ar_oneshot over them */
     AR_ALGO_BCAST = 5    /* ar_reduce_bcast */
 } ar_algo;

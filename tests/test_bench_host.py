@@ -28,8 +28,11 @@ def test_step_bytes_are_one_gpus_algorithmic_bytes():
     assert per["twoshot"] == S + (n - 1) * (S // n) + S // n + S
     W1, W2 = acc.wire_bytes("ll", S), acc.wire_bytes("ll128", S)
     assert W1 == 2 * S and W2 == 128 * -(-S // 120)
-    assert per["ll_pack"] == S + W1 and per["ll_reduce"] == n * W1 + S
-    assert per["ll128_pack"] == S + W2 and per["ll128_reduce"] == n * W2 + S
+    # LL / LL128 in one launch: own message read, own wire written, n-1 peers' wires read, output written
+    assert per["ll"] == S + W1 + (n - 1) * W1 + S
+    assert per["ll128"] == S + W2 + (n - 1) * W2 + S
+    # = pack (S + W) plus receive (n W + S) less the own wire the receive no longer reads
+    assert per["ll"] == acc.total(acc.ll_pack("ll", S)) + acc.total(acc.ll_reduce("ll", n, S)) - W1
     assert set(per) == set(bench.KERNELS)
 
 
