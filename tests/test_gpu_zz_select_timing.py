@@ -41,8 +41,7 @@ def share_calls(n, numel, flags, gen):
         calls["oneshot"].append(lambda s, one=one: one())
         calls["twoshot"].append(car.prepare_twoshot_rs(ins, segs, flags, 0, 1, [out] + [None] * (n - 1)))
         for name, w in (("ll", w1), ("ll128", w2)):
-            pk, rd = car.prepare_ll_pack([ins[0]], [w[0]], name), car.prepare_ll_reduce(w, out, flags, name)
-            calls[name].append(lambda s, pk=pk, rd=rd: (pk(s), rd(s)))
+            calls[name].append(car.prepare_ll_allreduce(ins[0], w, out, flags, name, 0))
         ps, po = car.prepare_push([ins[0]], [slots0]), car.prepare_oneshot(mine, out)
         calls["push"].append(lambda s, ps=ps, po=po: (ps(), po()))
         bc = car.prepare_reduce_bcast(ins, bouts, 0, 1)
