@@ -154,6 +154,11 @@ int main(void) {
         CHECK_HIP(hipDeviceSynchronize());
         ok &= same(&c, out, proto == AR_PROTO_LL ? "ar_ll_pack + ar_ll_reduce_unpack"
                                                  : "ar_ll_pack + ar_ll128_reduce_unpack");
+        /* rank 2's step in one launch: the others' wires as packed above, at step 7 */
+        CHECK_HIP(hipMemset(out, 0, c.bytes));
+        ok &= ar_ll_allreduce(c.dev[2], wires, c.n, 2, out, c.numel, c.dtype, proto, 7, flags, NULL) == AR_OK;
+        CHECK_HIP(hipDeviceSynchronize());
+        ok &= same(&c, out, proto == AR_PROTO_LL ? "ar_ll_allreduce (LL)" : "ar_ll_allreduce (LL128)");
         for (int i = 0; i < c.n; ++i) CHECK_HIP(hipFree(wires[i]));
     }
     CHECK_HIP(hipMemcpy(&status, flags, 4, hipMemcpyDeviceToHost));

@@ -71,6 +71,12 @@ def test_n16_64MiB_per_rank_all_paths_sampled(dt):
             torch.cuda.synchronize()
             car.raise_on_status(flags)
             assert np.array_equal(bits(out)[idx], want), proto
+            # rank 9's step in one launch: its wire written, the other 15 read
+            out.fill_(0)
+            car.ar_ll_allreduce(ins[9], wires, out, flags, proto, 9, 3)
+            torch.cuda.synchronize()
+            car.raise_on_status(flags)
+            assert np.array_equal(bits(out)[idx], want), proto + " in one launch"
             del wires
 
         # reduce-broadcast, rank 0's share and then the remaining ranks

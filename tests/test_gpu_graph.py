@@ -32,6 +32,10 @@ def test_graph_replays_of_every_path():
     w_128 = [torch.empty(car.ll_wire_bytes("ll128", S), dtype=torch.uint8, device="cuda") for _ in range(n)]
     out_ll = torch.empty(numel, dtype=tdt, device="cuda")
     out_128 = torch.empty(numel, dtype=tdt, device="cuda")
+    w1_ll = [torch.empty(car.ll_wire_bytes("ll", S), dtype=torch.uint8, device="cuda") for _ in range(n)]
+    w1_128 = [torch.empty(car.ll_wire_bytes("ll128", S), dtype=torch.uint8, device="cuda") for _ in range(n)]
+    out1_ll = torch.empty(numel, dtype=tdt, device="cuda")
+    out1_128 = torch.empty(numel, dtype=tdt, device="cuda")
     bc_full = [torch.empty(numel, dtype=tdt, device="cuda") for _ in range(n)]
     bc_share = [torch.empty(numel, dtype=tdt, device="cuda") for _ in range(n)]
     staging = [[torch.empty(numel, dtype=tdt, device="cuda") for _ in range(n)] for _ in range(n)]
@@ -53,6 +57,12 @@ def test_graph_replays_of_every_path():
         car.ar_ll_reduce_unpack(w_ll, out_ll, 2, flags)
         car.ar_ll_pack(ins, w_128, "ll128", 2)
         car.ar_ll128_reduce_unpack(w_128, out_128, 2, flags)
+        # rank 3's LL / LL128 step in one launch after the peers' packs
+        peers = [r for r in range(n) if r != 3]
+        car.ar_ll_pack([ins[r] for r in peers], [w1_ll[r] for r in peers], "ll", 2)
+        car.ar_ll_allreduce(ins[3], w1_ll, out1_ll, flags, "ll", 3, 2)
+        car.ar_ll_pack([ins[r] for r in peers], [w1_128[r] for r in peers], "ll128", 2)
+        car.ar_ll_allreduce(ins[3], w1_128, out1_128, flags, "ll128", 3, 2)
         car.ar_reduce_bcast(ins, bc_full)
         for r in range(n):  # every rank's share, one launch each
             car.ar_reduce_bcast(ins, bc_share, r, r + 1)
@@ -70,6 +80,6 @@ def test_graph_replays_of_every_path():
         torch.cuda.synchronize()
         assert car.read_status(flags)[0] == 0, f"replay {rep}"
         for name, t in [("oneshot", out_one), ("share", out_share), ("ll", out_ll), ("ll128", out_128),
-                        ("push", out_push)] + [(f"full{r}", outs_full[r]) for r in range(n)] + \
+                        ("ll one launch", out1_ll), ("ll128 one launch", out1_128), ("push", out_push)] + [(f"full{r}", outs_full[r]) for r in range(n)] + \
                        [(f"bcast{r}", bc_full[r]) for r in range(n)] + [(f"bshare{r}", bc_share[r]) for r in range(n)]:
             assert np.array_equal(bits(t), wants[k]), f"replay {rep}: {name}"

@@ -77,6 +77,24 @@ def test_ll_and_ll128(data):
         torch.cuda.empty_cache()
 
 
+def test_ll_and_ll128_send_and_receive_in_one_launch(data):
+    """Rank 1 packs its 2 GiB message and reduces rank 0's 4 GiB LL wire (or
+    its LL128 wire) in one launch."""
+    ins, idx, want = data
+    out = torch.empty(NUMEL, dtype=torch.bfloat16, device="cuda")
+    flags = car.new_flags(N)
+    for proto in ("ll", "ll128"):
+        W = car.ll_wire_bytes(proto, NUMEL * 2)
+        wires = [torch.empty(W, dtype=torch.uint8, device="cuda") for _ in range(N)]
+        car.ar_ll_pack(ins[:N - 1], wires[:N - 1], proto, 1)
+        car.ar_ll_allreduce(ins[N - 1], wires, out, flags, proto, N - 1, 1)
+        torch.cuda.synchronize()
+        car.raise_on_status(flags, proto)
+        check(out, idx, want, proto + " in one launch")
+        del wires
+        torch.cuda.empty_cache()
+
+
 def test_two_shot_divisible_prefix(data):
     """The two-shot needs n whole 16-byte segments: the first 2^30 elements."""
     ins, idx, want = data
