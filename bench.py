@@ -99,6 +99,10 @@ class BufferSet:
         self.ins = [t.clone() for t in src]
         self.out = torch.empty(numel, dtype=dt, device="cuda")
         self.segs = [torch.empty(numel // n, dtype=dt, device="cuda") for _ in range(n)]
+        # LL segment wires of the two-shot under LL, zeroed (flags below every step)
+        es_ = 4 if dt == torch.float32 else 2
+        self.segw = [torch.zeros(car.ll_wire_bytes("ll", numel // n * es_), dtype=torch.uint8, device="cuda")
+                     for _ in range(n)]
         self.outs = [torch.empty(numel, dtype=dt, device="cuda") for _ in range(n)]
         es = 4 if dt == torch.float32 else 2
         S = numel * es
@@ -108,7 +112,8 @@ class BufferSet:
         self.out_128 = torch.empty(numel, dtype=dt, device="cuda")
 
     def footprint(self):
-        ts = self.ins + [self.out] + self.segs + self.outs + self.w_ll + self.w_128 + [self.out_ll, self.out_128]
+        ts = self.ins + [self.out] + self.segs + self.segw + self.outs + self.w_ll + self.w_128 + \
+            [self.out_ll, self.out_128]
         return sum(t.numel() * t.element_size() for t in ts)
 
 
@@ -145,6 +150,7 @@ def publish_peers(car, b, flags):
     peers = [r for r in range(n) if r != ME]
     for r in peers:
         car.ar_twoshot_rs(b.ins, b.segs, flags, PEER_STEP, r0=r, r1=r + 1)
+        car.ar_twoshot_ll(b.ins, b.segw, flags, PEER_STEP, r0=r, r1=r + 1)
     car.ar_ll_pack([b.ins[r] for r in peers], [b.w_ll[r] for r in peers], "ll", PEER_STEP)
     car.ar_ll_pack([b.ins[r] for r in peers], [b.w_128[r] for r in peers], "ll128", PEER_STEP)
 
@@ -256,7 +262,7 @@ def sweep(args, torch, car, np, out_path):
                     src = [torch.from_numpy(a).cuda() for a in host]
                 else:
                     src = [torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda() for a in host]
-                fp = (n * 2 + 3) * S + n * (acc.wire_bytes("ll", S) + acc.wire_bytes("ll128", S))
+                fp = (n * 2 + 5) * S + n * (acc.wire_bytes("ll", S) + acc.wire_bytes("ll128", S))
                 nsets = max(2, int(np.ceil((1 << 30) / fp)))
                 sets = [BufferSet(torch, car, src, n, dt, numel) for _ in range(nsets)]
                 flags = car.new_flags(n)
@@ -272,6 +278,9 @@ def sweep(args, torch, car, np, out_path):
                                                   outs=[b.outs[r] if r == ME else None for r in range(n)])
                            for b in sets]
                 split = [split_ll_calls(car, b, flags) for b in sets]
+                tsll_one = [car.prepare_twoshot_ll(b.ins, b.segw, flags, ME, ME + 1,
+                                                   [b.outs[r] if r == ME else None for r in range(n)]) for b in sets]
+                tsll_all = [car.prepare_twoshot_ll(b.ins, b.segw, flags, outs=b.outs) for b in sets]
                 for b in sets:
                     publish_peers(car, b, flags)
                 run_step(calls[0], 1)
@@ -293,6 +302,8 @@ def sweep(args, torch, car, np, out_path):
                          ("stage", "stage", acc.push(S, 1)),
                          ("ag_copy", "ag_copy", acc.twoshot_ag(n, S, 1)),
                          ("twoshot_auto", "ts_auto", acc.twoshot(n, S, 1)),
+                         ("twoshot_ll", "tsll_one", acc.twoshot_ll(n, S, 1)),
+                         ("twoshot_ll_full", "tsll_all", acc.twoshot_ll(n, S, n)),
                          ("twoshot_full", None, acc.twoshot(n, S, n))]
                 extra = {"bc_one": bc_one, "bc_all": bc_all, "push": push, "stage": stage, "ts_auto": ts_auto,
                          "ag_copy": ag_copy}
@@ -311,6 +322,12 @@ def sweep(args, torch, car, np, out_path):
                                 split[i % nsets][name](1)  # every wire carries flags >= 1 by now
                             elif ki == "split":
                                 split[i % nsets][name](base + i)
+                            elif ki == "tsll_all":
+                                # above the peers' published step, so no line
+                                # left by the publishing counts as arrived
+                                tsll_all[i % nsets](PEER_STEP + base + i)
+                            elif ki == "tsll_one":
+                                tsll_one[i % nsets](base + i)
                             elif isinstance(ki, str):
                                 extra[ki][i % nsets]()
                             elif name == "oneshot":
@@ -337,6 +354,7 @@ def sweep(args, torch, car, np, out_path):
                         t_two[S] = us
                 car.raise_on_status(flags, "sweep")
                 del sets, calls, full, src, extra, bc_one, bc_all, push, stage, ts_auto, ag_copy, split
+                del tsll_one, tsll_all
                 torch.cuda.empty_cache()
             # crossover: first size where two-shot (one rank's share) beats one-shot,
             # log-linear interpolation of the time difference between the bracketing sizes
@@ -359,7 +377,7 @@ def sweep(args, torch, car, np, out_path):
 
 SELECT_SIZES = [16 << 10, 32 << 10, 64 << 10, 128 << 10, 256 << 10, 512 << 10, 1 << 20, 3 << 19, 2 << 20,
                 3 << 20, 4 << 20, 6 << 20, 8 << 20, 12 << 20, 16 << 20, 32 << 20, 64 << 20]
-SELECT_ALGOS = ["oneshot", "twoshot", "ll", "ll128", "push", "bcast"]
+SELECT_ALGOS = ["oneshot", "twoshot", "ll", "ll128", "push", "bcast", "twoshot_ll"]
 
 
 def select_table(args, torch, car, np, out_path):
@@ -378,7 +396,7 @@ def select_table(args, torch, car, np, out_path):
                 numel -= numel % (8 * n)  # whole 16-byte vectors in every segment
                 Sb = numel * 2
                 W1, W2 = car.ll_wire_bytes("ll", Sb), car.ll_wire_bytes("ll128", Sb)
-                fp = n * Sb + 3 * Sb + n * (W1 + W2) + (2 * n - 1) * Sb + n * Sb
+                fp = n * Sb + 5 * Sb + n * (W1 + W2) + (2 * n - 1) * Sb + n * Sb
                 nsets = max(2, int(np.ceil((1 << 30) / fp)))
                 gen.manual_seed(1000 * n + S.bit_length())
                 src = [torch.randn(numel, generator=gen, device="cuda").to(torch.bfloat16) for _ in range(n)]
@@ -396,9 +414,12 @@ def select_table(args, torch, car, np, out_path):
                     slots0 = [torch.empty(numel, dtype=torch.bfloat16, device="cuda") for _ in range(n)]
                     mine = [slots0[0]] + [torch.empty(numel, dtype=torch.bfloat16, device="cuda") for _ in range(1, n)]
                     bouts = [out] + [torch.empty(numel, dtype=torch.bfloat16, device="cuda") for _ in range(1, n)]
-                    keep.append((ins, segs, out, w1, w2, slots0, mine, bouts))
+                    segw = [torch.zeros(car.ll_wire_bytes("ll", numel // n * 2), dtype=torch.uint8, device="cuda")
+                            for _ in range(n)]
+                    keep.append((ins, segs, out, w1, w2, slots0, mine, bouts, segw))
                     for r in range(1, n):
                         car.ar_twoshot_rs(ins, segs, flags, PEER_STEP, r0=r, r1=r + 1)
+                        car.ar_twoshot_ll(ins, segw, flags, PEER_STEP, r0=r, r1=r + 1)
                     car.ar_ll_pack(ins[1:], w1[1:], "ll", PEER_STEP)
                     car.ar_ll_pack(ins[1:], w2[1:], "ll128", PEER_STEP)
                     one = car.prepare_oneshot(ins, out)
@@ -410,6 +431,8 @@ def select_table(args, torch, car, np, out_path):
                     calls["push"].append(lambda s, ps=ps, po=po: (ps(), po()))
                     bc = car.prepare_reduce_bcast(ins, bouts, 0, 1)
                     calls["bcast"].append(lambda s, bc=bc: bc())
+                    calls["twoshot_ll"].append(car.prepare_twoshot_ll(ins, segw, flags, 0, 1,
+                                                                      [out] + [None] * (n - 1)))
                 del src
                 torch.cuda.synchronize()
                 row = {"n": n, "bytes_per_rank": Sb}

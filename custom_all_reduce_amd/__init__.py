@@ -14,6 +14,7 @@ Functions mirror the C entry points and take ``torch.Tensor`` arguments:
     ar_ll_reduce_unpack(wires, out, step, flags)
     ar_ll128_reduce_unpack(wires, out, step, flags)
     ar_ll_allreduce(src, wires, out, flags, proto, me, step)   pack + reduce, one launch
+    ar_twoshot_ll(ins, segws, flags, step, r0=0, r1=None, outs=None)   two-shot, LL segments
     ar_flag_barrier_reset(flags, n)
 
 Each call enqueues on ``stream`` (default: torch's current stream) and
@@ -77,6 +78,7 @@ def _load(path: str = LIB_PATH):
     lib.ar_ll128_reduce_unpack.restype = i32
     lib.ar_ll_allreduce.argtypes = [vp, P, i32, i32, vp, sz, i32, i32, u32, vp, vp]
     lib.ar_ll_allreduce.restype = i32
+    lib.ar_twoshot_ll.argtypes, lib.ar_twoshot_ll.restype = [P, i32, P, sz, i32, i32, i32, vp, u32, P, vp], i32
     lib.ar_flag_barrier_reset.argtypes, lib.ar_flag_barrier_reset.restype = [vp, i32, vp], i32
     lib.ar_select_algo.argtypes, lib.ar_select_algo.restype = [i32, sz, i32, ctypes.c_double], i32
     lib.ar_algo_cost_us.argtypes, lib.ar_algo_cost_us.restype = [i32, i32, sz, i32, ctypes.c_double], ctypes.c_double
@@ -140,7 +142,7 @@ def get_poll_timeout_ns() -> int:
     return int(_lib.ar_get_poll_timeout_ns())
 
 
-ALGOS = ("oneshot", "twoshot", "ll", "ll128", "push", "bcast")  # ar_algo values 0..5
+ALGOS = ("oneshot", "twoshot", "ll", "ll128", "push", "bcast", "twoshot_ll")  # ar_algo values 0..6
 
 
 def _dtype_arg(dtype) -> int:
@@ -282,6 +284,25 @@ def prepare_twoshot_rs(ins, segs, flags, r0: int = 0, r1=None, outs=None) -> Pre
     return Prepared(_lib.ar_twoshot_rs, args, 8, "ar_twoshot_rs", (ins, segs, flags, outs))
 
 
+def prepare_twoshot_ll(ins, segws, flags, r0: int = 0, r1=None, outs=None) -> Prepared:
+    """Two-shot with LL segment wires (uint8 tensors of ll_wire_bytes("ll", m * element size))."""
+    n = len(ins)
+    r1 = n if r1 is None else r1
+    ins = [_dev_tensor(t, "input") for t in ins]
+    segws = [_dev_tensor(t, "segment wire") for t in segws]
+    flags = _dev_tensor(flags, "flags")
+    if len(segws) != n:
+        raise ValueError("need one segment wire per rank")
+    out_arr = None
+    if outs is not None:
+        if len(outs) != n:
+            raise ValueError("outs must hold n entries (None outside [r0, r1))")
+        out_arr = _ptr_array([(_dev_tensor(o, "out").data_ptr() if o is not None else 0) for o in outs])
+    args = [_ptr_array([t.data_ptr() for t in ins]), n, _ptr_array([t.data_ptr() for t in segws]), ins[0].numel(),
+            _dtype_code(ins[0]), r0, r1, flags.data_ptr(), 0, out_arr, None]
+    return Prepared(_lib.ar_twoshot_ll, args, 8, "ar_twoshot_ll", (ins, segws, flags, outs))
+
+
 def prepare_twoshot_ag(segs, outs, flags, r0: int = 0, r1=None, numel=None) -> Prepared:
     n = len(segs)
     r1 = n if r1 is None else r1
@@ -384,6 +405,12 @@ def ar_ll_reduce_unpack(wires, out, step: int, flags, stream=None):
 def ar_ll128_reduce_unpack(wires, out, step: int, flags, stream=None):
     prepare_ll_reduce(wires, out, flags, "ll128")(step, stream)
     return out
+
+
+def ar_twoshot_ll(ins, segws, flags, step: int, r0: int = 0, r1=None, outs=None, stream=None):
+    """Two-shot under LL: reduce-scatter into LL segment wires for ranks
+    [r0, r1); with ``outs`` also the all-gather in the same launch."""
+    prepare_twoshot_ll(ins, segws, flags, r0, r1, outs)(step, stream)
 
 
 def ar_ll_allreduce(src, wires, out, flags, proto, me: int, step: int, stream=None):

@@ -9,6 +9,8 @@ and every write, each byte once.  S = numel * element size (bytes per rank).
                           writes S/n (segment) + S (output)
   twoshot, all n ranks    n times the above
   twoshot RS only / AG only, per rank: reads S / S, writes S/n / S
+  twoshot under LL, one   reads S (RS) + (n-1)*2S/n (the peers' LL segment wires)
+    rank                  writes 2S/n (its segment wire) + S (output)
   reduce_bcast, one rank  reads S (its 1/n of n inputs)   writes S (1/n into n outputs)
   reduce_bcast, all n     reads n*S               writes n*S
   push, one sender        reads S                 writes ndst*S
@@ -44,6 +46,12 @@ def oneshot(n: int, S: int):
 def twoshot(n: int, S: int, ranks: int):
     """Fused two-shot; ranks = how many emulated ranks the launch computes (1 or n)."""
     return ranks * (S + (n - 1) * (S // n)), ranks * (S // n) + ranks * S
+
+
+def twoshot_ll(n: int, S: int, ranks: int):
+    """Fused two-shot with LL segment wires (2 bytes of wire per data byte)."""
+    m = S // n
+    return ranks * (S + (n - 1) * 2 * m), ranks * (2 * m + S)
 
 
 def twoshot_rs(n: int, S: int, ranks: int):

@@ -35,8 +35,10 @@ size_t elem_bytes(int dtype) { return dtype == AR_F32 ? 4 : 2; }
 // Semaphore synchronisations per call charged by the cost model, in ar_algo
 // order: start and end for the one-shot, the push and the reduce-broadcast;
 // two more around the two-shot's barrier; none for LL / LL128, whose
-// receivers learn of arrival from the flags in the lines.
-constexpr double kSemaphoreSyncs[kSelNumAlgos] = {2.0, 4.0, 0.0, 0.0, 2.0, 2.0};
+// receivers learn of arrival from the flags in the lines; start and end for
+// the two-shot under LL (it reads the peers' inputs; the barrier between its
+// phases is in the lines).
+constexpr double kSemaphoreSyncs[kSelNumAlgos] = {2.0, 4.0, 0.0, 0.0, 2.0, 2.0, 2.0};
 
 // Measured one-GPU time of algo at `bytes` per rank: piecewise linear in the
 // size between grid points, flat below the first (launch-bound), and
@@ -94,8 +96,10 @@ size_t wire_bytes(int proto, size_t nbytes) {
 }
 
 // Shared checks of the two-shot entry points.
+// seg_mult: segment buffer bytes per segment data byte (1; 2 for LL wires).
 int twoshot_check(const void* const* in, const void* const* seg, const void* const* out, int n,
-                  size_t numel, int dtype, int r0, int r1, const uint32_t* flags, uint32_t step) {
+                  size_t numel, int dtype, int r0, int r1, const uint32_t* flags, uint32_t step,
+                  size_t seg_mult = 1) {
     (void)step;  // 0 = the step id kept in the flag region (auto)
     if (!ranks_ok(n) || !dtype_ok(dtype) || numel == 0 || !seg || !flags) return AR_ERR_ARG;
     if (r0 < 0 || r1 > n || r0 >= r1) return AR_ERR_ARG;
@@ -121,7 +125,7 @@ int twoshot_check(const void* const* in, const void* const* seg, const void* con
     for (int j = 0; j < n; ++j) {
         // with an input present (reduce-scatter), seg[r0..r1) are written
         const bool written = in && j >= r0 && j < r1;
-        v.push_back(span(seg[j], m_bytes, written));
+        v.push_back(span(seg[j], m_bytes * seg_mult, written));
     }
     if (out)
         for (int r = r0; r < r1; ++r) v.push_back(span(out[r], S, true));
@@ -313,6 +317,16 @@ int ar_ll128_reduce_unpack(const void* const* wire, int n, void* out, size_t num
     return ll_reduce_common(wire, n, out, numel, dtype, step, flags, AR_PROTO_LL128, stream);
 }
 
+int ar_twoshot_ll(const void* const* in, int n, void* const* segw, size_t numel, int dtype, int r0, int r1,
+                  uint32_t* flags, uint32_t step, void* const* out, void* stream) {
+    if (!in || step == 0) return AR_ERR_ARG;  // the step id travels in the lines: explicit only
+    const int st = twoshot_check(in, segw, out, n, numel, dtype, r0, r1, flags, step, 2);
+    if (st != AR_OK) return st;
+    TwoShotRequest rq{in, segw, out, n, numel, dtype, r0, r1, flags, step, true, out != nullptr,
+                      timeout_ticks(), true};
+    return hip_status(launch_twoshot(rq, static_cast<hipStream_t>(stream)));
+}
+
 int ar_ll_allreduce(const void* src, void* const* wire, int n, int me, void* out, size_t numel, int dtype,
                     int proto, uint32_t step, uint32_t* flags, void* stream) {
     if (!ranks_ok(n) || me < 0 || me >= n || !dtype_ok(dtype) || numel == 0 || !src || !wire || !out || !flags ||
@@ -342,7 +356,9 @@ double ar_algo_cost_us(int algo, int n, size_t numel, int dtype, double sync_us)
         !(sync_us >= 0.0))
         return -1.0;
     const size_t es = elem_bytes(dtype);
-    if (algo == AR_ALGO_TWOSHOT && !(numel % size_t(n) == 0 && (numel / size_t(n) * es) % 16 == 0)) return -1.0;
+    if ((algo == AR_ALGO_TWOSHOT || algo == AR_ALGO_TWOSHOT_LL) &&
+        !(numel % size_t(n) == 0 && (numel / size_t(n) * es) % 16 == 0))
+        return -1.0;
     return share_us(algo, n, double(numel) * double(es)) + kSemaphoreSyncs[algo] * sync_us;
 }
 

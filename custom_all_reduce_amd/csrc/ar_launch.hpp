@@ -52,6 +52,7 @@ struct TwoShotRequest {
     uint32_t step;
     bool do_rs, do_ag;
     uint64_t timeout_ticks;
+    bool ll;  // segments are LL wires (4 data bytes + the step id per line); no slots
 };
 hipError_t launch_twoshot(const TwoShotRequest& rq, hipStream_t s);
 // All-gather on the copy engines: a one-workgroup slot wait, then n

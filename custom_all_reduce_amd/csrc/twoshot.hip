@@ -81,7 +81,7 @@ struct TwoShotParams {
     FastDiv div_per_out;  // all-gather items per output rank
 };
 
-template <typename T, int NR, int U>
+template <typename T, int NR, int U, bool kLL>
 __device__ __forceinline__ bool reduce_scatter_phase(const TwoShotParams& p, const uint32_t* epoch,
                                                      uint32_t& epoch_lane, uint32_t wave, uint32_t nwaves,
                                                      int lane) {
@@ -138,13 +138,22 @@ __device__ __forceinline__ bool reduce_scatter_phase(const TwoShotParams& p, con
                 // the tile of seg[r] as one wavefront-uniform buffer range
                 const uint32_t t0 = dst_t0[u];
                 const uint32_t tile_bytes = min(p.tile, p.mvec - t0) * 16u;
-                st_coherent(buffer_range(p.seg[dst_rank[u]] + t0, tile_bytes), (dst_idx[u] - t0) * 16u, v);
+                if constexpr (kLL) {
+                    // four LL lines: each 4 data bytes beside the step id
+                    const __amdgpu_buffer_rsrc_t rs = buffer_range(p.seg[dst_rank[u]] + 2 * t0, 2 * tile_bytes);
+                    st_coherent(rs, (dst_idx[u] - t0) * 32u, u32x4{v.x, p.step, v.y, p.step});
+                    st_coherent(rs, (dst_idx[u] - t0) * 32u + 16u, u32x4{v.z, p.step, v.w, p.step});
+                } else {
+                    st_coherent(buffer_range(p.seg[dst_rank[u]] + t0, tile_bytes), (dst_idx[u] - t0) * 16u, v);
+                }
                 // fused form: rank r's own segment of its output comes straight
                 // from registers (the all-gather copy of seg[r] into out[r])
                 if (p.do_ag) st_stream(p.out[dst_rank[u]] + size_t(dst_rank[u]) * p.mvec + dst_idx[u], v);
             }
         }
     }
+    // LL segments carry their flags: nothing to wait for or publish.
+    if constexpr (kLL) return true;
     // Publish: wait until this wavefront's coherent segment stores have
     // completed, then one slot store per produced tile (lane k stores the
     // slot of item k; the loop runs with every lane active so the step id
@@ -258,7 +267,93 @@ __device__ __forceinline__ void all_gather_phase(const TwoShotParams& p, const u
     }
 }
 
-template <typename T, int NR, int U>
+// LL all-gather: the segments are LL wires (each 4 data bytes beside the
+// step id in one 8-byte line), so a copy checks the flags of the lines it
+// reads instead of waiting on slots first: one memory round trip instead of
+// two.  A lane reads 32 wire bytes (16 data bytes) per unit with coherent
+// loads; one ballot decides whether every flag of the wavefront's units has
+// reached the step.  If not, the lanes re-read the units that are behind
+// until they are there or the wall-clock budget runs out (reported: phase 1,
+// segment, tile).
+__device__ __forceinline__ void all_gather_ll_phase(const TwoShotParams& p, int n, uint32_t wave, uint32_t nwaves,
+                                                    int lane) {
+    const uint32_t R = uint32_t(p.r1 - p.r0);
+    const bool skip_own = p.do_rs != 0;
+    const uint32_t per_out = uint32_t(skip_own ? n - 1 : n) * p.ktiles;
+    const uint32_t items = R * per_out;
+    if (wave >= items) return;
+    const uint32_t my_items = (items - wave + nwaves - 1) / nwaves;
+    const uint32_t upt = p.tile / kWave;
+    const uint32_t my_units = my_items * upt;
+    for (uint32_t q0 = 0; q0 < my_units; q0 += kCopyUnroll) {
+        u32x4 a[kCopyUnroll], b[kCopyUnroll];
+        u32x4* dst[kCopyUnroll];
+        __amdgpu_buffer_rsrc_t rs[kCopyUnroll];
+        uint32_t off[kCopyUnroll], seg_of[kCopyUnroll], tile_of[kCopyUnroll];
+        bool valid[kCopyUnroll];
+#pragma unroll
+        for (int u = 0; u < kCopyUnroll; ++u) {
+            const bool unit_ok = q0 + u < my_units;
+            const uint32_t q = unit_ok ? q0 + u : q0;
+            const uint32_t k = fdiv(q, p.div_upt), sub = q - k * upt;
+            const uint32_t it = wave + k * nwaves;
+            const uint32_t oo = fdiv(it, p.div_per_out);
+            const uint32_t ro = uint32_t(p.r0) + oo;
+            const uint32_t rem = it - oo * per_out;
+            const uint32_t jj = fdiv(rem, p.div_ktiles);
+            const uint32_t j = ag_source(jj, ro, skip_own);
+            const uint32_t t = rem - jj * p.ktiles;
+            const uint32_t idx = t * p.tile + sub * kWave + uint32_t(lane);
+            valid[u] = unit_ok && idx < p.mvec;
+            const uint32_t t0 = t * p.tile;
+            const uint32_t tile_bytes = min(p.tile, p.mvec - t0) * 16u;
+            rs[u] = buffer_range(p.seg[j] + 2 * t0, 2 * tile_bytes);
+            off[u] = (sub * kWave + uint32_t(lane)) * 32u;
+            a[u] = ld_coherent(rs[u], off[u]);
+            b[u] = ld_coherent(rs[u], off[u] + 16u);
+            dst[u] = p.out[ro] + size_t(j) * p.mvec + idx;
+            seg_of[u] = j;
+            tile_of[u] = t;
+        }
+        __builtin_amdgcn_sched_barrier(0);  // every load ahead of the first use
+        uint32_t fmin = 0xFFFFFFFFu;
+#pragma unroll
+        for (int u = 0; u < kCopyUnroll; ++u) {
+            const uint32_t f = min(min(a[u].y, a[u].w), min(b[u].y, b[u].w));
+            fmin = min(fmin, valid[u] ? f : 0xFFFFFFFFu);
+        }
+        if (wave_ballot(fmin < p.step) != 0) {
+            const uint64_t t_start = now_ticks();
+            while (true) {
+                bool good = true;
+                uint32_t bad_j = 0, bad_t = 0;
+#pragma unroll
+                for (int u = 0; u < kCopyUnroll; ++u) {
+                    const uint32_t f = min(min(a[u].y, a[u].w), min(b[u].y, b[u].w));
+                    if (valid[u] && f < p.step) {
+                        a[u] = ld_coherent(rs[u], off[u]);
+                        b[u] = ld_coherent(rs[u], off[u] + 16u);
+                        const uint32_t g = min(min(a[u].y, a[u].w), min(b[u].y, b[u].w));
+                        if (g < p.step && good) { good = false; bad_j = seg_of[u]; bad_t = tile_of[u]; }
+                    }
+                }
+                const uint64_t missing = ~wave_ballot(good) & wave_exec();
+                if (missing == 0) break;
+                if (now_ticks() - t_start > p.timeout_ticks) {
+                    const int bl = __ffsll((unsigned long long)missing) - 1;
+                    if (lane == bl) report_timeout(p.flags, 1u, bad_j, bad_t);
+                    return;  // skip every remaining copy of this wavefront
+                }
+                __builtin_amdgcn_s_sleep(1);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < kCopyUnroll; ++u)
+            if (valid[u]) st_stream(dst[u], u32x4{a[u].x, a[u].z, b[u].x, b[u].z});
+    }
+}
+
+template <typename T, int NR, int U, bool kLL>
 __global__ __launch_bounds__(kBlock) void twoshot_kernel(TwoShotParams p) {
     const int lane = threadIdx.x & (kWave - 1);
     // the wavefront index, made explicitly uniform so item arithmetic is scalar
@@ -275,7 +370,7 @@ __global__ __launch_bounds__(kBlock) void twoshot_kernel(TwoShotParams p) {
     // is stored back at the end if the launch reduces.
     uint32_t epoch_lane = 0;
     bool have_epoch = !p.auto_step;
-    if (p.do_rs && reduce_scatter_phase<T, NR, U>(p, epoch, epoch_lane, wave, nwaves, lane)) have_epoch = true;
+    if (p.do_rs && reduce_scatter_phase<T, NR, U, kLL>(p, epoch, epoch_lane, wave, nwaves, lane)) have_epoch = true;
     if (p.do_ag) {
         // In the fused form the all-gather items are dealt starting after the
         // wavefronts that hold reduce-scatter items, so that when the grid has
@@ -283,7 +378,8 @@ __global__ __launch_bounds__(kBlock) void twoshot_kernel(TwoShotParams p) {
         // after the other in the same wavefronts.
         const uint32_t rs_busy = p.do_rs ? min(R * p.ktiles, nwaves) : 0u;
         const uint32_t ag_wave = wave >= rs_busy ? wave - rs_busy : wave + (nwaves - rs_busy);
-        all_gather_phase(p, epoch, epoch_lane, have_epoch, p.do_rs ? 1u : 0u, NR, ag_wave, nwaves, lane);
+        if constexpr (kLL) all_gather_ll_phase(p, NR, ag_wave, nwaves, lane);
+        else all_gather_phase(p, epoch, epoch_lane, have_epoch, p.do_rs ? 1u : 0u, NR, ag_wave, nwaves, lane);
     }
     if (p.auto_step && p.do_rs) {
         if (!have_epoch && uint32_t(lane) < R) epoch_lane = flag_load_relaxed(epoch + lane);
@@ -343,8 +439,8 @@ void tile_params(TwoShotParams& p, size_t seg_bytes) {
     p.div_ktiles = make_fastdiv(p.ktiles);
 }
 
-template <typename T, int NR>
-hipError_t launch_t(const TwoShotRequest& rq, hipStream_t s) {
+template <typename T, int NR, bool kLL>
+hipError_t launch_k(const TwoShotRequest& rq, hipStream_t s) {
     // one unit in flight per wavefront in phase 1 (NR loads per lane), four in
     // phase 2: measured best for decode-sized messages, equal within noise
     // at 64 MiB per rank
@@ -370,7 +466,7 @@ hipError_t launch_t(const TwoShotRequest& rq, hipStream_t s) {
     p.do_ag = rq.do_ag;
     p.div_per_out = make_fastdiv(uint32_t(rq.do_rs ? NR - 1 : NR) * p.ktiles);
 
-    auto kern = twoshot_kernel<T, NR, U>;
+    auto kern = twoshot_kernel<T, NR, U, kLL>;
     const uint32_t R = uint32_t(rq.r1 - rq.r0);
     if (p.auto_step) {
         // every auto launch on a flag region uses the same grid, two
@@ -409,6 +505,11 @@ hipError_t launch_t(const TwoShotRequest& rq, hipStream_t s) {
     if (grid == 0) grid = 1;
     hipLaunchKernelGGL(kern, dim3(grid), dim3(kBlock), 0, s, p);
     return hipGetLastError();
+}
+
+template <typename T, int NR>
+hipError_t launch_t(const TwoShotRequest& rq, hipStream_t s) {
+    return rq.ll ? launch_k<T, NR, true>(rq, s) : launch_k<T, NR, false>(rq, s);
 }
 
 }  // namespace

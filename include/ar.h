@@ -248,7 +248,8 @@ int ar_ll128_reduce_unpack(const void* const* wire, int n, void* out, size_t num
  *    me's term taken from src (wire[me] is written, not read back).
  *  wire  : n wire buffers of ar_ll_wire_bytes(proto, numel * elem) bytes, in
  *          rank order; wire[me] is rank me's own (written), the others are
- *          read.
+ *          read.  Zeroed once before first use: a line counts as arrived
+ *          when its flag is >= step.
  *  me    : 0 <= me < n.
  *  flags : flag region (only the status words are used).
  * out, src and wire[me] may not overlap one another or any wire buffer;
@@ -258,6 +259,31 @@ int ar_ll128_reduce_unpack(const void* const* wire, int n, void* out, size_t num
  * missing line). */
 int ar_ll_allreduce(const void* src, void* const* wire, int n, int me, void* out, size_t numel, int dtype,
                     int proto, uint32_t step, uint32_t* flags, void* stream);
+
+/* Two-shot under the LL protocol ([NCCL] 算法, two-shot, with the 协议
+ * table's LL lines): as ar_twoshot_rs, but each reduced segment is written
+ * as an LL wire -- every 4 data bytes beside the step id in one 8-byte line,
+ * ar_ll_wire_bytes(AR_PROTO_LL, m * element size) = 2 * m * element size
+ * bytes -- and the all-gather reads the peers' lines and checks their flags
+ * (>= step) itself, so there are no arrival slots and no wait between a
+ * segment's stores and its flag.
+ *  segw  : n LL segment wires (segw[r0..r1) written, all n read with out),
+ *          zeroed once before first use: a line counts as arrived when its
+ *          flag is >= step, so a wire must never hold a flag at or above a
+ *          step that has not written it yet.
+ *  step  : 1..2^32-1, increasing from call to call (no auto ids: the flags
+ *          are in the lines); step 0 is AR_ERR_ARG.
+ *  out   : NULL for the reduce-scatter only; else the fused launch as in
+ *          ar_twoshot_rs (one persistent grid, out[r] for r in [r0, r1)).
+ *  flags : flag region (only the status words are used).
+ * The result is bit for bit that of ar_twoshot_rs and ar_oneshot.  Sizes,
+ * divisibility and errors as ar_twoshot_rs; asynchronously AR_ERR_TIMEOUT
+ * (phase AR_PHASE_TWOSHOT_AG, segment and tile of a line that stayed
+ * behind).  LL only: LL128 lines are read as separate 64-byte requests, so
+ * a flag seen at the end of a line says nothing of the data at its start
+ * while another wavefront of the same launch may still be writing it. */
+int ar_twoshot_ll(const void* const* in, int n, void* const* segw, size_t numel, int dtype, int r0, int r1,
+                  uint32_t* flags, uint32_t step, void* const* out, void* stream);
 
 /* Algorithm selection from measured costs ([NCCL] 算法 and 协议: no
  * algorithm or protocol is best at every size, so the choice goes by message
@@ -269,15 +295,17 @@ int ar_ll_allreduce(const void* src, void* const* wire, int n, int me, void* out
  *    two-shot; one rank's LL / LL128 send and receive in one launch
  *    (ar_ll_allreduce); one rank's push
  *    plus its one-shot over its staging slots; one rank's reduce-broadcast
- *    share), tabulated for
+ *    share; one rank's fused two-shot under LL), tabulated for
  *    n = 2..16 over 16 KiB..64 MiB per rank, interpolated linearly in the
  *    size, flat below the grid and extended with the last slope above it;
  *  - k is the number of cross-GPU semaphore synchronisations per call, the
  *    alpha terms of the [NCCL] 算法 alpha-beta model (2 for the one-shot, 4
  *    for the two-shot; 协议 names the semaphore as alpha's main source),
  *    2 for the push and the reduce-broadcast (start and end, as the one-shot;
- *    the broadcast has no barrier between its phases), and 0 for LL / LL128,
- *    whose flags travel with the data ([NCCL] 协议);
+ *    the broadcast has no barrier between its phases), 2 for the two-shot
+ *    under LL (its reduce-scatter still reads the peers' inputs, so start and
+ *    end stay; the barrier between the phases travels in the lines), and 0
+ *    for LL / LL128, whose flags travel with the data ([NCCL] 协议);
  *  - sync_us >= 0 is the cost of one such synchronisation on the caller's
  *    interconnect (0 when the ranks share one GPU).
  * ar_algo_cost_us returns that time in microseconds, or a negative value for
@@ -290,7 +318,8 @@ typedef enum {
     AR_ALGO_LL = 2,      /* ar_ll_allreduce, LL (or ar_ll_pack + ar_ll_reduce_unpack) */
     AR_ALGO_LL128 = 3,   /* ar_ll_allreduce, LL128 (or ar_ll_pack + ar_ll128_reduce_unpack) */
     AR_ALGO_PUSH = 4,    /* ar_push into the staging slots + ar_oneshot over them */
-    AR_ALGO_BCAST = 5    /* ar_reduce_bcast */
+    AR_ALGO_BCAST = 5,   /* ar_reduce_bcast */
+    AR_ALGO_TWOSHOT_LL = 6 /* ar_twoshot_ll with out (fused) */
 } ar_algo;
 double ar_algo_cost_us(int algo, int n, size_t numel, int dtype, double sync_us);
 int ar_select_algo(int n, size_t numel, int dtype, double sync_us);

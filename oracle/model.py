@@ -109,7 +109,8 @@ def hbm_bytes(op, S, n, proto=None):
     inputs (S bytes) and writes the reduced segment (S/n); the all-gather
     fills the output (S) -- rank r's own segment straight from the reduce,
     the other n-1 segments read from the peers (S (n-1)/n).  All n ranks: n
-    times that."""
+    times that.  Under LL a segment of S/n bytes travels as an LL wire of
+    twice its size."""
     if op == "oneshot":
         return n * S, S
     if op == "twoshot_share":
@@ -120,4 +121,12 @@ def hbm_bytes(op, S, n, proto=None):
         return S, ll_wire_bytes(proto, S)
     if op == "ll_reduce":
         return n * ll_wire_bytes(proto, S), S
+    if op == "ll_allreduce":
+        # one rank's step in one launch: its message read and its wire written,
+        # the n-1 peers' wires read, the output written
+        return S + (n - 1) * ll_wire_bytes(proto, S), ll_wire_bytes(proto, S) + S
+    if op == "twoshot_ll_share":
+        # as twoshot_share, with every segment an LL wire of its S/n bytes
+        w = ll_wire_bytes("ll", S // n)
+        return S + (n - 1) * w, w + S
     raise ValueError(op)

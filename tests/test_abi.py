@@ -210,6 +210,27 @@ def test_ll_argument_errors():
     assert L.ar_flag_barrier_reset(flags + 8, 4, NUL) == car.AR_ERR_ALIGN
 
 
+def test_twoshot_ll_argument_errors():
+    n = 4
+    ins = fake_ins(n)
+    segw = fake_ins(n, base=A + (64 << 30))
+    outs = fake_ins(n, base=A + (128 << 30))
+    flags = A + (200 << 30)
+    f = L.ar_twoshot_ll
+    numel = 4 * 64  # 64 fp32 per segment: 256 data bytes, a 512-byte LL wire
+    assert f(ins, n, segw, numel, 0, 0, n, flags, 0, outs, NUL) == car.AR_ERR_ARG  # step 0: no auto ids
+    assert f(None, n, segw, numel, 0, 0, n, flags, 1, outs, NUL) == car.AR_ERR_ARG
+    assert f(ins, n, None, numel, 0, 0, n, flags, 1, outs, NUL) == car.AR_ERR_ARG
+    assert f(ins, 1, segw, numel, 0, 0, 1, flags, 1, outs, NUL) == car.AR_ERR_ARG
+    assert f(ins, n, segw, numel, 0, 2, 1, flags, 1, outs, NUL) == car.AR_ERR_ARG  # r0 >= r1
+    assert f(ins, n, segw, 4 * 3, 0, 0, n, flags, 1, outs, NUL) == car.AR_ERR_DIVISIBLE  # 12-byte segments
+    assert f(ins, n, arr(A + (64 << 30) + 8, A + (65 << 30), A + (66 << 30), A + (67 << 30)), numel, 0, 0, n,
+             flags, 1, outs, NUL) == car.AR_ERR_ALIGN
+    # segw[0] is 512 bytes: an input 256 bytes in overlaps its second half (the first 256 would not tell)
+    assert f(arr(A + (64 << 30) + 256, A + (1 << 30), A + (2 << 30), A + (3 << 30)), n, segw, numel, 0, 0, n,
+             flags, 1, outs, NUL) == car.AR_ERR_ALIAS
+
+
 def test_ll_allreduce_argument_errors():
     n = 3
     src = A + (90 << 30)
@@ -250,9 +271,11 @@ def test_accounting_matches_oracle_model():
             assert accounting.oneshot(n, S) == model.hbm_bytes("oneshot", S, n)
             assert accounting.twoshot(n, S, 1) == model.hbm_bytes("twoshot_share", S, n)
             assert accounting.twoshot(n, S, n) == model.hbm_bytes("twoshot_full", S, n)
+            assert accounting.twoshot_ll(n, S, 1) == model.hbm_bytes("twoshot_ll_share", S, n)
             for proto in ("ll", "ll128"):
                 assert accounting.ll_pack(proto, S) == model.hbm_bytes("ll_pack", S, n, proto)
                 assert accounting.ll_reduce(proto, n, S) == model.hbm_bytes("ll_reduce", S, n, proto)
+                assert accounting.ll_allreduce(proto, n, S) == model.hbm_bytes("ll_allreduce", S, n, proto)
 
 
 # ---- algorithm selector (host logic) ------------------------------------------
@@ -279,9 +302,10 @@ def test_selector_picks_the_least_modelled_cost(n, sync_us):
 def test_selector_cost_model_terms():
     import torch
     bf = torch.bfloat16
-    # sync terms: 2 per call for the one-shot, 4 for the two-shot, none for LL / LL128
-    assert len(car.ALGOS) == 6
-    for a, k in zip(car.ALGOS, (2, 4, 0, 0, 2, 2)):
+    # sync terms: 2 per call for the one-shot, 4 for the two-shot, none for LL / LL128,
+    # 2 for the two-shot under LL (start and end; its barrier is in the lines)
+    assert len(car.ALGOS) == 7
+    for a, k in zip(car.ALGOS, (2, 4, 0, 0, 2, 2, 2)):
         assert car.algo_cost_us(a, 8, 1 << 20, bf, 10.0) == pytest.approx(car.algo_cost_us(a, 8, 1 << 20, bf, 0.0) + 10 * k)
     # flat below the grid, increasing in size above it, linear beyond the last point
     for a in car.ALGOS:
@@ -322,15 +346,17 @@ def test_selector_never_picks_an_inapplicable_two_shot():
     assert car.algo_cost_us("twoshot", 8, (16 << 20) // 2 + 1, bf) is None
     assert car.algo_cost_us("twoshot", 16, 16 * 4, bf) is None  # 8-byte segments
     assert car.algo_cost_us("twoshot", 8, (16 << 20) // 2, bf) is not None
+    assert car.algo_cost_us("twoshot_ll", 8, (16 << 20) // 2 + 1, bf) is None
+    assert car.algo_cost_us("twoshot_ll", 8, (16 << 20) // 2, bf) is not None
     for sync in (0.0, 0.5, 3.0):  # wherever the two-shot would be cheapest, it must not be chosen
-        assert car.select_algo(8, (16 << 20) // 2 + 1, bf, sync) != "twoshot"
+        assert car.select_algo(8, (16 << 20) // 2 + 1, bf, sync) not in ("twoshot", "twoshot_ll")
     assert car.lib.ar_select_algo(1, 10, 0, 0.0) == -car.AR_ERR_ARG
     assert car.lib.ar_select_algo(17, 10, 0, 0.0) == -car.AR_ERR_ARG
     assert car.lib.ar_select_algo(8, 0, 0, 0.0) == -car.AR_ERR_ARG
     assert car.lib.ar_select_algo(8, 10, 5, 0.0) == -car.AR_ERR_ARG
     assert car.lib.ar_select_algo(8, 10, 0, -1.0) == -car.AR_ERR_ARG
     assert car.lib.ar_select_algo(8, 10, 0, float("nan")) == -car.AR_ERR_ARG
-    assert car.lib.ar_algo_cost_us(6, 8, 10, 0, 0.0) < 0
+    assert car.lib.ar_algo_cost_us(7, 8, 10, 0, 0.0) < 0
     assert car.lib.ar_algo_cost_us(-1, 8, 10, 0, 0.0) < 0
 
 

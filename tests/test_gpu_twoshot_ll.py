@@ -1,0 +1,170 @@
+"""GPU parity of the two-shot under the LL protocol (ar_twoshot_ll): the
+reduced segments travel as LL wires (4 data bytes and the step id per 8-byte
+line) and the all-gather checks the flags of the lines it copies.  Outputs
+must equal the oracle's all-reduce bit for bit, and every segment wire the
+oracle's LL packing of the oracle's reduce-scatter segment."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from devtensors import bits, filled, first_mismatch, oracle_bits, to_dev
+
+pytestmark = pytest.mark.gpu
+
+car = pytest.importorskip("custom_all_reduce_amd")
+DT = {"f32": torch.float32, "bf16": torch.bfloat16}
+ES = {"f32": 4, "bf16": 2}
+
+
+class Ranks:
+    def __init__(self, host_ins, dt):
+        self.n = len(host_ins)
+        self.dt = dt
+        self.numel = host_ins[0].size
+        self.m = self.numel // self.n
+        self.W = car.ll_wire_bytes("ll", self.m * ES[dt])
+        self.ins = [to_dev(a) for a in host_ins]
+        # segment wires zeroed (every flag below the first step, as LL needs
+        # before first use), each with a 256-byte guard band after it
+        self.wbuf = [torch.full((self.W + 256,), 0xA5, dtype=torch.uint8, device="cuda") for _ in range(self.n)]
+        self.segw = [b[:self.W] for b in self.wbuf]
+        for w in self.segw:
+            w.zero_()
+        self.outs = [filled(self.numel, DT[dt]) for _ in range(self.n)]
+        self.flags = car.new_flags(self.n)
+
+    def load(self, host_ins):
+        for d, a in zip(self.ins, host_ins):
+            d.copy_(to_dev(a))
+
+
+def check(rk, host, step, ranks=None, wires=None):
+    segs, _ = oracle.twoshot(host, rk.dt)
+    want = oracle_bits(oracle.oneshot(host, rk.dt))
+    for r in (range(rk.n) if ranks is None else ranks):
+        got = bits(rk.outs[r])
+        assert np.array_equal(got, want), f"rank {r}: " + first_mismatch(got, want)
+    for j in (range(rk.n) if wires is None else wires):
+        got = bits(rk.wbuf[j])
+        want_w = oracle.ll_pack("ll", segs[j], step)
+        assert np.array_equal(got[:rk.W], want_w), f"segment wire {j}: " + first_mismatch(got[:rk.W], want_w)
+        assert np.all(got[rk.W:] == 0xA5), f"wrote past segment wire {j}"
+
+
+def assert_ok(flags):
+    word, detail = car.read_status(flags)
+    assert word == 0, f"status {car.decode_status(word)} detail {detail}"
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("n", [2, 3, 5, 8, 16])
+@pytest.mark.parametrize("seg_vectors", [1, 64, 65, 97, 64 * 1024])
+def test_full_emulation(n, dt, seg_vectors):
+    """Every rank in one persistent launch: the all-gather reads lines other
+    wavefronts of the same launch are writing."""
+    m = seg_vectors * (16 // ES[dt])
+    if n * m * ES[dt] > 64 << 20:
+        pytest.skip("keeps the oracle to seconds")
+    host = synth.rank_inputs(n, n * m, dt, "normal", config=300 + n)
+    rk = Ranks(host, dt)
+    car.ar_twoshot_ll(rk.ins, rk.segw, rk.flags, 5, outs=rk.outs)
+    torch.cuda.synchronize()
+    assert_ok(rk.flags)
+    check(rk, host, 5)
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("n, seg_vectors", [(8, 1024), (8, 64 * 1024), (16, 97), (2, 64 * 1024 + 7)])
+def test_one_gpu_share_steps_with_changing_data(n, dt, seg_vectors):
+    """Rank me's share after the peers' reduce-scatters of the same step,
+    three steps on the same buffers with new data each step."""
+    m = seg_vectors * (16 // ES[dt])
+    datasets = [synth.rank_inputs(n, n * m, dt, "normal", config=320 + k) for k in range(2)]
+    rk = Ranks(datasets[0], dt)
+    me = n // 2
+    outs = [rk.outs[r] if r == me else None for r in range(n)]
+    for step in (1, 2, 3):
+        host = datasets[step % 2]
+        rk.load(host)
+        for r in range(n):
+            if r != me:
+                car.ar_twoshot_ll(rk.ins, rk.segw, rk.flags, step, r0=r, r1=r + 1)
+        car.ar_twoshot_ll(rk.ins, rk.segw, rk.flags, step, r0=me, r1=me + 1, outs=outs)
+        torch.cuda.synchronize()
+        assert_ok(rk.flags)
+        check(rk, host, step, ranks=[me])
+
+
+def test_many_full_steps_without_reset():
+    """Steps 1..30 of every rank in one launch, data alternating: a copy of a
+    line left from the previous step would show."""
+    n, dt, m = 8, "bf16", 8 * 4096
+    datasets = [synth.rank_inputs(n, n * m, dt, "normal", config=330 + k) for k in range(3)]
+    wants = [oracle_bits(oracle.oneshot(h, dt)) for h in datasets]
+    rk = Ranks(datasets[0], dt)
+    for step in range(1, 31):
+        rk.load(datasets[step % 3])
+        car.ar_twoshot_ll(rk.ins, rk.segw, rk.flags, step, outs=rk.outs)
+        torch.cuda.synchronize()
+        assert_ok(rk.flags)
+        for r in (0, 5):
+            assert np.array_equal(bits(rk.outs[r]), wants[step % 3]), f"step {step} rank {r}"
+
+
+@pytest.mark.parametrize("seg_vectors", [1024, 64 * 1024])
+def test_missing_peer_times_out_and_names_its_segment(seg_vectors):
+    """Rank 6 reduced the previous step only: rank 0's share must report
+    (timeout, all-gather phase, segment 6) and exit; then a full step works."""
+    n, dt = 8, "bf16"
+    m = seg_vectors * 8
+    host = synth.rank_inputs(n, n * m, dt, "normal", config=340)
+    rk = Ranks(host, dt)
+    car.ar_twoshot_ll(rk.ins, rk.segw, rk.flags, 1, r0=6, r1=7)
+    for r in range(1, n):
+        if r != 6:
+            car.ar_twoshot_ll(rk.ins, rk.segw, rk.flags, 2, r0=r, r1=r + 1)
+    old = car.get_poll_timeout_ns()
+    car.set_poll_timeout_ns(2_000_000)
+    try:
+        car.ar_twoshot_ll(rk.ins, rk.segw, rk.flags, 2, r0=0, r1=1, outs=[rk.outs[0]] + [None] * (n - 1))
+        torch.cuda.synchronize()
+    finally:
+        car.set_poll_timeout_ns(old)
+    code, phase, seg = car.decode_status(car.read_status(rk.flags)[0])
+    assert (code, phase, seg) == (car.AR_ERR_TIMEOUT, car.PHASE_TWOSHOT_AG, 6)
+    car.ar_flag_barrier_reset(rk.flags, n)
+    car.ar_twoshot_ll(rk.ins, rk.segw, rk.flags, 3, outs=rk.outs)
+    torch.cuda.synchronize()
+    assert_ok(rk.flags)
+    check(rk, host, 3)
+
+
+def test_in_a_graph_with_increasing_steps():
+    """Six full steps with step ids 1..6 captured once, replayed with new
+    data.  The ids travel in the lines, so the wires are zeroed between
+    replays (outside the graph) to bring every line below step 1 again."""
+    n, dt, m = 4, "f32", 4 * 3000
+    datasets = [synth.rank_inputs(n, n * m, dt, "normal", config=350 + k) for k in range(2)]
+    wants = [oracle_bits(oracle.oneshot(h, dt)) for h in datasets]
+    rk = Ranks(datasets[0], dt)
+    torch.cuda.synchronize()
+
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for k in range(6):
+            car.ar_twoshot_ll(rk.ins, rk.segw, rk.flags, 1 + k, outs=rk.outs)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        rk.load(datasets[rep % 2])
+        for w in rk.segw:
+            w.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert_ok(rk.flags)
+        for r in range(n):
+            assert np.array_equal(bits(rk.outs[r]), wants[rep % 2]), f"replay {rep} rank {r}"
