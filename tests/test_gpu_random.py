@@ -4,8 +4,10 @@ Each case draws a rank count, a size (ragged for the paths that accept any
 size, divisible for the two-shot), a dtype and a value mix -- N(0,1) scaled by
 a random power of two per rank, small integers, values near the overflow and
 subnormal ranges, and a sprinkling of inf, NaN and -0 -- then compares the
-one-shot, the fused two-shot (every rank), the reduce-broadcast, LL and LL128
-with the CPU oracle bit for bit.  The cases are fixed by the seed."""
+one-shot, the fused two-shot (every rank; slots and LL segments), the
+reduce-broadcast, LL and LL128 (pack then receiver, and one rank's send and
+receive in one launch) with the CPU oracle bit for bit.  The cases are fixed
+by the seed."""
 from __future__ import annotations
 
 import numpy as np
@@ -84,6 +86,13 @@ def test_random_case_every_path(k):
         car.raise_on_status(flags, label)
         for r in range(n):
             assert np.array_equal(bits(outs[r]), want), label + f" two-shot rank {r}"
+        segw = [torch.zeros(car.ll_wire_bytes("ll", numel // n * es), dtype=torch.uint8, device="cuda")
+                for _ in range(n)]
+        car.ar_twoshot_ll(ins, segw, flags, 1, outs=outs)
+        torch.cuda.synchronize()
+        car.raise_on_status(flags, label)
+        for r in range(n):
+            assert np.array_equal(bits(outs[r]), want), label + f" two-shot under LL rank {r}"
 
     for proto in ("ll", "ll128"):
         W = car.ll_wire_bytes(proto, numel * es)
@@ -93,3 +102,10 @@ def test_random_case_every_path(k):
         torch.cuda.synchronize()
         car.raise_on_status(flags, label)
         assert np.array_equal(bits(out), want), label + " " + proto
+        # one rank's step in one launch over the same (already packed) peers' wires
+        me = k % n
+        out.zero_()
+        car.ar_ll_allreduce(ins[me], wires, out, flags, proto, me, 2)
+        torch.cuda.synchronize()
+        car.raise_on_status(flags, label)
+        assert np.array_equal(bits(out), want), label + f" {proto} in one launch, rank {me}"
