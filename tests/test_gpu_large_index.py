@@ -109,3 +109,13 @@ def test_two_shot_divisible_prefix(data):
     car.raise_on_status(flags)
     for r in range(N):
         check(outs[r], idx[keep], want[keep], f"two-shot rank {r}")
+    # the same under LL: 1 GiB segments travel as 2 GiB wires (byte offsets past 2^31)
+    del segs
+    segw = [torch.zeros(car.ll_wire_bytes("ll", m // N * 2), dtype=torch.uint8, device="cuda") for _ in range(N)]
+    for o in outs:
+        o.zero_()
+    car.ar_twoshot_ll(heads, segw, flags, 1, outs=outs)
+    torch.cuda.synchronize()
+    car.raise_on_status(flags)
+    for r in range(N):
+        check(outs[r], idx[keep], want[keep], f"two-shot under LL rank {r}")
