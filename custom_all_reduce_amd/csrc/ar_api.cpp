@@ -288,8 +288,8 @@ int ar_twoshot_ag(const void* const* seg, int n, void* const* out, size_t numel,
 
 int ar_ll_pack(const void* const* src, void* const* wire, int count, size_t numel, int dtype, int proto,
                uint32_t step, void* stream) {
-    if (!src || !wire || count < 1 || count > AR_MAX_RANKS || numel == 0 || !dtype_ok(dtype) || step == 0)
-        return AR_ERR_ARG;
+    // step 0: auto (each line's previous flag + 1)
+    if (!src || !wire || count < 1 || count > AR_MAX_RANKS || numel == 0 || !dtype_ok(dtype)) return AR_ERR_ARG;
     if (proto != AR_PROTO_LL && proto != AR_PROTO_LL128) return AR_ERR_ARG;
     const size_t es = elem_bytes(dtype);
     if (numel > kMaxBytes / es) return AR_ERR_ARG;
@@ -329,8 +329,8 @@ int ar_twoshot_ll(const void* const* in, int n, void* const* segw, size_t numel,
 
 int ar_ll_allreduce(const void* src, void* const* wire, int n, int me, void* out, size_t numel, int dtype,
                     int proto, uint32_t step, uint32_t* flags, void* stream) {
-    if (!ranks_ok(n) || me < 0 || me >= n || !dtype_ok(dtype) || numel == 0 || !src || !wire || !out || !flags ||
-        step == 0)
+    // step 0: auto (one past the previous flag of rank me's line, line by line)
+    if (!ranks_ok(n) || me < 0 || me >= n || !dtype_ok(dtype) || numel == 0 || !src || !wire || !out || !flags)
         return AR_ERR_ARG;
     if (proto != AR_PROTO_LL && proto != AR_PROTO_LL128) return AR_ERR_ARG;
     const size_t es = elem_bytes(dtype);

@@ -61,22 +61,28 @@ __global__ __launch_bounds__(kBlock) void ll_pack_kernel(PackParams p) {
     const size_t lines = (p.nbytes + 3) / 4;   // = words
     const size_t c0 = size_t(blockIdx.x) * (kBlock * kPackUnroll) + threadIdx.x;
     u32x2 v[kPackUnroll];
+    u32x4 old[kPackUnroll];  // auto step ids: the two lines as the last call left them
 #pragma unroll
     for (int u = 0; u < kPackUnroll; ++u) {
         const size_t c = c0 + size_t(u) * kBlock;
-        if (c < full) v[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(src) + c);
+        if (c < full) {
+            v[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(src) + c);
+            if (p.step == 0) old[u] = __builtin_nontemporal_load(wire + c);
+        }
     }
 #pragma unroll
     for (int u = 0; u < kPackUnroll; ++u) {
         const size_t c = c0 + size_t(u) * kBlock;
         if (c < full) {
-            st_stream(wire + c, u32x4{v[u].x, p.step, v[u].y, p.step});
+            const uint32_t s0 = p.step != 0 ? p.step : old[u].y + 1u;
+            const uint32_t s1 = p.step != 0 ? p.step : old[u].w + 1u;
+            st_stream(wire + c, u32x4{v[u].x, s0, v[u].y, s1});
         } else if (2 * c < lines) {
             uint32_t w[2] = {0u, 0u};
             for (size_t b = 8 * c; b < p.nbytes; ++b) w[(b >> 2) & 1] |= uint32_t(src[b]) << (8 * (b & 3));
             u32x2* ln = reinterpret_cast<u32x2*>(p.wire[blockIdx.y]);
-            ln[2 * c] = u32x2{w[0], p.step};
-            if (2 * c + 1 < lines) ln[2 * c + 1] = u32x2{w[1], p.step};
+            ln[2 * c] = u32x2{w[0], p.step != 0 ? p.step : ln[2 * c].y + 1u};
+            if (2 * c + 1 < lines) ln[2 * c + 1] = u32x2{w[1], p.step != 0 ? p.step : ln[2 * c + 1].y + 1u};
         }
     }
 }
@@ -104,7 +110,10 @@ __global__ __launch_bounds__(kBlock) void ll128_pack_kernel(PackParams p, size_t
         for (size_t b = off; b < p.nbytes && b < off + data_bytes; ++b)
             w[((b - off) >> 2) & 3] |= uint32_t(src[b]) << (8 * (b & 3));
     }
-    if (part == 7) { w[2] = p.step; w[3] = 0u; }  // 64-bit flag = step, little endian
+    if (part == 7) {  // 64-bit flag = step, little endian; auto: the line's last flag + 1
+        w[2] = p.step != 0 ? p.step : reinterpret_cast<const uint32_t*>(p.wire[blockIdx.y])[line * 32 + 30] + 1u;
+        w[3] = 0u;
+    }
     st_stream(wire + line * 8 + part, u32x4{w[0], w[1], w[2], w[3]});
 }
 
@@ -301,6 +310,9 @@ __global__ __launch_bounds__(kBlockLL) void ll_reduce1_kernel(ReduceParams p) {
     uint32_t own = 0;
     bool own_late = false;
     if (kFused && own_whole) own = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p.src) + c);
+    // auto step ids (step 0): rank me's line c as the last call left it
+    u32x2 own_old = u32x2{0u, 0u};
+    if (kFused && p.step == 0) own_old = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p.own_wire) + cc);
     u32x2 x[NR];
 #pragma unroll
     for (int r = 0; r < NR; ++r)
@@ -310,32 +322,37 @@ __global__ __launch_bounds__(kBlockLL) void ll_reduce1_kernel(ReduceParams p) {
         if (!own_whole && act)
             own = c < words ? reinterpret_cast<const uint32_t*>(p.src)[c]
                             : uint32_t(reinterpret_cast<const uint16_t*>(p.src)[2 * c]);
+    }
+    // the step id of this lane's line: the call's, or (auto) one past the
+    // last flag of rank me's line, every call advancing every line by one
+    const uint32_t step = kFused && p.step == 0 ? own_old.y + 1u : p.step;
+    if constexpr (kFused) {
         // rank me's line carries the step: the readiness checks pass it
 #pragma unroll
         for (int r = 0; r < NR; ++r)
-            if (r == p.me) x[r] = u32x2{own, p.step};
+            if (r == p.me) x[r] = u32x2{own, step};
     }
     uint32_t fmin = 0xFFFFFFFFu;
 #pragma unroll
     for (int r = 0; r < NR; ++r) fmin = min(fmin, x[r].y);
-    bool ok = !act | (fmin >= p.step);
+    bool ok = !act | (fmin >= step);
     // kFused: rank me's line for its peers goes out before any wait on a peer
     // (slow path) or, when every line is already there, last, after the
     // output (a store issued earlier is waited for by the compiler's later
     // waits: stores and loads count in one counter).
     if (wave_ballot(!ok) != 0) {
-        if (kFused && act) __builtin_nontemporal_store(u32x2{own, p.step}, reinterpret_cast<u32x2*>(p.own_wire) + c);
+        if (kFused && act) __builtin_nontemporal_store(u32x2{own, step}, reinterpret_cast<u32x2*>(p.own_wire) + c);
         const uint64_t t0 = now_ticks();
         while (true) {
             bool good = true;
             int bad_r = 0;
 #pragma unroll
             for (int r = 0; r < NR; ++r) {
-                if (act && x[r].y < p.step) {
+                if (act && x[r].y < step) {
                     const uint64_t a = line_load_relaxed(reinterpret_cast<const uint64_t*>(p.wire[r]) + c);
                     x[r].x = uint32_t(a);
                     x[r].y = uint32_t(a >> 32);
-                    if (x[r].y < p.step && good) { good = false; bad_r = r; }
+                    if (x[r].y < step && good) { good = false; bad_r = r; }
                 }
             }
             const uint64_t missing = ~wave_ballot(good) & wave_exec();
@@ -370,7 +387,7 @@ __global__ __launch_bounds__(kBlockLL) void ll_reduce1_kernel(ReduceParams p) {
         const uint32_t rw[1] = {word};
         store_out_bytes<T>(p.out, 4 * c, p.nbytes, rw);
     }
-    if (kFused && own_late) __builtin_nontemporal_store(u32x2{own, p.step}, reinterpret_cast<u32x2*>(p.own_wire) + c);
+    if (kFused && own_late) __builtin_nontemporal_store(u32x2{own, step}, reinterpret_cast<u32x2*>(p.own_wire) + c);
 }
 
 // kFused: rank me's term at a lane is the message bytes its line position
@@ -405,9 +422,18 @@ __global__ __launch_bounds__(kBlock128) void ll128_reduce_kernel(ReduceParams p)
     uint32_t own[U][4] = {};
     u32x4 mine[U];
     bool own_whole[U];
+    // the step id of each unit's line: the call's, or (auto, step 0) one past
+    // the last flag of rank me's line, read by the line's lanes with the loads
+    uint32_t step[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) step[u] = p.step;
     if constexpr (kFused) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
+            if (p.step == 0) {
+                const size_t ll = valid[u] ? line[u] : p.nlines - 1;
+                step[u] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p.own_wire) + ll * 32 + 30);
+            }
             // wavefront-uniform: every data byte of the unit's 8 lines exists
             own_whole[u] = ((wave * U + u) * 8 + 8) * 120 <= p.nbytes;
             if (own_whole[u]) {
@@ -423,6 +449,7 @@ __global__ __launch_bounds__(kBlock128) void ll128_reduce_kernel(ReduceParams p)
     if constexpr (kFused) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
+            if (p.step == 0) step[u] += 1u;
             if (!own_whole[u] && valid[u]) {
                 // the last wavefront: each word on its own, independent loads
                 // (4-byte aligned: 120 line + 16 part is a multiple of 8); a
@@ -437,7 +464,7 @@ __global__ __launch_bounds__(kBlock128) void ll128_reduce_kernel(ReduceParams p)
                     }
                 }
             }
-            if (part == 7u) { own[u][2] = p.step; own[u][3] = 0u; }  // 64-bit flag = step
+            if (part == 7u) { own[u][2] = step[u]; own[u][3] = 0u; }  // 64-bit flag = step
             mine[u] = u32x4{own[u][0], own[u][1], own[u][2], own[u][3]};
             if (valid[u]) st_stream(reinterpret_cast<u32x4*>(p.own_wire) + line[u] * 8 + part, mine[u]);
         }
@@ -450,7 +477,7 @@ __global__ __launch_bounds__(kBlock128) void ll128_reduce_kernel(ReduceParams p)
         uint32_t fmin = 0xFFFFFFFFu;
 #pragma unroll
         for (int r = 0; r < NR; ++r) fmin = min(fmin, x[u][r].w != 0u ? 0xFFFFFFFFu : x[u][r].z);
-        ok &= !valid[u] | (part != 7u) | (fmin >= p.step);
+        ok &= !valid[u] | (part != 7u) | (fmin >= step[u]);
     }
     if (wave_ballot(!ok) != 0) {
         // Slow path: poll the flags with coherent 64-bit loads, then re-read
@@ -467,7 +494,7 @@ __global__ __launch_bounds__(kBlock128) void ll128_reduce_kernel(ReduceParams p)
                     if (valid[u] && part == 7u) {
                         const uint64_t f = line_load_relaxed(
                             reinterpret_cast<const uint64_t*>(p.wire[r] + line[u] * 128 + 120));
-                        if (f < uint64_t(p.step) && ready) { ready = false; bad_r = r; bad_line = line[u]; }
+                        if (f < uint64_t(step[u]) && ready) { ready = false; bad_r = r; bad_line = line[u]; }
                     }
                 }
             }

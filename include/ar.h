@@ -219,6 +219,10 @@ int ar_twoshot_ag_copy(const void* const* seg, int n, void* const* out, size_t n
  * numel elements of dtype taken as bytes, into their wire buffers
  * (ar_ll_wire_bytes(proto, numel * element size) bytes each).  Every line
  * carries step as its flag (32-bit for LL, 64-bit for LL128), after its data.
+ * step 0 (auto): each line's flag becomes its previous flag + 1, so that
+ * calls captured once into a HIP graph advance every line by one per replay
+ * with no step id from the host ([CAR] step 5, graph path); the wire must
+ * start zeroed and must not mix explicit and auto ids.
  * count >= 1 (1 = this GPU's own message; n = every emulated rank at once).
  * Errors: AR_ERR_ARG, AR_ERR_ALIGN, AR_ERR_ALIAS, AR_ERR_HIP. */
 int ar_ll_pack(const void* const* src, void* const* wire, int count, size_t numel, int dtype,
@@ -251,6 +255,11 @@ int ar_ll128_reduce_unpack(const void* const* wire, int n, void* out, size_t num
  *          read.  Zeroed once before first use: a line counts as arrived
  *          when its flag is >= step.
  *  me    : 0 <= me < n.
+ *  step  : 1..2^32-1, increasing from call to call; or 0 (auto): each line
+ *          of wire[me] takes its previous flag + 1, and the peers' line at
+ *          the same position must carry at least that -- every rank's call
+ *          advances every one of its lines by one, so the ranks' auto calls
+ *          stay in step (the same rule for ar_ll_pack with step 0).
  *  flags : flag region (only the status words are used).
  * out, src and wire[me] may not overlap one another or any wire buffer;
  * all pointers 16-byte aligned.  LL uses one line per lane at every size.

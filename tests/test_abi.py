@@ -193,7 +193,6 @@ def test_ll_argument_errors():
     srcs, wires = fake_ins(n), fake_ins(n, base=A + (64 << 30))
     assert L.ar_ll_pack(srcs, wires, 0, 10, 0, 0, 1, NUL) == car.AR_ERR_ARG  # count 0
     assert L.ar_ll_pack(srcs, wires, n, 10, 0, 2, 1, NUL) == car.AR_ERR_ARG  # proto
-    assert L.ar_ll_pack(srcs, wires, n, 10, 0, 0, 0, NUL) == car.AR_ERR_ARG  # step 0
     assert L.ar_ll_pack(srcs, arr(A + (64 << 30) + 8, A + (65 << 30), A + (66 << 30)), n, 10, 0, 0, 1, NUL) == \
         car.AR_ERR_ALIGN
     # wire of 10 fp32 (80 bytes) overlapping the source
@@ -241,7 +240,6 @@ def test_ll_allreduce_argument_errors():
         assert f(src, wires, 1, 0, out, 10, 0, proto, 1, flags, NUL) == car.AR_ERR_ARG  # n
         assert f(src, wires, n, -1, out, 10, 0, proto, 1, flags, NUL) == car.AR_ERR_ARG  # me
         assert f(src, wires, n, n, out, 10, 0, proto, 1, flags, NUL) == car.AR_ERR_ARG
-        assert f(src, wires, n, 1, out, 10, 0, proto, 0, flags, NUL) == car.AR_ERR_ARG  # step 0
         assert f(src, wires, n, 1, out, 0, 0, proto, 1, flags, NUL) == car.AR_ERR_ARG  # numel 0
         assert f(None, wires, n, 1, out, 10, 0, proto, 1, flags, NUL) == car.AR_ERR_ARG
         assert f(src, wires, n, 1, out, 10, 0, proto, 1, None, NUL) == car.AR_ERR_ARG

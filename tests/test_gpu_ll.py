@@ -287,3 +287,100 @@ def test_allreduce_ll_above_16MiB(dt, numel):
     got, want = bits(out), oracle_bits(oracle.oneshot(host, dt))
     assert np.array_equal(got, want), first_mismatch(got, want)
     assert np.array_equal(bits(bufs[1])[:W], oracle.ll_pack("ll", host[1], 5))
+
+
+# ------------------------------------------------------------ auto step ids --
+def zeroed_wires(n, numel, dt, proto):
+    bufs, W = wires_for(n, numel, dt, proto)
+    for b in bufs:
+        b[:W].zero_()
+    return bufs, W
+
+
+@pytest.mark.parametrize("proto", ["ll", "ll128"])
+@pytest.mark.parametrize("dt, numel", [("f32", 4096 + 3), ("bf16", 61), ("bf16", 30 * 64 * 3 + 11)])
+def test_pack_auto_steps_advance_every_line(proto, dt, numel):
+    """Step 0: every line's flag becomes its previous flag + 1; after three
+    calls from zeroed wires the wire is the oracle's packing at step 3."""
+    n = 2
+    host = synth.rank_inputs(n, numel, dt, "normal", config=180)
+    srcs = [to_dev(a) for a in host]
+    bufs, W = zeroed_wires(n, numel, dt, proto)
+    for _ in range(3):
+        car.ar_ll_pack(srcs, [b[:W] for b in bufs], proto, 0)
+    torch.cuda.synchronize()
+    for r in range(n):
+        got = bits(bufs[r])
+        want = oracle.ll_pack(proto, host[r], 3)
+        assert np.array_equal(got[:W], want), first_mismatch(got[:W], want)
+        assert np.all(got[W:] == 0xA5), "pack wrote past the wire buffer"
+
+
+@pytest.mark.parametrize("proto", ["ll", "ll128"])
+@pytest.mark.parametrize("dt, numel", [("bf16", 8 * 8192), ("f32", 100000 + 1)])
+def test_allreduce_auto_steps_replayed_in_a_graph(proto, dt, numel):
+    """The peers' packs and rank 3's send-and-receive, all with step 0,
+    captured once and replayed with new data and nothing reset in between:
+    every replay matches the oracle and advances every line by one."""
+    n, me = 8, 3
+    datasets = [synth.rank_inputs(n, numel, dt, "normal", config=190 + k) for k in range(3)]
+    wants = [oracle_bits(oracle.oneshot(h, dt)) for h in datasets]
+    srcs = [to_dev(a) for a in datasets[0]]
+    bufs, W = zeroed_wires(n, numel, dt, proto)
+    wires = [b[:W] for b in bufs]
+    flags = car.new_flags(n)
+    out = torch.empty(numel, dtype=DT[dt], device="cuda")
+    peers = [r for r in range(n) if r != me]
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        car.ar_ll_pack([srcs[r] for r in peers], [wires[r] for r in peers], proto, 0)
+        car.ar_ll_allreduce(srcs[me], wires, out, flags, proto, me, 0)
+    torch.cuda.synchronize()
+    for rep in range(6):
+        k = rep % 3
+        for d, a in zip(srcs, datasets[k]):  # eager work between replays
+            d.copy_(to_dev(a))
+        out.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert car.read_status(flags)[0] == 0, f"replay {rep}"
+        got = bits(out)
+        assert np.array_equal(got, wants[k]), f"replay {rep}: " + first_mismatch(got, wants[k])
+        for r in (me, peers[0]):
+            w = bits(bufs[r])[:W]
+            assert np.array_equal(w, oracle.ll_pack(proto, datasets[k][r], rep + 1)), f"replay {rep}: wire {r}"
+
+
+@pytest.mark.parametrize("proto, phase", [("ll", 2), ("ll128", 3)])
+def test_allreduce_auto_steps_peer_left_behind_times_out(proto, phase):
+    """Two auto steps for every rank, then a third where rank 6 does not
+    pack: rank 0's lines move to 3, rank 6's stay at 2, and the launch
+    reports (timeout, phase, rank 6)."""
+    n, numel, dt, me = 8, 4096, "f32", 0
+    host = synth.rank_inputs(n, numel, dt, "normal", config=195)
+    srcs = [to_dev(a) for a in host]
+    bufs, W = zeroed_wires(n, numel, dt, proto)
+    wires = [b[:W] for b in bufs]
+    flags = car.new_flags(n)
+    out = torch.empty(numel, device="cuda")
+    peers = [r for r in range(n) if r != me]
+    for _ in range(2):
+        car.ar_ll_pack([srcs[r] for r in peers], [wires[r] for r in peers], proto, 0)
+        car.ar_ll_allreduce(srcs[me], wires, out, flags, proto, me, 0)
+    torch.cuda.synchronize()
+    assert car.read_status(flags)[0] == 0
+    assert np.array_equal(bits(out), oracle_bits(oracle.oneshot(host, dt)))
+    late = [r for r in peers if r != 6]
+    car.ar_ll_pack([srcs[r] for r in late], [wires[r] for r in late], proto, 0)
+    old = car.get_poll_timeout_ns()
+    car.set_poll_timeout_ns(20_000)
+    try:
+        car.ar_ll_allreduce(srcs[me], wires, out, flags, proto, me, 0)
+        torch.cuda.synchronize()
+    finally:
+        car.set_poll_timeout_ns(old)
+    code, ph, rank = car.decode_status(car.read_status(flags)[0])
+    assert (code, ph, rank) == (car.AR_ERR_TIMEOUT, phase, 6)
+    assert np.array_equal(bits(bufs[me])[:W], oracle.ll_pack(proto, host[me], 3))
