@@ -259,7 +259,9 @@ int ar_ll128_reduce_unpack(const void* const* wire, int n, void* out, size_t num
  *          of wire[me] takes its previous flag + 1, and the peers' line at
  *          the same position must carry at least that -- every rank's call
  *          advances every one of its lines by one, so the ranks' auto calls
- *          stay in step (the same rule for ar_ll_pack with step 0).
+ *          stay in step (the same rule for ar_ll_pack with step 0).  After a
+ *          timeout the ranks' wires may be a step apart: zero every wire (and
+ *          reset the status words) before the next auto call.
  *  flags : flag region (only the status words are used).
  * out, src and wire[me] may not overlap one another or any wire buffer;
  * all pointers 16-byte aligned.  LL uses one line per lane at every size.
