@@ -182,6 +182,30 @@ __device__ __forceinline__ uint32_t ag_source(uint32_t jj, uint32_t ro, bool ski
     return jj + (((ro - jj - 1u) >> 31) & uint32_t(skip_own));
 }
 
+// Unit q (64 consecutive vectors, one per lane) of a wavefront's all-gather
+// list: the output rank ro, the source segment j, the tile t, the unit's
+// place sub in its tile, and this lane's vector index idx in the segment.
+// Every field but idx is wavefront-uniform.
+struct AgUnit {
+    uint32_t ro, j, t, sub, idx;
+};
+
+__device__ __forceinline__ AgUnit ag_unit(const TwoShotParams& p, uint32_t per_out, bool skip_own, uint32_t wave,
+                                          uint32_t nwaves, uint32_t upt, uint32_t q, int lane) {
+    AgUnit a;
+    const uint32_t k = fdiv(q, p.div_upt);
+    a.sub = q - k * upt;
+    const uint32_t it = wave + k * nwaves;
+    const uint32_t oo = fdiv(it, p.div_per_out);
+    a.ro = uint32_t(p.r0) + oo;
+    const uint32_t rem = it - oo * per_out;
+    const uint32_t jj = fdiv(rem, p.div_ktiles);
+    a.j = ag_source(jj, a.ro, skip_own);
+    a.t = rem - jj * p.ktiles;
+    a.idx = a.t * p.tile + a.sub * kWave + uint32_t(lane);
+    return a;
+}
+
 // With auto step ids and no epoch loaded yet (have_epoch false), the
 // wavefront loads its epoch copies right behind its first slot poll, so the
 // two loads share one round trip; the step id a slot must reach is epoch +
@@ -246,20 +270,12 @@ __device__ __forceinline__ void all_gather_phase(const TwoShotParams& p, const u
         for (int u = 0; u < kCopyUnroll; ++u) {
             const bool unit_ok = q0 + u < my_units;
             const uint32_t q = unit_ok ? q0 + u : q0;
-            const uint32_t k = fdiv(q, p.div_upt), sub = q - k * upt;
-            const uint32_t it = wave + k * nwaves;
-            const uint32_t oo = fdiv(it, p.div_per_out);
-            const uint32_t ro = uint32_t(p.r0) + oo;
-            const uint32_t rem = it - oo * per_out;
-            const uint32_t jj = fdiv(rem, p.div_ktiles);
-            const uint32_t j = ag_source(jj, ro, skip_own);
-            const uint32_t t = rem - jj * p.ktiles;
-            const uint32_t idx = t * p.tile + sub * kWave + uint32_t(lane);
-            valid[u] = unit_ok && idx < p.mvec;
-            const uint32_t t0 = t * p.tile;
+            const AgUnit a = ag_unit(p, per_out, skip_own, wave, nwaves, upt, q, lane);
+            valid[u] = unit_ok && a.idx < p.mvec;
+            const uint32_t t0 = a.t * p.tile;
             const uint32_t tile_bytes = min(p.tile, p.mvec - t0) * 16u;
-            x[u] = ld_coherent(buffer_range(p.seg[j] + t0, tile_bytes), (sub * kWave + uint32_t(lane)) * 16u);
-            dst[u] = p.out[ro] + size_t(j) * p.mvec + idx;
+            x[u] = ld_coherent(buffer_range(p.seg[a.j] + t0, tile_bytes), (a.sub * kWave + uint32_t(lane)) * 16u);
+            dst[u] = p.out[a.ro] + size_t(a.j) * p.mvec + a.idx;
         }
 #pragma unroll
         for (int u = 0; u < kCopyUnroll; ++u)
@@ -295,25 +311,17 @@ __device__ __forceinline__ void all_gather_ll_phase(const TwoShotParams& p, int 
         for (int u = 0; u < kCopyUnroll; ++u) {
             const bool unit_ok = q0 + u < my_units;
             const uint32_t q = unit_ok ? q0 + u : q0;
-            const uint32_t k = fdiv(q, p.div_upt), sub = q - k * upt;
-            const uint32_t it = wave + k * nwaves;
-            const uint32_t oo = fdiv(it, p.div_per_out);
-            const uint32_t ro = uint32_t(p.r0) + oo;
-            const uint32_t rem = it - oo * per_out;
-            const uint32_t jj = fdiv(rem, p.div_ktiles);
-            const uint32_t j = ag_source(jj, ro, skip_own);
-            const uint32_t t = rem - jj * p.ktiles;
-            const uint32_t idx = t * p.tile + sub * kWave + uint32_t(lane);
-            valid[u] = unit_ok && idx < p.mvec;
-            const uint32_t t0 = t * p.tile;
+            const AgUnit au = ag_unit(p, per_out, skip_own, wave, nwaves, upt, q, lane);
+            valid[u] = unit_ok && au.idx < p.mvec;
+            const uint32_t t0 = au.t * p.tile;
             const uint32_t tile_bytes = min(p.tile, p.mvec - t0) * 16u;
-            rs[u] = buffer_range(p.seg[j] + 2 * t0, 2 * tile_bytes);
-            off[u] = (sub * kWave + uint32_t(lane)) * 32u;
+            rs[u] = buffer_range(p.seg[au.j] + 2 * t0, 2 * tile_bytes);
+            off[u] = (au.sub * kWave + uint32_t(lane)) * 32u;
             a[u] = ld_coherent(rs[u], off[u]);
             b[u] = ld_coherent(rs[u], off[u] + 16u);
-            dst[u] = p.out[ro] + size_t(j) * p.mvec + idx;
-            seg_of[u] = j;
-            tile_of[u] = t;
+            dst[u] = p.out[au.ro] + size_t(au.j) * p.mvec + au.idx;
+            seg_of[u] = au.j;
+            tile_of[u] = au.t;
         }
         __builtin_amdgcn_sched_barrier(0);  // every load ahead of the first use
         uint32_t fmin = 0xFFFFFFFFu;
