@@ -319,7 +319,7 @@ int ar_ll128_reduce_unpack(const void* const* wire, int n, void* out, size_t num
 
 int ar_twoshot_ll(const void* const* in, int n, void* const* segw, size_t numel, int dtype, int r0, int r1,
                   uint32_t* flags, uint32_t step, void* const* out, void* stream) {
-    if (!in || step == 0) return AR_ERR_ARG;  // the step id travels in the lines: explicit only
+    if (!in) return AR_ERR_ARG;  // step 0: auto ids, as ar_twoshot_rs
     const int st = twoshot_check(in, segw, out, n, numel, dtype, r0, r1, flags, step, 2);
     if (st != AR_OK) return st;
     TwoShotRequest rq{in, segw, out, n, numel, dtype, r0, r1, flags, step, true, out != nullptr,

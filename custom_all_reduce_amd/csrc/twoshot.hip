@@ -134,6 +134,11 @@ __device__ __forceinline__ bool reduce_scatter_phase(const TwoShotParams& p, con
 #pragma unroll
             for (int i = 0; i < NR; ++i) acc.add(x[u][i]);
             const u32x4 v = acc.result();
+            // LL lines carry the step id of the unit's rank (every lane
+            // active here: auto ids are read from lane r - r0)
+            uint32_t lstep = p.step;
+            if constexpr (kLL)
+                if (p.auto_step) lstep = __shfl(epoch_lane + 1u, int(dst_rank[u]) - p.r0);
             if (valid[u]) {
                 // the tile of seg[r] as one wavefront-uniform buffer range
                 const uint32_t t0 = dst_t0[u];
@@ -141,8 +146,8 @@ __device__ __forceinline__ bool reduce_scatter_phase(const TwoShotParams& p, con
                 if constexpr (kLL) {
                     // four LL lines: each 4 data bytes beside the step id
                     const __amdgpu_buffer_rsrc_t rs = buffer_range(p.seg[dst_rank[u]] + 2 * t0, 2 * tile_bytes);
-                    st_coherent(rs, (dst_idx[u] - t0) * 32u, u32x4{v.x, p.step, v.y, p.step});
-                    st_coherent(rs, (dst_idx[u] - t0) * 32u + 16u, u32x4{v.z, p.step, v.w, p.step});
+                    st_coherent(rs, (dst_idx[u] - t0) * 32u, u32x4{v.x, lstep, v.y, lstep});
+                    st_coherent(rs, (dst_idx[u] - t0) * 32u + 16u, u32x4{v.z, lstep, v.w, lstep});
                 } else {
                     st_coherent(buffer_range(p.seg[dst_rank[u]] + t0, tile_bytes), (dst_idx[u] - t0) * 16u, v);
                 }
@@ -290,9 +295,13 @@ __device__ __forceinline__ void all_gather_phase(const TwoShotParams& p, const u
 // loads; one ballot decides whether every flag of the wavefront's units has
 // reached the step.  If not, the lanes re-read the units that are behind
 // until they are there or the wall-clock budget runs out (reported: phase 1,
-// segment, tile).
-__device__ __forceinline__ void all_gather_ll_phase(const TwoShotParams& p, int n, uint32_t wave, uint32_t nwaves,
-                                                    int lane) {
+// segment, tile).  With auto step ids a unit waits for its output rank's
+// epoch + 1 (the id that rank's reduce-scatter of this launch writes); a
+// wavefront without reduce-scatter items loads its epoch copies with its
+// first unit's loads.
+__device__ __forceinline__ void all_gather_ll_phase(const TwoShotParams& p, const uint32_t* epoch,
+                                                    uint32_t& epoch_lane, bool& have_epoch, int n, uint32_t wave,
+                                                    uint32_t nwaves, int lane) {
     const uint32_t R = uint32_t(p.r1 - p.r0);
     const bool skip_own = p.do_rs != 0;
     const uint32_t per_out = uint32_t(skip_own ? n - 1 : n) * p.ktiles;
@@ -305,7 +314,7 @@ __device__ __forceinline__ void all_gather_ll_phase(const TwoShotParams& p, int 
         u32x4 a[kCopyUnroll], b[kCopyUnroll];
         u32x4* dst[kCopyUnroll];
         __amdgpu_buffer_rsrc_t rs[kCopyUnroll];
-        uint32_t off[kCopyUnroll], seg_of[kCopyUnroll], tile_of[kCopyUnroll];
+        uint32_t off[kCopyUnroll], seg_of[kCopyUnroll], tile_of[kCopyUnroll], out_of[kCopyUnroll];
         bool valid[kCopyUnroll];
 #pragma unroll
         for (int u = 0; u < kCopyUnroll; ++u) {
@@ -322,15 +331,22 @@ __device__ __forceinline__ void all_gather_ll_phase(const TwoShotParams& p, int 
             dst[u] = p.out[au.ro] + size_t(au.j) * p.mvec + au.idx;
             seg_of[u] = au.j;
             tile_of[u] = au.t;
+            out_of[u] = au.ro;
+        }
+        if (!have_epoch) {
+            if (uint32_t(lane) < R) epoch_lane = flag_load_relaxed(epoch + lane);
+            have_epoch = true;
         }
         __builtin_amdgcn_sched_barrier(0);  // every load ahead of the first use
-        uint32_t fmin = 0xFFFFFFFFu;
+        uint32_t want[kCopyUnroll];
+        bool behind = false;
 #pragma unroll
         for (int u = 0; u < kCopyUnroll; ++u) {
+            want[u] = p.auto_step ? __shfl(epoch_lane + 1u, int(out_of[u]) - p.r0) : p.step;
             const uint32_t f = min(min(a[u].y, a[u].w), min(b[u].y, b[u].w));
-            fmin = min(fmin, valid[u] ? f : 0xFFFFFFFFu);
+            behind |= valid[u] && f < want[u];
         }
-        if (wave_ballot(fmin < p.step) != 0) {
+        if (wave_ballot(behind) != 0) {
             const uint64_t t_start = now_ticks();
             while (true) {
                 bool good = true;
@@ -338,11 +354,11 @@ __device__ __forceinline__ void all_gather_ll_phase(const TwoShotParams& p, int 
 #pragma unroll
                 for (int u = 0; u < kCopyUnroll; ++u) {
                     const uint32_t f = min(min(a[u].y, a[u].w), min(b[u].y, b[u].w));
-                    if (valid[u] && f < p.step) {
+                    if (valid[u] && f < want[u]) {
                         a[u] = ld_coherent(rs[u], off[u]);
                         b[u] = ld_coherent(rs[u], off[u] + 16u);
                         const uint32_t g = min(min(a[u].y, a[u].w), min(b[u].y, b[u].w));
-                        if (g < p.step && good) { good = false; bad_j = seg_of[u]; bad_t = tile_of[u]; }
+                        if (g < want[u] && good) { good = false; bad_j = seg_of[u]; bad_t = tile_of[u]; }
                     }
                 }
                 const uint64_t missing = ~wave_ballot(good) & wave_exec();
@@ -386,7 +402,7 @@ __global__ __launch_bounds__(kBlock) void twoshot_kernel(TwoShotParams p) {
         // after the other in the same wavefronts.
         const uint32_t rs_busy = p.do_rs ? min(R * p.ktiles, nwaves) : 0u;
         const uint32_t ag_wave = wave >= rs_busy ? wave - rs_busy : wave + (nwaves - rs_busy);
-        if constexpr (kLL) all_gather_ll_phase(p, NR, ag_wave, nwaves, lane);
+        if constexpr (kLL) all_gather_ll_phase(p, epoch, epoch_lane, have_epoch, NR, ag_wave, nwaves, lane);
         else all_gather_phase(p, epoch, epoch_lane, have_epoch, p.do_rs ? 1u : 0u, NR, ag_wave, nwaves, lane);
     }
     if (p.auto_step && p.do_rs) {

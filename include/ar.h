@@ -282,11 +282,13 @@ int ar_ll_allreduce(const void* src, void* const* wire, int n, int me, void* out
  *          zeroed once before first use: a line counts as arrived when its
  *          flag is >= step, so a wire must never hold a flag at or above a
  *          step that has not written it yet.
- *  step  : 1..2^32-1, increasing from call to call (no auto ids: the flags
- *          are in the lines); step 0 is AR_ERR_ARG.
+ *  step  : 1..2^32-1, increasing from call to call; or 0 (auto), with the
+ *          epochs, fixed grid and rules of ar_twoshot_rs's auto ids: rank r's
+ *          lines carry its epoch + 1 and the all-gather waits for that.
  *  out   : NULL for the reduce-scatter only; else the fused launch as in
  *          ar_twoshot_rs (one persistent grid, out[r] for r in [r0, r1)).
- *  flags : flag region (only the status words are used).
+ *  flags : flag region of ar_flag_bytes(n) bytes (the status words; with
+ *          auto ids also the epochs).
  * The result is bit for bit that of ar_twoshot_rs and ar_oneshot.  Sizes,
  * divisibility and errors as ar_twoshot_rs; asynchronously AR_ERR_TIMEOUT
  * (phase AR_PHASE_TWOSHOT_AG, segment and tile of a line that stayed

@@ -217,7 +217,6 @@ def test_twoshot_ll_argument_errors():
     flags = A + (200 << 30)
     f = L.ar_twoshot_ll
     numel = 4 * 64  # 64 fp32 per segment: 256 data bytes, a 512-byte LL wire
-    assert f(ins, n, segw, numel, 0, 0, n, flags, 0, outs, NUL) == car.AR_ERR_ARG  # step 0: no auto ids
     assert f(None, n, segw, numel, 0, 0, n, flags, 1, outs, NUL) == car.AR_ERR_ARG
     assert f(ins, n, None, numel, 0, 0, n, flags, 1, outs, NUL) == car.AR_ERR_ARG
     assert f(ins, 1, segw, numel, 0, 0, 1, flags, 1, outs, NUL) == car.AR_ERR_ARG

@@ -168,3 +168,97 @@ def test_in_a_graph_with_increasing_steps():
         assert_ok(rk.flags)
         for r in range(n):
             assert np.array_equal(bits(rk.outs[r]), wants[rep % 2]), f"replay {rep} rank {r}"
+
+
+# ------------------------------------------------------------ auto step ids --
+def epochs(flags, n):
+    """Rank r's epoch, equal in every wavefront copy of an auto launch (two
+    4-wave workgroups per CU)."""
+    grid = 8 * torch.cuda.get_device_properties(0).multi_processor_count
+    base = 32 + n * car.AR_SLOTS_PER_RANK
+    w = flags[base:base + n * car.AR_EPOCH_COPIES].cpu().numpy().astype(np.int64).reshape(-1, n)
+    for r in range(n):
+        assert (w[:grid, r] == w[0, r]).all(), f"rank {r}: epoch copies differ"
+    return w[0, :].tolist()
+
+
+@pytest.mark.parametrize("n, dt, seg_vectors", [(8, "bf16", 1024), (5, "f32", 97), (16, "bf16", 64 * 1024)])
+def test_full_emulation_auto_steps_replayed_without_reset(n, dt, seg_vectors):
+    """Every rank in one auto launch, captured once, replayed with new data
+    and nothing reset: each replay matches the oracle, its lines carry the
+    new epoch, and every epoch advances by one."""
+    m = seg_vectors * (16 // ES[dt])
+    datasets = [synth.rank_inputs(n, n * m, dt, "normal", config=360 + k) for k in range(3)]
+    rk = Ranks(datasets[0], dt)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        car.ar_twoshot_ll(rk.ins, rk.segw, rk.flags, 0, outs=rk.outs)
+    torch.cuda.synchronize()
+    for rep in range(6):
+        host = datasets[rep % 3]
+        rk.load(host)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert_ok(rk.flags)
+        assert epochs(rk.flags, n) == [rep + 1] * n
+        check(rk, host, rep + 1, ranks=[0, n - 1])
+
+
+def test_one_rank_shares_auto_steps_in_a_graph():
+    """The peers' reduce-scatters and rank 0's fused share, all auto, in one
+    graph; eager auto calls between replays keep the epochs in step."""
+    n, dt, m = 8, "bf16", 8 * 4096
+    datasets = [synth.rank_inputs(n, n * m, dt, "normal", config=370 + k) for k in range(2)]
+    rk = Ranks(datasets[0], dt)
+    out0 = [rk.outs[0]] + [None] * (n - 1)
+
+    def one_step():
+        for r in range(1, n):
+            car.ar_twoshot_ll(rk.ins, rk.segw, rk.flags, 0, r0=r, r1=r + 1)
+        car.ar_twoshot_ll(rk.ins, rk.segw, rk.flags, 0, r0=0, r1=1, outs=out0)
+
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        one_step()
+    torch.cuda.synchronize()
+    for rep in range(6):
+        host = datasets[rep % 2]
+        rk.load(host)
+        if rep % 3 == 2:
+            one_step()  # the same calls, eager
+        else:
+            g.replay()
+        torch.cuda.synchronize()
+        assert_ok(rk.flags)
+        assert epochs(rk.flags, n) == [rep + 1] * n
+        check(rk, host, rep + 1, ranks=[0])
+
+
+def test_auto_steps_missing_peer_times_out():
+    """Step 1 completes; at step 2 rank 3 does not reduce: rank 0's share
+    reports (timeout, all-gather phase, segment 3) instead of copying rank
+    3's step-1 lines."""
+    n, dt, m = 8, "bf16", 8 * 4096
+    host = synth.rank_inputs(n, n * m, dt, "normal", config=380)
+    rk = Ranks(host, dt)
+    out0 = [rk.outs[0]] + [None] * (n - 1)
+    for r in range(1, n):
+        car.ar_twoshot_ll(rk.ins, rk.segw, rk.flags, 0, r0=r, r1=r + 1)
+    car.ar_twoshot_ll(rk.ins, rk.segw, rk.flags, 0, r0=0, r1=1, outs=out0)
+    torch.cuda.synchronize()
+    assert_ok(rk.flags)
+    for r in range(1, n):
+        if r != 3:
+            car.ar_twoshot_ll(rk.ins, rk.segw, rk.flags, 0, r0=r, r1=r + 1)
+    old = car.get_poll_timeout_ns()
+    car.set_poll_timeout_ns(2_000_000)
+    try:
+        car.ar_twoshot_ll(rk.ins, rk.segw, rk.flags, 0, r0=0, r1=1, outs=out0)
+        torch.cuda.synchronize()
+    finally:
+        car.set_poll_timeout_ns(old)
+    code, phase, seg = car.decode_status(car.read_status(rk.flags)[0])
+    assert (code, phase, seg) == (car.AR_ERR_TIMEOUT, car.PHASE_TWOSHOT_AG, 3)
