@@ -17,6 +17,14 @@
 // SIMDs.  Measured (n = 8 / 16): 16-byte lanes 2.75 us at 128 KiB, 8-byte
 // lanes 2.60, 4-byte lanes 2.52 / 2.71 (8-byte: 2.63 / 2.96); from 1 MiB on
 // 8-byte lanes are the fastest (13.8 us at 8 MiB against 14.6 and 14.1).
+//
+// Why one vector per lane and a workgroup per 64 vectors, not more work per
+// wave: two or four consecutive 64-vector units per wave (all loads first)
+// measured 14.7 / 15.2 us at n = 8, 8 MiB bf16 against 13.5; a persistent
+// grid of 1024-8192 one-wave workgroups that loads the next unit while it
+// sums the current one measured 13.6-16.3 us at 8 MiB and 100-113 us at
+// 64 MiB against 95 us.  Letting the dispatcher refill finished waves keeps
+// more loads in flight than either.
 #include "ar_device.hpp"
 #include "ar_launch.hpp"
 
