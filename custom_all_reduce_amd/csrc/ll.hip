@@ -132,12 +132,14 @@ struct ReduceParams {
     uint8_t* own_wire;
 };
 
-// Bounded wait for the lines [2c, 2c + nl) of every rank (nl = 1 or 2), re-read
-// with agent-coherent atomic 64-bit loads into x (data in .x/.z, flags in
-// .y/.w).  Lanes with nl == 0 just take part in the ballots.  Returns false
-// on timeout (reported).
+// Bounded wait for the lines [2c, 2c + nl) of every rank (nl = 1 or 2) to
+// reach step ids s0 (line 2c) and s1 (line 2c + 1), re-read with
+// agent-coherent atomic 64-bit loads into x (data in .x/.z, flags in .y/.w).
+// Lanes with nl == 0 just take part in the ballots.  Returns false on
+// timeout (reported).
 template <int NR>
-__device__ bool ll_slow_wait(const ReduceParams& p, size_t c, uint32_t nl, u32x4 (&x)[NR], int lane) {
+__device__ bool ll_slow_wait(const ReduceParams& p, size_t c, uint32_t nl, u32x4 (&x)[NR], int lane, uint32_t s0,
+                             uint32_t s1) {
     const uint64_t t0 = now_ticks();
     while (true) {
         bool ok = true;
@@ -146,17 +148,17 @@ __device__ bool ll_slow_wait(const ReduceParams& p, size_t c, uint32_t nl, u32x4
 #pragma unroll
         for (int r = 0; r < NR; ++r) {
             const uint64_t* w = reinterpret_cast<const uint64_t*>(p.wire[r]) + 2 * c;
-            if (nl > 0 && x[r].y < p.step) {
+            if (nl > 0 && x[r].y < s0) {
                 const uint64_t a = line_load_relaxed(w);
                 x[r].x = uint32_t(a);
                 x[r].y = uint32_t(a >> 32);
-                if (x[r].y < p.step && ok) { ok = false; bad_r = r; bad_l = 0; }
+                if (x[r].y < s0 && ok) { ok = false; bad_r = r; bad_l = 0; }
             }
-            if (nl > 1 && x[r].w < p.step) {
+            if (nl > 1 && x[r].w < s1) {
                 const uint64_t b = line_load_relaxed(w + 1);
                 x[r].z = uint32_t(b);
                 x[r].w = uint32_t(b >> 32);
-                if (x[r].w < p.step && ok) { ok = false; bad_r = r; bad_l = 1; }
+                if (x[r].w < s1 && ok) { ok = false; bad_r = r; bad_l = 1; }
             }
         }
         const uint64_t missing = ~wave_ballot(ok) & wave_exec();
@@ -185,23 +187,61 @@ __device__ __forceinline__ void store_out_bytes(uint8_t* out, size_t off, size_t
 // main path is branch-free: lanes past the last two-line chunk load a valid
 // clamped chunk and discard it, so all U * n loads issue back to back.  A
 // final single line (odd line count) is finished by one lane on its own.
-template <typename T, int NR, int U>
+//
+// kFused (one chunk per lane): rank me's term is bytes [8c, 8c+8) of its
+// message, loaded with the peers' lines by every wavefront whose 64 chunks
+// all exist and word by word in the last one (a lone bf16 in the chunk's
+// second line is zero-extended); lines 2c and 2c+1 of rank me's wire are
+// written from it, each with its step id, before the wavefront waits on any
+// peer, or last when nothing has to be waited for.  The odd last line is
+// sent the same way by its lane.
+template <typename T, int NR, int U, bool kFused>
 __global__ __launch_bounds__(kBlockLL) void ll_reduce_kernel(ReduceParams p) {
+    static_assert(!kFused || U == 1, "send and receive take one chunk per lane");
     const int lane = threadIdx.x & (kWave - 1);
     const size_t nfull = p.nlines / 2;  // chunks that hold two lines
     const size_t c0 = size_t(blockIdx.x) * (kBlockLL * U) + threadIdx.x;
     const u32x4* w[NR];
 #pragma unroll
     for (int r = 0; r < NR; ++r) w[r] = reinterpret_cast<const u32x4*>(p.wire[r]);
+    // A last chunk with a single line (odd line count): chunk nfull, finished
+    // by the one lane of the grid that owns that chunk index.
+    const size_t rel = nfull - size_t(blockIdx.x) * (kBlockLL * U);
+    const bool odd_owner = (p.nlines & 1) && nfull >= size_t(blockIdx.x) * (kBlockLL * U) &&
+                           rel < size_t(kBlockLL) * U && rel % kBlockLL == threadIdx.x;
+    // kFused: that lane sends rank me's last line (message bytes
+    // [8 nfull, nbytes), 2 or 4) first, before its wavefront waits on anything
+    uint32_t odd_own = 0u, odd_step = p.step;
+    if constexpr (kFused) {
+        if (odd_owner) {
+            odd_own = 8 * nfull + 4 <= p.nbytes ? reinterpret_cast<const uint32_t*>(p.src)[2 * nfull]
+                                                : uint32_t(reinterpret_cast<const uint16_t*>(p.src)[4 * nfull]);
+            u32x2* ln = reinterpret_cast<u32x2*>(p.own_wire) + 2 * nfull;
+            if (p.step == 0) odd_step = ln->y + 1u;
+            *ln = u32x2{odd_own, odd_step};
+        }
+    }
 
     if (nfull > 0) {
         u32x4 x[U][NR];
         bool act[U];
+        // kFused: rank me's 8 message bytes and (auto step ids, step 0) its
+        // two lines as the last call left them
+        const bool own_whole = kFused && (size_t(blockIdx.x) + 1) * kBlockLL * 8 <= p.nbytes;  // wavefront-uniform
+        u32x2 own = u32x2{0u, 0u};
+        u32x4 own_old = u32x4{0u, 0u, 0u, 0u};
+        if constexpr (kFused) {
+            const size_t cc = c0 < nfull ? c0 : nfull - 1;
+            if (own_whole) own = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p.src) + c0);
+            if (p.step == 0) own_old = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p.own_wire) + cc);
+        }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const size_t c = c0 + size_t(u) * kBlockLL;
             act[u] = c < nfull;
             const size_t cc = act[u] ? c : nfull - 1;
+            // kFused: rank me's slot too (it holds a peer's wire; the term is
+            // replaced below) -- skipping it, the compiler waited between loads
 #pragma unroll
             for (int r = 0; r < NR; ++r) x[u][r] = ld_stream(w[r] + cc);
         }
@@ -209,20 +249,50 @@ __global__ __launch_bounds__(kBlockLL) void ll_reduce_kernel(ReduceParams p) {
         // sometimes hoists a flag compare between the loads, and the wait it
         // needs then serialises two memory round trips.
         __builtin_amdgcn_sched_barrier(0);
+        // the step ids of lines 2c and 2c+1: the call's, or (auto) one past
+        // the last flag of each of rank me's two lines
+        uint32_t s0 = p.step, s1 = p.step;
+        bool own_late = false;
+        if constexpr (kFused) {
+            if (!own_whole && act[0]) {
+                // the last wavefront: line 2c is whole (the chunk has two
+                // lines); line 2c+1 may hold a lone bf16
+                own.x = reinterpret_cast<const uint32_t*>(p.src)[2 * c0];
+                own.y = 8 * c0 + 8 <= p.nbytes ? reinterpret_cast<const uint32_t*>(p.src)[2 * c0 + 1]
+                                               : uint32_t(reinterpret_cast<const uint16_t*>(p.src)[4 * c0 + 2]);
+            }
+            if (p.step == 0) { s0 = own_old.y + 1u; s1 = own_old.w + 1u; }
+            // rank me's lines carry their step ids: the readiness checks pass them
+#pragma unroll
+            for (int r = 0; r < NR; ++r)
+                if (r == p.me) x[0][r] = u32x4{own.x, s0, own.y, s1};
+        }
         // Readiness without short-circuit branches: the smallest flag a lane
         // holds, folded with min as the loads land.
         bool ok = true;
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            uint32_t fmin = 0xFFFFFFFFu;
+            if constexpr (kFused) {
+                uint32_t f0 = 0xFFFFFFFFu, f1 = 0xFFFFFFFFu;
 #pragma unroll
-            for (int r = 0; r < NR; ++r) fmin = min(fmin, min(x[u][r].y, x[u][r].w));
-            ok &= !act[u] | (fmin >= p.step);
+                for (int r = 0; r < NR; ++r) { f0 = min(f0, x[u][r].y); f1 = min(f1, x[u][r].w); }
+                ok &= !act[u] | ((f0 >= s0) & (f1 >= s1));
+            } else {
+                uint32_t fmin = 0xFFFFFFFFu;
+#pragma unroll
+                for (int r = 0; r < NR; ++r) fmin = min(fmin, min(x[u][r].y, x[u][r].w));
+                ok &= !act[u] | (fmin >= p.step);
+            }
         }
         if (wave_ballot(!ok) != 0) {
+            // kFused: rank me's lines go out before any wait on a peer
+            if (kFused && act[0]) st_stream(reinterpret_cast<u32x4*>(p.own_wire) + c0, u32x4{own.x, s0, own.y, s1});
 #pragma unroll
             for (int u = 0; u < U; ++u)
-                if (!ll_slow_wait<NR>(p, c0 + size_t(u) * kBlockLL, act[u] ? 2u : 0u, x[u], lane)) return;
+                if (!ll_slow_wait<NR>(p, c0 + size_t(u) * kBlockLL, act[u] ? 2u : 0u, x[u], lane, s0, s1)) return;
+            if constexpr (kFused) wait_stores();  // nothing of this path left to wait for where the paths join
+        } else if (kFused && act[0]) {
+            own_late = true;
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
@@ -240,21 +310,24 @@ __global__ __launch_bounds__(kBlockLL) void ll_reduce_kernel(ReduceParams p) {
                 }
             }
         }
+        if (kFused && own_late) st_stream(reinterpret_cast<u32x4*>(p.own_wire) + c0, u32x4{own.x, s0, own.y, s1});
     }
-    // A last chunk with a single line (odd line count): chunk nfull, finished
-    // by the one lane of the grid that owns that chunk index.
-    const size_t rel = nfull - size_t(blockIdx.x) * (kBlockLL * U);
-    if ((p.nlines & 1) && nfull >= size_t(blockIdx.x) * (kBlockLL * U) && rel < size_t(kBlockLL) * U &&
-        rel % kBlockLL == threadIdx.x) {
+    if (odd_owner) {
         u32x4 x[NR];
+        const uint32_t step = odd_step;
 #pragma unroll
         for (int r = 0; r < NR; ++r) {
             const u32x2 a = reinterpret_cast<const u32x2*>(p.wire[r])[2 * nfull];
             x[r] = u32x4{a.x, a.y, 0u, 0xFFFFFFFFu};
         }
+        if constexpr (kFused) {
+#pragma unroll
+            for (int r = 0; r < NR; ++r)
+                if (r == p.me) x[r] = u32x4{odd_own, step, 0u, 0xFFFFFFFFu};
+        }
         bool ok = true;
 #pragma unroll
-        for (int r = 0; r < NR; ++r) ok = ok && x[r].y >= p.step;
+        for (int r = 0; r < NR; ++r) ok = ok && x[r].y >= step;
         if (!ok) {
             // single lane: poll alone (its own wave's ballot sees only it)
             const uint64_t t0 = now_ticks();
@@ -263,12 +336,12 @@ __global__ __launch_bounds__(kBlockLL) void ll_reduce_kernel(ReduceParams p) {
                 int bad_r = 0;
 #pragma unroll
                 for (int r = 0; r < NR; ++r) {
-                    if (x[r].y < p.step) {
+                    if (x[r].y < step) {
                         const uint64_t a =
                             line_load_relaxed(reinterpret_cast<const uint64_t*>(p.wire[r]) + 2 * nfull);
                         x[r].x = uint32_t(a);
                         x[r].y = uint32_t(a >> 32);
-                        if (x[r].y < p.step && ok) { ok = false; bad_r = r; }
+                        if (x[r].y < step && ok) { ok = false; bad_r = r; }
                     }
                 }
                 if (!ok && now_ticks() - t0 > p.timeout_ticks) {
@@ -581,7 +654,7 @@ hipError_t launch_reduce_t(const ReduceParams& p, int proto, hipStream_t s) {
         constexpr int U = 1;
         const size_t chunks = (p.nlines + 1) / 2;
         const size_t grid = (chunks + kBlockLL * U - 1) / (kBlockLL * U);
-        hipLaunchKernelGGL((ll_reduce_kernel<T, NR, U>), dim3(uint32_t(grid)), dim3(kBlockLL), 0, s, p);
+        hipLaunchKernelGGL((ll_reduce_kernel<T, NR, U, false>), dim3(uint32_t(grid)), dim3(kBlockLL), 0, s, p);
     } else {
         // One 8-line unit per wavefront: measured faster than two for every
         // size, and the two-unit fp32 instantiation stalls badly.
@@ -594,11 +667,15 @@ hipError_t launch_reduce_t(const ReduceParams& p, int proto, hipStream_t s) {
     return hipGetLastError();
 }
 
-// Send and receive in one launch.  LL takes the one-line receiver at every
-// size (the two-line one is 6% faster only above 16 MiB per rank).
+// Send and receive in one launch, LL with the receivers' line split: one
+// line per lane up to 16 MiB per rank, two above.
 template <typename T, int NR>
 hipError_t launch_fused_t(const ReduceParams& p, int proto, hipStream_t s) {
-    if (proto == 0) {
+    if (proto == 0 && p.nbytes > kOneLineMaxBytes) {
+        const size_t chunks = (p.nlines + 1) / 2;
+        const size_t grid = (chunks + kBlockLL - 1) / kBlockLL;
+        hipLaunchKernelGGL((ll_reduce_kernel<T, NR, 1, true>), dim3(uint32_t(grid)), dim3(kBlockLL), 0, s, p);
+    } else if (proto == 0) {
         const size_t grid = (p.nlines + kBlockLL - 1) / kBlockLL;
         hipLaunchKernelGGL((ll_reduce1_kernel<T, NR, true>), dim3(uint32_t(grid)), dim3(kBlockLL), 0, s, p);
     } else {

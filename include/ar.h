@@ -264,7 +264,8 @@ int ar_ll128_reduce_unpack(const void* const* wire, int n, void* out, size_t num
  *          reset the status words) before the next auto call.
  *  flags : flag region (only the status words are used).
  * out, src and wire[me] may not overlap one another or any wire buffer;
- * all pointers 16-byte aligned.  LL uses one line per lane at every size.
+ * all pointers 16-byte aligned.  LL takes one line per lane up to 16 MiB
+ * per rank and two above, as ar_ll_reduce_unpack does.
  * Errors: AR_ERR_ARG, AR_ERR_ALIGN, AR_ERR_ALIAS, AR_ERR_HIP; asynchronously
  * AR_ERR_TIMEOUT (phase AR_PHASE_LL or AR_PHASE_LL128, rank and line of a
  * missing line). */

@@ -279,14 +279,70 @@ def test_allreduce_stale_peer_times_out_after_packing(proto, phase):
     assert np.array_equal(bits(bufs[me])[:W], oracle.ll_pack(proto, host[me], 11))
 
 
-@pytest.mark.parametrize("dt, numel", [("f32", ONE_LINE_MAX // 4 + 3), ("bf16", ONE_LINE_MAX // 2 + 5)])
-def test_allreduce_ll_above_16MiB(dt, numel):
-    """The send-and-receive LL launch uses one line per lane at every size."""
-    host, bufs, W, flags, outbuf, out = allreduce_case("ll", dt, 2, 1, numel, 5, 170)
+# Above 16 MiB per rank the send-and-receive LL launch takes two lines per
+# lane.  Tails: f32 + 3 and bf16 + 5 leave an odd last line (4 and 2 bytes),
+# finished by one lane; bf16 + 3 leaves an even line count whose last chunk
+# ends in a lone bf16.
+@pytest.mark.parametrize("dt, numel, n, me", [("f32", ONE_LINE_MAX // 4, 2, 0), ("f32", ONE_LINE_MAX // 4 + 3, 2, 1),
+                                              ("bf16", ONE_LINE_MAX // 2 + 5, 2, 1), ("bf16", ONE_LINE_MAX // 2 + 3, 3, 1),
+                                              ("f32", ONE_LINE_MAX // 4 + 3, 3, 2)])
+def test_allreduce_ll_either_side_of_the_kernel_switch(dt, numel, n, me):
+    host, bufs, W, flags, outbuf, out = allreduce_case("ll", dt, n, me, numel, 5, 170 + n)
     assert car.read_status(flags)[0] == 0
     got, want = bits(out), oracle_bits(oracle.oneshot(host, dt))
     assert np.array_equal(got, want), first_mismatch(got, want)
-    assert np.array_equal(bits(bufs[1])[:W], oracle.ll_pack("ll", host[1], 5))
+    assert np.array_equal(bits(outbuf[numel:]), bits(filled(64, DT[dt]))), "wrote past the output"
+    wire = bits(bufs[me])
+    assert np.array_equal(wire[:W], oracle.ll_pack("ll", host[me], 5)), "own wire"
+    assert np.all(wire[W:] == 0xA5), "wrote past rank me's wire"
+
+
+@pytest.mark.parametrize("dt, numel", [("f32", ONE_LINE_MAX // 4 + 3), ("bf16", ONE_LINE_MAX // 2 + 3)])
+def test_allreduce_ll_above_16MiB_auto_steps(dt, numel):
+    """Step 0 above the switch: three rounds of the peer's auto pack and rank
+    0's auto send-and-receive from zeroed wires, new data each round; every
+    output matches the oracle and rank 0's wire is its packing at step 3."""
+    n, me = 2, 0
+    rounds = [synth.rank_inputs(n, numel, dt, "normal", config=175 + k) for k in range(3)]
+    bufs, W = wires_for(n, numel, dt, "ll")
+    for b in bufs:
+        b[:W].zero_()
+    wires = [b[:W] for b in bufs]
+    flags = car.new_flags(n)
+    out = torch.empty(numel, dtype=DT[dt], device="cuda")
+    for k, host in enumerate(rounds):
+        srcs = [to_dev(a) for a in host]
+        car.ar_ll_pack([srcs[1]], [wires[1]], "ll", 0)
+        car.ar_ll_allreduce(srcs[me], wires, out, flags, "ll", me, 0)
+        torch.cuda.synchronize()
+        assert car.read_status(flags)[0] == 0, f"round {k}"
+        got, want = bits(out), oracle_bits(oracle.oneshot(host, dt))
+        assert np.array_equal(got, want), f"round {k}: " + first_mismatch(got, want)
+    assert np.array_equal(bits(bufs[me])[:W], oracle.ll_pack("ll", rounds[-1][me], 3))
+
+
+def test_allreduce_ll_above_16MiB_stale_peer_times_out_after_packing():
+    """Two lines per lane: rank 1 packed the previous step; rank 0's launch
+    still writes its wire for step s (odd last line included), then reports
+    (timeout, LL, rank 1)."""
+    n, numel, dt, me = 2, ONE_LINE_MAX // 4 + 3, "f32", 0
+    host = synth.rank_inputs(n, numel, dt, "normal", config=179)
+    srcs = [to_dev(a) for a in host]
+    bufs, W = wires_for(n, numel, dt, "ll")
+    wires = [b[:W] for b in bufs]
+    flags = car.new_flags(n)
+    car.ar_ll_pack([srcs[1]], [wires[1]], "ll", step=30)
+    out = torch.empty(numel, device="cuda")
+    old = car.get_poll_timeout_ns()
+    car.set_poll_timeout_ns(20_000)
+    try:
+        car.ar_ll_allreduce(srcs[me], wires, out, flags, "ll", me, 31)
+        torch.cuda.synchronize()
+    finally:
+        car.set_poll_timeout_ns(old)
+    code, ph, rank = car.decode_status(car.read_status(flags)[0])
+    assert (code, ph, rank) == (car.AR_ERR_TIMEOUT, car.PHASE_LL, 1)
+    assert np.array_equal(bits(bufs[me])[:W], oracle.ll_pack("ll", host[me], 31))
 
 
 # ------------------------------------------------------------ auto step ids --
