@@ -250,6 +250,10 @@ int ar_ll128_reduce_unpack(const void* const* wire, int n, void* out, size_t num
  *  - wait for every line of every other rank's wire[r] to carry a flag >=
  *    step and reduce the n messages into out exactly as ar_oneshot, rank
  *    me's term taken from src (wire[me] is written, not read back).
+ *  Each wavefront writes its lines of wire[me] before it waits on any peer
+ *  line, so no rank's launch waits on a line that a peer's launch holds back
+ *  behind a wait of its own, and after a timeout wire[me] still holds the
+ *  whole packed message.
  *  wire  : n wire buffers of ar_ll_wire_bytes(proto, numel * elem) bytes, in
  *          rank order; wire[me] is rank me's own (written), the others are
  *          read.  Zeroed once before first use: a line counts as arrived
