@@ -409,6 +409,39 @@ def test_allreduce_auto_steps_replayed_in_a_graph(proto, dt, numel):
             assert np.array_equal(w, oracle.ll_pack(proto, datasets[k][r], rep + 1)), f"replay {rep}: wire {r}"
 
 
+def test_allreduce_ll_two_lines_auto_steps_replayed_in_a_graph():
+    """As above with LL above 16 MiB per rank (two lines per lane, odd last
+    line): the peers' auto packs and rank 1's auto send-and-receive captured
+    once, replayed three times with new data and nothing reset."""
+    n, me, dt, numel = 4, 1, "f32", ONE_LINE_MAX // 4 + 3
+    datasets = [synth.rank_inputs(n, numel, dt, "normal", config=197 + k) for k in range(3)]
+    wants = [oracle_bits(oracle.oneshot(h, dt)) for h in datasets]
+    srcs = [to_dev(a) for a in datasets[0]]
+    bufs, W = zeroed_wires(n, numel, dt, "ll")
+    wires = [b[:W] for b in bufs]
+    flags = car.new_flags(n)
+    out = torch.empty(numel, dtype=DT[dt], device="cuda")
+    peers = [r for r in range(n) if r != me]
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        car.ar_ll_pack([srcs[r] for r in peers], [wires[r] for r in peers], "ll", 0)
+        car.ar_ll_allreduce(srcs[me], wires, out, flags, "ll", me, 0)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for d, a in zip(srcs, datasets[rep]):  # eager work between replays
+            d.copy_(to_dev(a))
+        out.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert car.read_status(flags)[0] == 0, f"replay {rep}"
+        got = bits(out)
+        assert np.array_equal(got, wants[rep]), f"replay {rep}: " + first_mismatch(got, wants[rep])
+        w = bits(bufs[me])[:W]
+        assert np.array_equal(w, oracle.ll_pack("ll", datasets[rep][me], rep + 1)), f"replay {rep}: own wire"
+
+
 @pytest.mark.parametrize("proto, phase", [("ll", 2), ("ll128", 3)])
 def test_allreduce_auto_steps_peer_left_behind_times_out(proto, phase):
     """Two auto steps for every rank, then a third where rank 6 does not
