@@ -5,12 +5,13 @@ allocations on that GPU: every read of a rank buffer, segment or wire buffer
 and every write, each byte once.  S = numel * element size (bytes per rank).
 
   oneshot                 reads n*S               writes S
-  twoshot, one rank       reads S (RS) + (n-1)*S/n (AG of the peers' segments)
+  twoshot, one rank       reads S (RS: segment r of n inputs) + S (AG: all n segments)
                           writes S/n (segment) + S (output)
   twoshot, all n ranks    n times the above
   twoshot RS only / AG only, per rank: reads S / S, writes S/n / S
-  twoshot under LL, one   reads S (RS) + (n-1)*2S/n (the peers' LL segment wires)
+  twoshot under LL, one   reads S (RS) + n*2S/n (AG: all n LL segment wires)
     rank                  writes 2S/n (its segment wire) + S (output)
+  twoshot under LL128     as under LL with LL128 segment wires W(S/n)
   reduce_bcast, one rank  reads S (its 1/n of n inputs)   writes S (1/n into n outputs)
   reduce_bcast, all n     reads n*S               writes n*S
   push, one sender        reads S                 writes ndst*S
@@ -19,9 +20,11 @@ and every write, each byte once.  S = numel * element size (bytes per rank).
   LL / LL128 send and     reads S (own message) + (n-1)*W(S) (the peers' wires)
     receive, one launch   writes W(S) (own wire) + S
 
-In the fused two-shot the reduce-scatter writes rank r's own segment of its
-output straight from registers, so the all-gather reads only the other n-1
-segments.  W(S) = 8*ceil(S/4) for LL (4 data bytes per 8-byte line) and
+The fused two-shot kernel writes rank r's own segment of its output straight
+from the reduce-scatter's registers and never reads it back, so it moves
+S/n (S/n wire bytes under LL) fewer reads per rank than the method's count;
+twoshot_kernel() gives that kernel count, which is reported beside the
+algorithmic one but never used for a rate.  W(S) = 8*ceil(S/4) for LL (4 data bytes per 8-byte line) and
 128*ceil(S/120) for LL128 (120 data bytes per 128-byte line) -- the line
 formats of the protocol table on "集合通信：NCCL 的算法、协议与推理框架的定制
 all-reduce".  The flag region (a few KiB) is left out.
@@ -45,13 +48,19 @@ def oneshot(n: int, S: int):
 
 def twoshot(n: int, S: int, ranks: int):
     """Fused two-shot; ranks = how many emulated ranks the launch computes (1 or n)."""
+    return ranks * 2 * S, ranks * (S // n) + ranks * S
+
+
+def twoshot_kernel(n: int, S: int, ranks: int):
+    """What the fused two-shot kernel itself moves: the all-gather does not
+    read back the rank's own segment (it is stored from registers)."""
     return ranks * (S + (n - 1) * (S // n)), ranks * (S // n) + ranks * S
 
 
-def twoshot_ll(n: int, S: int, ranks: int):
-    """Fused two-shot with LL segment wires (2 bytes of wire per data byte)."""
-    m = S // n
-    return ranks * (S + (n - 1) * 2 * m), ranks * (2 * m + S)
+def twoshot_ll(n: int, S: int, ranks: int, proto: str = "ll"):
+    """Fused two-shot with LL (or LL128) segment wires."""
+    w = wire_bytes(proto, S // n)
+    return ranks * (S + n * w), ranks * (w + S)
 
 
 def twoshot_rs(n: int, S: int, ranks: int):

@@ -19,7 +19,10 @@ Parity status of each function:
   ll_pack / ll_unpack (O5, O6)     pinned: round trip, sizes, flag positions, efficiencies
   ll_reduce (O7)                   pinned: equals O2 of payloads; stale flag -> timeout
   FlagBarrier (O8)                 pinned: steps 1..1000, withheld flag, reset
-  model.* (O9)                     pinned: the printed alpha-beta table and exercises
+  model.* (O9)                     pinned: the printed alpha-beta table and exercises;
+                                   hbm_bytes by a byte-counting walk of each operation's
+                                   steps, the stated configuration values, and the pages'
+                                   remote byte counts
 """
 from __future__ import annotations
 

@@ -102,31 +102,43 @@ def ll_wire_bytes(proto, S):
 
 
 def hbm_bytes(op, S, n, proto=None):
-    """HBM bytes (reads, writes) one GPU's kernel must move when the n ranks'
-    buffers are n allocations on that GPU (local reads and all writes count).
+    """HBM bytes (reads, writes) the method moves on one GPU when the n ranks'
+    buffers are n allocations on that GPU: every read of a rank buffer,
+    segment or wire buffer and every write, each byte once.
 
-    Two-shot, one rank's share: the reduce-scatter reads segment r of all n
-    inputs (S bytes) and writes the reduced segment (S/n); the all-gather
-    fills the output (S) -- rank r's own segment straight from the reduce,
-    the other n-1 segments read from the peers (S (n-1)/n).  All n ranks: n
-    times that.  Under LL a segment of S/n bytes travels as an LL wire of
-    twice its size."""
+    Written from the steps of each operation, not from any kernel:
+    one-shot -- read every rank's message, write the sum (算法, one-shot).
+    Two-shot, one rank's share -- the reduce-scatter reads segment r of all
+    n messages (S bytes) and writes the reduced segment (S/n); the
+    all-gather reads all n reduced segments (S) and writes the output (S)
+    (算法, two-shot: reduce-scatter then all-gather; "多 GPU 与 NCCL", 集合通信).
+    All n ranks: n times that.  LL / LL128 -- the sender reads its message
+    and writes its wire; the receiver reads n wires and writes the sum
+    (协议 table: 4 data bytes per 8-byte line, 120 per 128-byte line).  The
+    two-shot under LL carries each segment as an LL wire of twice its bytes.
+    A kernel may move fewer bytes than this (the fused two-shot writes its
+    own segment of the output from registers and never reads it back); that
+    saving is the kernel's, not the method's, and is not counted here."""
     if op == "oneshot":
         return n * S, S
     if op == "twoshot_share":
-        return S + (n - 1) * S // n, S // n + S
+        return 2 * S, S // n + S
     if op == "twoshot_full":
-        return n * S + (n - 1) * S, S + n * S
+        return 2 * n * S, (n + 1) * S
     if op == "ll_pack":
         return S, ll_wire_bytes(proto, S)
     if op == "ll_reduce":
         return n * ll_wire_bytes(proto, S), S
     if op == "ll_allreduce":
-        # one rank's step in one launch: its message read and its wire written,
-        # the n-1 peers' wires read, the output written
+        # one rank's step: its message read and its wire written (the pack),
+        # the n-1 peers' wires read and the sum written (the receiver; its own
+        # term is its message, already read)
         return S + (n - 1) * ll_wire_bytes(proto, S), ll_wire_bytes(proto, S) + S
     if op == "twoshot_ll_share":
         # as twoshot_share, with every segment an LL wire of its S/n bytes
         w = ll_wire_bytes("ll", S // n)
-        return S + (n - 1) * w, w + S
+        return S + n * w, w + S
+    if op == "twoshot_ll128_share":
+        w = ll_wire_bytes("ll128", S // n)
+        return S + n * w, w + S
     raise ValueError(op)

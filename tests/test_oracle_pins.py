@@ -384,3 +384,125 @@ def test_remote_byte_counts():
     assert model.remote_bytes_per_rank("one-shot", S, 8) == 7 * S
     assert model.remote_bytes_per_rank("two-shot", S, 8) == 2 * 7 / 8 * S
     assert model.busbw(S, 1.0, 8) == S * 2 * 7 / 8
+
+
+# ------------------------------------------------------ O9: HBM byte model --
+class _Counted:
+    """A buffer that counts the bytes read from and written to it."""
+
+    def __init__(self, nbytes):
+        self.nbytes, self.r, self.w = nbytes, 0, 0
+
+    def read(self, lo, hi):
+        assert 0 <= lo <= hi <= self.nbytes
+        self.r += hi - lo
+
+    def write(self, lo, hi):
+        assert 0 <= lo <= hi <= self.nbytes
+        self.w += hi - lo
+
+
+def _brute_bytes(op, S, n, proto=None, es=2):
+    """Walk each operation element by element (line by line for the wires),
+    as its steps are written, touching counted buffers; return the totals.
+    Independent of model.hbm_bytes: no formula, only the steps."""
+    N, m = S // es, S // es // n
+    ins = [_Counted(S) for _ in range(n)]
+    bufs = list(ins)
+
+    def new(nb):
+        b = _Counted(nb)
+        bufs.append(b)
+        return b
+
+    def lines(nbytes, proto):
+        data, line = (4, 8) if proto == "ll" else (120, 128)
+        return [(k * data, min((k + 1) * data, nbytes), k * line, (k + 1) * line)
+                for k in range((nbytes + data - 1) // data)]
+
+    if op == "oneshot":
+        out = new(S)
+        for k in range(N):
+            for i in range(n):
+                ins[i].read(k * es, (k + 1) * es)
+            out.write(k * es, (k + 1) * es)
+    elif op in ("twoshot_share", "twoshot_full"):
+        segs = [new(m * es) for _ in range(n)]
+        ranks = range(n) if op == "twoshot_full" else [n // 2]
+        for r in ranks:  # reduce-scatter: segment r of every rank's message
+            for k in range(m):
+                for i in range(n):
+                    ins[i].read((r * m + k) * es, (r * m + k + 1) * es)
+                segs[r].write(k * es, (k + 1) * es)
+        if op == "twoshot_share":  # the peers' segments: other GPUs' work
+            for j in range(n):
+                if j != n // 2:
+                    segs[j].w += m * es
+        for r in ranks:  # all-gather: every segment into rank r's output
+            out = new(S)
+            for j in range(n):
+                for k in range(m):
+                    segs[j].read(k * es, (k + 1) * es)
+                    out.write((j * m + k) * es, (j * m + k + 1) * es)
+        if op == "twoshot_share":
+            for j in range(n):
+                if j != n // 2:
+                    segs[j].w -= m * es
+    elif op in ("ll_reduce", "ll_pack"):
+        L = lines(S, proto)
+        W = L[-1][3]
+        if op == "ll_pack":
+            w = new(W)
+            for d0, d1, l0, l1 in L:
+                ins[0].read(d0, d1)
+                w.write(l0, l1)
+            for b in ins[1:]:
+                b.r = b.w = 0
+        else:
+            wires = [new(W) for _ in range(n)]
+            out = new(S)
+            for d0, d1, l0, l1 in L:
+                for w in wires:
+                    w.read(l0, l1)
+                out.write(d0, d1)
+    else:
+        raise ValueError(op)
+    return sum(b.r for b in bufs), sum(b.w for b in bufs)
+
+
+@pytest.mark.parametrize("n", [2, 3, 8])
+@pytest.mark.parametrize("S", [96, 240, 1920])
+def test_hbm_bytes_by_brute_force(n, S):
+    """model.hbm_bytes against a step-by-step walk of each operation that
+    counts every byte read and written (S divisible by n and by 2 bytes)."""
+    if S % (2 * n):
+        pytest.skip("two-shot needs whole bf16 segments")
+    for op in ("oneshot", "twoshot_share", "twoshot_full"):
+        assert model.hbm_bytes(op, S, n) == _brute_bytes(op, S, n), op
+    for proto in ("ll", "ll128"):
+        assert model.hbm_bytes("ll_pack", S, n, proto) == _brute_bytes("ll_pack", S, n, proto), proto
+        assert model.hbm_bytes("ll_reduce", S, n, proto) == _brute_bytes("ll_reduce", S, n, proto), proto
+
+
+def test_hbm_bytes_at_the_stated_configurations():
+    for cfg, op, n, S, r, w in read_golden("hbm_bytes.txt"):
+        n, S, r, w = int(n), int(S), int(r), int(w)
+        if op.startswith("ll"):
+            proto = op.split("_")[0]
+            got = model.hbm_bytes("ll_reduce", S, n, proto)
+        else:
+            got = model.hbm_bytes(op, S, n)
+        assert got == (r, w), (cfg, op, n, S, got)
+
+
+@pytest.mark.parametrize("n", [2, 4, 8, 16])
+def test_hbm_reads_minus_local_reads_are_the_pages_remote_bytes(n):
+    """The pages count only the bytes a GPU pulls from its peers: (n-1)S for
+    the one-shot and 2(n-1)/n S for the two-shot (算法).  Taking the local
+    reads (a rank's own buffer; for the two-shot its own input segment and its
+    own reduced segment) out of the HBM reads must give exactly those."""
+    S = 1 << 20
+    r, _ = model.hbm_bytes("oneshot", S, n)
+    assert r - S == model.remote_bytes_per_rank("one-shot", S, n)
+    r, _ = model.hbm_bytes("twoshot_share", S, n)
+    assert r - 2 * (S // n) == model.remote_bytes_per_rank("two-shot", S, n)
