@@ -4,13 +4,17 @@ A step is one pass of the whole hot path, one GPU's share of it, over one
 message of the workload, with the n ranks' registered buffers emulated as n
 HBM allocations on this GPU; this GPU plays rank `me` = 0:
 
-  1. one-shot: the full output of rank me            (ar_oneshot)
+  1. one-shot: the full output of rank me                (ar_oneshot)
   2. two-shot: reduce-scatter of segment me, flag barrier, all-gather into
-     rank me's output, in one persistent launch      (ar_twoshot_rs, fused, [me, me+1))
-  3. LL: pack rank me's message into its wire buffer and poll/unpack/reduce
+     rank me's output, in one launch                     (ar_twoshot_rs, fused, [me, me+1))
+  3. the two-shot under LL: the same with the segments as LL wires
+                                                         (ar_twoshot_ll, fused, [me, me+1))
+  4. the two-shot under LL128: the segments as LL128 wires, each line's data
+     ordered before its flag                             (ar_twoshot_ll128, fused, [me, me+1))
+  5. LL: pack rank me's message into its wire buffer and poll/unpack/reduce
      the peers' wire buffers, rank me's term from its message, in one launch
-     (ar_ll_allreduce)
-  4. LL128: the same with 128-byte lines
+                                                         (ar_ll_allreduce)
+  6. LL128: the same with 128-byte lines
 
 The peers' shares (their segments and slots, their packed wire buffers) are
 other GPUs' work: they are published once before timing with a step id above
@@ -20,14 +24,19 @@ resident in HBM before timing starts; caches are kept cold by rotating
 through identical buffer sets totalling more than 1 GiB (MI355X has 256 MiB
 of memory-side cache).
 
-Timing: the K steps are captured once into a HIP graph and replayed once
-between two events (a decode engine runs this path under graph replay).
-Per-kernel durations: K launches of one kernel, graph-replayed, total / K.
+Timing.
+  - The timed region: K steps captured once into a HIP graph and replayed
+    once between two events (a decode engine runs this path under graph
+    replay); the driver's K (--steps) sets only this.
+  - Each kernel alone: a graph of KERNEL_LAUNCHES launches of it over the
+    rotated sets, replayed once to warm up and then KERNEL_REPLAYS times;
+    its time is the median replay / KERNEL_LAUNCHES.  Independent of --steps.
+  - The same per-kernel timing at 128 KiB, 1 MiB, 8 MiB and 64 MiB per rank
+    (n = 8, bf16): the metric's curve, in the same JSON line.
 
-Output: one JSON line with the whole-step throughput (algorithmic HBM bytes
-per second, see custom_all_reduce_amd/accounting.py), the roofline of the
-dominant kernel, and the CPU oracle's throughput on a bounded sample of the
-same workload.
+Rates use the algorithmic HBM bytes of each operation (oracle/model.py and
+custom_all_reduce_amd/accounting.py hold the same counts), against the
+published 8 TB/s and against a plain device copy measured in the same run.
 """
 from __future__ import annotations
 
@@ -36,6 +45,7 @@ import hashlib
 import json
 import os
 import re
+import statistics
 import sys
 import time
 
@@ -46,19 +56,28 @@ METRIC = "reduce-kernel GB/s and % of HBM peak vs message size/rank, n=8, 1×MI3
 HBM_PEAK = 8000.0  # GB/s, MI355X HBM3E published peak
 
 WORKLOADS = {
-    # name: (n ranks, dtype, elements per rank, description)
-    "decode": (8, "bf16", 8 * 8192, "one-shot-sized decode message: n=8 ranks, bf16 [8 x 8192] = 128 KiB per rank"),
-    "prefill": (8, "bf16", 512 * 8192, "prefill message: n=8 ranks, bf16 [512 x 8192] = 8 MiB per rank"),
-    "ll64k": (8, "f32", 16384, "LL-sized message: n=8 ranks, fp32 64 KiB per rank"),
-    "ll1m": (8, "f32", 262144, "n=8 ranks, fp32 1 MiB per rank"),
+    # name: (n ranks, dtype, elements per rank, the kernel the configuration names, description)
+    "prefill": (8, "bf16", 512 * 8192, "twoshot",
+                "two-shot prefill message: n=8 ranks, bf16 [512 x 8192] = 8 MiB per rank"),
+    "decode": (8, "bf16", 8 * 8192, "oneshot",
+               "one-shot decode message: n=8 ranks, bf16 [8 x 8192] = 128 KiB per rank"),
+    "ll64k": (8, "f32", 16384, "ll128", "LL / LL128 message: n=8 ranks, fp32 64 KiB per rank"),
+    "ll1m": (8, "f32", 262144, "ll128", "LL / LL128 message: n=8 ranks, fp32 1 MiB per rank"),
 }
-KERNELS = ["oneshot", "twoshot", "ll", "ll128"]
+KERNELS = ["oneshot", "twoshot", "twoshot_ll", "twoshot_ll128", "ll", "ll128"]
 KERNEL_SOURCES = {
     "oneshot": ["oneshot.hip"],
     "twoshot": ["twoshot.hip", "fastdiv.hpp"],
+    "twoshot_ll": ["twoshot.hip", "fastdiv.hpp"],
+    "twoshot_ll128": ["twoshot.hip", "fastdiv.hpp"],
     "ll": ["ll.hip"],
     "ll128": ["ll.hip"],
 }
+KERNEL_LAUNCHES = 200  # launches per per-kernel timing graph
+KERNEL_REPLAYS = 5     # timed replays of it (after one warm-up replay); the median counts
+CURVE_SIZES = [128 << 10, 1 << 20, 8 << 20, 64 << 20]
+ME = 0
+PEER_STEP = 1 << 31  # step id of the peers' published shares, above every timed step
 
 
 def code_text(src: str) -> str:
@@ -80,68 +99,81 @@ def kernel_src_sha(kernel: str) -> str:
     return h.hexdigest()[:16]
 
 
+def kernel_bytes(n, S):
+    """Algorithmic (reads, writes) of one launch of each step kernel."""
+    from custom_all_reduce_amd import accounting as acc
+
+    return {
+        "oneshot": acc.oneshot(n, S),
+        "twoshot": acc.twoshot(n, S, 1),
+        "twoshot_ll": acc.twoshot_ll(n, S, 1, "ll"),
+        "twoshot_ll128": acc.twoshot_ll(n, S, 1, "ll128"),
+        "ll": acc.ll_allreduce("ll", n, S),
+        "ll128": acc.ll_allreduce("ll128", n, S),
+    }
+
+
 def step_bytes(n, S):
     from custom_all_reduce_amd import accounting as acc
 
-    per = {
-        "oneshot": acc.total(acc.oneshot(n, S)),
-        "twoshot": acc.total(acc.twoshot(n, S, 1)),
-        "ll": acc.total(acc.ll_allreduce("ll", n, S)),
-        "ll128": acc.total(acc.ll_allreduce("ll128", n, S)),
-    }
-    return per
+    return {k: acc.total(rw) for k, rw in kernel_bytes(n, S).items()}
 
 
 class BufferSet:
-    """All device buffers of one step for n ranks."""
+    """All device buffers of one step for n ranks (rank ME's outputs; every
+    rank's with full=True, for the all-rank launches of the sweep)."""
 
-    def __init__(self, torch, car, src, n, dt, numel):
-        self.ins = [t.clone() for t in src]
-        self.out = torch.empty(numel, dtype=dt, device="cuda")
-        self.segs = [torch.empty(numel // n, dtype=dt, device="cuda") for _ in range(n)]
-        # LL segment wires of the two-shot under LL, zeroed (flags below every step)
-        es_ = 4 if dt == torch.float32 else 2
-        self.segw = [torch.zeros(car.ll_wire_bytes("ll", numel // n * es_), dtype=torch.uint8, device="cuda")
-                     for _ in range(n)]
-        self.outs = [torch.empty(numel, dtype=dt, device="cuda") for _ in range(n)]
+    def __init__(self, torch, car, src, n, dt, numel, full=False):
         es = 4 if dt == torch.float32 else 2
-        S = numel * es
-        self.w_ll = [torch.empty(car.ll_wire_bytes("ll", S), dtype=torch.uint8, device="cuda") for _ in range(n)]
-        self.w_128 = [torch.empty(car.ll_wire_bytes("ll128", S), dtype=torch.uint8, device="cuda") for _ in range(n)]
-        self.out_ll = torch.empty(numel, dtype=dt, device="cuda")
-        self.out_128 = torch.empty(numel, dtype=dt, device="cuda")
+        S, m = numel * es, numel // n
+        dev = "cuda"
+        self.ins = [t.clone() for t in src]
+        self.out = torch.empty(numel, dtype=dt, device=dev)
+        self.segs = [torch.empty(m, dtype=dt, device=dev) for _ in range(n)]
+        # segment wires of the two-shot under LL / LL128, zeroed (flags below every step)
+        self.segw = [torch.zeros(car.ll_wire_bytes("ll", m * es), dtype=torch.uint8, device=dev) for _ in range(n)]
+        self.segw128 = [torch.zeros(car.ll_wire_bytes("ll128", m * es), dtype=torch.uint8, device=dev)
+                        for _ in range(n)]
+        self.outs = [torch.empty(numel, dtype=dt, device=dev) if (full or r == ME) else None for r in range(n)]
+        self.out_tsll = torch.empty(numel, dtype=dt, device=dev)
+        self.out_ts128 = torch.empty(numel, dtype=dt, device=dev)
+        self.w_ll = [torch.empty(car.ll_wire_bytes("ll", S), dtype=torch.uint8, device=dev) for _ in range(n)]
+        self.w_128 = [torch.empty(car.ll_wire_bytes("ll128", S), dtype=torch.uint8, device=dev) for _ in range(n)]
+        self.out_ll = torch.empty(numel, dtype=dt, device=dev)
+        self.out_128 = torch.empty(numel, dtype=dt, device=dev)
+
+    def tensors(self):
+        return ([*self.ins, self.out, *self.segs, *self.segw, *self.segw128, self.out_tsll, self.out_ts128,
+                 *self.w_ll, *self.w_128, self.out_ll, self.out_128] + [o for o in self.outs if o is not None])
 
     def footprint(self):
-        ts = self.ins + [self.out] + self.segs + self.segw + self.outs + self.w_ll + self.w_128 + \
-            [self.out_ll, self.out_128]
-        return sum(t.numel() * t.element_size() for t in ts)
+        return sum(t.numel() * t.element_size() for t in self.tensors())
+
+    def step_outputs(self):
+        """The output of every step kernel, in KERNELS order."""
+        return [self.out, self.outs[ME], self.out_tsll, self.out_ts128, self.out_ll, self.out_128]
 
 
-ME = 0
-PEER_STEP = 1 << 31  # step id of the peers' published shares, above every timed step
+def only_me(b, outs):
+    return [outs[r] if r == ME else None for r in range(len(b.ins))]
 
 
-def step_calls(car, b, flags):
-    """The four launches of one step on buffer set b (rank ME's share)."""
+def kernel_calls(car, b, flags):
+    """Prepared launches of one buffer set: name -> call(step)."""
     n = len(b.ins)
-    outs = [b.outs[r] if r == ME else None for r in range(n)]
-    return [
-        car.prepare_oneshot(b.ins, b.out),
-        car.prepare_twoshot_rs(b.ins, b.segs, flags, r0=ME, r1=ME + 1, outs=outs),
-        car.prepare_ll_allreduce(b.ins[ME], b.w_ll, b.out_ll, flags, "ll", ME),
-        car.prepare_ll_allreduce(b.ins[ME], b.w_128, b.out_128, flags, "ll128", ME),
-    ]
-
-
-def split_ll_calls(car, b, flags):
-    """The LL / LL128 step as two launches each (pack, then receive), for
-    the sweep."""
-    return {
-        "ll_pack": car.prepare_ll_pack([b.ins[ME]], [b.w_ll[ME]], "ll"),
-        "ll_reduce": car.prepare_ll_reduce(b.w_ll, b.out_ll, flags, "ll"),
-        "ll128_pack": car.prepare_ll_pack([b.ins[ME]], [b.w_128[ME]], "ll128"),
-        "ll128_reduce": car.prepare_ll_reduce(b.w_128, b.out_128, flags, "ll128"),
+    one = car.prepare_oneshot(b.ins, b.out)
+    ts_outs = only_me(b, b.outs)
+    calls = {
+        "oneshot": lambda s, one=one: one(),
+        "twoshot": car.prepare_twoshot_rs(b.ins, b.segs, flags, ME, ME + 1, ts_outs),
+        "twoshot_ll": car.prepare_twoshot_ll(b.ins, b.segw, flags, ME, ME + 1,
+                                             only_me(b, [b.out_tsll] * n)),
+        "twoshot_ll128": car.prepare_twoshot_ll128(b.ins, b.segw128, flags, ME, ME + 1,
+                                                   only_me(b, [b.out_ts128] * n)),
+        "ll": car.prepare_ll_allreduce(b.ins[ME], b.w_ll, b.out_ll, flags, "ll", ME),
+        "ll128": car.prepare_ll_allreduce(b.ins[ME], b.w_128, b.out_128, flags, "ll128", ME),
     }
+    return calls
 
 
 def publish_peers(car, b, flags):
@@ -151,14 +183,69 @@ def publish_peers(car, b, flags):
     for r in peers:
         car.ar_twoshot_rs(b.ins, b.segs, flags, PEER_STEP, r0=r, r1=r + 1)
         car.ar_twoshot_ll(b.ins, b.segw, flags, PEER_STEP, r0=r, r1=r + 1)
+        car.ar_twoshot_ll128(b.ins, b.segw128, flags, PEER_STEP, r0=r, r1=r + 1)
     car.ar_ll_pack([b.ins[r] for r in peers], [b.w_ll[r] for r in peers], "ll", PEER_STEP)
     car.ar_ll_pack([b.ins[r] for r in peers], [b.w_128[r] for r in peers], "ll128", PEER_STEP)
 
 
-def run_step(calls, step):
-    calls[0]()
-    for c in calls[1:]:
-        c(step)
+class Rig:
+    """Rotated buffer sets of one (n, dtype, numel), the peers published, and
+    an increasing step id for every explicit-id launch."""
+
+    def __init__(self, torch, car, np, n, dt_name, numel, rotate_bytes, src=None, warm=False, full=False):
+        self.torch, self.car = torch, car
+        self.n, self.dt_name, self.numel = n, dt_name, numel
+        self.dt = torch.float32 if dt_name == "f32" else torch.bfloat16
+        self.es = 4 if dt_name == "f32" else 2
+        self.S = numel * self.es
+        if src is None:
+            gen = torch.Generator(device="cuda")
+            gen.manual_seed(1000 * n + self.S.bit_length())
+            src = [torch.randn(numel, generator=gen, device="cuda").to(self.dt) for _ in range(n)]
+        first = BufferSet(torch, car, src, n, self.dt, numel, full)
+        self.fp = first.footprint()
+        self.nsets = 1 if warm else max(2, int(np.ceil(rotate_bytes / self.fp)))
+        self.sets = [first] + [BufferSet(torch, car, src, n, self.dt, numel, full) for _ in range(self.nsets - 1)]
+        self.flags = car.new_flags(n)
+        for b in self.sets:
+            publish_peers(car, b, self.flags)
+        self.calls = [kernel_calls(car, b, self.flags) for b in self.sets]
+        self.step = 1
+        torch.cuda.synchronize()
+        car.raise_on_status(self.flags, "publishing the peers")
+
+    def next_steps(self, k):
+        s = self.step
+        self.step += k
+        return s
+
+    def run_step(self, i, step):
+        c = self.calls[i % self.nsets]
+        for name in KERNELS:
+            c[name](step)
+
+    def time_kernel(self, name, launches=KERNEL_LAUNCHES, replays=KERNEL_REPLAYS):
+        """Median per-launch time (us) of `launches` graph-replayed launches
+        of one kernel over the rotated sets."""
+        torch = self.torch
+        s0 = self.next_steps(launches)
+        cs = self.calls
+        g = graph_of(torch, lambda: [cs[i % self.nsets][name](s0 + i) for i in range(launches)])
+        timed_replay(torch, g)  # warm-up replay
+        reps = [timed_replay(torch, g) for _ in range(replays)]
+        del g
+        self.car.raise_on_status(self.flags, f"timing {name}")
+        return statistics.median(reps) * 1e3 / launches, [round(r * 1e3 / launches, 3) for r in reps]
+
+    def check_outputs(self, i):
+        """Every step kernel's output of set i equals the one-shot's, bit for bit."""
+        torch = self.torch
+        b = self.sets[i % self.nsets]
+        outs = b.step_outputs()
+        iv = torch.int16 if self.es == 2 else torch.int32
+        ref = outs[0].view(iv)
+        for name, t in zip(KERNELS[1:], outs[1:]):
+            assert torch.equal(t.view(iv), ref), f"{name} output differs from the one-shot's"
 
 
 def graph_of(torch, fn):
@@ -181,60 +268,155 @@ def timed_replay(torch, g):
     return a.elapsed_time(b)
 
 
-def launch_floor_us(torch, K):
-    """Average time of one graph-replayed launch that does almost nothing (a
-    one-element fill), timed like the kernels: the floor under every launch."""
+def launch_floor_us(torch, K=KERNEL_LAUNCHES):
+    """Per-launch time of a graph-replayed one-element fill, timed like the
+    kernels: the floor under every launch."""
     t = torch.zeros(1, device="cuda")
     g = graph_of(torch, lambda: [t.fill_(float(i)) for i in range(K)])
     timed_replay(torch, g)
-    return round(timed_replay(torch, g) * 1e3 / K, 3)
+    return round(statistics.median(timed_replay(torch, g) for _ in range(KERNEL_REPLAYS)) * 1e3 / K, 3)
+
+
+def copy_gbps(torch, nbytes=1 << 30, copies=10):
+    """A plain device-to-device copy of nbytes (torch's copy kernel), graph-
+    replayed, median of KERNEL_REPLAYS: read + write bytes per second.  A
+    second, measured denominator beside the published peak."""
+    a = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(1)
+    b = torch.empty_like(a)
+    g = graph_of(torch, lambda: [b.copy_(a) for _ in range(copies)])
+    timed_replay(torch, g)
+    ms = statistics.median(timed_replay(torch, g) for _ in range(KERNEL_REPLAYS))
+    del g, a, b
+    torch.cuda.empty_cache()
+    return round(2 * nbytes * copies / (ms * 1e-3) / 1e9, 1)
 
 
 def read_traffic(kernel: str, workload: str):
-    """HBM bytes per launch from a committed counter summary, if it was taken
-    on the current kernel source; else None."""
+    """HBM bytes per launch from a committed rocprofv3 counter summary, if it
+    was taken on the current kernel source; else None."""
     path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_counters.md")
     if not os.path.exists(path):
-        return None
+        return None, None
     text = open(path, encoding="utf-8").read()
     m = re.search(r"traffic_bytes_per_launch:\s*(\d+)\s+src_sha:\s*([0-9a-f]+)", text)
     if not m or m.group(2) != kernel_src_sha(kernel):
-        return None
-    return int(m.group(1))
+        return None, os.path.relpath(path, ROOT) + " (taken on an older kernel source: not used)"
+    return int(m.group(1)), os.path.relpath(path, ROOT)
 
 
-def cpu_baseline(host, dt_name, n, numel, per_kernel_bytes, budget_s):
-    """The C oracle doing the same step (rank 0's share) on the host, single
-    thread, for about budget_s seconds of work.  The peers' wire buffers are
-    packed once outside the timed loop, as on the GPU."""
+def host_cpu():
+    model = None
+    try:
+        with open("/proc/cpuinfo", encoding="utf-8") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except AttributeError:
+        usable = os.cpu_count()
+    return model, os.cpu_count(), usable
+
+
+def oracle_step_bytes(n, S):
+    """HBM bytes the oracle's own step moves: the one-shot, the two-shot of
+    every rank (the oracle has no one-rank form), and per protocol the pack
+    of rank 0's message plus the reduce of all n wires."""
+    from oracle import model
+
+    tot = sum(model.hbm_bytes("oneshot", S, n)) + sum(model.hbm_bytes("twoshot_full", S, n))
+    for p in ("ll", "ll128"):
+        tot += sum(model.hbm_bytes("ll_pack", S, n, p)) + sum(model.hbm_bytes("ll_reduce", S, n, p))
+    return tot
+
+
+def cpu_baseline(host, dt_name, n, budget_s):
+    """The C oracle doing the same message on the host: single-threaded for
+    about budget_s / 2 seconds, then with one thread per usable core (element
+    ranges of every rank split between the threads; the C calls run without
+    Python's lock) for about as long.  Credits the bytes the oracle's step
+    actually moves."""
+    from concurrent.futures import ThreadPoolExecutor
+
     import oracle
 
     lib = oracle.load()
-    peer_wires = {p: [oracle.ll_pack(p, a, 1 << 31, lib) for a in host] for p in ("ll", "ll128")}
-    steps = 0
-    t0 = time.perf_counter()
-    while True:
-        s = steps + 1
-        oracle.oneshot(host, dt_name, lib)
-        oracle.twoshot(host, dt_name, lib)  # the oracle's two-shot computes every rank's RS and AG
+    numel = host[0].size
+    es = 4 if dt_name == "f32" else 2
+
+    def one_step(ins, s):
+        oracle.oneshot(ins, dt_name, lib)
+        oracle.twoshot(ins, dt_name, lib)
         for proto in ("ll", "ll128"):
-            wires = list(peer_wires[proto])
-            wires[0] = oracle.ll_pack(proto, host[0], s, lib)
-            oracle.ll_reduce(proto, wires, numel, dt_name, s, lib)
-        steps += 1
-        el = time.perf_counter() - t0
-        if el >= budget_s:
-            break
-    total = sum(per_kernel_bytes.values()) * steps
+            wires = [oracle.ll_pack(proto, a, s, lib) for a in ins[:1]] + peer_wires[id(ins[0])][proto]
+            oracle.ll_reduce(proto, wires, ins[0].size, dt_name, s, lib)
+
+    def prep(ins):
+        peer_wires[id(ins[0])] = {p: [oracle.ll_pack(p, a, PEER_STEP, lib) for a in ins[1:]] for p in ("ll", "ll128")}
+
+    peer_wires = {}
+    prep(host)
+    model_name, nproc, usable = host_cpu()
+    threads = max(1, min(16, usable))
+    # element ranges: whole two-shot segments and whole LL128 lines in every range
+    unit = n * 480
+    bounds = [min(numel, (numel * t // threads) // unit * unit) for t in range(threads)] + [numel]
+    slices = [[a[bounds[t]:bounds[t + 1]].copy() for a in host] for t in range(threads)]
+    slices = [s for s in slices if s[0].size > 0]
+    for s in slices:
+        prep(s)
+
+    def run(fn, budget):
+        steps, t0 = 0, time.perf_counter()
+        while True:
+            fn(steps + 1)
+            steps += 1
+            el = time.perf_counter() - t0
+            if el >= budget:
+                return steps, el
+
+    s1, e1 = run(lambda s: one_step(host, s), budget_s / 2)
+    with ThreadPoolExecutor(len(slices)) as ex:
+        sT, eT = run(lambda s: list(ex.map(lambda sl: one_step(sl, s), slices)), budget_s / 2)
+    per_step = oracle_step_bytes(n, numel * es)
     return {
-        "value": round(total / el / 1e9, 4),
+        "value": round(per_step * sT / eT / 1e9, 4),
         "unit": "GB/s",
-        "cores": 1,
+        "cores": len(slices),
         "kind": "oracle",
-        "sample": f"{steps} steps of the same workload and data (one-shot; two-shot, where the oracle computes all "
-                  f"{n} ranks' RS+AG; pack of rank 0 + reduce of {n} wires for LL and LL128), {el:.1f} s, "
-                  "single-threaded C oracle; bytes credited as for rank 0's share",
+        "sample": f"{sT} steps on the workload's own data with {len(slices)} threads over element ranges, "
+                  f"{eT:.1f} s; a step is the oracle's one-shot, its two-shot of all {n} ranks, and per protocol "
+                  "the pack of rank 0's message plus the reduce of all n wires (the peers' wires packed once "
+                  f"beforehand); credited with the {per_step} HBM bytes that step moves",
+        "single_thread": {"value": round(per_step * s1 / e1 / 1e9, 4), "unit": "GB/s", "cores": 1,
+                          "steps": s1, "seconds": round(e1, 1)},
+        "host": {"cpu_model": model_name, "nproc": nproc, "usable_cores": usable},
     }
+
+
+def curve(args, torch, car, np):
+    """Per-kernel time and rate at CURVE_SIZES bytes per rank, n = 8, bf16."""
+    from custom_all_reduce_amd import accounting as acc
+
+    rows = []
+    for S in CURVE_SIZES:
+        rig = Rig(torch, car, np, 8, "bf16", S // 2, args.rotate_gib * (1 << 30))
+        row = {"bytes_per_rank": S}
+        for name in KERNELS:
+            us, _ = rig.time_kernel(name, replays=3)
+            by = acc.total(kernel_bytes(8, S)[name])
+            gbps = by / (us * 1e-6) / 1e9
+            row[name] = {"us": round(us, 3), "GBps": round(gbps, 1), "frac": round(gbps / HBM_PEAK, 4)}
+        row["ll128_vs_oneshot"] = round(row["ll128"]["GBps"] / row["oneshot"]["GBps"], 3)
+        rig.check_outputs(0)
+        rows.append(row)
+        print("curve " + json.dumps(row), file=sys.stderr, flush=True)
+        del rig
+        torch.cuda.empty_cache()
+    return rows
 
 
 SWEEP_SIZES = [16 << 10, 256 << 10, 1 << 20, 8 << 20, 64 << 20]
@@ -242,119 +424,75 @@ SWEEP_SIZES = [16 << 10, 256 << 10, 1 << 20, 8 << 20, 64 << 20]
 
 def sweep(args, torch, car, np, out_path):
     """Per-kernel GB/s and fraction of HBM peak vs bytes per rank, for n = 8
-    and n = 16, fp32 and bf16 (cold caches, graph-replayed launches).  Writes
-    one JSON object per (n, dtype, size, kernel) to out_path and returns the
-    one-shot / two-shot crossover per (n, dtype)."""
-    import synth
+    and n = 16, fp32 and bf16 (cold caches, graph-replayed launches), for the
+    step kernels and the other entry points.  Writes one JSON object per
+    (n, dtype, size, kernel) to out_path and returns the one-shot / two-shot
+    crossover per (n, dtype)."""
     from custom_all_reduce_amd import accounting as acc
 
     rows = []
     cross = {}
     for n in (8, 16):
         for dt_name in ("bf16", "f32"):
-            dt = torch.float32 if dt_name == "f32" else torch.bfloat16
             es = 4 if dt_name == "f32" else 2
             t_one, t_two = {}, {}
             for S in SWEEP_SIZES:
-                numel = S // es
-                host = synth.rank_inputs(n, numel, dt_name, "normal", config=4)
-                if dt_name == "f32":
-                    src = [torch.from_numpy(a).cuda() for a in host]
-                else:
-                    src = [torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda() for a in host]
-                fp = (n * 2 + 5) * S + n * (acc.wire_bytes("ll", S) + acc.wire_bytes("ll128", S))
-                nsets = max(2, int(np.ceil((1 << 30) / fp)))
-                sets = [BufferSet(torch, car, src, n, dt, numel) for _ in range(nsets)]
-                flags = car.new_flags(n)
-                calls = [step_calls(car, b, flags) for b in sets]
-                full = [car.prepare_twoshot_rs(b.ins, b.segs, flags, outs=b.outs) for b in sets]
-                bc_one = [car.prepare_reduce_bcast(b.ins, b.outs, ME, ME + 1) for b in sets]
-                bc_all = [car.prepare_reduce_bcast(b.ins, b.outs) for b in sets]
-                push = [car.prepare_push([b.ins[ME]], [b.outs]) for b in sets]
-                stage = [car.prepare_push([b.ins[ME]], [[b.out]]) for b in sets]
-                ag_copy = [car.prepare_twoshot_ag_copy(b.segs, [b.outs[r] if r == ME else None for r in range(n)],
-                                                       flags, ME, ME + 1) for b in sets]
-                ts_auto = [car.prepare_twoshot_rs(b.ins, b.segs, flags, r0=ME, r1=ME + 1,
-                                                  outs=[b.outs[r] if r == ME else None for r in range(n)])
-                           for b in sets]
-                split = [split_ll_calls(car, b, flags) for b in sets]
-                tsll_one = [car.prepare_twoshot_ll(b.ins, b.segw, flags, ME, ME + 1,
-                                                   [b.outs[r] if r == ME else None for r in range(n)]) for b in sets]
-                tsll_all = [car.prepare_twoshot_ll(b.ins, b.segw, flags, outs=b.outs) for b in sets]
-                for b in sets:
-                    publish_peers(car, b, flags)
-                run_step(calls[0], 1)
-                torch.cuda.synchronize()
-                car.raise_on_status(flags, "sweep warm-up")
-                # K launches per timing: enough for ~20 ms at 5 TB/s, within [16, 400]
-                K = int(min(400, max(16, 0.02 * 5e12 / (n * S))))
-                step = 3
-                # the full emulation rewrites every rank's slots, so it goes last
-                kinds = [("oneshot", 0, acc.oneshot(n, S)), ("twoshot", 1, acc.twoshot(n, S, 1)),
-                         ("ll", 2, acc.ll_allreduce("ll", n, S)), ("ll128", 3, acc.ll_allreduce("ll128", n, S)),
-                         ("ll_pack", "split", acc.ll_pack("ll", S, 1)),
-                         ("ll_reduce", "split", acc.ll_reduce("ll", n, S)),
-                         ("ll128_pack", "split", acc.ll_pack("ll128", S, 1)),
-                         ("ll128_reduce", "split", acc.ll_reduce("ll128", n, S)),
-                         ("bcast", "bc_one", acc.reduce_bcast(n, S, 1)),
-                         ("bcast_full", "bc_all", acc.reduce_bcast(n, S, n)),
-                         ("push", "push", acc.push(S, n)),
-                         ("stage", "stage", acc.push(S, 1)),
-                         ("ag_copy", "ag_copy", acc.twoshot_ag(n, S, 1)),
-                         ("twoshot_auto", "ts_auto", acc.twoshot(n, S, 1)),
-                         ("twoshot_ll", "tsll_one", acc.twoshot_ll(n, S, 1)),
-                         ("twoshot_ll_full", "tsll_all", acc.twoshot_ll(n, S, n)),
-                         ("twoshot_full", None, acc.twoshot(n, S, n))]
-                extra = {"bc_one": bc_one, "bc_all": bc_all, "push": push, "stage": stage, "ts_auto": ts_auto,
-                         "ag_copy": ag_copy}
-                for name, ki, rw in kinds:
-                    base = step
-
-                    def launches(ki=ki, base=base, name=name):
-                        for i in range(K):
-                            if ki is None:
-                                full[i % nsets](base + i)
-                            elif ki == "ts_auto":
-                                extra[ki][i % nsets](0)  # step id from the flag region
-                            elif ki == "ag_copy":
-                                extra[ki][i % nsets](1)  # every slot holds a later step by now
-                            elif ki == "split" and name.endswith("reduce"):
-                                split[i % nsets][name](1)  # every wire carries flags >= 1 by now
-                            elif ki == "split":
-                                split[i % nsets][name](base + i)
-                            elif ki == "tsll_all":
-                                # above the peers' published step, so no line
-                                # left by the publishing counts as arrived
-                                tsll_all[i % nsets](PEER_STEP + base + i)
-                            elif ki == "tsll_one":
-                                tsll_one[i % nsets](base + i)
-                            elif isinstance(ki, str):
-                                extra[ki][i % nsets]()
-                            elif name == "oneshot":
-                                calls[i % nsets][0]()
-                            else:
-                                calls[i % nsets][ki](base + i)
-
-                    g = graph_of(torch, launches)
-                    ms = timed_replay(torch, g)
-                    del g
-                    step = base + K
-                    us = ms * 1e3 / K
+                rig = Rig(torch, car, np, n, dt_name, S // es, args.rotate_gib * (1 << 30), full=True)
+                fl = rig.flags
+                extra = {}
+                for i, b in enumerate(rig.sets):
+                    c = rig.calls[i]
+                    c["ll_pack"] = car.prepare_ll_pack([b.ins[ME]], [b.w_ll[ME]], "ll")
+                    c["ll_reduce"] = car.prepare_ll_reduce(b.w_ll, b.out_ll, fl, "ll")
+                    c["ll128_pack"] = car.prepare_ll_pack([b.ins[ME]], [b.w_128[ME]], "ll128")
+                    c["ll128_reduce"] = car.prepare_ll_reduce(b.w_128, b.out_128, fl, "ll128")
+                    bc1 = car.prepare_reduce_bcast(b.ins, b.outs, ME, ME + 1)
+                    bca = car.prepare_reduce_bcast(b.ins, b.outs)
+                    push = car.prepare_push([b.ins[ME]], [b.outs])
+                    stage = car.prepare_push([b.ins[ME]], [[b.out]])
+                    agc = car.prepare_twoshot_ag_copy(b.segs, only_me(b, b.outs), fl, ME, ME + 1)
+                    tsa = car.prepare_twoshot_rs(b.ins, b.segs, fl, ME, ME + 1, only_me(b, b.outs))
+                    c["bcast"] = lambda s, f=bc1: f()
+                    c["bcast_full"] = lambda s, f=bca: f()
+                    c["push"] = lambda s, f=push: f()
+                    c["stage"] = lambda s, f=stage: f()
+                    c["ag_copy"] = lambda s, f=agc: f(1)  # every slot holds a later step by now
+                    c["twoshot_auto"] = lambda s, f=tsa: f(0)  # step id from the flag region
+                    # the receivers alone: every wire carries flags >= 1 by now
+                    for k in ("ll_reduce", "ll128_reduce"):
+                        c[k] = (lambda s, f=c[k]: f(1))
+                    ful = car.prepare_twoshot_rs(b.ins, b.segs, fl, outs=b.outs)
+                    tsll_all = car.prepare_twoshot_ll(b.ins, b.segw, fl, outs=b.outs)
+                    ts128_all = car.prepare_twoshot_ll128(b.ins, b.segw128, fl, outs=b.outs)
+                    # all-rank launches rewrite every rank's segments: their ids go above
+                    # the peers' published step, so nothing the publishing left counts
+                    c["twoshot_full"] = lambda s, f=ful: f(PEER_STEP + s)
+                    c["twoshot_ll_full"] = lambda s, f=tsll_all: f(PEER_STEP + s)
+                    c["twoshot_ll128_full"] = lambda s, f=ts128_all: f(PEER_STEP + s)
+                kinds = [(k, kernel_bytes(n, S)[k]) for k in KERNELS] + [
+                    ("ll_pack", acc.ll_pack("ll", S, 1)), ("ll_reduce", acc.ll_reduce("ll", n, S)),
+                    ("ll128_pack", acc.ll_pack("ll128", S, 1)), ("ll128_reduce", acc.ll_reduce("ll128", n, S)),
+                    ("bcast", acc.reduce_bcast(n, S, 1)), ("bcast_full", acc.reduce_bcast(n, S, n)),
+                    ("push", acc.push(S, n)), ("stage", acc.push(S, 1)), ("ag_copy", acc.twoshot_ag(n, S, 1)),
+                    ("twoshot_auto", acc.twoshot(n, S, 1)),
+                    # the all-rank launches last: they rewrite every rank's segments
+                    ("twoshot_full", acc.twoshot(n, S, n)), ("twoshot_ll_full", acc.twoshot_ll(n, S, n, "ll")),
+                    ("twoshot_ll128_full", acc.twoshot_ll(n, S, n, "ll128"))]
+                K = int(min(KERNEL_LAUNCHES, max(16, 0.02 * 5e12 / (n * S))))
+                for name, rw in kinds:
+                    us, _ = rig.time_kernel(name, launches=K, replays=3)
                     gbps = acc.total(rw) / (us * 1e-6) / 1e9
-                    row = {"n": n, "dtype": dt_name, "bytes_per_rank": S, "kernel": name, "avg_us": round(us, 3),
-                           "algorithmic_bytes": acc.total(rw), "GBps": round(gbps, 1),
-                           "frac_of_peak": round(gbps / HBM_PEAK, 4), "launches": K, "buffer_sets": nsets}
-                    rows.append(row)
-                    car.raise_on_status(flags, f"sweep {name} n={n} {dt_name} S={S}")
+                    rows.append({"n": n, "dtype": dt_name, "bytes_per_rank": S, "kernel": name,
+                                 "avg_us": round(us, 3), "algorithmic_bytes": acc.total(rw), "GBps": round(gbps, 1),
+                                 "frac_of_peak": round(gbps / HBM_PEAK, 4), "launches": K,
+                                 "buffer_sets": rig.nsets})
                     print(f"sweep n={n} {dt_name} S={S} {name}: {us:.2f} us {gbps:.0f} GB/s", file=sys.stderr,
                           flush=True)
                     if name == "oneshot":
                         t_one[S] = us
                     elif name == "twoshot":
                         t_two[S] = us
-                car.raise_on_status(flags, "sweep")
-                del sets, calls, full, src, extra, bc_one, bc_all, push, stage, ts_auto, ag_copy, split
-                del tsll_one, tsll_all
+                del rig, extra
                 torch.cuda.empty_cache()
             # crossover: first size where two-shot (one rank's share) beats one-shot,
             # log-linear interpolation of the time difference between the bracketing sizes
@@ -377,80 +515,47 @@ def sweep(args, torch, car, np, out_path):
 
 SELECT_SIZES = [16 << 10, 32 << 10, 64 << 10, 128 << 10, 256 << 10, 512 << 10, 1 << 20, 3 << 19, 2 << 20,
                 3 << 20, 4 << 20, 6 << 20, 8 << 20, 12 << 20, 16 << 20, 32 << 20, 64 << 20]
-SELECT_ALGOS = ["oneshot", "twoshot", "ll", "ll128", "push", "bcast", "twoshot_ll"]
+SELECT_ALGOS = ["oneshot", "twoshot", "ll", "ll128", "push", "bcast", "twoshot_ll", "twoshot_ll128"]
 
 
 def select_table(args, torch, car, np, out_path):
     """One GPU's share of an all-reduce by each algorithm, n = 2..16, bf16,
     over SELECT_SIZES bytes per rank (cold: buffer sets rotated over >= 1 GiB;
-    graph-replayed).  The shares: one-shot; rank 0's fused two-shot after the
-    peers' reduce-scatter; rank 0's LL / LL128 send and receive in one launch
-    (ar_ll_allreduce), the peers' wires packed beforehand.  Each time
-    is the median of three replays.  Writes one JSON object per (n, size)."""
+    graph-replayed).  The shares: one-shot; rank 0's fused two-shot (slots,
+    LL and LL128 segments) after the peers' reduce-scatter; rank 0's LL /
+    LL128 send and receive in one launch (ar_ll_allreduce), the peers' wires
+    packed beforehand; rank 0's push plus its one-shot over its staging
+    slots; rank 0's reduce-broadcast share.  Each time is the median of
+    three replays.  Writes one JSON object per (n, size)."""
     rows = []
-    gen = torch.Generator(device="cuda")
     with open(out_path, "w", encoding="utf-8") as f:
         for n in range(2, 17):
             for S in SELECT_SIZES:
                 numel = S // 2
                 numel -= numel % (8 * n)  # whole 16-byte vectors in every segment
                 Sb = numel * 2
-                W1, W2 = car.ll_wire_bytes("ll", Sb), car.ll_wire_bytes("ll128", Sb)
-                fp = n * Sb + 5 * Sb + n * (W1 + W2) + (2 * n - 1) * Sb + n * Sb
-                nsets = max(2, int(np.ceil((1 << 30) / fp)))
-                gen.manual_seed(1000 * n + S.bit_length())
-                src = [torch.randn(numel, generator=gen, device="cuda").to(torch.bfloat16) for _ in range(n)]
-                flags = car.new_flags(n)
-                calls = {a: [] for a in SELECT_ALGOS}
+                rig = Rig(torch, car, np, n, "bf16", numel, 1 << 30)
                 keep = []
-                for _ in range(nsets):
-                    ins = [t.clone() for t in src]
-                    segs = [torch.empty(numel // n, dtype=torch.bfloat16, device="cuda") for _ in range(n)]
-                    out = torch.empty(numel, dtype=torch.bfloat16, device="cuda")
-                    w1 = [torch.empty(W1, dtype=torch.uint8, device="cuda") for _ in range(n)]
-                    w2 = [torch.empty(W2, dtype=torch.uint8, device="cuda") for _ in range(n)]
-                    # push: rank 0's slot in every rank's staging buffer, and rank 0's
-                    # staging buffer (slot 0 is its own push target)
+                for i, b in enumerate(rig.sets):
                     slots0 = [torch.empty(numel, dtype=torch.bfloat16, device="cuda") for _ in range(n)]
                     mine = [slots0[0]] + [torch.empty(numel, dtype=torch.bfloat16, device="cuda") for _ in range(1, n)]
-                    bouts = [out] + [torch.empty(numel, dtype=torch.bfloat16, device="cuda") for _ in range(1, n)]
-                    segw = [torch.zeros(car.ll_wire_bytes("ll", numel // n * 2), dtype=torch.uint8, device="cuda")
-                            for _ in range(n)]
-                    keep.append((ins, segs, out, w1, w2, slots0, mine, bouts, segw))
-                    for r in range(1, n):
-                        car.ar_twoshot_rs(ins, segs, flags, PEER_STEP, r0=r, r1=r + 1)
-                        car.ar_twoshot_ll(ins, segw, flags, PEER_STEP, r0=r, r1=r + 1)
-                    car.ar_ll_pack(ins[1:], w1[1:], "ll", PEER_STEP)
-                    car.ar_ll_pack(ins[1:], w2[1:], "ll128", PEER_STEP)
-                    one = car.prepare_oneshot(ins, out)
-                    calls["oneshot"].append(lambda s, one=one: one())
-                    calls["twoshot"].append(car.prepare_twoshot_rs(ins, segs, flags, 0, 1, [out] + [None] * (n - 1)))
-                    for name, w in (("ll", w1), ("ll128", w2)):
-                        calls[name].append(car.prepare_ll_allreduce(ins[0], w, out, flags, name, 0))
-                    ps, po = car.prepare_push([ins[0]], [slots0]), car.prepare_oneshot(mine, out)
-                    calls["push"].append(lambda s, ps=ps, po=po: (ps(), po()))
-                    bc = car.prepare_reduce_bcast(ins, bouts, 0, 1)
-                    calls["bcast"].append(lambda s, bc=bc: bc())
-                    calls["twoshot_ll"].append(car.prepare_twoshot_ll(ins, segw, flags, 0, 1,
-                                                                      [out] + [None] * (n - 1)))
-                del src
+                    bouts = [b.out] + [torch.empty(numel, dtype=torch.bfloat16, device="cuda") for _ in range(1, n)]
+                    keep.append((slots0, mine, bouts))
+                    ps, po = car.prepare_push([b.ins[0]], [slots0]), car.prepare_oneshot(mine, b.out)
+                    bc = car.prepare_reduce_bcast(b.ins, bouts, 0, 1)
+                    rig.calls[i]["push"] = lambda s, ps=ps, po=po: (ps(), po())
+                    rig.calls[i]["bcast"] = lambda s, bc=bc: bc()
                 torch.cuda.synchronize()
                 row = {"n": n, "bytes_per_rank": Sb}
                 K = int(min(200, max(16, 0.004 * 4e12 / ((n + 1) * Sb))))
                 for a in SELECT_ALGOS:
-                    cs = calls[a]
-                    g = graph_of(torch, lambda cs=cs: [cs[i % nsets](1 + i) for i in range(K)])
-                    timed_replay(torch, g)
-                    # median of three replays: one disturbed replay does not move the table
-                    reps = sorted(timed_replay(torch, g) for _ in range(3))
-                    row[a + "_us"] = round(reps[1] * 1e3 / K, 3)
-                    del g
-                car.raise_on_status(flags, f"select-table n={n} S={Sb}")
+                    us, _ = rig.time_kernel(a, launches=K, replays=3)
+                    row[a + "_us"] = round(us, 3)
                 rows.append(row)
                 f.write(json.dumps(row) + "\n")
                 f.flush()
                 print("select-table " + " ".join(f"{k}={v}" for k, v in row.items()), file=sys.stderr, flush=True)
-                del calls, keep
+                del rig, keep
                 torch.cuda.empty_cache()
     return rows
 
@@ -465,19 +570,22 @@ def device_summary(torch):
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=400)
-    ap.add_argument("--warmup", type=int, default=40)
-    ap.add_argument("--workload", default="decode", choices=sorted(WORKLOADS))
+    ap.add_argument("--steps", type=int, default=200, help="steps in the timed region")
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="prefill", choices=sorted(WORKLOADS))
     ap.add_argument("--rotate-gib", type=float, default=1.0, help="total size of the rotated buffer sets")
     ap.add_argument("--warm", action="store_true", help="one buffer set (cache-warm); labelled as such")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="oracle budget; 0 skips the CPU baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=16.0, help="oracle budget; 0 skips the CPU baseline")
     ap.add_argument("--eager", action="store_true", help="time eager launches instead of one graph replay")
     ap.add_argument("--no-kernel-times", action="store_true", help="skip the per-kernel timing graphs")
+    ap.add_argument("--no-curve", action="store_true", help="skip the per-kernel timing at 128 KiB..64 MiB")
     ap.add_argument("--sweep", metavar="OUT.jsonl", help="also run the size sweep (n = 8, 16; fp32, bf16) into a file")
     ap.add_argument("--select-table", metavar="OUT.jsonl",
                     help="only time one GPU's share by each algorithm for n = 2..16 over a size grid, then exit")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run ten 256 MiB device-to-device copies (reference for HBM byte counters), then exit")
+    ap.add_argument("--profile-kernel", choices=KERNELS,
+                    help="only launch this kernel 20 times on the workload (for counter runs), then exit")
     args = ap.parse_args(argv)
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -504,59 +612,59 @@ def main(argv=None):
     import custom_all_reduce_amd as car
     import synth
 
-    if args.select_table:
-        torch.cuda.set_device(0)
-        car.set_poll_timeout_ns(50_000_000)
-        rows = select_table(args, torch, car, np, args.select_table)
-        print(json.dumps({"select_table_rows": len(rows), "file": args.select_table}), flush=True)
-        return 0
-
-    n, dt_name, numel, desc = WORKLOADS[args.workload]
-    dt = torch.float32 if dt_name == "f32" else torch.bfloat16
-    es = 4 if dt_name == "f32" else 2
-    S = numel * es
     torch.cuda.set_device(0)
     # No wait on this path should take more than microseconds: a protocol
     # mistake then shows up as a reported timeout after 50 ms, not 1 s.
     car.set_poll_timeout_ns(50_000_000)
 
+    if args.select_table:
+        rows = select_table(args, torch, car, np, args.select_table)
+        print(json.dumps({"select_table_rows": len(rows), "file": args.select_table}), flush=True)
+        return 0
+
+    n, dt_name, numel, config_kernel, desc = WORKLOADS[args.workload]
+    es = 4 if dt_name == "f32" else 2
+    S = numel * es
     host = synth.rank_inputs(n, numel, dt_name, "normal", config=1)
     if dt_name == "f32":
         src = [torch.from_numpy(a).cuda() for a in host]
     else:
         src = [torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda() for a in host]
 
-    first = BufferSet(torch, car, src, n, dt, numel)
-    fp = first.footprint()
-    nsets = 1 if args.warm else max(2, int(np.ceil(args.rotate_gib * (1 << 30) / fp)))
-    sets = [first] + [BufferSet(torch, car, src, n, dt, numel) for _ in range(nsets - 1)]
-    flags = car.new_flags(n)
-    calls = [step_calls(car, b, flags) for b in sets]
-    for b in sets:
-        publish_peers(car, b, flags)
-    torch.cuda.synchronize()
+    if args.profile_kernel:
+        rig = Rig(torch, car, np, n, dt_name, numel, args.rotate_gib * (1 << 30), src=src)
+        s0 = rig.next_steps(20)
+        for i in range(20):
+            rig.calls[i % rig.nsets][args.profile_kernel](s0 + i)
+        torch.cuda.synchronize()
+        car.raise_on_status(rig.flags, "profile")
+        print(json.dumps({"profiled_kernel": args.profile_kernel, "launches": 20, "workload": args.workload}),
+              flush=True)
+        return 0
 
+    rig = Rig(torch, car, np, n, dt_name, numel, args.rotate_gib * (1 << 30), src=src, warm=args.warm)
+    nsets, fp = rig.nsets, rig.fp
+    per_rw = kernel_bytes(n, S)
     per_bytes = step_bytes(n, S)
     bytes_per_step = sum(per_bytes.values())
     print(f"bench: {args.workload}: {nsets} buffer sets of {fp / 2**20:.1f} MiB ready", file=sys.stderr, flush=True)
 
     # Untimed warm-up, eager.
-    step = 1
+    s0 = rig.next_steps(args.warmup)
     for i in range(args.warmup):
-        run_step(calls[i % nsets], step)
-        step += 1
+        rig.run_step(i, s0 + i)
     torch.cuda.synchronize()
-    car.raise_on_status(flags, "warm-up")
+    car.raise_on_status(rig.flags, "warm-up")
 
     # Timed region: exactly K steps, captured once into a HIP graph (as a
     # decode engine would run them) with fresh step ids, replayed once
     # between a synchronize and two events.
     K = args.steps
-    s0 = step
+    s0 = rig.next_steps(K)
 
     def k_steps():
         for i in range(K):
-            run_step(calls[(args.warmup + i) % nsets], s0 + i)
+            rig.run_step(args.warmup + i, s0 + i)
 
     if args.eager:
         torch.cuda.synchronize()
@@ -574,47 +682,29 @@ def main(argv=None):
         ms_total = timed_replay(torch, g)
         wall = time.perf_counter() - wall0
         del g
-    step = s0 + K
-    car.raise_on_status(flags, "timed steps")
+    car.raise_on_status(rig.flags, "timed steps")
     ms_per_step = ms_total / K
+    # Every output of the last set the timed steps wrote equals the one-shot's (bitwise).
+    rig.check_outputs(args.warmup + K - 1)
+    print(f"bench: timed {K} steps, {ms_per_step * 1e3:.2f} us per step", file=sys.stderr, flush=True)
 
-    # Every output of the last set must equal the one-shot output (bitwise).
-    last = sets[(args.warmup + K - 1) % nsets]
-    ref = last.out.view(torch.int16 if es == 2 else torch.int32)
-    for t in [last.outs[ME], last.out_ll, last.out_128]:
-        assert torch.equal(t.view(ref.dtype), ref), "outputs of the step disagree"
-
-    # Per-kernel launch durations: K launches of one kernel, rotating sets,
-    # captured into a graph and replayed between two events; average = total / K.
     kernels = {}
+    copy_rate = None
+    floor_us = None
     if not args.no_kernel_times:
-        for ki, name in enumerate(KERNELS):
-            base = step
-
-            def k_launches(ki=ki, base=base, name=name):
-                for i in range(K):
-                    c = calls[i % nsets][ki]
-                    if name == "oneshot":
-                        c()
-                    else:
-                        c(base + i)
-
-            g = graph_of(torch, k_launches)
-            ms = timed_replay(torch, g)
-            del g
-            if name != "oneshot":
-                step = base + K
-            us = ms * 1e3 / K
-            kernels[name] = {
-                "avg_us": round(us, 3),
-                "bytes": per_bytes[name],
-                "GBps": round(per_bytes[name] / (us * 1e-6) / 1e9, 1),
-            }
-        car.raise_on_status(flags, "per-kernel timing")
-    dominant = max(kernels, key=lambda k: kernels[k]["avg_us"]) if kernels else None
-    floor_us = launch_floor_us(torch, K) if kernels else None
-    print(f"bench: timed {K} steps, {ms_per_step * 1e3:.2f} us per step; kernels {kernels}", file=sys.stderr,
-          flush=True)
+        for name in KERNELS:
+            us, reps = rig.time_kernel(name)
+            gb = per_bytes[name] / (us * 1e-6) / 1e9
+            kernels[name] = {"us": round(us, 3), "replays_us": reps, "algorithmic_bytes": per_bytes[name],
+                             "GBps": round(gb, 1), "frac": round(gb / HBM_PEAK, 4)}
+        floor_us = launch_floor_us(torch)
+        print(f"bench: kernels {json.dumps(kernels)}", file=sys.stderr, flush=True)
+    del rig
+    torch.cuda.empty_cache()
+    if not args.no_kernel_times:
+        copy_rate = copy_gbps(torch)
+        for k in kernels.values():
+            k["frac_of_copy"] = round(k["GBps"] / copy_rate, 4)
 
     value = bytes_per_step * K / (ms_total * 1e-3) / 1e9
     line = {
@@ -635,43 +725,54 @@ def main(argv=None):
             "n_ranks": n,
             "bytes_per_rank": S,
             "arithmetic": f"{dt_name} data, fp32 accumulation in rank order, one rounding to {dt_name}",
-            "step": "rank 0's share: oneshot + twoshot(RS seg 0 -> barrier -> AG out 0, fused) + "
-                    "LL(pack own, reduce n; one launch) + LL128(same); peers' shares published before timing",
+            "step": "rank 0's share, six launches: one-shot; two-shot (RS of segment 0 -> barrier -> AG into "
+                    "output 0, one launch) with slots, with LL segments and with LL128 segments; LL and LL128 "
+                    "(pack own, reduce n; one launch each); the peers' shares published before timing",
             "algorithmic_bytes_per_step": bytes_per_step,
             "cache": "warm (one buffer set)" if args.warm else
                      f"cold: {nsets} rotated buffer sets, {nsets * fp / 2**30:.2f} GiB",
-            "timing": "eager launches" if args.eager else "one HIP-graph replay of the K steps",
+            "timing": ("eager launches" if args.eager else "one HIP-graph replay of the K steps") +
+                      f"; kernels: {KERNEL_LAUNCHES} graph-replayed launches, median of {KERNEL_REPLAYS} replays",
             "wall_s": round(wall, 3),
         },
         "kernels": kernels,
+        "copy_GBps": copy_rate,
+        "launch_floor_us": floor_us,
         "device": device_summary(torch),
     }
-    if dominant:
-        A = kernels[dominant]["GBps"]
-        tb = read_traffic(dominant, args.workload)
+    if kernels:
+        # the roofline of the kernel the configuration names (the two-shot for the
+        # prefill message), with the algorithmic bytes of one launch
+        rk = config_kernel
+        A = kernels[rk]["GBps"]
+        tb, tsrc = read_traffic(rk, args.workload)
+        longest = max(kernels, key=lambda k: kernels[k]["us"])
         line["roofline"] = {
-            "kernel": dominant,
+            "kernel": rk,
             "bound": "hbm",
             "achieved": A,
             "peak": HBM_PEAK,
             "unit": "GB/s",
             "frac": round(A / HBM_PEAK, 4),
             "traffic": tb,
-            "algorithmic_bytes_per_launch": per_bytes[dominant],
-            "avg_us": kernels[dominant]["avg_us"],
-            "launch_floor_us": floor_us,
+            "traffic_source": tsrc,
+            "algorithmic_bytes_per_launch": per_bytes[rk],
+            "reads_writes": list(per_rw[rk]),
+            "us": kernels[rk]["us"],
+            "frac_of_copy": kernels[rk].get("frac_of_copy"),
+            "longest_kernel": {"kernel": longest, "us": kernels[longest]["us"], "frac": kernels[longest]["frac"]},
         }
+    if not args.no_curve and not args.no_kernel_times:
+        line["curve_n8_bf16"] = curve(args, torch, car, np)
+        for row in line["curve_n8_bf16"]:
+            for k in KERNELS:
+                row[k]["frac_of_copy"] = round(row[k]["GBps"] / copy_rate, 4)
     if args.cpu_seconds > 0:
-        line["cpu_baseline"] = cpu_baseline(host, dt_name, n, numel, per_bytes, args.cpu_seconds)
+        line["cpu_baseline"] = cpu_baseline(host, dt_name, n, args.cpu_seconds)
     if args.sweep:
-        del sets, calls
         torch.cuda.empty_cache()
         rows, cross = sweep(args, torch, car, np, args.sweep)
-        best = max((r for r in rows if r["bytes_per_rank"] >= (1 << 20) and r["n"] == 8),
-                   key=lambda r: r["frac_of_peak"])
-        line["sweep"] = {"file": args.sweep, "crossover_bytes_per_rank": cross,
-                         "best_n8_at_or_above_1MiB": {k: best[k] for k in ("kernel", "dtype", "bytes_per_rank",
-                                                                            "GBps", "frac_of_peak")}}
+        line["sweep"] = {"file": args.sweep, "crossover_bytes_per_rank": cross}
     print(json.dumps(line), flush=True)
     return 0
 

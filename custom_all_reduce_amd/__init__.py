@@ -15,11 +15,16 @@ Functions mirror the C entry points and take ``torch.Tensor`` arguments:
     ar_ll128_reduce_unpack(wires, out, step, flags)
     ar_ll_allreduce(src, wires, out, flags, proto, me, step)   pack + reduce, one launch
     ar_twoshot_ll(ins, segws, flags, step, r0=0, r1=None, outs=None)   two-shot, LL segments
+    ar_twoshot_ll128(ins, segws, flags, step, r0=0, r1=None, outs=None) two-shot, LL128 segments
     ar_flag_barrier_reset(flags, n)
 
 Each call enqueues on ``stream`` (default: torch's current stream) and
 raises :class:`ArError` on a synchronous error.  Asynchronous timeouts are
 read with :func:`read_status` after synchronising.
+
+The C ABI sees pointers, not sizes, so the ``prepare_*`` helpers check every
+tensor's size against what the call will read or write (segments, wires,
+flag regions, outputs) and raise ``ValueError`` before anything is enqueued.
 """
 from __future__ import annotations
 
@@ -79,6 +84,8 @@ def _load(path: str = LIB_PATH):
     lib.ar_ll_allreduce.argtypes = [vp, P, i32, i32, vp, sz, i32, i32, u32, vp, vp]
     lib.ar_ll_allreduce.restype = i32
     lib.ar_twoshot_ll.argtypes, lib.ar_twoshot_ll.restype = [P, i32, P, sz, i32, i32, i32, vp, u32, P, vp], i32
+    lib.ar_twoshot_ll128.argtypes = [P, i32, P, sz, i32, i32, i32, vp, u32, P, vp]
+    lib.ar_twoshot_ll128.restype = i32
     lib.ar_flag_barrier_reset.argtypes, lib.ar_flag_barrier_reset.restype = [vp, i32, vp], i32
     lib.ar_select_algo.argtypes, lib.ar_select_algo.restype = [i32, sz, i32, ctypes.c_double], i32
     lib.ar_algo_cost_us.argtypes, lib.ar_algo_cost_us.restype = [i32, i32, sz, i32, ctypes.c_double], ctypes.c_double
@@ -126,6 +133,48 @@ def _check(code: int, where: str):
         raise ArError(code, where)
 
 
+def _nbytes(t: torch.Tensor) -> int:
+    return t.numel() * t.element_size()
+
+
+def _need_bytes(ts, nbytes: int, what: str):
+    for t in ts:
+        if _nbytes(t) < nbytes:
+            raise ValueError(f"{what} holds {_nbytes(t)} bytes, the call needs {nbytes}")
+
+
+def _need_like(ts, dtype, numel: int, what: str):
+    for t in ts:
+        if t.dtype != dtype or t.numel() != numel:
+            raise ValueError(f"{what} must be {numel} elements of {dtype}, got {t.numel()} of {t.dtype}")
+
+
+# bytes of the status words every flag-waiting call writes (the first line of
+# a flag region)
+STATUS_BYTES = 128
+
+
+def _twoshot_sizes(ins, segs, flags, outs, seg_proto=None):
+    """Size checks of the two-shot calls: equal inputs, segments of numel/n
+    elements (or LL / LL128 wires of them), a whole flag region, outputs of
+    numel elements.  A numel the call cannot split is left to the C ABI
+    (AR_ERR_DIVISIBLE)."""
+    n = len(segs)
+    if ins:
+        _need_like(ins, ins[0].dtype, ins[0].numel(), "every input")
+    _need_bytes([flags], flag_bytes(n), "the flag region")
+    ref = ins[0] if ins else segs[0]
+    numel = ref.numel() if ins else segs[0].numel() * n
+    if numel % n == 0:
+        m = numel // n
+        if seg_proto is None:
+            _need_like(segs, ref.dtype, m, "every segment")
+        else:
+            _need_bytes(segs, ll_wire_bytes(seg_proto, m * ref.element_size()), "every segment wire")
+    if outs is not None:
+        _need_like([o for o in outs if o is not None], ref.dtype, numel, "every output")
+
+
 def flag_bytes(n: int) -> int:
     return int(_lib.ar_flag_bytes(n))
 
@@ -142,7 +191,7 @@ def get_poll_timeout_ns() -> int:
     return int(_lib.ar_get_poll_timeout_ns())
 
 
-ALGOS = ("oneshot", "twoshot", "ll", "ll128", "push", "bcast", "twoshot_ll")  # ar_algo values 0..6
+ALGOS = ("oneshot", "twoshot", "ll", "ll128", "push", "bcast", "twoshot_ll", "twoshot_ll128")  # ar_algo 0..7
 
 
 def _dtype_arg(dtype) -> int:
@@ -279,13 +328,13 @@ def prepare_twoshot_rs(ins, segs, flags, r0: int = 0, r1=None, outs=None) -> Pre
         if len(outs) != n:
             raise ValueError("outs must hold n entries (None outside [r0, r1))")
         out_arr = _ptr_array([(_dev_tensor(o, "out").data_ptr() if o is not None else 0) for o in outs])
+    _twoshot_sizes(ins, segs, flags, outs)
     args = [_ptr_array([t.data_ptr() for t in ins]), n, _ptr_array([t.data_ptr() for t in segs]), ins[0].numel(),
             _dtype_code(ins[0]), r0, r1, flags.data_ptr(), 0, out_arr, None]
     return Prepared(_lib.ar_twoshot_rs, args, 8, "ar_twoshot_rs", (ins, segs, flags, outs))
 
 
-def prepare_twoshot_ll(ins, segws, flags, r0: int = 0, r1=None, outs=None) -> Prepared:
-    """Two-shot with LL segment wires (uint8 tensors of ll_wire_bytes("ll", m * element size))."""
+def _prepare_twoshot_wire(fn, name, proto, ins, segws, flags, r0, r1, outs) -> Prepared:
     n = len(ins)
     r1 = n if r1 is None else r1
     ins = [_dev_tensor(t, "input") for t in ins]
@@ -298,9 +347,21 @@ def prepare_twoshot_ll(ins, segws, flags, r0: int = 0, r1=None, outs=None) -> Pr
         if len(outs) != n:
             raise ValueError("outs must hold n entries (None outside [r0, r1))")
         out_arr = _ptr_array([(_dev_tensor(o, "out").data_ptr() if o is not None else 0) for o in outs])
+    _twoshot_sizes(ins, segws, flags, outs, seg_proto=proto)
     args = [_ptr_array([t.data_ptr() for t in ins]), n, _ptr_array([t.data_ptr() for t in segws]), ins[0].numel(),
             _dtype_code(ins[0]), r0, r1, flags.data_ptr(), 0, out_arr, None]
-    return Prepared(_lib.ar_twoshot_ll, args, 8, "ar_twoshot_ll", (ins, segws, flags, outs))
+    return Prepared(fn, args, 8, name, (ins, segws, flags, outs))
+
+
+def prepare_twoshot_ll(ins, segws, flags, r0: int = 0, r1=None, outs=None) -> Prepared:
+    """Two-shot with LL segment wires (uint8 tensors of ll_wire_bytes("ll", m * element size))."""
+    return _prepare_twoshot_wire(_lib.ar_twoshot_ll, "ar_twoshot_ll", "ll", ins, segws, flags, r0, r1, outs)
+
+
+def prepare_twoshot_ll128(ins, segws, flags, r0: int = 0, r1=None, outs=None) -> Prepared:
+    """Two-shot with LL128 segment wires (uint8 tensors of ll_wire_bytes("ll128", m * element size))."""
+    return _prepare_twoshot_wire(_lib.ar_twoshot_ll128, "ar_twoshot_ll128", "ll128", ins, segws, flags, r0, r1,
+                                 outs)
 
 
 def prepare_twoshot_ag(segs, outs, flags, r0: int = 0, r1=None, numel=None) -> Prepared:
@@ -310,6 +371,13 @@ def prepare_twoshot_ag(segs, outs, flags, r0: int = 0, r1=None, numel=None) -> P
     flags = _dev_tensor(flags, "flags")
     numel = segs[0].numel() * n if numel is None else numel
     out_arr = _ptr_array([(_dev_tensor(o, "out").data_ptr() if o is not None else 0) for o in outs])
+    if len(outs) != n:
+        raise ValueError("outs must hold n entries (None outside [r0, r1))")
+    _need_like(segs, segs[0].dtype, segs[0].numel(), "every segment")
+    _need_bytes([flags], flag_bytes(n), "the flag region")
+    if numel % n == 0:
+        _need_like(segs, segs[0].dtype, numel // n, "every segment")
+    _need_like([o for o in outs if o is not None], segs[0].dtype, numel, "every output")
     args = [_ptr_array([t.data_ptr() for t in segs]), n, out_arr, numel, _dtype_code(segs[0]), r0, r1,
             flags.data_ptr(), 0, None]
     return Prepared(_lib.ar_twoshot_ag, args, 8, "ar_twoshot_ag", (segs, outs, flags))
@@ -322,6 +390,13 @@ def prepare_twoshot_ag_copy(segs, outs, flags, r0: int = 0, r1=None, numel=None)
     flags = _dev_tensor(flags, "flags")
     numel = segs[0].numel() * n if numel is None else numel
     out_arr = _ptr_array([(_dev_tensor(o, "out").data_ptr() if o is not None else 0) for o in outs])
+    if len(outs) != n:
+        raise ValueError("outs must hold n entries (None outside [r0, r1))")
+    _need_like(segs, segs[0].dtype, segs[0].numel(), "every segment")
+    _need_bytes([flags], flag_bytes(n), "the flag region")
+    if numel % n == 0:
+        _need_like(segs, segs[0].dtype, numel // n, "every segment")
+    _need_like([o for o in outs if o is not None], segs[0].dtype, numel, "every output")
     args = [_ptr_array([t.data_ptr() for t in segs]), n, out_arr, numel, _dtype_code(segs[0]), r0, r1,
             flags.data_ptr(), 0, None]
     return Prepared(_lib.ar_twoshot_ag_copy, args, 8, "ar_twoshot_ag_copy", (segs, outs, flags))
@@ -330,6 +405,10 @@ def prepare_twoshot_ag_copy(segs, outs, flags, r0: int = 0, r1=None, numel=None)
 def prepare_ll_pack(srcs, wires, proto) -> Prepared:
     srcs = [_dev_tensor(t, "src") for t in srcs]
     wires = [_dev_tensor(t, "wire") for t in wires]
+    if len(wires) != len(srcs):
+        raise ValueError("need one wire per message")
+    _need_like(srcs, srcs[0].dtype, srcs[0].numel(), "every message")
+    _need_bytes(wires, ll_wire_bytes(proto, _nbytes(srcs[0])), "every wire")
     args = [_ptr_array([t.data_ptr() for t in srcs]), _ptr_array([t.data_ptr() for t in wires]), len(srcs),
             srcs[0].numel(), _dtype_code(srcs[0]), _PROTOS[proto], 0, None]
     return Prepared(_lib.ar_ll_pack, args, 6, "ar_ll_pack", (srcs, wires))
@@ -341,6 +420,8 @@ def prepare_ll_reduce(wires, out, flags, proto) -> Prepared:
     flags = _dev_tensor(flags, "flags")
     fn, name = ((_lib.ar_ll_reduce_unpack, "ar_ll_reduce_unpack") if _PROTOS[proto] == AR_PROTO_LL
                 else (_lib.ar_ll128_reduce_unpack, "ar_ll128_reduce_unpack"))
+    _need_bytes(wires, ll_wire_bytes(proto, _nbytes(out)), "every wire")
+    _need_bytes([flags], STATUS_BYTES, "the flag region")
     args = [_ptr_array([t.data_ptr() for t in wires]), len(wires), out.data_ptr(), out.numel(), _dtype_code(out), 0,
             flags.data_ptr(), None]
     return Prepared(fn, args, 5, name, (wires, out, flags))
@@ -355,6 +436,8 @@ def prepare_ll_allreduce(src, wires, out, flags, proto, me: int) -> Prepared:
     flags = _dev_tensor(flags, "flags")
     if src.dtype != out.dtype or src.numel() != out.numel():
         raise ValueError("src and out must share dtype and numel")
+    _need_bytes(wires, ll_wire_bytes(proto, _nbytes(src)), "every wire")
+    _need_bytes([flags], STATUS_BYTES, "the flag region")
     args = [src.data_ptr(), _ptr_array([t.data_ptr() for t in wires]), len(wires), int(me), out.data_ptr(),
             out.numel(), _dtype_code(out), _PROTOS[proto], 0, flags.data_ptr(), None]
     return Prepared(_lib.ar_ll_allreduce, args, 8, "ar_ll_allreduce", (src, wires, out, flags))
@@ -411,6 +494,12 @@ def ar_twoshot_ll(ins, segws, flags, step: int, r0: int = 0, r1=None, outs=None,
     """Two-shot under LL: reduce-scatter into LL segment wires for ranks
     [r0, r1); with ``outs`` also the all-gather in the same launch."""
     prepare_twoshot_ll(ins, segws, flags, r0, r1, outs)(step, stream)
+
+
+def ar_twoshot_ll128(ins, segws, flags, step: int, r0: int = 0, r1=None, outs=None, stream=None):
+    """Two-shot under LL128: reduce-scatter into LL128 segment wires for
+    ranks [r0, r1); with ``outs`` also the all-gather in the same launch."""
+    prepare_twoshot_ll128(ins, segws, flags, r0, r1, outs)(step, stream)
 
 
 def ar_ll_allreduce(src, wires, out, flags, proto, me: int, step: int, stream=None):

@@ -36,9 +36,10 @@ size_t elem_bytes(int dtype) { return dtype == AR_F32 ? 4 : 2; }
 // order: start and end for the one-shot, the push and the reduce-broadcast;
 // two more around the two-shot's barrier; none for LL / LL128, whose
 // receivers learn of arrival from the flags in the lines; start and end for
-// the two-shot under LL (it reads the peers' inputs; the barrier between its
-// phases is in the lines).
-constexpr double kSemaphoreSyncs[kSelNumAlgos] = {2.0, 4.0, 0.0, 0.0, 2.0, 2.0, 2.0};
+// the two-shot under LL and under LL128 (they read the peers' inputs; the
+// barrier between their phases is in the lines).
+constexpr double kSemaphoreSyncs[] = {2.0, 4.0, 0.0, 0.0, 2.0, 2.0, 2.0, 2.0};
+static_assert(kSelNumAlgos <= int(sizeof(kSemaphoreSyncs) / sizeof(kSemaphoreSyncs[0])), "one count per algorithm");
 
 // Measured one-GPU time of algo at `bytes` per rank: piecewise linear in the
 // size between grid points, flat below the first (launch-bound), and
@@ -96,10 +97,11 @@ size_t wire_bytes(int proto, size_t nbytes) {
 }
 
 // Shared checks of the two-shot entry points.
-// seg_mult: segment buffer bytes per segment data byte (1; 2 for LL wires).
+// seg_proto: the segment buffers hold the reduced data (-1) or an LL /
+// LL128 wire of it (AR_PROTO_LL, AR_PROTO_LL128).
 int twoshot_check(const void* const* in, const void* const* seg, const void* const* out, int n,
                   size_t numel, int dtype, int r0, int r1, const uint32_t* flags, uint32_t step,
-                  size_t seg_mult = 1) {
+                  int seg_proto = -1) {
     (void)step;  // 0 = the step id kept in the flag region (auto)
     if (!ranks_ok(n) || !dtype_ok(dtype) || numel == 0 || !seg || !flags) return AR_ERR_ARG;
     if (r0 < 0 || r1 > n || r0 >= r1) return AR_ERR_ARG;
@@ -125,7 +127,7 @@ int twoshot_check(const void* const* in, const void* const* seg, const void* con
     for (int j = 0; j < n; ++j) {
         // with an input present (reduce-scatter), seg[r0..r1) are written
         const bool written = in && j >= r0 && j < r1;
-        v.push_back(span(seg[j], m_bytes * seg_mult, written));
+        v.push_back(span(seg[j], seg_proto < 0 ? m_bytes : wire_bytes(seg_proto, m_bytes), written));
     }
     if (out)
         for (int r = r0; r < r1; ++r) v.push_back(span(out[r], S, true));
@@ -320,10 +322,20 @@ int ar_ll128_reduce_unpack(const void* const* wire, int n, void* out, size_t num
 int ar_twoshot_ll(const void* const* in, int n, void* const* segw, size_t numel, int dtype, int r0, int r1,
                   uint32_t* flags, uint32_t step, void* const* out, void* stream) {
     if (!in) return AR_ERR_ARG;  // step 0: auto ids, as ar_twoshot_rs
-    const int st = twoshot_check(in, segw, out, n, numel, dtype, r0, r1, flags, step, 2);
+    const int st = twoshot_check(in, segw, out, n, numel, dtype, r0, r1, flags, step, AR_PROTO_LL);
     if (st != AR_OK) return st;
     TwoShotRequest rq{in, segw, out, n, numel, dtype, r0, r1, flags, step, true, out != nullptr,
                       timeout_ticks(), true};
+    return hip_status(launch_twoshot(rq, static_cast<hipStream_t>(stream)));
+}
+
+int ar_twoshot_ll128(const void* const* in, int n, void* const* segw, size_t numel, int dtype, int r0, int r1,
+                     uint32_t* flags, uint32_t step, void* const* out, void* stream) {
+    if (!in) return AR_ERR_ARG;  // step 0: auto ids, as ar_twoshot_rs
+    const int st = twoshot_check(in, segw, out, n, numel, dtype, r0, r1, flags, step, AR_PROTO_LL128);
+    if (st != AR_OK) return st;
+    TwoShotRequest rq{in, segw, out, n, numel, dtype, r0, r1, flags, step, true, out != nullptr,
+                      timeout_ticks(), false, true};
     return hip_status(launch_twoshot(rq, static_cast<hipStream_t>(stream)));
 }
 
@@ -356,7 +368,7 @@ double ar_algo_cost_us(int algo, int n, size_t numel, int dtype, double sync_us)
         !(sync_us >= 0.0))
         return -1.0;
     const size_t es = elem_bytes(dtype);
-    if ((algo == AR_ALGO_TWOSHOT || algo == AR_ALGO_TWOSHOT_LL) &&
+    if ((algo == AR_ALGO_TWOSHOT || algo == AR_ALGO_TWOSHOT_LL || algo == AR_ALGO_TWOSHOT_LL128) &&
         !(numel % size_t(n) == 0 && (numel / size_t(n) * es) % 16 == 0))
         return -1.0;
     return share_us(algo, n, double(numel) * double(es)) + kSemaphoreSyncs[algo] * sync_us;

@@ -55,6 +55,13 @@ __device__ __forceinline__ void st_coherent(__amdgpu_buffer_rsrc_t r, uint32_t b
 __device__ __forceinline__ u32x4 ld_coherent(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
     return __builtin_amdgcn_raw_buffer_load_b128(r, int(byte_off), 0, kCachePolicySc1);
 }
+// The same for 8 bytes (an LL128 line's flag, or its last 8 data bytes).
+__device__ __forceinline__ void st_coherent8(__amdgpu_buffer_rsrc_t r, uint32_t byte_off, u32x2 v) {
+    __builtin_amdgcn_raw_buffer_store_b64(v, r, int(byte_off), 0, kCachePolicySc1);
+}
+__device__ __forceinline__ u32x2 ld_coherent8(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+    return __builtin_amdgcn_raw_buffer_load_b64(r, int(byte_off), 0, kCachePolicySc1);
+}
 // Wait until every memory operation this wavefront issued has completed
 // (s_waitcnt with all counters at zero).
 __device__ __forceinline__ void wait_stores() { __builtin_amdgcn_s_waitcnt(0); }

@@ -53,6 +53,7 @@ struct TwoShotRequest {
     bool do_rs, do_ag;
     uint64_t timeout_ticks;
     bool ll;  // segments are LL wires (4 data bytes + the step id per line); no slots
+    bool ll128 = false;  // segments are LL128 wires (120 data bytes + a 64-bit step id per line)
 };
 hipError_t launch_twoshot(const TwoShotRequest& rq, hipStream_t s);
 // All-gather on the copy engines: a one-workgroup slot wait, then n

@@ -58,6 +58,19 @@ namespace {
 constexpr int kBlock = 256;
 constexpr int kWavesPerBlock = kBlock / kWave;
 constexpr int kCopyUnroll = 4;
+// One-rank share kernel (explicit step ids): 64-vector units per all-gather
+// wavefront; reduce-scatter units in flight per wavefront by rank count
+// (NR loads each; more units per wavefront only where NR loads are few);
+// 4-wavefront workgroups from this many wavefronts per CU on, one-wavefront
+// workgroups below.  Measured on MI355X, n = 8 bf16: 4-wave workgroups
+// 6.07 us at 8 MiB per rank against 6.51 with one wave (dispatching 8192
+// one-wave workgroups alone costs 2.8 us), one wave 3.66 us at 1 MiB
+// against 3.83.  Reduce-scatter units in flight at 64 MiB per rank: n = 2,
+// 4 units 30.6 us against 36.2 with one; n = 8, 1 unit 31.4 against 32.6
+// with two; n = 16, 1 unit 32.1 against 38.8 with two.
+constexpr int kShareChunk = 1;
+constexpr int kShareWideMinWavesPerCu = 16;
+template <int NR> constexpr int share_rs_unroll() { return NR <= 4 ? 4 : (NR <= 6 ? 2 : 1); }
 
 // n / d for the launch-invariant divisors of the tiling (FastDiv, built on
 // the host by make_fastdiv): a multiply-high, an add and a shift.
@@ -79,6 +92,8 @@ struct TwoShotParams {
     FastDiv div_upt;      // units per tile
     FastDiv div_ktiles;   // tiles per segment
     FastDiv div_per_out;  // all-gather items per output rank
+    uint32_t ag_chunks;   // one-rank share kernel: all-gather chunks per segment
+    FastDiv div_chunks;   // ... as a divisor
 };
 
 template <typename T, int NR, int U, bool kLL>
@@ -411,6 +426,363 @@ __global__ __launch_bounds__(kBlock) void twoshot_kernel(TwoShotParams p) {
     }
 }
 
+// One GPU's share, [me, me+1) with an explicit step id: a grid sized to the
+// work, not a persistent one.  The all-gather copies only the peers'
+// segments (rank me's own comes from the reduce-scatter's registers), and
+// those were published by the peers' launches, not by this one, so no
+// wavefront of this launch waits on another and the grid may be as large as
+// the work; workgroups the device cannot hold yet simply start later.
+//   wavefronts [0, ktiles)     reduce-scatter: one tile of segment me each,
+//                              then its slot (after the tile's stores)
+//   wavefronts [ktiles, ...)   all-gather: one chunk of C
+//                              64-vector units of one peer segment each --
+//                              poll the chunk's slots, then every load of
+//                              the chunk, then its stores
+// No wavefront holds both kinds of work, so neither chain of memory round
+// trips (load, store, store wait, slot; slot, load, store) waits behind the
+// other.  The reduce-scatter wavefronts come first in the grid, so they are
+// dispatched first: a wavefront that waits on a late peer never keeps this
+// launch's own reduce-scatter (which that peer may be waiting for) from
+// starting.
+template <typename T, int NR, int C, int WB, int RU>
+__global__ __launch_bounds__(kWave * WB) void twoshot_share_kernel(TwoShotParams p) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(blockIdx.x * WB + threadIdx.x / kWave);
+    const uint32_t me = uint32_t(p.r0);
+    uint32_t* slots = p.flags + kStatusWords;
+    if (wave < p.ktiles) {
+        const uint32_t t0 = wave * p.tile;
+        const uint32_t tv = min(p.tile, p.mvec - t0);  // vectors in this tile
+        const uint32_t units = (tv + kWave - 1) / kWave;
+        const __amdgpu_buffer_rsrc_t rs = buffer_range(p.seg[me] + t0, tv * 16u);
+        u32x4* own = p.out[me] + size_t(me) * p.mvec + t0;
+        const size_t base = size_t(me) * p.mvec + t0;
+        const u32x4* in[NR];
+#pragma unroll
+        for (int i = 0; i < NR; ++i) in[i] = p.in[i];
+        // RU whole units in flight while at least that many are left (every
+        // load unconditional), then one unit at a time, the partial last one
+        // with its lanes past the tile clamped
+        const uint32_t whole = tv / kWave;
+        uint32_t u = 0;
+        for (; u + RU <= whole; u += RU) {
+            u32x4 x[RU][NR];
+#pragma unroll
+            for (int w = 0; w < RU; ++w)
+#pragma unroll
+                for (int i = 0; i < NR; ++i) x[w][i] = ld_stream(in[i] + base + (u + w) * kWave + uint32_t(lane));
+            __builtin_amdgcn_sched_barrier(0);  // every load ahead of the first add
+#pragma unroll
+            for (int w = 0; w < RU; ++w) {
+                Acc<T> acc;
+#pragma unroll
+                for (int i = 0; i < NR; ++i) acc.add(x[w][i]);
+                const u32x4 r = acc.result();
+                const uint32_t v = (u + w) * kWave + uint32_t(lane);
+                st_coherent(rs, v * 16u, r);
+                st_stream(own + v, r);
+            }
+        }
+        for (; u < units; ++u) {
+            const uint32_t v = u * kWave + uint32_t(lane);
+            const bool valid = v < tv;
+            const size_t src = base + (valid ? v : 0u);
+            u32x4 x[NR];
+#pragma unroll
+            for (int i = 0; i < NR; ++i) x[i] = ld_stream(in[i] + src);
+            __builtin_amdgcn_sched_barrier(0);  // every load ahead of the first add
+            Acc<T> acc;
+#pragma unroll
+            for (int i = 0; i < NR; ++i) acc.add(x[i]);
+            const u32x4 r = acc.result();
+            if (valid) {
+                st_coherent(rs, v * 16u, r);
+                st_stream(own + v, r);
+            }
+        }
+        // publish the tile once its segment stores have completed
+        wait_stores();
+        if (lane == 0) flag_store_relaxed(slots + me * kSlotsPerRank + wave, p.step);
+        return;
+    }
+    const uint32_t c = wave - p.ktiles;
+    const uint32_t jj = fdiv(c, p.div_chunks);
+    if (jj >= uint32_t(NR - 1)) return;  // past the last chunk (grid rounding)
+    const uint32_t k = c - jj * p.ag_chunks;
+    const uint32_t j = ag_source(jj, me, true);
+    const uint32_t v0 = k * uint32_t(C * kWave);
+    const uint32_t vend = min(v0 + uint32_t(C * kWave), p.mvec);
+    // the tiles the chunk covers (tiles are whole 64-vector units): at most C
+    const uint32_t tf = fdiv(k * uint32_t(C), p.div_upt);
+    const uint32_t tl = fdiv((vend - 1u) / kWave, p.div_upt);
+    const bool need = uint32_t(lane) <= tl - tf;
+    const uint32_t* slot = slots + j * kSlotsPerRank + tf + (need ? uint32_t(lane) : 0u);
+    uint32_t seen = need ? flag_load_relaxed(slot) : 0u;
+    const uint64_t t_start = now_ticks();
+    while (true) {
+        const uint64_t missing = ~wave_ballot(!need || seen >= p.step) & wave_exec();
+        if (missing == 0) break;
+        if (now_ticks() - t_start > p.timeout_ticks) {
+            const int bad_lane = __ffsll((unsigned long long)missing) - 1;
+            if (lane == 0) report_timeout(p.flags, 1u, j, tf + uint32_t(bad_lane));
+            return;  // skip the chunk's copies
+        }
+        __builtin_amdgcn_s_sleep(1);
+        if (need) seen = flag_load_relaxed(slot);
+    }
+    const __amdgpu_buffer_rsrc_t rs = buffer_range(p.seg[j] + v0, (vend - v0) * 16u);
+    u32x4 x[C];
+#pragma unroll
+    for (int u = 0; u < C; ++u) x[u] = ld_coherent(rs, (uint32_t(u * kWave) + uint32_t(lane)) * 16u);
+    u32x4* dst = p.out[me] + size_t(j) * p.mvec + v0;
+#pragma unroll
+    for (int u = 0; u < C; ++u) {
+        const uint32_t v = uint32_t(u * kWave) + uint32_t(lane);
+        if (v0 + v < vend) st_stream(dst + v, x[u]);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Two-shot under LL128: each reduced segment travels as an LL128 wire (128-
+// byte lines of 120 data bytes and a 64-bit flag, "集合通信：NCCL 的算法、协议与
+// 推理框架的定制 all-reduce", 协议 table).  The pages' LL128 rests on a 128-byte
+// line being written and read whole.  Here a line is written by 8 lanes and
+// read as separate 64-byte requests, so a reader that takes the data it
+// loaded beside a flag could see the flag of step s with data of step s-1.
+// The protocol is therefore made to hold by ordering:
+//   producer  the 120 data bytes of its lines (sc1 stores), a wait until
+//             those stores are complete, then each line's flag;
+//   consumer  the flags of its lines first, and the data only once every
+//             flag it needs is >= step.
+// A flag seen >= step then means that its line's data was complete before
+// the data loads were issued, also when the producer runs at the same time
+// (another workgroup of the same launch, or another GPU).  The price is two
+// dependent memory round trips on each side, as with the arrival slots;
+// what LL128 still changes is the flag granularity (one per line, not one
+// per tile).
+//
+// Work.  A segment of SB = m * element bytes is nlines = ceil(SB / 120)
+// lines; a unit is 8 lines (one wavefront: lane l holds wire bytes
+// [16 (l % 8), +16) of line l / 8, i.e. data bytes [120 line + 16 part, +16),
+// at part 7 8 data bytes and then the flag).  Items: reduce-scatter units of
+// segments r0..r1-1, then all-gather chunks of C units of every peer segment
+// for every output in [r0, r1).  With a grid of one wavefront per item (one
+// GPU's share with an explicit step id, or the reduce-scatter alone) each
+// wavefront has one item; otherwise the grid is persistent (no larger than
+// the device holds at once; with auto step ids the fixed grid of every auto
+// launch) and items are dealt round-robin, all-gather items starting after
+// the wavefronts with reduce-scatter items, as in the slot kernel.
+struct TwoShot128Params {
+    const uint8_t* in[kMaxRanks];
+    uint8_t* segw[kMaxRanks];
+    uint8_t* out[kMaxRanks];
+    uint32_t* flags;
+    uint64_t timeout_ticks;
+    size_t seg_bytes;    // SB, a multiple of 16
+    uint32_t nlines;     // lines per segment wire
+    uint32_t nunits;     // 8-line units per segment
+    uint32_t ag_chunks;  // all-gather chunks (C units) per segment
+    uint32_t step;
+    int auto_step;
+    int r0, r1;
+    int do_ag;
+    FastDiv div_units;    // nunits
+    FastDiv div_per_out;  // all-gather items per output rank: (n - 1) * ag_chunks
+    FastDiv div_chunks;   // ag_chunks
+};
+
+template <typename T, int NR>
+__device__ __forceinline__ void ll128_rs_unit(const TwoShot128Params& p, uint32_t r, uint32_t u, uint32_t lstep,
+                                              int lane) {
+    const uint32_t line = u * 8u + uint32_t(lane) / 8u;
+    const uint32_t part = uint32_t(lane) & 7u;
+    const bool has_line = line < p.nlines;
+    const size_t d = size_t(line) * 120u + size_t(part) * 16u;
+    // valid data bytes of this lane: 16, 8 (part 7, or the segment's end) or 0
+    const uint32_t db = part == 7u ? 8u : 16u;
+    const uint32_t vb = (has_line && d < p.seg_bytes) ? uint32_t(min(size_t(db), p.seg_bytes - d)) : 0u;
+    const size_t seg0 = size_t(r) * p.seg_bytes;
+    // 8-byte aligned (120 line + 16 part is a multiple of 8): two 8-byte loads
+    // per rank; a lane without data re-reads the segment's first bytes
+    const size_t lo = seg0 + (vb != 0u ? d : 0u);
+    const size_t hi = vb == 16u ? lo + 8u : lo;
+    u32x2 a[NR], b[NR];
+#pragma unroll
+    for (int i = 0; i < NR; ++i) {
+        a[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p.in[i] + lo));
+        b[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p.in[i] + hi));
+    }
+    __builtin_amdgcn_sched_barrier(0);  // every load ahead of the first add
+    Acc<T> acc;
+#pragma unroll
+    for (int i = 0; i < NR; ++i) acc.add(u32x4{a[i].x, a[i].y, b[i].x, b[i].y});
+    u32x4 v = acc.result();
+    if (vb < 16u) v.z = v.w = 0u;
+    if (vb == 0u) v.x = v.y = 0u;  // zero padding past the segment's end
+    // rank r's own segment of its output, straight from registers (fused form)
+    if (p.do_ag && vb != 0u) {
+        uint8_t* o = p.out[r] + seg0 + d;
+        __builtin_nontemporal_store(u32x2{v.x, v.y}, reinterpret_cast<u32x2*>(o));
+        if (vb == 16u) __builtin_nontemporal_store(u32x2{v.z, v.w}, reinterpret_cast<u32x2*>(o + 8));
+    }
+    const uint32_t lines_here = min(8u, p.nlines - min(p.nlines, u * 8u));
+    const __amdgpu_buffer_rsrc_t rs = buffer_range(p.segw[r] + size_t(u) * 1024u, lines_here * 128u);
+    if (has_line) {
+        if (part != 7u) st_coherent(rs, uint32_t(lane) * 16u, v);
+        else st_coherent8(rs, uint32_t(lane) * 16u, u32x2{v.x, v.y});
+    }
+    // every data byte of the unit's lines complete before any of their flags
+    wait_stores();
+    if (has_line && part == 7u) st_coherent8(rs, uint32_t(lane) * 16u + 8u, u32x2{lstep, 0u});
+}
+
+template <int NR, int C>
+__device__ __forceinline__ void ll128_ag_chunk(const TwoShot128Params& p, uint32_t ro, uint32_t j, uint32_t k,
+                                               uint32_t want, int lane) {
+    const uint32_t u0 = k * uint32_t(C);
+    const uint32_t line0 = u0 * 8u;
+    const uint32_t nl = min(uint32_t(8 * C), p.nlines - line0);  // lines of this chunk
+    const __amdgpu_buffer_rsrc_t rs = buffer_range(p.segw[j] + size_t(line0) * 128u, nl * 128u);
+    // the chunk's flags: lane l < nl polls line line0 + l
+    const bool need = uint32_t(lane) < nl;
+    const uint32_t foff = uint32_t(lane) * 128u + 120u;
+    uint32_t seen = need ? ld_coherent8(rs, foff).x : 0u;
+    const uint64_t t_start = now_ticks();
+    while (true) {
+        const uint64_t missing = ~wave_ballot(!need || seen >= want) & wave_exec();
+        if (missing == 0) break;
+        if (now_ticks() - t_start > p.timeout_ticks) {
+            const int bad = __ffsll((unsigned long long)missing) - 1;
+            if (lane == 0) report_timeout(p.flags, 1u, j, line0 + uint32_t(bad));
+            return;  // skip the chunk's copies
+        }
+        __builtin_amdgcn_s_sleep(1);
+        if (need) seen = ld_coherent8(rs, foff).x;
+    }
+    // every flag seen: now the data (out-of-range loads read zero)
+    u32x4 x[C];
+#pragma unroll
+    for (int c = 0; c < C; ++c) x[c] = ld_coherent(rs, uint32_t(c) * 1024u + uint32_t(lane) * 16u);
+    const uint32_t part = uint32_t(lane) & 7u;
+    const uint32_t db = part == 7u ? 8u : 16u;
+    uint8_t* o = p.out[ro] + size_t(j) * p.seg_bytes;
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+        const uint32_t line = line0 + uint32_t(c) * 8u + uint32_t(lane) / 8u;
+        const size_t d = size_t(line) * 120u + size_t(part) * 16u;
+        if (line < p.nlines && d < p.seg_bytes) {
+            const uint32_t vb = uint32_t(min(size_t(db), p.seg_bytes - d));
+            __builtin_nontemporal_store(u32x2{x[c].x, x[c].y}, reinterpret_cast<u32x2*>(o + d));
+            if (vb == 16u) __builtin_nontemporal_store(u32x2{x[c].z, x[c].w}, reinterpret_cast<u32x2*>(o + d + 8));
+        }
+    }
+}
+
+template <typename T, int NR, int C, int WB>
+__global__ __launch_bounds__(kWave * WB) void twoshot_ll128_kernel(TwoShot128Params p) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(blockIdx.x * WB + threadIdx.x / kWave);
+    const uint32_t nwaves = gridDim.x * WB;
+    const uint32_t R = uint32_t(p.r1 - p.r0);
+    // auto step ids: lane l < R holds this wavefront's epoch copy of rank r0 + l
+    uint32_t* epoch = p.flags + kStatusWords + NR * kSlotsPerRank + size_t(wave) * NR + p.r0;
+    uint32_t epoch_lane = 0;
+    if (p.auto_step && uint32_t(lane) < R) epoch_lane = flag_load_relaxed(epoch + lane);
+    const uint32_t rs_items = R * p.nunits;
+    for (uint32_t it = wave; it < rs_items; it += nwaves) {
+        const uint32_t rr = fdiv(it, p.div_units);
+        const uint32_t r = uint32_t(p.r0) + rr;
+        const uint32_t u = it - rr * p.nunits;
+        const uint32_t lstep = p.auto_step ? __shfl(epoch_lane + 1u, int(rr)) : p.step;
+        ll128_rs_unit<T, NR>(p, r, u, lstep, lane);
+    }
+    if (p.do_ag) {
+        const uint32_t per_out = uint32_t(NR - 1) * p.ag_chunks;
+        const uint32_t items = R * per_out;
+        const uint32_t rs_busy = min(rs_items, nwaves);
+        const uint32_t ag_wave = wave >= rs_busy ? wave - rs_busy : wave + (nwaves - rs_busy);
+        for (uint32_t it = ag_wave; it < items; it += nwaves) {
+            const uint32_t oo = fdiv(it, p.div_per_out);
+            const uint32_t ro = uint32_t(p.r0) + oo;
+            const uint32_t rem = it - oo * per_out;
+            const uint32_t jj = fdiv(rem, p.div_chunks);
+            const uint32_t j = ag_source(jj, ro, true);
+            const uint32_t k = rem - jj * p.ag_chunks;
+            // the output rank's step id (its reduce-scatter in this launch, for
+            // auto ids: every rank's epoch moves in step)
+            const uint32_t want = p.auto_step ? __shfl(epoch_lane + 1u, int(oo)) : p.step;
+            ll128_ag_chunk<NR, C>(p, ro, j, k, want, lane);
+        }
+    }
+    if (p.auto_step && uint32_t(lane) < R) flag_store_relaxed(epoch + lane, epoch_lane + 1u);
+}
+
+// all-gather chunk of the LL128 two-shot: 8-line units per wavefront
+constexpr int kLL128Chunk = 1;
+
+template <typename T, int NR>
+hipError_t launch_ll128(const TwoShotRequest& rq, hipStream_t s) {
+    DeviceInfo info;
+    hipError_t e = device_info(&info);
+    if (e != hipSuccess) return e;
+    TwoShot128Params p{};
+    for (int r = 0; r < NR; ++r) {
+        p.in[r] = static_cast<const uint8_t*>(rq.in[r]);
+        p.segw[r] = static_cast<uint8_t*>(rq.seg[r]);
+        p.out[r] = (rq.out && r >= rq.r0 && r < rq.r1) ? static_cast<uint8_t*>(rq.out[r]) : nullptr;
+    }
+    p.seg_bytes = rq.numel / size_t(NR) * size_t(elem<T>::bytes);
+    p.nlines = uint32_t((p.seg_bytes + 119) / 120);
+    p.nunits = (p.nlines + 7u) / 8u;
+    p.ag_chunks = (p.nunits + uint32_t(kLL128Chunk) - 1) / uint32_t(kLL128Chunk);
+    p.flags = rq.flags;
+    p.timeout_ticks = rq.timeout_ticks;
+    p.step = rq.step;
+    p.auto_step = rq.step == 0;
+    p.r0 = rq.r0;
+    p.r1 = rq.r1;
+    p.do_ag = rq.do_ag;
+    p.div_units = make_fastdiv(p.nunits);
+    p.div_per_out = make_fastdiv(uint32_t(NR - 1) * p.ag_chunks);
+    p.div_chunks = make_fastdiv(p.ag_chunks);
+    const uint32_t R = uint32_t(rq.r1 - rq.r0);
+    const uint64_t items = uint64_t(R) * p.nunits + (rq.do_ag ? uint64_t(R) * (NR - 1) * p.ag_chunks : 0u);
+    if (p.auto_step) {
+        // the fixed grid of every auto launch on a flag region (two 256-lane
+        // workgroups per CU), so each wavefront's epoch copies see every call
+        const uint32_t grid = uint32_t(info.cu_count) * 2u;
+        if (grid * 4u > uint32_t(kEpochCopies)) return hipErrorInvalidConfiguration;
+        hipLaunchKernelGGL((twoshot_ll128_kernel<T, NR, kLL128Chunk, 4>), dim3(grid), dim3(kBlock), 0, s, p);
+        return hipGetLastError();
+    }
+    if (!rq.do_ag || R == 1) {
+        // nothing in this launch waits on another wavefront of it: one
+        // wavefront per item, four-wavefront workgroups for large grids
+        if (items >= uint64_t(kShareWideMinWavesPerCu) * uint64_t(info.cu_count)) {
+            hipLaunchKernelGGL((twoshot_ll128_kernel<T, NR, kLL128Chunk, 4>), dim3(uint32_t((items + 3) / 4)),
+                               dim3(kBlock), 0, s, p);
+        } else {
+            hipLaunchKernelGGL((twoshot_ll128_kernel<T, NR, kLL128Chunk, 1>), dim3(uint32_t(items)), dim3(kWave),
+                               0, s, p);
+        }
+        return hipGetLastError();
+    }
+    // consumers wait on producers of the same launch: a persistent grid
+    static int per_cu = -1;
+    static hipError_t occ_err = hipSuccess;
+    static std::once_flag once;
+    auto kern = twoshot_ll128_kernel<T, NR, kLL128Chunk, 4>;
+    std::call_once(once, [&] { occ_err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, kBlock, 0); });
+    if (occ_err != hipSuccess) return occ_err;
+    if (per_cu < 1) return hipErrorLaunchOutOfResources;
+    const uint32_t resident = uint32_t(info.cu_count) * uint32_t(per_cu < 2 ? per_cu : 2);
+    uint64_t grid = (items + 3) / 4;
+    if (grid > resident) grid = resident;
+    if (grid < 1) grid = 1;
+    hipLaunchKernelGGL(kern, dim3(uint32_t(grid)), dim3(kBlock), 0, s, p);
+    return hipGetLastError();
+}
+
 // The barrier of a copy-engine all-gather: one workgroup waits until the
 // arrival slot of every tile of every segment is >= the step id (the
 // largest of the ranks' in [r0, r1) in auto mode, where wavefront 0's epoch
@@ -492,6 +864,24 @@ hipError_t launch_k(const TwoShotRequest& rq, hipStream_t s) {
 
     auto kern = twoshot_kernel<T, NR, U, kLL>;
     const uint32_t R = uint32_t(rq.r1 - rq.r0);
+    if constexpr (!kLL) {
+        if (!p.auto_step && R == 1 && rq.do_rs && rq.do_ag) {
+            // one GPU's share: a grid of one wavefront per reduce-scatter
+            // tile plus one per all-gather chunk
+            p.ag_chunks = (p.mvec + uint32_t(kShareChunk * kWave) - 1) / uint32_t(kShareChunk * kWave);
+            p.div_chunks = make_fastdiv(p.ag_chunks);
+            const uint64_t waves = uint64_t(p.ktiles) + uint64_t(NR - 1) * p.ag_chunks;
+            constexpr int RU = share_rs_unroll<NR>();
+            if (waves >= uint64_t(kShareWideMinWavesPerCu) * uint64_t(info.cu_count)) {
+                hipLaunchKernelGGL((twoshot_share_kernel<T, NR, kShareChunk, 4, RU>), dim3(uint32_t((waves + 3) / 4)),
+                                   dim3(kWave * 4), 0, s, p);
+            } else {
+                hipLaunchKernelGGL((twoshot_share_kernel<T, NR, kShareChunk, 1, RU>), dim3(uint32_t(waves)),
+                                   dim3(kWave), 0, s, p);
+            }
+            return hipGetLastError();
+        }
+    }
     if (p.auto_step) {
         // every auto launch on a flag region uses the same grid, two
         // workgroups per CU (resident at once: the occupancy of every
@@ -533,6 +923,7 @@ hipError_t launch_k(const TwoShotRequest& rq, hipStream_t s) {
 
 template <typename T, int NR>
 hipError_t launch_t(const TwoShotRequest& rq, hipStream_t s) {
+    if (rq.ll128) return launch_ll128<T, NR>(rq, s);
     return rq.ll ? launch_k<T, NR, true>(rq, s) : launch_k<T, NR, false>(rq, s);
 }
 

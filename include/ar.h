@@ -297,11 +297,40 @@ int ar_ll_allreduce(const void* src, void* const* wire, int n, int me, void* out
  * The result is bit for bit that of ar_twoshot_rs and ar_oneshot.  Sizes,
  * divisibility and errors as ar_twoshot_rs; asynchronously AR_ERR_TIMEOUT
  * (phase AR_PHASE_TWOSHOT_AG, segment and tile of a line that stayed
- * behind).  LL only: LL128 lines are read as separate 64-byte requests, so
- * a flag seen at the end of a line says nothing of the data at its start
- * while another wavefront of the same launch may still be writing it. */
+ * behind).  A line's 4 data bytes and its flag are one 8-byte word, written
+ * and read whole, so a reader never sees a flag without its data: this
+ * holds against producers that run at the same time (another workgroup of
+ * the same launch, or another GPU). */
 int ar_twoshot_ll(const void* const* in, int n, void* const* segw, size_t numel, int dtype, int r0, int r1,
                   uint32_t* flags, uint32_t step, void* const* out, void* stream);
+
+/* Two-shot under the LL128 protocol ([NCCL] 算法, two-shot, with the 协议
+ * table's LL128 lines): as ar_twoshot_ll, with each reduced segment written
+ * as an LL128 wire -- 128-byte lines of 120 data bytes (zero past the
+ * segment's end) and a 64-bit flag, ar_ll_wire_bytes(AR_PROTO_LL128,
+ * m * element size) bytes per segment.  The pages' LL128 relies on a
+ * 128-byte line being written and read whole; here a line is written by 8
+ * lanes and read as separate 64-byte requests, so the protocol is kept by
+ * ordering instead: the producer writes a line's 120 data bytes, waits until
+ * they are complete, then writes its flag; the all-gather first polls the
+ * flags of the lines it copies and loads their data only after every flag
+ * is >= step.  The result is therefore correct also when the producers run
+ * at the same time as the consumer (another workgroup of the same launch,
+ * or another GPU), at the cost of a second dependent memory round trip per
+ * line, as with the arrival slots of ar_twoshot_rs.
+ *  segw  : n LL128 segment wires (segw[r0..r1) written, all n read with out),
+ *          zeroed once before first use.
+ *  step  : 1..2^32-1, increasing from call to call; or 0 (auto), with the
+ *          epochs, fixed grid and rules of ar_twoshot_rs's auto ids.
+ *  out   : NULL for the reduce-scatter only; else the fused launch: one
+ *          wavefront per item when r1 - r0 == 1 with an explicit step (no
+ *          wave of the launch waits on another), a persistent grid otherwise.
+ * The result is bit for bit that of ar_twoshot_rs and ar_oneshot.  Sizes,
+ * divisibility and errors as ar_twoshot_rs; asynchronously AR_ERR_TIMEOUT
+ * (phase AR_PHASE_TWOSHOT_AG, segment and line of a line that stayed
+ * behind). */
+int ar_twoshot_ll128(const void* const* in, int n, void* const* segw, size_t numel, int dtype, int r0, int r1,
+                     uint32_t* flags, uint32_t step, void* const* out, void* stream);
 
 /* Algorithm selection from measured costs ([NCCL] 算法 and 协议: no
  * algorithm or protocol is best at every size, so the choice goes by message
@@ -313,7 +342,7 @@ int ar_twoshot_ll(const void* const* in, int n, void* const* segw, size_t numel,
  *    two-shot; one rank's LL / LL128 send and receive in one launch
  *    (ar_ll_allreduce); one rank's push
  *    plus its one-shot over its staging slots; one rank's reduce-broadcast
- *    share; one rank's fused two-shot under LL), tabulated for
+ *    share; one rank's fused two-shot under LL and under LL128), tabulated for
  *    n = 2..16 over 16 KiB..64 MiB per rank, interpolated linearly in the
  *    size, flat below the grid and extended with the last slope above it;
  *  - k is the number of cross-GPU semaphore synchronisations per call, the
@@ -321,8 +350,9 @@ int ar_twoshot_ll(const void* const* in, int n, void* const* segw, size_t numel,
  *    for the two-shot; 协议 names the semaphore as alpha's main source),
  *    2 for the push and the reduce-broadcast (start and end, as the one-shot;
  *    the broadcast has no barrier between its phases), 2 for the two-shot
- *    under LL (its reduce-scatter still reads the peers' inputs, so start and
- *    end stay; the barrier between the phases travels in the lines), and 0
+ *    under LL and under LL128 (their reduce-scatter still reads the peers'
+ *    inputs, so start and end stay; the barrier between the phases travels
+ *    in the lines), and 0
  *    for LL / LL128, whose flags travel with the data ([NCCL] 协议);
  *  - sync_us >= 0 is the cost of one such synchronisation on the caller's
  *    interconnect (0 when the ranks share one GPU).
@@ -337,7 +367,8 @@ typedef enum {
     AR_ALGO_LL128 = 3,   /* ar_ll_allreduce, LL128 (or ar_ll_pack + ar_ll128_reduce_unpack) */
     AR_ALGO_PUSH = 4,    /* ar_push into the staging slots + ar_oneshot over them */
     AR_ALGO_BCAST = 5,   /* ar_reduce_bcast */
-    AR_ALGO_TWOSHOT_LL = 6 /* ar_twoshot_ll with out (fused) */
+    AR_ALGO_TWOSHOT_LL = 6, /* ar_twoshot_ll with out (fused) */
+    AR_ALGO_TWOSHOT_LL128 = 7 /* ar_twoshot_ll128 with out (fused) */
 } ar_algo;
 double ar_algo_cost_us(int algo, int n, size_t numel, int dtype, double sync_us);
 int ar_select_algo(int n, size_t numel, int dtype, double sync_us);

@@ -269,6 +269,10 @@ def test_accounting_matches_oracle_model():
             assert accounting.twoshot(n, S, 1) == model.hbm_bytes("twoshot_share", S, n)
             assert accounting.twoshot(n, S, n) == model.hbm_bytes("twoshot_full", S, n)
             assert accounting.twoshot_ll(n, S, 1) == model.hbm_bytes("twoshot_ll_share", S, n)
+            assert accounting.twoshot_ll(n, S, 1, "ll128") == model.hbm_bytes("twoshot_ll128_share", S, n)
+            # the fused kernel's own count: the rank's own segment is never read back
+            kr, kw = accounting.twoshot_kernel(n, S, 1)
+            assert (kr + S // n, kw) == accounting.twoshot(n, S, 1)
             for proto in ("ll", "ll128"):
                 assert accounting.ll_pack(proto, S) == model.hbm_bytes("ll_pack", S, n, proto)
                 assert accounting.ll_reduce(proto, n, S) == model.hbm_bytes("ll_reduce", S, n, proto)
@@ -300,9 +304,9 @@ def test_selector_cost_model_terms():
     import torch
     bf = torch.bfloat16
     # sync terms: 2 per call for the one-shot, 4 for the two-shot, none for LL / LL128,
-    # 2 for the two-shot under LL (start and end; its barrier is in the lines)
-    assert len(car.ALGOS) == 7
-    for a, k in zip(car.ALGOS, (2, 4, 0, 0, 2, 2, 2)):
+    # 2 for the two-shot under LL and LL128 (start and end; the barrier is in the lines)
+    assert len(car.ALGOS) == 8
+    for a, k in zip(car.ALGOS, (2, 4, 0, 0, 2, 2, 2, 2)):
         assert car.algo_cost_us(a, 8, 1 << 20, bf, 10.0) == pytest.approx(car.algo_cost_us(a, 8, 1 << 20, bf, 0.0) + 10 * k)
     # flat below the grid, increasing in size above it, linear beyond the last point
     for a in car.ALGOS:
@@ -393,3 +397,39 @@ def test_overlap_check_finds_one_planted_overlap_anywhere():
             other = rnd.choice([d for i, d in enumerate(dst) if i != k])
             dst[k] = other + 16 * rnd.randint(0, S // 16 - 1)  # sharing bytes with another destination
         assert L.ar_push(arr(*src), nsrc, arr(*dst), ndst, S // 2, 1, NUL) == car.AR_ERR_ALIAS, trial
+
+
+# ---- size checks of the binding (host logic, CPU tensors) ----------------------
+def test_size_checks_reject_undersized_buffers():
+    """The C ABI sees only pointers, so the binding checks every buffer's size
+    before a call enqueues anything: undersized segments, segment wires, flag
+    regions and wrong-sized outputs raise ValueError; exact sizes pass."""
+    import torch
+
+    n, m = 8, 8 * 100
+    numel = n * m
+    bf = torch.bfloat16
+    ins = [torch.zeros(numel, dtype=bf) for _ in range(n)]
+    segs = [torch.zeros(m, dtype=bf) for _ in range(n)]
+    outs = [torch.zeros(numel, dtype=bf)] + [None] * (n - 1)
+    flags = torch.zeros(car.flag_bytes(n) // 4, dtype=torch.int32)
+    car._twoshot_sizes(ins, segs, flags, outs)  # exact sizes
+    with pytest.raises(ValueError):
+        car._twoshot_sizes(ins, segs[:-1] + [torch.zeros(m - 8, dtype=bf)], flags, outs)
+    with pytest.raises(ValueError):
+        car._twoshot_sizes(ins, segs, flags[:-1], outs)
+    with pytest.raises(ValueError):
+        car._twoshot_sizes(ins, segs, flags, [torch.zeros(numel - 1, dtype=bf)] + outs[1:])
+    with pytest.raises(ValueError):
+        car._twoshot_sizes(ins[:-1] + [torch.zeros(numel, dtype=torch.float32)], segs, flags, outs)
+    for proto in ("ll", "ll128"):
+        W = car.ll_wire_bytes(proto, m * 2)
+        wires = [torch.zeros(W, dtype=torch.uint8) for _ in range(n)]
+        car._twoshot_sizes(ins, wires, flags, outs, seg_proto=proto)
+        with pytest.raises(ValueError):
+            car._twoshot_sizes(ins, wires[:-1] + [torch.zeros(W - 1, dtype=torch.uint8)], flags, outs,
+                               seg_proto=proto)
+    # LL128 wires are larger than LL wires of the same message only past 120 bytes
+    assert car.ll_wire_bytes("ll128", m * 2) < car.ll_wire_bytes("ll", m * 2)
+    with pytest.raises(ValueError):
+        car._need_bytes([torch.zeros(127, dtype=torch.uint8)], car.STATUS_BYTES, "flags")

@@ -24,8 +24,13 @@ def test_step_bytes_are_one_gpus_algorithmic_bytes():
     n, S = 8, 128 << 10
     per = bench.step_bytes(n, S)
     assert per["oneshot"] == n * S + S
-    # one rank's fused two-shot: S read for its segment, (n-1)/n S of peers' segments; S/n + S written
-    assert per["twoshot"] == S + (n - 1) * (S // n) + S // n + S
+    # one rank's two-shot: S read by the reduce-scatter (its segment of n inputs), S by the
+    # all-gather (all n segments); S/n (its segment) + S (its output) written
+    assert per["twoshot"] == 2 * S + S // n + S
+    # under LL / LL128 every segment is a wire of its S/n bytes
+    for p in ("ll", "ll128"):
+        w = acc.wire_bytes(p, S // n)
+        assert per["twoshot_" + p] == S + n * w + w + S
     W1, W2 = acc.wire_bytes("ll", S), acc.wire_bytes("ll128", S)
     assert W1 == 2 * S and W2 == 128 * -(-S // 120)
     # LL / LL128 in one launch: own message read, own wire written, n-1 peers' wires read, output written
@@ -37,13 +42,36 @@ def test_step_bytes_are_one_gpus_algorithmic_bytes():
 
 
 def test_workloads_are_the_pages_message_shapes():
-    n, dt, numel, _ = bench.WORKLOADS["decode"]
-    assert (n, dt, numel) == (8, "bf16", 8 * 8192)  # [8 tokens x hidden 8192]
-    n, dt, numel, _ = bench.WORKLOADS["prefill"]
-    assert (n, dt, numel) == (8, "bf16", 512 * 8192)
+    n, dt, numel, k, _ = bench.WORKLOADS["decode"]
+    assert (n, dt, numel, k) == (8, "bf16", 8 * 8192, "oneshot")  # [8 tokens x hidden 8192]
+    n, dt, numel, k, _ = bench.WORKLOADS["prefill"]
+    assert (n, dt, numel, k) == (8, "bf16", 512 * 8192, "twoshot")
     for w, bytes_per_rank in (("ll64k", 64 << 10), ("ll1m", 1 << 20)):
-        n, dt, numel, _ = bench.WORKLOADS[w]
+        n, dt, numel, _, _ = bench.WORKLOADS[w]
         assert dt == "f32" and numel * 4 == bytes_per_rank
+
+
+def test_default_workload_is_the_two_shot_prefill_message():
+    """With no flags bench.py measures the n = 8, bf16 [512 x 8192] message
+    (8 MiB per rank), and the roofline is the two-shot's."""
+    import inspect
+
+    src = inspect.getsource(bench.main)
+    assert 'ap.add_argument("--workload", default="prefill"' in src
+    assert bench.WORKLOADS["prefill"][3] == "twoshot"
+    assert bench.KERNEL_LAUNCHES >= 200 and bench.KERNEL_REPLAYS >= 3
+    assert bench.CURVE_SIZES == [128 << 10, 1 << 20, 8 << 20, 64 << 20]
+
+
+def test_oracle_step_bytes_are_what_the_oracle_moves():
+    from oracle import model
+
+    n, S = 8, 1 << 20
+    want = (n + 1) * S + 2 * n * S + (n + 1) * S
+    for p in ("ll", "ll128"):
+        W = model.ll_wire_bytes(p, S)
+        want += S + W + n * W + S
+    assert bench.oracle_step_bytes(n, S) == want
 
 
 def test_store_path_accounting():

@@ -110,9 +110,15 @@ def test_missing_peer_is_a_reported_timeout():
 def test_synchronous_errors():
     n = 4
     rk = Ranks(n, 4 * 8 * 100, "bf16", config=740)
-    with pytest.raises(car.ArError) as e:
+    # an output too small for the all-gather is refused before anything runs
+    with pytest.raises(ValueError):
         car.ar_twoshot_ag_copy(rk.segs, [rk.segs[0]] + rk.outs[1:], rk.flags, 1)
-    assert e.value.code in (car.AR_ERR_ALIAS, car.AR_ERR_ARG)
+    # an output of the right size that overlaps a segment
+    big = torch.zeros(rk.outs[0].numel(), dtype=rk.outs[0].dtype, device="cuda")
+    segs = [big[:rk.segs[0].numel()]] + rk.segs[1:]
+    with pytest.raises(car.ArError) as e:
+        car.ar_twoshot_ag_copy(segs, [big] + rk.outs[1:], rk.flags, 1)
+    assert e.value.code == car.AR_ERR_ALIAS
     with pytest.raises(car.ArError) as e:
         car.ar_twoshot_ag_copy(rk.segs, rk.outs, rk.flags, 1, r0=3, r1=3)
     assert e.value.code == car.AR_ERR_ARG

@@ -1,10 +1,11 @@
 """GPU parity of exactly what bench.py times: for each of its workloads
-(decode: n = 8 bf16 [8 x 8192]; prefill: n = 8 bf16 [512 x 8192]; ll64k and
-ll1m: n = 8 fp32, 64 KiB and 1 MiB per rank), the step's four launches --
-one-shot, rank 0's fused two-shot, and rank 0's LL and LL128 each sent and
-received in one launch -- on bench.py's own buffer sets, with the peers'
-shares published the way bench.py publishes them, over several steps.
-Every output is compared with the oracle element by element."""
+(prefill: n = 8 bf16 [512 x 8192]; decode: n = 8 bf16 [8 x 8192]; ll64k and
+ll1m: n = 8 fp32, 64 KiB and 1 MiB per rank), the step's six launches --
+one-shot; rank 0's fused two-shot with slots, with LL segments and with LL128
+segments; rank 0's LL and LL128 each sent and received in one launch -- on
+bench.py's own rotated buffer sets, with the peers' shares published the way
+bench.py publishes them, over several steps.  Every output is compared with
+the oracle element by element."""
 from __future__ import annotations
 
 import numpy as np
@@ -23,8 +24,9 @@ car = pytest.importorskip("custom_all_reduce_amd")
 
 @pytest.mark.parametrize("workload", sorted(bench.WORKLOADS))
 def test_bench_step_matches_the_oracle(workload):
-    n, dt_name, numel, _ = bench.WORKLOADS[workload]
-    dt = torch.float32 if dt_name == "f32" else torch.bfloat16
+    import numpy
+
+    n, dt_name, numel, _, _ = bench.WORKLOADS[workload]
     host = synth.rank_inputs(n, numel, dt_name, "normal", config=1)  # bench.py's inputs
     if dt_name == "f32":
         src = [torch.from_numpy(a).cuda() for a in host]
@@ -33,21 +35,36 @@ def test_bench_step_matches_the_oracle(workload):
     want = oracle_bits(oracle.oneshot(host, dt_name))
     car.set_poll_timeout_ns(50_000_000)
     try:
-        sets = [bench.BufferSet(torch, car, src, n, dt, numel) for _ in range(2)]
-        flags = car.new_flags(n)
-        calls = [bench.step_calls(car, b, flags) for b in sets]
-        for b in sets:
-            bench.publish_peers(car, b, flags)
-        for step in range(1, 5):
-            b = sets[step % 2]
-            for t in (b.out, b.outs[bench.ME], b.out_ll, b.out_128):
+        rig = bench.Rig(torch, car, numpy, n, dt_name, numel, 0, src=src)  # two sets
+        assert rig.nsets == 2
+        for i in range(4):
+            b = rig.sets[i % 2]
+            for t in b.step_outputs():
                 t.zero_()
-            bench.run_step(calls[step % 2], step)
+            rig.run_step(i, rig.next_steps(1))
             torch.cuda.synchronize()
-            car.raise_on_status(flags, f"{workload} step {step}")
-            for name, t in (("one-shot", b.out), ("two-shot", b.outs[bench.ME]), ("LL", b.out_ll),
-                            ("LL128", b.out_128)):
+            car.raise_on_status(rig.flags, f"{workload} step {i}")
+            for name, t in zip(bench.KERNELS, b.step_outputs()):
                 got = bits(t)
-                assert np.array_equal(got, want), f"{workload} step {step} {name}: " + first_mismatch(got, want)
+                assert np.array_equal(got, want), f"{workload} step {i} {name}: " + first_mismatch(got, want)
     finally:
         car.set_poll_timeout_ns(0)
+
+
+def test_per_kernel_timing_graph_keeps_the_outputs():
+    """A kernel's timing graph (launches over the rotated sets, replayed
+    several times with the same step ids) leaves correct outputs."""
+    import numpy
+
+    rig = bench.Rig(torch, car, numpy, 8, "bf16", 8 * 4096, 0)
+    ref = torch.empty(8 * 4096, dtype=torch.bfloat16, device="cuda")
+    car.ar_oneshot(rig.sets[0].ins, ref)
+    for name in bench.KERNELS:
+        for b in rig.sets:
+            for t in b.step_outputs():
+                t.zero_()
+        us, reps = rig.time_kernel(name, launches=8, replays=3)
+        assert us > 0 and len(reps) == 3
+        k = bench.KERNELS.index(name)
+        for b in rig.sets:
+            assert torch.equal(b.step_outputs()[k].view(torch.int16), ref.view(torch.int16)), name

@@ -82,3 +82,46 @@ def test_receiver_polls_until_the_host_writes_the_lines(proto, dt):
         car.set_poll_timeout_ns(old)
     assert car.read_status(flags)[0] == 0
     assert np.array_equal(bits(out), want)
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_twoshot_ll128_share_waits_for_the_host_written_peer_segments(dt):
+    """Rank 0's two-shot under LL128 with the peers' segment wires in pinned
+    host memory, all flags 0 at launch: the all-gather polls the flags; the
+    host then writes every peer line's data and afterwards its flag.  The
+    output must be the oracle's all-reduce, and rank 0's own segment wire the
+    oracle's LL128 packing of its segment."""
+    n, es = 4, 4 if dt == "f32" else 2
+    m = (16 // es) * 150  # 150 vectors: 20 lines per segment, a partial last line
+    numel = n * m
+    host = synth.rank_inputs(n, numel, dt, "normal", config=311)
+    segs, _ = oracle.twoshot(host, dt)
+    want = oracle_bits(oracle.oneshot(host, dt))
+    W = car.ll_wire_bytes("ll128", m * es)
+    ins = [to_dev(a) for a in host]
+    own = torch.zeros(W, dtype=torch.uint8, device="cuda")
+    bufs = [None] + [pinned_device_view(W) for _ in range(1, n)]
+    out = torch.empty(numel, dtype=ins[0].dtype, device="cuda")
+    flags = car.new_flags(n)
+    torch.cuda.synchronize()
+    P = ctypes.c_void_p
+    in_p = (P * n)(*[t.data_ptr() for t in ins])
+    seg_p = (P * n)(own.data_ptr(), *[b[2] for b in bufs[1:]])
+    out_p = (P * n)(out.data_ptr(), *([None] * (n - 1)))
+    old = car.get_poll_timeout_ns()
+    car.set_poll_timeout_ns(3_000_000_000)
+    try:
+        st = P(torch.cuda.current_stream().cuda_stream)
+        rc = car.lib.ar_twoshot_ll128(in_p, n, seg_p, numel, 0 if dt == "f32" else 1, 0, 1, flags.data_ptr(), 7,
+                                      out_p, st)
+        assert rc == 0
+        time.sleep(0.05)  # the all-gather is polling now
+        for j in range(1, n):
+            t, off, _ = bufs[j]
+            write_lines(t.numpy()[off:], "ll128", segs[j], 7)
+        torch.cuda.synchronize()
+    finally:
+        car.set_poll_timeout_ns(old)
+    assert car.read_status(flags)[0] == 0
+    assert np.array_equal(bits(out), want)
+    assert np.array_equal(bits(own), oracle.ll_pack("ll128", segs[0], 7))

@@ -310,3 +310,29 @@ def test_largest_step_id_then_reset_and_restart():
     car.raise_on_status(rk.flags)
     for r in range(n):
         assert np.array_equal(bits(rk.outs[r]), want)
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("n", [2, 3, 8, 16])
+@pytest.mark.parametrize("seg_vectors", [1, 63, 64, 65, 255, 257, 64 * 1024 + 64 * 3, 200003])
+def test_share_tilings(n, dt, seg_vectors):
+    """One rank's share (grid sized to the work: a wavefront per reduce-scatter
+    tile, one per all-gather chunk) at segment sizes around the unit, chunk and
+    tile boundaries, including tiles of 128 and 256 vectors with a short last
+    tile; the rank in the middle of the table, so the all-gather skips an
+    inner segment."""
+    es = 4 if dt == "f32" else 2
+    m = seg_vectors * (16 // es)
+    if n * m * es > 256 << 20:
+        pytest.skip("keeps the oracle to seconds")
+    host = synth.rank_inputs(n, n * m, dt, "normal", config=90 + n)
+    rk = Ranks(host, dt)
+    me = n // 2
+    for r in range(n):
+        if r != me:
+            car.ar_twoshot_rs(rk.ins, rk.segs, rk.flags, step=3, r0=r, r1=r + 1)
+    outs = [rk.outs[r] if r == me else None for r in range(n)]
+    car.ar_twoshot_rs(rk.ins, rk.segs, rk.flags, step=3, r0=me, r1=me + 1, outs=outs)
+    torch.cuda.synchronize()
+    assert_ok(rk.flags)
+    check_outputs(rk, host, ranks=[me])

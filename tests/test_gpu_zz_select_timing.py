@@ -1,6 +1,6 @@
 """The algorithm selector against live timings: at sync cost 0 (all ranks on
 one GPU) the algorithm it picks must time within 30% (plus 0.5 us of launch
-jitter) of the fastest of the seven, measured here the way its table was
+jitter) of the fastest of the eight, measured here the way its table was
 measured (one GPU's share, buffer sets rotated over 512 MiB, graph-replayed
 launches)."""
 from __future__ import annotations
@@ -20,7 +20,7 @@ def share_calls(n, numel, flags, gen):
     S = numel * 2
     W1, W2 = car.ll_wire_bytes("ll", S), car.ll_wire_bytes("ll128", S)
     src = [torch.randn(numel, generator=gen, device="cuda").to(bf) for _ in range(n)]
-    fp = n * S + 5 * S + n * (W1 + W2) + (3 * n - 1) * S
+    fp = n * S + 5 * S + n * (W1 + W2) + (3 * n - 1) * S + n * (car.ll_wire_bytes("ll128", S // n) + 2 * S // n)
     calls = {a: [] for a in car.ALGOS}
     keep = []
     for _ in range(max(2, -(-(512 << 20) // fp))):
@@ -34,10 +34,13 @@ def share_calls(n, numel, flags, gen):
         bouts = [out] + [torch.empty(numel, dtype=bf, device="cuda") for _ in range(1, n)]
         segw = [torch.zeros(car.ll_wire_bytes("ll", numel // n * 2), dtype=torch.uint8, device="cuda")
                 for _ in range(n)]
-        keep.append((ins, segs, out, w1, w2, slots0, mine, bouts, segw))
+        segw128 = [torch.zeros(car.ll_wire_bytes("ll128", numel // n * 2), dtype=torch.uint8, device="cuda")
+                   for _ in range(n)]
+        keep.append((ins, segs, out, w1, w2, slots0, mine, bouts, segw, segw128))
         for r in range(1, n):
             car.ar_twoshot_rs(ins, segs, flags, PEER, r0=r, r1=r + 1)
             car.ar_twoshot_ll(ins, segw, flags, PEER, r0=r, r1=r + 1)
+            car.ar_twoshot_ll128(ins, segw128, flags, PEER, r0=r, r1=r + 1)
         car.ar_ll_pack(ins[1:], w1[1:], "ll", PEER)
         car.ar_ll_pack(ins[1:], w2[1:], "ll128", PEER)
         one = car.prepare_oneshot(ins, out)
@@ -50,6 +53,8 @@ def share_calls(n, numel, flags, gen):
         bc = car.prepare_reduce_bcast(ins, bouts, 0, 1)
         calls["bcast"].append(lambda s, bc=bc: bc())
         calls["twoshot_ll"].append(car.prepare_twoshot_ll(ins, segw, flags, 0, 1, [out] + [None] * (n - 1)))
+        calls["twoshot_ll128"].append(car.prepare_twoshot_ll128(ins, segw128, flags, 0, 1,
+                                                                [out] + [None] * (n - 1)))
     return calls, keep
 
 
