@@ -211,7 +211,12 @@ int ar_twoshot_ag(const void* const* seg, int n, void* const* out, size_t numel,
  * eagerly on one device it may run them as copy kernels instead.  On a
  * timeout the status is written as for ar_twoshot_ag, but the copies still
  * run: their output is then not valid.  Arguments and errors as
- * ar_twoshot_ag (AR_ERR_HIP also when the runtime refuses a copy). */
+ * ar_twoshot_ag (AR_ERR_HIP also when the runtime refuses a copy).
+ * A fallback for callers whose compute units must stay free, not a fast
+ * path: the n copies of an output run one after another, measured on MI355X
+ * (graph-replayed, n = 8) at 43 us per rank at 16 KiB and 223 us at 64 MiB
+ * per rank, against 4.4 us and 37.7 us for the whole fused two-shot on the
+ * compute units.  ar_select_algo never returns it. */
 int ar_twoshot_ag_copy(const void* const* seg, int n, void* const* out, size_t numel, int dtype,
                        int r0, int r1, uint32_t* flags, uint32_t step, void* stream);
 
@@ -238,7 +243,16 @@ int ar_ll_reduce_unpack(const void* const* wire, int n, void* out, size_t numel,
                         uint32_t step, uint32_t* flags, void* stream);
 
 /* Receiver side of LL128: as ar_ll_reduce_unpack with 128-byte lines holding
- * 120 data bytes and a 64-bit flag.  Phase AR_PHASE_LL128 on timeout. */
+ * 120 data bytes and a 64-bit flag.  Phase AR_PHASE_LL128 on timeout.
+ * Producers must be ordered before this call: the pack of every wire must
+ * be complete when the call starts (earlier on the same stream, or behind
+ * an event the stream waits for).  A line is accepted on its flag alone, and
+ * the pages' LL128 premise -- a 128-byte line written and read whole
+ * ([NCCL] 协议 table) -- does not hold here: a line is read as separate
+ * 64-byte requests, so against a pack running at the same time the data
+ * beside a flag of step s may still be that of step s-1.  For producers
+ * that run at the same time use LL (a line's data and flag are one 8-byte
+ * word, read whole) or the ordered LL128 of ar_twoshot_ll128. */
 int ar_ll128_reduce_unpack(const void* const* wire, int n, void* out, size_t numel, int dtype,
                            uint32_t step, uint32_t* flags, void* stream);
 
@@ -251,9 +265,13 @@ int ar_ll128_reduce_unpack(const void* const* wire, int n, void* out, size_t num
  *    step and reduce the n messages into out exactly as ar_oneshot, rank
  *    me's term taken from src (wire[me] is written, not read back).
  *  Each wavefront writes its lines of wire[me] before it waits on any peer
- *  line, so no rank's launch waits on a line that a peer's launch holds back
- *  behind a wait of its own, and after a timeout wire[me] still holds the
- *  whole packed message.
+ *  line, and after a timeout wire[me] still holds the whole packed message.
+ *  With LL, peers' launches may run at the same time as this one: no rank's
+ *  launch waits on a line that a peer's launch holds back behind a wait of
+ *  its own, and a line's 4 data bytes and flag are one 8-byte word, read
+ *  whole.  With LL128 the peers' packs must be complete before this call
+ *  starts (stream-ordered), for the reason given at ar_ll128_reduce_unpack:
+ *  a line's flag is read beside, not before, its data.
  *  wire  : n wire buffers of ar_ll_wire_bytes(proto, numel * elem) bytes, in
  *          rank order; wire[me] is rank me's own (written), the others are
  *          read.  Zeroed once before first use: a line counts as arrived
