@@ -17,6 +17,7 @@ Functions mirror the C entry points and take ``torch.Tensor`` arguments:
     ar_twoshot_ll(ins, segws, flags, step, r0=0, r1=None, outs=None)   two-shot, LL segments
     ar_twoshot_ll128(ins, segws, flags, step, r0=0, r1=None, outs=None) two-shot, LL128 segments
     ar_flag_barrier_reset(flags, n)
+    ar_twoshot_noalloc(ins, outs)                two-shot, no allocation (library scratch)
 
 Each call enqueues on ``stream`` (default: torch's current stream) and
 raises :class:`ArError` on a synchronous error.  Asynchronous timeouts are
@@ -38,7 +39,8 @@ from . import accounting  # noqa: F401  (re-exported helper module)
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libar.so")
 
-AR_OK, AR_ERR_ARG, AR_ERR_ALIGN, AR_ERR_DIVISIBLE, AR_ERR_ALIAS, AR_ERR_TIMEOUT, AR_ERR_HIP = range(7)
+AR_OK, AR_ERR_ARG, AR_ERR_ALIGN, AR_ERR_DIVISIBLE, AR_ERR_ALIAS, AR_ERR_TIMEOUT, AR_ERR_HIP, AR_ERR_SIZE = range(8)
+AR_NOALLOC_MAX_BYTES = 64 << 20
 AR_F32, AR_BF16 = 0, 1
 AR_PROTO_LL, AR_PROTO_LL128 = 0, 1
 AR_MAX_RANKS = 16
@@ -87,6 +89,7 @@ def _load(path: str = LIB_PATH):
     lib.ar_twoshot_ll128.argtypes = [P, i32, P, sz, i32, i32, i32, vp, u32, P, vp]
     lib.ar_twoshot_ll128.restype = i32
     lib.ar_flag_barrier_reset.argtypes, lib.ar_flag_barrier_reset.restype = [vp, i32, vp], i32
+    lib.ar_twoshot_noalloc.argtypes, lib.ar_twoshot_noalloc.restype = [P, i32, P, sz, i32, vp], i32
     lib.ar_select_algo.argtypes, lib.ar_select_algo.restype = [i32, sz, i32, ctypes.c_double], i32
     lib.ar_algo_cost_us.argtypes, lib.ar_algo_cost_us.restype = [i32, i32, sz, i32, ctypes.c_double], ctypes.c_double
     return lib
@@ -505,6 +508,20 @@ def ar_twoshot_ll128(ins, segws, flags, step: int, r0: int = 0, r1=None, outs=No
 def ar_ll_allreduce(src, wires, out, flags, proto, me: int, step: int, stream=None):
     prepare_ll_allreduce(src, wires, out, flags, proto, me)(step, stream)
     return out
+
+
+def ar_twoshot_noalloc(ins, outs, stream=None):
+    """Every rank's two-shot in one launch, segments and slots in the
+    library's own device array (no allocation; at most AR_NOALLOC_MAX_BYTES
+    per rank)."""
+    ins = [_dev_tensor(t, "input") for t in ins]
+    outs = [_dev_tensor(t, "out") for t in outs]
+    if len(outs) != len(ins):
+        raise ValueError("need one output per rank")
+    _need_like(ins + outs, ins[0].dtype, ins[0].numel(), "every input and output")
+    _check(_lib.ar_twoshot_noalloc(_ptr_array([t.data_ptr() for t in ins]), len(ins),
+                                   _ptr_array([t.data_ptr() for t in outs]), ins[0].numel(), _dtype_code(ins[0]),
+                                   _stream(stream)), "ar_twoshot_noalloc")
 
 
 def ar_flag_barrier_reset(flags, n: int, stream=None):

@@ -11,6 +11,8 @@
 #include "ar.h"
 #include "ar_launch.hpp"
 
+static_assert(ar::kNoAllocMaxBytes == AR_NOALLOC_MAX_BYTES, "the header states the scratch limit");
+
 namespace ar {
 
 namespace {
@@ -206,6 +208,7 @@ const char* ar_status_string(int status) {
         case AR_ERR_ALIAS: return "written buffer overlaps another buffer";
         case AR_ERR_TIMEOUT: return "flag wait timed out";
         case AR_ERR_HIP: return "HIP runtime error";
+        case AR_ERR_SIZE: return "message larger than the allocation-free call's scratch memory";
         default: return "unknown status";
     }
 }
@@ -393,6 +396,34 @@ int ar_twoshot_ag_copy(const void* const* seg, int n, void* const* out, size_t n
     TwoShotRequest rq{nullptr, const_cast<void* const*>(seg), out, n, numel, dtype, r0, r1, flags, step,
                       false, true, timeout_ticks()};
     return hip_status(launch_twoshot_ag_copy(rq, static_cast<hipStream_t>(stream)));
+}
+
+int ar_twoshot_noalloc(const void* const* in, int n, void* const* out, size_t numel, int dtype, void* stream) {
+    if (!in || !out || !ranks_ok(n) || !dtype_ok(dtype) || numel == 0) return AR_ERR_ARG;
+    const size_t es = elem_bytes(dtype);
+    if (numel > kNoAllocMaxBytes / es) return AR_ERR_SIZE;
+    for (int i = 0; i < n; ++i) {
+        if (!in[i] || !out[i]) return AR_ERR_ARG;
+        if (!aligned16(in[i]) || !aligned16(out[i])) return AR_ERR_ALIGN;
+    }
+    if (numel % size_t(n) != 0 || (numel / size_t(n) * es) % 16 != 0) return AR_ERR_DIVISIBLE;
+    const size_t S = numel * es, m_bytes = S / size_t(n);
+    std::vector<Span> v;
+    for (int i = 0; i < n; ++i) v.push_back(span(in[i], S, false));
+    for (int r = 0; r < n; ++r) v.push_back(span(out[r], S, true));
+    if (!spans_ok(v)) return AR_ERR_ALIAS;
+    void* base = nullptr;
+    if (noalloc_scratch(&base) != hipSuccess) return AR_ERR_HIP;
+    uint32_t* flags = static_cast<uint32_t*>(base);
+    void* seg[AR_MAX_RANKS];
+    for (int j = 0; j < n; ++j) seg[j] = static_cast<unsigned char*>(base) + kNoAllocFlagBytes + size_t(j) * m_bytes;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    // every call starts from zeroed slots and uses step 1: nothing a previous
+    // call left (another n, a timeout) can let a wait pass early
+    hipError_t e = launch_flag_reset(flags, size_t(kStatusWords) + size_t(n) * kSlotsPerRank, s);
+    if (e != hipSuccess) return AR_ERR_HIP;
+    TwoShotRequest rq{in, seg, out, n, numel, dtype, 0, n, flags, 1u, true, true, timeout_ticks()};
+    return hip_status(launch_twoshot(rq, s));
 }
 
 int ar_flag_barrier_reset(uint32_t* flags, int n, void* stream) {

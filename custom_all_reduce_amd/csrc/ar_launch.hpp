@@ -75,6 +75,16 @@ hipError_t launch_ll_allreduce(const void* src, const void* const* wire, int n, 
 
 hipError_t launch_flag_reset(uint32_t* flags, size_t words, hipStream_t s);
 
+// Allocation-free two-shot: a device array holding the arrival slots of up to
+// kMaxRanks ranks (the flag region without its epoch area, padded to 256
+// bytes) followed by up to kNoAllocMaxBytes of segments (the n segments of
+// one message of at most that many bytes per rank).
+constexpr size_t kNoAllocMaxBytes = size_t(64) << 20;
+constexpr size_t kNoAllocFlagBytes = ((size_t(kStatusWords) + size_t(kMaxRanks) * kSlotsPerRank) * 4 + 255) / 256 * 256;
+constexpr size_t kNoAllocScratchBytes = kNoAllocFlagBytes + kNoAllocMaxBytes;
+// Device address of this device's scratch array (looked up once per device).
+hipError_t noalloc_scratch(void** base);
+
 // Call f(std::integral_constant<int, N>{}) for the rank count n in [2, 16].
 template <typename F>
 auto dispatch_ranks(int n, F&& f) {

@@ -77,7 +77,8 @@ typedef enum {
     AR_ERR_DIVISIBLE = 3, /* two-shot: numel % n != 0 or a segment is not a whole number of 16-byte vectors */
     AR_ERR_ALIAS = 4,     /* a written buffer overlaps another buffer of the call */
     AR_ERR_TIMEOUT = 5,   /* asynchronous only: a flag wait ran out (status word of the flag region) */
-    AR_ERR_HIP = 6        /* a HIP runtime call failed (launch, device query, cooperative launch) */
+    AR_ERR_HIP = 6,       /* a HIP runtime call failed (launch, device query, cooperative launch) */
+    AR_ERR_SIZE = 7       /* ar_twoshot_noalloc: more than AR_NOALLOC_MAX_BYTES per rank */
 } ar_status;
 
 typedef enum { AR_F32 = 0, AR_BF16 = 1 } ar_dtype;
@@ -390,6 +391,29 @@ typedef enum {
 } ar_algo;
 double ar_algo_cost_us(int algo, int n, size_t numel, int dtype, double sync_us);
 int ar_select_algo(int n, size_t numel, int dtype, double sync_us);
+
+/* Allocation-free two-shot, for callers that cannot allocate: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation.  The
+ * same all-reduce as ar_twoshot_rs with out (fused, every rank [0, n) in one
+ * launch), but the n segments and the arrival slots live in a device array
+ * of the library (AR_NOALLOC_MAX_BYTES of segments plus the slots of 16
+ * ranks), which every device that runs the call holds from its first call
+ * until the process ends.  The caller passes only the inputs and outputs.
+ *  in, out : n device pointers each, numel elements of dtype, 16-byte
+ *            aligned; outputs must not overlap each other or any input.
+ * Each call first clears the slots with a fill kernel on stream, then runs
+ * the fused two-shot with step id 1, so no state carries over from one call
+ * to the next (another n, an earlier timeout).  The first call on a device
+ * looks up that device's copy of the array (hipGetSymbolAddress); it
+ * allocates nothing, and no call does.  Calls share their device's array:
+ * calls that overlap in time on one device race (issue them on one stream).
+ * A wait that times out cannot be reported (the status words are in the
+ * array); in one launch that holds every rank it would need another kernel
+ * to keep the device's compute units for the whole wait budget.
+ * Errors: AR_ERR_ARG, AR_ERR_ALIGN, AR_ERR_DIVISIBLE, AR_ERR_ALIAS,
+ * AR_ERR_SIZE (numel * element size above AR_NOALLOC_MAX_BYTES), AR_ERR_HIP. */
+#define AR_NOALLOC_MAX_BYTES (64u << 20)
+int ar_twoshot_noalloc(const void* const* in, int n, void* const* out, size_t numel, int dtype, void* stream);
 
 /* Zero the whole flag region of ar_flag_bytes(n) bytes (status words and
  * every arrival slot) with a fill kernel, so that steps may start again at
