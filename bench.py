@@ -293,15 +293,18 @@ def copy_gbps(torch, nbytes=1 << 30, copies=10):
 
 def read_traffic(kernel: str, workload: str):
     """HBM bytes per launch from a committed rocprofv3 counter summary, if it
-    was taken on the current kernel source; else None."""
+    was taken on the current kernel source: (FETCH_SIZE / WRITE_SIZE scaled
+    by a plain copy, the memory-sector count, source); else (None, None, note)."""
     path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_counters.md")
     if not os.path.exists(path):
-        return None, None
+        return None, None, None
     text = open(path, encoding="utf-8").read()
     m = re.search(r"traffic_bytes_per_launch:\s*(\d+)\s+src_sha:\s*([0-9a-f]+)", text)
+    rel = os.path.relpath(path, ROOT)
     if not m or m.group(2) != kernel_src_sha(kernel):
-        return None, os.path.relpath(path, ROOT) + " (taken on an older kernel source: not used)"
-    return int(m.group(1)), os.path.relpath(path, ROOT)
+        return None, None, rel + " (taken on an older kernel source: not used)"
+    sect = re.search(r"\| HBM bytes per launch, sectors \| (\d+) \|", text)
+    return int(m.group(1)), (int(sect.group(1)) if sect else None), rel
 
 
 def host_cpu():
@@ -745,7 +748,7 @@ def main(argv=None):
         # prefill message), with the algorithmic bytes of one launch
         rk = config_kernel
         A = kernels[rk]["GBps"]
-        tb, tsrc = read_traffic(rk, args.workload)
+        tb, tsect, tsrc = read_traffic(rk, args.workload)
         longest = max(kernels, key=lambda k: kernels[k]["us"])
         line["roofline"] = {
             "kernel": rk,
@@ -755,6 +758,7 @@ def main(argv=None):
             "unit": "GB/s",
             "frac": round(A / HBM_PEAK, 4),
             "traffic": tb,
+            "traffic_sectors": tsect,
             "traffic_source": tsrc,
             "algorithmic_bytes_per_launch": per_bytes[rk],
             "reads_writes": list(per_rw[rk]),
