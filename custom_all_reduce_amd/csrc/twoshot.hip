@@ -444,7 +444,7 @@ __global__ __launch_bounds__(kBlock) void twoshot_kernel(TwoShotParams p) {
 // dispatched first: a wavefront that waits on a late peer never keeps this
 // launch's own reduce-scatter (which that peer may be waiting for) from
 // starting.
-template <typename T, int NR, int C, int WB, int RU>
+template <typename T, int NR, int C, int WB, int RU, bool kLL>
 __global__ __launch_bounds__(kWave * WB) void twoshot_share_kernel(TwoShotParams p) {
     const int lane = threadIdx.x & (kWave - 1);
     const uint32_t wave = __builtin_amdgcn_readfirstlane(blockIdx.x * WB + threadIdx.x / kWave);
@@ -454,7 +454,9 @@ __global__ __launch_bounds__(kWave * WB) void twoshot_share_kernel(TwoShotParams
         const uint32_t t0 = wave * p.tile;
         const uint32_t tv = min(p.tile, p.mvec - t0);  // vectors in this tile
         const uint32_t units = (tv + kWave - 1) / kWave;
-        const __amdgpu_buffer_rsrc_t rs = buffer_range(p.seg[me] + t0, tv * 16u);
+        // the tile of seg[me]: 16-byte vectors, or as LL lines 32 wire bytes each
+        const __amdgpu_buffer_rsrc_t rs = buffer_range(p.seg[me] + (kLL ? 2u : 1u) * t0, tv * (kLL ? 32u : 16u));
+        const uint32_t st = p.step;
         u32x4* own = p.out[me] + size_t(me) * p.mvec + t0;
         const size_t base = size_t(me) * p.mvec + t0;
         const u32x4* in[NR];
@@ -479,7 +481,12 @@ __global__ __launch_bounds__(kWave * WB) void twoshot_share_kernel(TwoShotParams
                 for (int i = 0; i < NR; ++i) acc.add(x[w][i]);
                 const u32x4 r = acc.result();
                 const uint32_t v = (u + w) * kWave + uint32_t(lane);
-                st_coherent(rs, v * 16u, r);
+                if constexpr (kLL) {
+                    st_coherent(rs, v * 32u, u32x4{r.x, st, r.y, st});
+                    st_coherent(rs, v * 32u + 16u, u32x4{r.z, st, r.w, st});
+                } else {
+                    st_coherent(rs, v * 16u, r);
+                }
                 st_stream(own + v, r);
             }
         }
@@ -496,10 +503,17 @@ __global__ __launch_bounds__(kWave * WB) void twoshot_share_kernel(TwoShotParams
             for (int i = 0; i < NR; ++i) acc.add(x[i]);
             const u32x4 r = acc.result();
             if (valid) {
-                st_coherent(rs, v * 16u, r);
+                if constexpr (kLL) {
+                    st_coherent(rs, v * 32u, u32x4{r.x, st, r.y, st});
+                    st_coherent(rs, v * 32u + 16u, u32x4{r.z, st, r.w, st});
+                } else {
+                    st_coherent(rs, v * 16u, r);
+                }
                 st_stream(own + v, r);
             }
         }
+        // LL lines carry their flags: nothing to wait for or publish
+        if constexpr (kLL) return;
         // publish the tile once its segment stores have completed
         wait_stores();
         if (lane == 0) flag_store_relaxed(slots + me * kSlotsPerRank + wave, p.step);
@@ -514,31 +528,84 @@ __global__ __launch_bounds__(kWave * WB) void twoshot_share_kernel(TwoShotParams
     const uint32_t vend = min(v0 + uint32_t(C * kWave), p.mvec);
     // the tiles the chunk covers (tiles are whole 64-vector units): at most C
     const uint32_t tf = fdiv(k * uint32_t(C), p.div_upt);
-    const uint32_t tl = fdiv((vend - 1u) / kWave, p.div_upt);
-    const bool need = uint32_t(lane) <= tl - tf;
-    const uint32_t* slot = slots + j * kSlotsPerRank + tf + (need ? uint32_t(lane) : 0u);
-    uint32_t seen = need ? flag_load_relaxed(slot) : 0u;
-    const uint64_t t_start = now_ticks();
-    while (true) {
-        const uint64_t missing = ~wave_ballot(!need || seen >= p.step) & wave_exec();
-        if (missing == 0) break;
-        if (now_ticks() - t_start > p.timeout_ticks) {
-            const int bad_lane = __ffsll((unsigned long long)missing) - 1;
-            if (lane == 0) report_timeout(p.flags, 1u, j, tf + uint32_t(bad_lane));
-            return;  // skip the chunk's copies
-        }
-        __builtin_amdgcn_s_sleep(1);
-        if (need) seen = flag_load_relaxed(slot);
-    }
-    const __amdgpu_buffer_rsrc_t rs = buffer_range(p.seg[j] + v0, (vend - v0) * 16u);
-    u32x4 x[C];
-#pragma unroll
-    for (int u = 0; u < C; ++u) x[u] = ld_coherent(rs, (uint32_t(u * kWave) + uint32_t(lane)) * 16u);
     u32x4* dst = p.out[me] + size_t(j) * p.mvec + v0;
+    if constexpr (kLL) {
+        // LL segment lines: load the chunk's wire bytes (32 per vector), check
+        // their flags with one ballot, re-read the units that are behind
+        const __amdgpu_buffer_rsrc_t rs = buffer_range(p.seg[j] + 2u * v0, (vend - v0) * 32u);
+        u32x4 a[C], b[C];
 #pragma unroll
-    for (int u = 0; u < C; ++u) {
-        const uint32_t v = uint32_t(u * kWave) + uint32_t(lane);
-        if (v0 + v < vend) st_stream(dst + v, x[u]);
+        for (int u = 0; u < C; ++u) {
+            const uint32_t off = (uint32_t(u * kWave) + uint32_t(lane)) * 32u;
+            a[u] = ld_coherent(rs, off);
+            b[u] = ld_coherent(rs, off + 16u);
+        }
+        __builtin_amdgcn_sched_barrier(0);  // every load ahead of the first use
+        bool behind = false;
+#pragma unroll
+        for (int u = 0; u < C; ++u) {
+            const bool valid = v0 + uint32_t(u * kWave) + uint32_t(lane) < vend;
+            behind |= valid && min(min(a[u].y, a[u].w), min(b[u].y, b[u].w)) < p.step;
+        }
+        if (wave_ballot(behind) != 0) {
+            const uint64_t t_start = now_ticks();
+            while (true) {
+                bool good = true;
+                uint32_t bad_u = 0;
+#pragma unroll
+                for (int u = 0; u < C; ++u) {
+                    const bool valid = v0 + uint32_t(u * kWave) + uint32_t(lane) < vend;
+                    if (valid && min(min(a[u].y, a[u].w), min(b[u].y, b[u].w)) < p.step) {
+                        const uint32_t off = (uint32_t(u * kWave) + uint32_t(lane)) * 32u;
+                        a[u] = ld_coherent(rs, off);
+                        b[u] = ld_coherent(rs, off + 16u);
+                        if (min(min(a[u].y, a[u].w), min(b[u].y, b[u].w)) < p.step && good) {
+                            good = false;
+                            bad_u = uint32_t(u);
+                        }
+                    }
+                }
+                const uint64_t missing = ~wave_ballot(good) & wave_exec();
+                if (missing == 0) break;
+                if (now_ticks() - t_start > p.timeout_ticks) {
+                    const int bl = __ffsll((unsigned long long)missing) - 1;
+                    if (lane == bl) report_timeout(p.flags, 1u, j, fdiv(k * uint32_t(C) + bad_u, p.div_upt));
+                    return;  // skip the chunk's copies
+                }
+                __builtin_amdgcn_s_sleep(1);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < C; ++u) {
+            const uint32_t v = uint32_t(u * kWave) + uint32_t(lane);
+            if (v0 + v < vend) st_stream(dst + v, u32x4{a[u].x, a[u].z, b[u].x, b[u].z});
+        }
+    } else {
+        const uint32_t tl = fdiv((vend - 1u) / kWave, p.div_upt);
+        const bool need = uint32_t(lane) <= tl - tf;
+        const uint32_t* slot = slots + j * kSlotsPerRank + tf + (need ? uint32_t(lane) : 0u);
+        uint32_t seen = need ? flag_load_relaxed(slot) : 0u;
+        const uint64_t t_start = now_ticks();
+        while (true) {
+            const uint64_t missing = ~wave_ballot(!need || seen >= p.step) & wave_exec();
+            if (missing == 0) break;
+            if (now_ticks() - t_start > p.timeout_ticks) {
+                const int bad_lane = __ffsll((unsigned long long)missing) - 1;
+                if (lane == 0) report_timeout(p.flags, 1u, j, tf + uint32_t(bad_lane));
+                return;  // skip the chunk's copies
+            }
+            __builtin_amdgcn_s_sleep(1);
+            if (need) seen = flag_load_relaxed(slot);
+        }
+        const __amdgpu_buffer_rsrc_t rs = buffer_range(p.seg[j] + v0, (vend - v0) * 16u);
+        u32x4 x[C];
+#pragma unroll
+        for (int u = 0; u < C; ++u) x[u] = ld_coherent(rs, (uint32_t(u * kWave) + uint32_t(lane)) * 16u);
+#pragma unroll
+        for (int u = 0; u < C; ++u) {
+            const uint32_t v = uint32_t(u * kWave) + uint32_t(lane);
+            if (v0 + v < vend) st_stream(dst + v, x[u]);
+        }
     }
 }
 
@@ -591,9 +658,23 @@ struct TwoShot128Params {
     FastDiv div_chunks;   // ag_chunks
 };
 
+// The flags of reduce-scatter unit u of segment r (lane at part 7 of each of
+// the unit's lines).  Only once the unit's data stores are complete.
+__device__ __forceinline__ void ll128_rs_flags(const TwoShot128Params& p, uint32_t r, uint32_t u, uint32_t lstep,
+                                               int lane) {
+    const uint32_t line = u * 8u + uint32_t(lane) / 8u;
+    const uint32_t lines_here = min(8u, p.nlines - min(p.nlines, u * 8u));
+    const __amdgpu_buffer_rsrc_t rs = buffer_range(p.segw[r] + size_t(u) * 1024u, lines_here * 128u);
+    if (line < p.nlines && (uint32_t(lane) & 7u) == 7u) st_coherent8(rs, uint32_t(lane) * 16u + 8u, u32x2{lstep, 0u});
+}
+
+// Reduce-scatter unit u of segment r: loads, then (once they and every
+// earlier memory operation of the wavefront are complete) the pending flags
+// of the previous unit, if any, then the fold and the unit's data stores.
+// Its own flags are left to the caller, after a later wait.
 template <typename T, int NR>
-__device__ __forceinline__ void ll128_rs_unit(const TwoShot128Params& p, uint32_t r, uint32_t u, uint32_t lstep,
-                                              int lane) {
+__device__ __forceinline__ void ll128_rs_data(const TwoShot128Params& p, uint32_t r, uint32_t u, bool pend,
+                                              uint32_t pend_r, uint32_t pend_u, uint32_t pend_step, int lane) {
     const uint32_t line = u * 8u + uint32_t(lane) / 8u;
     const uint32_t part = uint32_t(lane) & 7u;
     const bool has_line = line < p.nlines;
@@ -612,7 +693,10 @@ __device__ __forceinline__ void ll128_rs_unit(const TwoShot128Params& p, uint32_
         a[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p.in[i] + lo));
         b[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p.in[i] + hi));
     }
-    __builtin_amdgcn_sched_barrier(0);  // every load ahead of the first add
+    // this wait covers the loads and the previous unit's data stores (issued
+    // before them): that unit's flags may go now, a round trip after its data
+    wait_stores();
+    if (pend) ll128_rs_flags(p, pend_r, pend_u, pend_step, lane);
     Acc<T> acc;
 #pragma unroll
     for (int i = 0; i < NR; ++i) acc.add(u32x4{a[i].x, a[i].y, b[i].x, b[i].y});
@@ -631,9 +715,6 @@ __device__ __forceinline__ void ll128_rs_unit(const TwoShot128Params& p, uint32_
         if (part != 7u) st_coherent(rs, uint32_t(lane) * 16u, v);
         else st_coherent8(rs, uint32_t(lane) * 16u, u32x2{v.x, v.y});
     }
-    // every data byte of the unit's lines complete before any of their flags
-    wait_stores();
-    if (has_line && part == 7u) st_coherent8(rs, uint32_t(lane) * 16u + 8u, u32x2{lstep, 0u});
 }
 
 template <int NR, int C>
@@ -689,12 +770,26 @@ __global__ __launch_bounds__(kWave * WB) void twoshot_ll128_kernel(TwoShot128Par
     uint32_t epoch_lane = 0;
     if (p.auto_step && uint32_t(lane) < R) epoch_lane = flag_load_relaxed(epoch + lane);
     const uint32_t rs_items = R * p.nunits;
+    // Each unit's flags are written while the next unit's loads are waited
+    // for (that wait also covers the unit's data stores), the last unit's
+    // after a wait of its own: every flag after its line's data, with no
+    // store round trip inside the loop.
+    bool pend = false;
+    uint32_t pend_r = 0, pend_u = 0, pend_step = 0;
     for (uint32_t it = wave; it < rs_items; it += nwaves) {
         const uint32_t rr = fdiv(it, p.div_units);
         const uint32_t r = uint32_t(p.r0) + rr;
         const uint32_t u = it - rr * p.nunits;
         const uint32_t lstep = p.auto_step ? __shfl(epoch_lane + 1u, int(rr)) : p.step;
-        ll128_rs_unit<T, NR>(p, r, u, lstep, lane);
+        ll128_rs_data<T, NR>(p, r, u, pend, pend_r, pend_u, pend_step, lane);
+        pend = true;
+        pend_r = r;
+        pend_u = u;
+        pend_step = lstep;
+    }
+    if (pend) {
+        wait_stores();  // every data byte of the last unit's lines complete before its flags
+        ll128_rs_flags(p, pend_r, pend_u, pend_step, lane);
     }
     if (p.do_ag) {
         const uint32_t per_out = uint32_t(NR - 1) * p.ag_chunks;
@@ -717,8 +812,11 @@ __global__ __launch_bounds__(kWave * WB) void twoshot_ll128_kernel(TwoShot128Par
     if (p.auto_step && uint32_t(lane) < R) flag_store_relaxed(epoch + lane, epoch_lane + 1u);
 }
 
-// all-gather chunk of the LL128 two-shot: 8-line units per wavefront
-constexpr int kLL128Chunk = 1;
+// all-gather chunk of the LL128 two-shot, 8-line units per wavefront: one
+// where a wavefront has one item, eight (64 lines, one flag per lane) in the
+// persistent grid, where a wavefront walks many
+constexpr int kLL128ChunkShare = 1;
+constexpr int kLL128ChunkPersistent = 8;
 
 template <typename T, int NR>
 hipError_t launch_ll128(const TwoShotRequest& rq, hipStream_t s) {
@@ -734,7 +832,9 @@ hipError_t launch_ll128(const TwoShotRequest& rq, hipStream_t s) {
     p.seg_bytes = rq.numel / size_t(NR) * size_t(elem<T>::bytes);
     p.nlines = uint32_t((p.seg_bytes + 119) / 120);
     p.nunits = (p.nlines + 7u) / 8u;
-    p.ag_chunks = (p.nunits + uint32_t(kLL128Chunk) - 1) / uint32_t(kLL128Chunk);
+    const bool sized = rq.step != 0 && (!rq.do_ag || rq.r1 - rq.r0 == 1);  // a wavefront per item
+    const uint32_t chunk = sized ? kLL128ChunkShare : kLL128ChunkPersistent;
+    p.ag_chunks = (p.nunits + chunk - 1) / chunk;
     p.flags = rq.flags;
     p.timeout_ticks = rq.timeout_ticks;
     p.step = rq.step;
@@ -752,17 +852,18 @@ hipError_t launch_ll128(const TwoShotRequest& rq, hipStream_t s) {
         // workgroups per CU), so each wavefront's epoch copies see every call
         const uint32_t grid = uint32_t(info.cu_count) * 2u;
         if (grid * 4u > uint32_t(kEpochCopies)) return hipErrorInvalidConfiguration;
-        hipLaunchKernelGGL((twoshot_ll128_kernel<T, NR, kLL128Chunk, 4>), dim3(grid), dim3(kBlock), 0, s, p);
+        hipLaunchKernelGGL((twoshot_ll128_kernel<T, NR, kLL128ChunkPersistent, 4>), dim3(grid), dim3(kBlock), 0, s,
+                           p);
         return hipGetLastError();
     }
     if (!rq.do_ag || R == 1) {
         // nothing in this launch waits on another wavefront of it: one
         // wavefront per item, four-wavefront workgroups for large grids
         if (items >= uint64_t(kShareWideMinWavesPerCu) * uint64_t(info.cu_count)) {
-            hipLaunchKernelGGL((twoshot_ll128_kernel<T, NR, kLL128Chunk, 4>), dim3(uint32_t((items + 3) / 4)),
+            hipLaunchKernelGGL((twoshot_ll128_kernel<T, NR, kLL128ChunkShare, 4>), dim3(uint32_t((items + 3) / 4)),
                                dim3(kBlock), 0, s, p);
         } else {
-            hipLaunchKernelGGL((twoshot_ll128_kernel<T, NR, kLL128Chunk, 1>), dim3(uint32_t(items)), dim3(kWave),
+            hipLaunchKernelGGL((twoshot_ll128_kernel<T, NR, kLL128ChunkShare, 1>), dim3(uint32_t(items)), dim3(kWave),
                                0, s, p);
         }
         return hipGetLastError();
@@ -771,7 +872,7 @@ hipError_t launch_ll128(const TwoShotRequest& rq, hipStream_t s) {
     static int per_cu = -1;
     static hipError_t occ_err = hipSuccess;
     static std::once_flag once;
-    auto kern = twoshot_ll128_kernel<T, NR, kLL128Chunk, 4>;
+    auto kern = twoshot_ll128_kernel<T, NR, kLL128ChunkPersistent, 4>;
     std::call_once(once, [&] { occ_err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, kBlock, 0); });
     if (occ_err != hipSuccess) return occ_err;
     if (per_cu < 1) return hipErrorLaunchOutOfResources;
@@ -864,7 +965,7 @@ hipError_t launch_k(const TwoShotRequest& rq, hipStream_t s) {
 
     auto kern = twoshot_kernel<T, NR, U, kLL>;
     const uint32_t R = uint32_t(rq.r1 - rq.r0);
-    if constexpr (!kLL) {
+    {
         if (!p.auto_step && R == 1 && rq.do_rs && rq.do_ag) {
             // one GPU's share: a grid of one wavefront per reduce-scatter
             // tile plus one per all-gather chunk
@@ -873,10 +974,10 @@ hipError_t launch_k(const TwoShotRequest& rq, hipStream_t s) {
             const uint64_t waves = uint64_t(p.ktiles) + uint64_t(NR - 1) * p.ag_chunks;
             constexpr int RU = share_rs_unroll<NR>();
             if (waves >= uint64_t(kShareWideMinWavesPerCu) * uint64_t(info.cu_count)) {
-                hipLaunchKernelGGL((twoshot_share_kernel<T, NR, kShareChunk, 4, RU>), dim3(uint32_t((waves + 3) / 4)),
+                hipLaunchKernelGGL((twoshot_share_kernel<T, NR, kShareChunk, 4, RU, kLL>), dim3(uint32_t((waves + 3) / 4)),
                                    dim3(kWave * 4), 0, s, p);
             } else {
-                hipLaunchKernelGGL((twoshot_share_kernel<T, NR, kShareChunk, 1, RU>), dim3(uint32_t(waves)),
+                hipLaunchKernelGGL((twoshot_share_kernel<T, NR, kShareChunk, 1, RU, kLL>), dim3(uint32_t(waves)),
                                    dim3(kWave), 0, s, p);
             }
             return hipGetLastError();
