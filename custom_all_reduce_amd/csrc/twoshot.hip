@@ -431,16 +431,19 @@ __global__ __launch_bounds__(kBlock) void twoshot_kernel(TwoShotParams p) {
 // segments (rank me's own comes from the reduce-scatter's registers), and
 // those were published by the peers' launches, not by this one, so no
 // wavefront of this launch waits on another and the grid may be as large as
-// the work; workgroups the device cannot hold yet simply start later.
+// the work; workgroups the device cannot hold yet simply start later (the
+// dispatcher starting a fresh wavefront measured faster than wavefronts
+// looping over several items).
 //   wavefronts [0, ktiles)     reduce-scatter: one tile of segment me each,
-//                              then its slot (after the tile's stores)
-//   wavefronts [ktiles, ...)   all-gather: one chunk of C
-//                              64-vector units of one peer segment each --
-//                              poll the chunk's slots, then every load of
-//                              the chunk, then its stores
-// No wavefront holds both kinds of work, so neither chain of memory round
-// trips (load, store, store wait, slot; slot, load, store) waits behind the
-// other.  The reduce-scatter wavefronts come first in the grid, so they are
+//                              then its slot (after the tile's stores); with
+//                              kLL the tile goes out as LL lines carrying the
+//                              step id, with no store wait and no slot
+//   wavefronts [ktiles, ...)   all-gather: one chunk of C 64-vector units of
+//                              one peer segment each -- poll the chunk's
+//                              slots, then every load of the chunk, then its
+//                              stores (kLL: load the chunk's lines, check
+//                              their flags, re-read the ones behind)
+// The reduce-scatter wavefronts come first in the grid, so they are
 // dispatched first: a wavefront that waits on a late peer never keeps this
 // launch's own reduce-scatter (which that peer may be waiting for) from
 // starting.
