@@ -386,16 +386,20 @@ __global__ __launch_bounds__(kBlockLL) void ll_reduce1_kernel(ReduceParams p) {
     // auto step ids (step 0): rank me's line c as the last call left it
     u32x2 own_old = u32x2{0u, 0u};
     if (kFused && p.step == 0) own_old = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p.own_wire) + cc);
-    u32x2 x[NR];
-#pragma unroll
-    for (int r = 0; r < NR; ++r)
-        if (!kFused || r != p.me) x[r] = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p.wire[r]) + cc);
-    __builtin_amdgcn_sched_barrier(0);  // every load ahead of the first use
+    // the last wavefront's word of rank me, ahead of the peers' loads, so
+    // that the wait for it where the paths join leaves those in flight
     if constexpr (kFused) {
         if (!own_whole && act)
             own = c < words ? reinterpret_cast<const uint32_t*>(p.src)[c]
                             : uint32_t(reinterpret_cast<const uint16_t*>(p.src)[2 * c]);
     }
+    // every slot, rank me's too (in the send-and-receive form it holds a
+    // peer's wire, and its term is replaced below): a branch around one load
+    // makes the merge of the paths wait for every load
+    u32x2 x[NR];
+#pragma unroll
+    for (int r = 0; r < NR; ++r) x[r] = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p.wire[r]) + cc);
+    __builtin_amdgcn_sched_barrier(0);  // every load ahead of the first use
     // the step id of this lane's line: the call's, or (auto) one past the
     // last flag of rank me's line, every call advancing every line by one
     const uint32_t step = kFused && p.step == 0 ? own_old.y + 1u : p.step;
@@ -405,6 +409,22 @@ __global__ __launch_bounds__(kBlockLL) void ll_reduce1_kernel(ReduceParams p) {
         for (int r = 0; r < NR; ++r)
             if (r == p.me) x[r] = u32x2{own, step};
     }
+    // The fold runs as the loads land, ahead of the flag check, and is done
+    // again on the slow path.
+    auto fold = [&]() -> uint32_t {
+        if (elem<T>::bytes == 4) {
+            float a = 0.0f;
+#pragma unroll
+            for (int r = 0; r < NR; ++r) a = a + __uint_as_float(x[r].x);
+            return __float_as_uint(a);
+        } else {
+            float a0 = 0.0f, a1 = 0.0f;
+#pragma unroll
+            for (int r = 0; r < NR; ++r) { a0 = a0 + bf16_lo(x[r].x); a1 = a1 + bf16_hi(x[r].x); }
+            return pack_bf16x2(a0, a1);
+        }
+    };
+    uint32_t word = fold();
     uint32_t fmin = 0xFFFFFFFFu;
 #pragma unroll
     for (int r = 0; r < NR; ++r) fmin = min(fmin, x[r].y);
@@ -438,22 +458,11 @@ __global__ __launch_bounds__(kBlockLL) void ll_reduce1_kernel(ReduceParams p) {
             __builtin_amdgcn_s_sleep(1);
         }
         wait_stores();  // nothing of this path left to wait for where the paths join
+        word = fold();
     } else if (kFused && act) {
         own_late = true;
     }
     if (!act) return;
-    uint32_t word;
-    if (elem<T>::bytes == 4) {
-        float a = 0.0f;
-#pragma unroll
-        for (int r = 0; r < NR; ++r) a = a + __uint_as_float(x[r].x);
-        word = __float_as_uint(a);
-    } else {
-        float a0 = 0.0f, a1 = 0.0f;
-#pragma unroll
-        for (int r = 0; r < NR; ++r) { a0 = a0 + bf16_lo(x[r].x); a1 = a1 + bf16_hi(x[r].x); }
-        word = pack_bf16x2(a0, a1);
-    }
     if (4 * c + 4 <= p.nbytes) {
         __builtin_nontemporal_store(word, reinterpret_cast<uint32_t*>(p.out) + c);
     } else {
@@ -482,15 +491,10 @@ __global__ __launch_bounds__(kBlock128) void ll128_reduce_kernel(ReduceParams p)
     const u32x4* w[NR];
 #pragma unroll
     for (int r = 0; r < NR; ++r) w[r] = reinterpret_cast<const u32x4*>(p.wire[r]);
-    // Branch-free loads: lines past the end read the last line instead and
-    // are discarded.
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         line[u] = (wave * U + u) * 8 + size_t(lane) / 8;
         valid[u] = line[u] < p.nlines;
-        const size_t ll = valid[u] ? line[u] : p.nlines - 1;
-#pragma unroll
-        for (int r = 0; r < NR; ++r) x[u][r] = ld_stream(w[r] + ll * 8 + part);
     }
     uint32_t own[U][4] = {};
     u32x4 mine[U];
@@ -500,6 +504,8 @@ __global__ __launch_bounds__(kBlock128) void ll128_reduce_kernel(ReduceParams p)
     uint32_t step[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) step[u] = p.step;
+    // kFused: rank me's bytes first, so that the fold, which runs as the loads
+    // land, is not held up by the last load for rank me's term
     if constexpr (kFused) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
@@ -518,15 +524,15 @@ __global__ __launch_bounds__(kBlock128) void ll128_reduce_kernel(ReduceParams p)
             }
         }
     }
-    __builtin_amdgcn_sched_barrier(0);  // every load ahead of the first use
     if constexpr (kFused) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            if (p.step == 0) step[u] += 1u;
             if (!own_whole[u] && valid[u]) {
                 // the last wavefront: each word on its own, independent loads
                 // (4-byte aligned: 120 line + 16 part is a multiple of 8); a
-                // final lone bf16 is zero-extended, bytes past it stay zero
+                // final lone bf16 is zero-extended, bytes past it stay zero.
+                // Issued before the peers' loads: a wait for these where the
+                // paths join then leaves the peers' loads in flight
                 const size_t off = line[u] * 120 + size_t(part) * 16;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
@@ -537,10 +543,48 @@ __global__ __launch_bounds__(kBlock128) void ll128_reduce_kernel(ReduceParams p)
                     }
                 }
             }
+        }
+    }
+    // Branch-free loads: lines past the end read the last line instead and
+    // are discarded.
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const size_t ll = valid[u] ? line[u] : p.nlines - 1;
+#pragma unroll
+        for (int r = 0; r < NR; ++r) x[u][r] = ld_stream(w[r] + ll * 8 + part);
+    }
+    __builtin_amdgcn_sched_barrier(0);  // every load ahead of the first use
+    if constexpr (kFused) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if (p.step == 0) step[u] += 1u;
             if (part == 7u) { own[u][2] = step[u]; own[u][3] = 0u; }  // 64-bit flag = step
             mine[u] = u32x4{own[u][0], own[u][1], own[u][2], own[u][3]};
-            if (valid[u]) st_stream(reinterpret_cast<u32x4*>(p.own_wire) + line[u] * 8 + part, mine[u]);
         }
+    }
+    // The fold runs as the loads land, ahead of the flag check, and is done
+    // again on the slow path.  Every lane adds all 16 bytes, so the wavefront
+    // does not split: at part 7 the upper 8 are the flag, and the result words
+    // they give are never stored.
+    u32x4 res[U];
+    auto fold = [&]() {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            Acc<T> acc;
+#pragma unroll
+            for (int r = 0; r < NR; ++r) acc.add(kFused && r == p.me ? mine[u] : x[u][r]);
+            res[u] = acc.result();
+        }
+    };
+    fold();
+    // rank me's line for the peers once every load has landed: a store among
+    // loads still in flight would make each later load wait a wait for the
+    // store too (one counter), so it is kept below the fold
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (kFused) {
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            if (valid[u]) st_stream(reinterpret_cast<u32x4*>(p.own_wire) + line[u] * 8 + part, mine[u]);
     }
     // Readiness without short-circuit branches: the lane at part 7 folds the
     // low flag words with min, a nonzero high word counting as ready.
@@ -554,7 +598,7 @@ __global__ __launch_bounds__(kBlock128) void ll128_reduce_kernel(ReduceParams p)
     }
     if (wave_ballot(!ok) != 0) {
         // Slow path: poll the flags with coherent 64-bit loads, then re-read
-        // the data of every line after an acquire fence.
+        // the data of every line after an acquire fence and fold again.
         const uint64_t t0 = now_ticks();
         while (true) {
             bool ready = true;
@@ -591,12 +635,13 @@ __global__ __launch_bounds__(kBlock128) void ll128_reduce_kernel(ReduceParams p)
                     x[u][r] = ld_plain(reinterpret_cast<const u32x4*>(p.wire[r]) + line[u] * 8 + part);
         // Wait for the re-reads here, so that where the two paths join the
         // compiler has no load of this path to wait for; its wait would also
-        // cover rank me's line store of the fast path (stores count in the same
-        // counter), a memory round trip.
+        // cover rank me's line store (stores count in the same counter), a
+        // memory round trip.
         wait_stores();
+        fold();
     }
-    // Reduce, then repack through LDS: the 8 lines of a wavefront unit hold
-    // 960 contiguous output bytes (16-byte aligned, as 960 = 60 * 16), but a
+    // Repack through LDS: the 8 lines of a wavefront unit hold 960
+    // contiguous output bytes (16-byte aligned, as 960 = 60 * 16), but a
     // lane's piece starts at 120 * line + 16 * part, only 8-byte aligned.
     // Write the pieces to a wavefront-private LDS strip, then let lanes 0..59
     // store 16 aligned bytes each.
@@ -604,18 +649,9 @@ __global__ __launch_bounds__(kBlock128) void ll128_reduce_kernel(ReduceParams p)
     uint8_t* my = &strip[threadIdx.x / kWave][0][0];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-        Acc<T> acc;
-        if (part != 7u) {
-#pragma unroll
-            for (int r = 0; r < NR; ++r) acc.add(kFused && r == p.me ? mine[u] : x[u][r]);
-        } else {
-#pragma unroll
-            for (int r = 0; r < NR; ++r) acc.add_half(kFused && r == p.me ? mine[u] : x[u][r]);
-        }
-        const u32x4 res = acc.result();
         u32x2* d = reinterpret_cast<u32x2*>(my + u * 960 + (lane / 8) * 120 + part * 16);
-        d[0] = u32x2{res.x, res.y};
-        if (part != 7u) d[1] = u32x2{res.z, res.w};
+        d[0] = u32x2{res[u].x, res[u].y};
+        if (part != 7u) d[1] = u32x2{res[u].z, res[u].w};
     }
     // LDS-only fences: a workgroup fence over every address space would also
     // wait for this wavefront's outstanding global stores (rank me's line in
