@@ -671,58 +671,74 @@ __device__ __forceinline__ void ll128_rs_flags(const TwoShot128Params& p, uint32
     if (line < p.nlines && (uint32_t(lane) & 7u) == 7u) st_coherent8(rs, uint32_t(lane) * 16u + 8u, u32x2{lstep, 0u});
 }
 
-// Reduce-scatter unit u of segment r: loads, then (once they and every
-// earlier memory operation of the wavefront are complete) the pending flags
-// of the previous unit, if any, then the fold and the unit's data stores.
-// Its own flags are left to the caller, after a later wait.
+// The 960 data bytes of an 8-line unit are contiguous in a segment and
+// 16-byte aligned (960 = 60 * 16), but a lane's part of a line starts at
+// 120 line + 16 part, only 8-byte aligned.  The reduce-scatter loads and
+// folds a unit as 60 aligned 16-byte chunks (lane i < 60: chunk i) and puts
+// the sums in line order through a wavefront-private LDS strip; the
+// all-gather puts line data back in chunk order the same way and stores
+// aligned 16-byte chunks.
+constexpr uint32_t kUnitBytes = 960;
+
+// LDS-only ordering between a wavefront's strip writes and its reads (a
+// fence over every address space would also wait for its global stores).
+__device__ __forceinline__ void strip_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// Reduce-scatter unit u of segment r: loads; if a previous unit's flags are
+// pending, a wait for every earlier memory operation of the wavefront (its
+// data stores among them) and those flags; the fold, which otherwise runs
+// as the loads land; rank r's own output chunk; the unit's line data.  Its
+// own flags are left to the caller, after a later wait.
 template <typename T, int NR>
-__device__ __forceinline__ void ll128_rs_data(const TwoShot128Params& p, uint32_t r, uint32_t u, bool pend,
-                                              uint32_t pend_r, uint32_t pend_u, uint32_t pend_step, int lane) {
+__device__ __forceinline__ void ll128_rs_data(const TwoShot128Params& p, uint8_t* strip, uint32_t r, uint32_t u,
+                                              bool pend, uint32_t pend_r, uint32_t pend_u, uint32_t pend_step,
+                                              int lane) {
     const uint32_t line = u * 8u + uint32_t(lane) / 8u;
     const uint32_t part = uint32_t(lane) & 7u;
-    const bool has_line = line < p.nlines;
-    const size_t d = size_t(line) * 120u + size_t(part) * 16u;
-    // valid data bytes of this lane: 16, 8 (part 7, or the segment's end) or 0
-    const uint32_t db = part == 7u ? 8u : 16u;
-    const uint32_t vb = (has_line && d < p.seg_bytes) ? uint32_t(min(size_t(db), p.seg_bytes - d)) : 0u;
     const size_t seg0 = size_t(r) * p.seg_bytes;
-    // 8-byte aligned (120 line + 16 part is a multiple of 8): two 8-byte loads
-    // per rank; a lane without data re-reads the segment's first bytes
-    const size_t lo = seg0 + (vb != 0u ? d : 0u);
-    const size_t hi = vb == 16u ? lo + 8u : lo;
-    u32x2 a[NR], b[NR];
+    const size_t ubase = size_t(u) * kUnitBytes;
+    const uint32_t ub = uint32_t(min(size_t(kUnitBytes), p.seg_bytes - ubase));  // a multiple of 16
+    // lanes past the unit's chunks re-read chunk 0 and contribute zeros
+    const bool has_chunk = uint32_t(lane) * 16u < ub;
+    const size_t src = seg0 + ubase + (has_chunk ? uint32_t(lane) * 16u : 0u);
+    u32x4 x[NR];
 #pragma unroll
-    for (int i = 0; i < NR; ++i) {
-        a[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p.in[i] + lo));
-        b[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p.in[i] + hi));
+    for (int i = 0; i < NR; ++i) x[i] = ld_stream(reinterpret_cast<const u32x4*>(p.in[i] + src));
+    if (pend) {
+        // covers the loads and the previous unit's data stores (issued before
+        // them): that unit's flags may go now, a round trip after its data
+        wait_stores();
+        ll128_rs_flags(p, pend_r, pend_u, pend_step, lane);
     }
-    // this wait covers the loads and the previous unit's data stores (issued
-    // before them): that unit's flags may go now, a round trip after its data
-    wait_stores();
-    if (pend) ll128_rs_flags(p, pend_r, pend_u, pend_step, lane);
     Acc<T> acc;
 #pragma unroll
-    for (int i = 0; i < NR; ++i) acc.add(u32x4{a[i].x, a[i].y, b[i].x, b[i].y});
+    for (int i = 0; i < NR; ++i) acc.add(x[i]);
     u32x4 v = acc.result();
-    if (vb < 16u) v.z = v.w = 0u;
-    if (vb == 0u) v.x = v.y = 0u;  // zero padding past the segment's end
+    if (!has_chunk) v = u32x4{0u, 0u, 0u, 0u};  // zero padding past the segment's end
     // rank r's own segment of its output, straight from registers (fused form)
-    if (p.do_ag && vb != 0u) {
-        uint8_t* o = p.out[r] + seg0 + d;
-        __builtin_nontemporal_store(u32x2{v.x, v.y}, reinterpret_cast<u32x2*>(o));
-        if (vb == 16u) __builtin_nontemporal_store(u32x2{v.z, v.w}, reinterpret_cast<u32x2*>(o + 8));
-    }
+    if (p.do_ag && has_chunk) st_stream(reinterpret_cast<u32x4*>(p.out[r] + seg0 + ubase) + lane, v);
+    // chunk order -> line order
+    if (lane < 60) *reinterpret_cast<u32x4*>(strip + lane * 16) = v;
+    strip_sync();
+    const uint32_t d = uint32_t(lane / 8) * 120u + part * 16u;
+    const u32x2 lo = *reinterpret_cast<const u32x2*>(strip + d);
+    const u32x2 hi = part != 7u ? *reinterpret_cast<const u32x2*>(strip + d + 8) : u32x2{0u, 0u};
+    strip_sync();  // the strip's next writes after these reads
     const uint32_t lines_here = min(8u, p.nlines - min(p.nlines, u * 8u));
     const __amdgpu_buffer_rsrc_t rs = buffer_range(p.segw[r] + size_t(u) * 1024u, lines_here * 128u);
-    if (has_line) {
-        if (part != 7u) st_coherent(rs, uint32_t(lane) * 16u, v);
-        else st_coherent8(rs, uint32_t(lane) * 16u, u32x2{v.x, v.y});
+    if (line < p.nlines) {
+        if (part != 7u) st_coherent(rs, uint32_t(lane) * 16u, u32x4{lo.x, lo.y, hi.x, hi.y});
+        else st_coherent8(rs, uint32_t(lane) * 16u, lo);
     }
 }
 
 template <int NR, int C>
-__device__ __forceinline__ void ll128_ag_chunk(const TwoShot128Params& p, uint32_t ro, uint32_t j, uint32_t k,
-                                               uint32_t want, int lane) {
+__device__ __forceinline__ void ll128_ag_chunk(const TwoShot128Params& p, uint8_t* strip, uint32_t ro, uint32_t j,
+                                               uint32_t k, uint32_t want, int lane) {
     const uint32_t u0 = k * uint32_t(C);
     const uint32_t line0 = u0 * 8u;
     const uint32_t nl = min(uint32_t(8 * C), p.nlines - line0);  // lines of this chunk
@@ -748,17 +764,20 @@ __device__ __forceinline__ void ll128_ag_chunk(const TwoShot128Params& p, uint32
 #pragma unroll
     for (int c = 0; c < C; ++c) x[c] = ld_coherent(rs, uint32_t(c) * 1024u + uint32_t(lane) * 16u);
     const uint32_t part = uint32_t(lane) & 7u;
-    const uint32_t db = part == 7u ? 8u : 16u;
+    const uint32_t d = uint32_t(lane / 8) * 120u + part * 16u;
     uint8_t* o = p.out[ro] + size_t(j) * p.seg_bytes;
 #pragma unroll
     for (int c = 0; c < C; ++c) {
-        const uint32_t line = line0 + uint32_t(c) * 8u + uint32_t(lane) / 8u;
-        const size_t d = size_t(line) * 120u + size_t(part) * 16u;
-        if (line < p.nlines && d < p.seg_bytes) {
-            const uint32_t vb = uint32_t(min(size_t(db), p.seg_bytes - d));
-            __builtin_nontemporal_store(u32x2{x[c].x, x[c].y}, reinterpret_cast<u32x2*>(o + d));
-            if (vb == 16u) __builtin_nontemporal_store(u32x2{x[c].z, x[c].w}, reinterpret_cast<u32x2*>(o + d + 8));
-        }
+        const size_t ubase = size_t(u0 + uint32_t(c)) * kUnitBytes;
+        if (ubase >= p.seg_bytes) break;  // wavefront-uniform
+        const uint32_t ub = uint32_t(min(size_t(kUnitBytes), p.seg_bytes - ubase));
+        // line order -> chunk order: the data half of part 7 only, the flag stays out
+        *reinterpret_cast<u32x2*>(strip + d) = u32x2{x[c].x, x[c].y};
+        if (part != 7u) *reinterpret_cast<u32x2*>(strip + d + 8) = u32x2{x[c].z, x[c].w};
+        strip_sync();
+        const u32x4 v = *reinterpret_cast<const u32x4*>(strip + lane * 16);
+        strip_sync();  // the strip's next writes after these reads
+        if (uint32_t(lane) * 16u < ub) st_stream(reinterpret_cast<u32x4*>(o + ubase) + lane, v);
     }
 }
 
@@ -768,6 +787,8 @@ __global__ __launch_bounds__(kWave * WB) void twoshot_ll128_kernel(TwoShot128Par
     const uint32_t wave = __builtin_amdgcn_readfirstlane(blockIdx.x * WB + threadIdx.x / kWave);
     const uint32_t nwaves = gridDim.x * WB;
     const uint32_t R = uint32_t(p.r1 - p.r0);
+    __shared__ __attribute__((aligned(16))) uint8_t strips[WB][kUnitBytes];
+    uint8_t* strip = &strips[threadIdx.x / kWave][0];
     // auto step ids: lane l < R holds this wavefront's epoch copy of rank r0 + l
     uint32_t* epoch = p.flags + kStatusWords + NR * kSlotsPerRank + size_t(wave) * NR + p.r0;
     uint32_t epoch_lane = 0;
@@ -784,7 +805,7 @@ __global__ __launch_bounds__(kWave * WB) void twoshot_ll128_kernel(TwoShot128Par
         const uint32_t r = uint32_t(p.r0) + rr;
         const uint32_t u = it - rr * p.nunits;
         const uint32_t lstep = p.auto_step ? __shfl(epoch_lane + 1u, int(rr)) : p.step;
-        ll128_rs_data<T, NR>(p, r, u, pend, pend_r, pend_u, pend_step, lane);
+        ll128_rs_data<T, NR>(p, strip, r, u, pend, pend_r, pend_u, pend_step, lane);
         pend = true;
         pend_r = r;
         pend_u = u;
@@ -809,7 +830,7 @@ __global__ __launch_bounds__(kWave * WB) void twoshot_ll128_kernel(TwoShot128Par
             // the output rank's step id (its reduce-scatter in this launch, for
             // auto ids: every rank's epoch moves in step)
             const uint32_t want = p.auto_step ? __shfl(epoch_lane + 1u, int(oo)) : p.step;
-            ll128_ag_chunk<NR, C>(p, ro, j, k, want, lane);
+            ll128_ag_chunk<NR, C>(p, strip, ro, j, k, want, lane);
         }
     }
     if (p.auto_step && uint32_t(lane) < R) flag_store_relaxed(epoch + lane, epoch_lane + 1u);
