@@ -634,7 +634,9 @@ __global__ __launch_bounds__(kWave * WB) void twoshot_share_kernel(TwoShotParams
 // Work.  A segment of SB = m * element bytes is nlines = ceil(SB / 120)
 // lines; a unit is 8 lines (one wavefront: lane l holds wire bytes
 // [16 (l % 8), +16) of line l / 8, i.e. data bytes [120 line + 16 part, +16),
-// at part 7 8 data bytes and then the flag).  Items: reduce-scatter units of
+// at part 7 8 data bytes and then the flag; on the data side lane i < 60
+// holds the unit's aligned 16-byte chunk i, the two orders exchanged through
+// LDS, below).  Items: reduce-scatter units of
 // segments r0..r1-1, then all-gather chunks of C units of every peer segment
 // for every output in [r0, r1).  With a grid of one wavefront per item (one
 // GPU's share with an explicit step id, or the reduce-scatter alone) each
