@@ -84,6 +84,51 @@ def test_receiver_polls_until_the_host_writes_the_lines(proto, dt):
     assert np.array_equal(bits(out), want)
 
 
+@pytest.mark.parametrize("proto", ["ll", "ll128"])
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_send_and_receive_waits_for_late_peers(proto, dt):
+    """One GPU's LL / LL128 step in one launch (ar_ll_allreduce) started while
+    its peers' lines are still zero: the peers' wires are pinned host buffers
+    the host fills after a delay, so the fold the kernel runs as its first
+    loads land is on stale lines and must be redone after the slow path's
+    re-read.  Rank me's wire (device memory) must hold its packed message and
+    the output the oracle's all-reduce.  The sizes leave a partial last
+    wavefront (rank me's bytes loaded word by word) and, in bf16, a lone
+    final element."""
+    n, me = 4, 2
+    numel = 1500 + (1 if dt == "bf16" else 0)
+    es = 4 if dt == "f32" else 2
+    host = synth.rank_inputs(n, numel, dt, "normal", config=312)
+    want = oracle_bits(oracle.oneshot(host, dt))
+    W = car.ll_wire_bytes(proto, numel * es)
+    bufs = [pinned_device_view(W) if r != me else None for r in range(n)]
+    own = torch.zeros(W, dtype=torch.uint8, device="cuda")
+    src = to_dev(host[me])
+    out = torch.empty(numel, dtype=src.dtype, device="cuda")
+    flags = car.new_flags(n)
+    torch.cuda.synchronize()
+    P = ctypes.c_void_p
+    wires = (P * n)(*[own.data_ptr() if r == me else bufs[r][2] for r in range(n)])
+    old = car.get_poll_timeout_ns()
+    car.set_poll_timeout_ns(3_000_000_000)
+    try:
+        st = P(torch.cuda.current_stream().cuda_stream)
+        rc = car.lib.ar_ll_allreduce(src.data_ptr(), wires, n, me, out.data_ptr(), numel, 0 if dt == "f32" else 1,
+                                     car.AR_PROTO_LL if proto == "ll" else car.AR_PROTO_LL128, 9, flags.data_ptr(), st)
+        assert rc == 0
+        time.sleep(0.05)  # the launch is polling now
+        for r in range(n):
+            if r != me:
+                t, off, _ = bufs[r]
+                write_lines(t.numpy()[off:], proto, host[r], 9)
+        torch.cuda.synchronize()
+    finally:
+        car.set_poll_timeout_ns(old)
+    assert car.read_status(flags)[0] == 0
+    assert np.array_equal(bits(out), want)
+    assert np.array_equal(bits(own), oracle.ll_pack(proto, bits(src), 9))
+
+
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
 def test_twoshot_ll128_share_waits_for_the_host_written_peer_segments(dt):
     """Rank 0's two-shot under LL128 with the peers' segment wires in pinned
