@@ -237,6 +237,40 @@ class Rig:
         self.car.raise_on_status(self.flags, f"timing {name}")
         return statistics.median(reps) * 1e3 / launches, [round(r * 1e3 / launches, 3) for r in reps]
 
+    def event_timings(self, name, warm=20, calls=200, batch=20):
+        """The two further timings beside the graph-replay median: eager
+        launches after `warm` untimed ones, `calls` launches each between two
+        events on the launching stream (median per call), then `calls` more in
+        batches of `batch` between two events (median batch / batch).  Eager
+        per-call figures include the host's launch gaps."""
+        torch = self.torch
+        cs, ns = self.calls, self.nsets
+        s0 = self.next_steps(warm + 2 * calls)
+        for i in range(warm):
+            cs[i % ns][name](s0 + i)
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(calls)]
+        for i, (a, b) in enumerate(ev):
+            a.record()
+            cs[(warm + i) % ns][name](s0 + warm + i)
+            b.record()
+        torch.cuda.synchronize()
+        per = [a.elapsed_time(b) * 1e3 for a, b in ev]
+        nb = calls // batch
+        evb = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(nb)]
+        base = warm + calls
+        for g, (a, b) in enumerate(evb):
+            a.record()
+            for j in range(batch):
+                i = base + g * batch + j
+                cs[i % ns][name](s0 + i)
+            b.record()
+        torch.cuda.synchronize()
+        self.car.raise_on_status(self.flags, f"event timings of {name}")
+        bat = [a.elapsed_time(b) * 1e3 / batch for a, b in evb]
+        return {"event_per_call_us": round(statistics.median(per), 3), "batched_mean_us": round(statistics.median(bat), 3),
+                "calls": calls, "batch": batch, "warmup_calls": warm, "launch": "eager"}
+
     def check_outputs(self, i):
         """Every step kernel's output of set i equals the one-shot's, bit for bit."""
         torch = self.torch
@@ -694,6 +728,7 @@ def main(argv=None):
     kernels = {}
     copy_rate = None
     floor_us = None
+    other_timings = None
     if not args.no_kernel_times:
         for name in KERNELS:
             us, reps = rig.time_kernel(name)
@@ -701,6 +736,7 @@ def main(argv=None):
             kernels[name] = {"us": round(us, 3), "replays_us": reps, "algorithmic_bytes": per_bytes[name],
                              "GBps": round(gb, 1), "frac": round(gb / HBM_PEAK, 4)}
         floor_us = launch_floor_us(torch)
+        other_timings = rig.event_timings(config_kernel)
         print(f"bench: kernels {json.dumps(kernels)}", file=sys.stderr, flush=True)
     del rig
     torch.cuda.empty_cache()
@@ -747,6 +783,7 @@ def main(argv=None):
         # the roofline of the kernel the configuration names (the two-shot for the
         # prefill message), with the algorithmic bytes of one launch
         rk = config_kernel
+        trace_summary = f"profiles/{args.workload}_step_kernel_trace.md"
         A = kernels[rk]["GBps"]
         tb, tsect, tsrc = read_traffic(rk, args.workload)
         longest = max(kernels, key=lambda k: kernels[k]["us"])
@@ -765,6 +802,10 @@ def main(argv=None):
             "us": kernels[rk]["us"],
             "frac_of_copy": kernels[rk].get("frac_of_copy"),
             "longest_kernel": {"kernel": longest, "us": kernels[longest]["us"], "frac": kernels[longest]["frac"]},
+            # the same kernel timed the other ways: kernel-only durations in the
+            # committed rocprofv3 trace summary; eager launches between events here
+            "other_timings": dict(other_timings or {}, kernel_trace=trace_summary if os.path.exists(
+                os.path.join(ROOT, trace_summary)) else None),
         }
     if not args.no_curve and not args.no_kernel_times:
         line["curve_n8_bf16"] = curve(args, torch, car, np)
