@@ -663,14 +663,21 @@ struct TwoShot128Params {
     FastDiv div_chunks;   // ag_chunks
 };
 
-// The flags of reduce-scatter unit u of segment r (lane at part 7 of each of
-// the unit's lines).  Only once the unit's data stores are complete.
+// The flags of reduce-scatter unit u of segment r, only once the unit's data
+// stores are complete.  A line's flag shares its last 32-byte sector with
+// data bytes [96, 120); an 8-byte store of the flag alone is a partial
+// sector write, which measured slower than whole sectors, so the lanes at
+// parts 6 and 7 store that sector whole: their data again (the values the
+// data pass stored, so a reader can see nothing new but the flag) and the
+// flag.  ld = the lane's 16 wire bytes from the data pass.
 __device__ __forceinline__ void ll128_rs_flags(const TwoShot128Params& p, uint32_t r, uint32_t u, uint32_t lstep,
-                                               int lane) {
+                                               u32x4 ld, int lane) {
     const uint32_t line = u * 8u + uint32_t(lane) / 8u;
+    const uint32_t part = uint32_t(lane) & 7u;
     const uint32_t lines_here = min(8u, p.nlines - min(p.nlines, u * 8u));
     const __amdgpu_buffer_rsrc_t rs = buffer_range(p.segw[r] + size_t(u) * 1024u, lines_here * 128u);
-    if (line < p.nlines && (uint32_t(lane) & 7u) == 7u) st_coherent8(rs, uint32_t(lane) * 16u + 8u, u32x2{lstep, 0u});
+    if (line < p.nlines && part >= 6u)
+        st_coherent(rs, uint32_t(lane) * 16u, part == 7u ? u32x4{ld.x, ld.y, lstep, 0u} : ld);
 }
 
 // The 960 data bytes of an 8-line unit are contiguous in a segment and
@@ -696,9 +703,9 @@ __device__ __forceinline__ void strip_sync() {
 // as the loads land; rank r's own output chunk; the unit's line data.  Its
 // own flags are left to the caller, after a later wait.
 template <typename T, int NR>
-__device__ __forceinline__ void ll128_rs_data(const TwoShot128Params& p, uint8_t* strip, uint32_t r, uint32_t u,
-                                              bool pend, uint32_t pend_r, uint32_t pend_u, uint32_t pend_step,
-                                              int lane) {
+__device__ __forceinline__ u32x4 ll128_rs_data(const TwoShot128Params& p, uint8_t* strip, uint32_t r, uint32_t u,
+                                               uint32_t lstep, bool pend, uint32_t pend_r, uint32_t pend_u,
+                                               uint32_t pend_step, u32x4 pend_ld, int lane) {
     const uint32_t line = u * 8u + uint32_t(lane) / 8u;
     const uint32_t part = uint32_t(lane) & 7u;
     const size_t seg0 = size_t(r) * p.seg_bytes;
@@ -714,7 +721,7 @@ __device__ __forceinline__ void ll128_rs_data(const TwoShot128Params& p, uint8_t
         // covers the loads and the previous unit's data stores (issued before
         // them): that unit's flags may go now, a round trip after its data
         wait_stores();
-        ll128_rs_flags(p, pend_r, pend_u, pend_step, lane);
+        ll128_rs_flags(p, pend_r, pend_u, pend_step, pend_ld, lane);
     }
     Acc<T> acc;
 #pragma unroll
@@ -732,10 +739,12 @@ __device__ __forceinline__ void ll128_rs_data(const TwoShot128Params& p, uint8_t
     strip_sync();  // the strip's next writes after these reads
     const uint32_t lines_here = min(8u, p.nlines - min(p.nlines, u * 8u));
     const __amdgpu_buffer_rsrc_t rs = buffer_range(p.segw[r] + size_t(u) * 1024u, lines_here * 128u);
-    if (line < p.nlines) {
-        if (part != 7u) st_coherent(rs, uint32_t(lane) * 16u, u32x4{lo.x, lo.y, hi.x, hi.y});
-        else st_coherent8(rs, uint32_t(lane) * 16u, lo);
-    }
+    // part 7: its 8 data bytes with the flag word at the previous step id
+    // (below lstep, so no reader takes the line yet, and not below any id
+    // the line carried before), one whole 16-byte store
+    const u32x4 ld = part != 7u ? u32x4{lo.x, lo.y, hi.x, hi.y} : u32x4{lo.x, lo.y, lstep - 1u, 0u};
+    if (line < p.nlines) st_coherent(rs, uint32_t(lane) * 16u, ld);
+    return ld;
 }
 
 template <int NR, int C>
@@ -802,12 +811,13 @@ __global__ __launch_bounds__(kWave * WB) void twoshot_ll128_kernel(TwoShot128Par
     // store round trip inside the loop.
     bool pend = false;
     uint32_t pend_r = 0, pend_u = 0, pend_step = 0;
+    u32x4 pend_ld = u32x4{0u, 0u, 0u, 0u};
     for (uint32_t it = wave; it < rs_items; it += nwaves) {
         const uint32_t rr = fdiv(it, p.div_units);
         const uint32_t r = uint32_t(p.r0) + rr;
         const uint32_t u = it - rr * p.nunits;
         const uint32_t lstep = p.auto_step ? __shfl(epoch_lane + 1u, int(rr)) : p.step;
-        ll128_rs_data<T, NR>(p, strip, r, u, pend, pend_r, pend_u, pend_step, lane);
+        pend_ld = ll128_rs_data<T, NR>(p, strip, r, u, lstep, pend, pend_r, pend_u, pend_step, pend_ld, lane);
         pend = true;
         pend_r = r;
         pend_u = u;
@@ -815,7 +825,7 @@ __global__ __launch_bounds__(kWave * WB) void twoshot_ll128_kernel(TwoShot128Par
     }
     if (pend) {
         wait_stores();  // every data byte of the last unit's lines complete before its flags
-        ll128_rs_flags(p, pend_r, pend_u, pend_step, lane);
+        ll128_rs_flags(p, pend_r, pend_u, pend_step, pend_ld, lane);
     }
     if (p.do_ag) {
         const uint32_t per_out = uint32_t(NR - 1) * p.ag_chunks;
