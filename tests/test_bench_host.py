@@ -90,3 +90,18 @@ def test_kernel_hash_ignores_comments_but_not_code():
     assert bench.code_text(src) == bench.code_text(src.replace("    ", "\t"))
     assert bench.code_text(src) != bench.code_text(src.replace("a + 1", "a + 2"))
     assert "//" not in bench.code_text(src) and "/*" not in bench.code_text(src)
+
+
+def test_roofline_kernel_is_also_timed_per_call_and_in_batches():
+    """The configuration's kernel is timed the two further ways the survey's
+    timing row names (per call between events, batched), beside the
+    graph-replay median; the rocprofv3 summary is named for the kernel-only
+    durations."""
+    import inspect
+
+    src = inspect.getsource(bench.main)
+    assert "other_timings = rig.event_timings(config_kernel)" in src
+    assert '"other_timings": dict(other_timings or {}' in src
+    ev = inspect.getsource(bench.Rig.event_timings)
+    assert "warm=20, calls=200, batch=20" in ev
+    assert "statistics.median(per)" in ev and "statistics.median(bat)" in ev
