@@ -27,7 +27,7 @@ of memory-side cache).
 Timing.
   - The timed region: K steps captured once into a HIP graph and replayed
     once between two events (a decode engine runs this path under graph
-    replay); the driver's K (--steps) sets only this.
+    replay); --steps K sets only this.
   - Each kernel alone: a graph of KERNEL_LAUNCHES launches of it over the
     rotated sets, replayed once to warm up and then KERNEL_REPLAYS times;
     its time is the median replay / KERNEL_LAUNCHES.  Independent of --steps.

@@ -93,10 +93,9 @@ def test_kernel_hash_ignores_comments_but_not_code():
 
 
 def test_roofline_kernel_is_also_timed_per_call_and_in_batches():
-    """The configuration's kernel is timed the two further ways the survey's
-    timing row names (per call between events, batched), beside the
-    graph-replay median; the rocprofv3 summary is named for the kernel-only
-    durations."""
+    """The configuration's kernel is also timed per call between events and
+    in batches, beside the graph-replay median; the rocprofv3 summary is
+    named for the kernel-only durations."""
     import inspect
 
     src = inspect.getsource(bench.main)
