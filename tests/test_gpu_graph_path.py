@@ -105,6 +105,47 @@ def test_one_rank_shares_in_a_graph(numel):
         assert np.array_equal(bits(s.outs[0]), s.want[rep % 2]), f"step {rep}"
 
 
+@pytest.mark.parametrize("proto", ["slots", "ll", "ll128"])
+def test_auto_steps_with_changing_sizes_on_one_flag_region(proto):
+    """Auto step ids on one flag region while the message size changes from
+    call to call (every rank's two-shot in one launch): three sizes whose
+    tilings differ (64-vector tiles at the two smaller sizes, 128-vector tiles
+    at 8 MiB per rank), visited in an order where each follows a different
+    one.  The fixed grid keeps every wavefront's epoch copies in step whatever
+    the size, so each call must match the oracle, and the epochs must count
+    the calls."""
+    n, dt = 4, "bf16"
+    numels = [4 * 8 * 37, 4 * 8 * 5000, 4 * (4 << 20)]
+    data = [synth.rank_inputs(n, k, dt, "normal", config=660 + i) for i, k in enumerate(numels)]
+    wants = [oracle_bits(oracle.oneshot(h, dt)) for h in data]
+    flags = car.new_flags(n)
+    bufs = []
+    for k, h in zip(numels, data):
+        ins = [to_dev(a) for a in h]
+        tdt = ins[0].dtype
+        m = k // n
+        if proto == "slots":
+            segs = [torch.empty(m, dtype=tdt, device="cuda") for _ in range(n)]
+        else:
+            W = car.ll_wire_bytes(proto, m * 2)
+            segs = [torch.zeros(W, dtype=torch.uint8, device="cuda") for _ in range(n)]
+        outs = [torch.empty(k, dtype=tdt, device="cuda") for _ in range(n)]
+        bufs.append((ins, segs, outs))
+    fn = {"slots": car.ar_twoshot_rs, "ll": car.ar_twoshot_ll, "ll128": car.ar_twoshot_ll128}[proto]
+    torch.cuda.synchronize()
+    order = [0, 2, 1, 2, 0, 1, 1, 2]
+    for call, i in enumerate(order):
+        ins, segs, outs = bufs[i]
+        for o in outs:
+            o.fill_(7)
+        fn(ins, segs, flags, 0, outs=outs)
+        torch.cuda.synchronize()
+        car.raise_on_status(flags, f"call {call} (size {numels[i]})")
+        for r in range(n):
+            assert np.array_equal(bits(outs[r]), wants[i]), f"call {call} size {numels[i]} rank {r}"
+    assert epochs(flags, n) == [len(order)] * n
+
+
 def test_split_rs_then_ag_with_auto_steps():
     n, numel, dt = 4, 4 * 8 * 700, "bf16"
     s = Set(n, numel, dt, [620, 621])
