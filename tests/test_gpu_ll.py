@@ -373,6 +373,37 @@ def test_pack_auto_steps_advance_every_line(proto, dt, numel):
 
 
 @pytest.mark.parametrize("proto", ["ll", "ll128"])
+def test_allreduce_auto_steps_with_changing_sizes_on_the_same_wires(proto):
+    """One GPU's LL / LL128 step with auto step ids (each line's previous
+    flag + 1) on wire buffers sized for the largest message, used as prefixes
+    while the message size changes from call to call (bf16: 1000, 70001 and,
+    past the LL receiver's one-line limit, 17 MiB per rank).  Lines past a
+    smaller message keep their flags; the peers' packs advance the same lines
+    as rank me, so every call pairs its lines with the peers' and matches the
+    oracle."""
+    n, me, dt = 4, 1, "bf16"
+    numels = [1000, 70001, (ONE_LINE_MAX + (1 << 20)) // 2]
+    data = [synth.rank_inputs(n, k, dt, "normal", config=480 + i) for i, k in enumerate(numels)]
+    wants = [oracle_bits(oracle.oneshot(h, dt)) for h in data]
+    srcs = [[to_dev(a) for a in h] for h in data]
+    Wmax = car.ll_wire_bytes(proto, numels[-1] * 2)
+    bufs = [torch.zeros(Wmax, dtype=torch.uint8, device="cuda") for _ in range(n)]
+    flags = car.new_flags(n)
+    peers = [r for r in range(n) if r != me]
+    torch.cuda.synchronize()
+    for call, i in enumerate([0, 2, 1, 2, 0, 1]):
+        W = car.ll_wire_bytes(proto, numels[i] * 2)
+        wires = [b[:W] for b in bufs]
+        out = torch.full((numels[i],), 7, dtype=torch.bfloat16, device="cuda")
+        car.ar_ll_pack([srcs[i][r] for r in peers], [wires[r] for r in peers], proto, 0)
+        car.ar_ll_allreduce(srcs[i][me], wires, out, flags, proto, me, 0)
+        torch.cuda.synchronize()
+        car.raise_on_status(flags, f"call {call} (numel {numels[i]})")
+        got = bits(out)
+        assert np.array_equal(got, wants[i]), f"call {call} numel {numels[i]}: " + first_mismatch(got, wants[i])
+
+
+@pytest.mark.parametrize("proto", ["ll", "ll128"])
 @pytest.mark.parametrize("dt, numel", [("bf16", 8 * 8192), ("f32", 100000 + 1)])
 def test_allreduce_auto_steps_replayed_in_a_graph(proto, dt, numel):
     """The peers' packs and rank 3's send-and-receive, all with step 0,
