@@ -170,3 +170,50 @@ def test_twoshot_ll128_share_waits_for_the_host_written_peer_segments(dt):
     assert car.read_status(flags)[0] == 0
     assert np.array_equal(bits(out), want)
     assert np.array_equal(bits(own), oracle.ll_pack("ll128", segs[0], 7))
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_slot_share_waits_for_host_published_peers(dt):
+    """Rank 0's fused two-shot share with arrival slots (one wavefront per
+    tile and per all-gather chunk), launched while its peers have published
+    nothing: the peers' segments and the flag region are pinned host memory,
+    and the host writes every peer segment and afterwards its slots (x86
+    store order keeps the data first) while the all-gather polls.  The
+    output must be the oracle's all-reduce and rank 0's segment the oracle's
+    reduce-scatter."""
+    n, es = 4, 4 if dt == "f32" else 2
+    m = (16 // es) * 64 * 5 + (16 // es) * 3  # 5 whole 64-vector tiles and a partial one
+    numel = n * m
+    host = synth.rank_inputs(n, numel, dt, "normal", config=313)
+    segs, _ = oracle.twoshot(host, dt)
+    want = oracle_bits(oracle.oneshot(host, dt))
+    ins = [to_dev(a) for a in host]
+    own = torch.zeros(m, dtype=ins[0].dtype, device="cuda")
+    bufs = [None] + [pinned_device_view(m * es) for _ in range(1, n)]
+    fl_t, fl_off, fl_dev = pinned_device_view(car.flag_bytes(n))
+    out = torch.empty(numel, dtype=ins[0].dtype, device="cuda")
+    torch.cuda.synchronize()
+    P = ctypes.c_void_p
+    in_p = (P * n)(*[t.data_ptr() for t in ins])
+    seg_p = (P * n)(own.data_ptr(), *[b[2] for b in bufs[1:]])
+    out_p = (P * n)(out.data_ptr(), *([None] * (n - 1)))
+    slots = fl_t.numpy()[fl_off:].view(np.uint32)
+    old = car.get_poll_timeout_ns()
+    car.set_poll_timeout_ns(3_000_000_000)
+    try:
+        st = P(torch.cuda.current_stream().cuda_stream)
+        rc = car.lib.ar_twoshot_rs(in_p, n, seg_p, numel, 0 if dt == "f32" else 1, 0, 1, P(fl_dev), 7, out_p, st)
+        assert rc == 0
+        time.sleep(0.05)  # the all-gather is polling now
+        for j in range(1, n):
+            t, off, _ = bufs[j]
+            t.numpy()[off:off + m * es] = segs[j].view(np.uint8)
+        for j in range(1, n):
+            base = 32 + j * car.AR_SLOTS_PER_RANK
+            slots[base:base + car.AR_SLOTS_PER_RANK] = 7
+        torch.cuda.synchronize()
+    finally:
+        car.set_poll_timeout_ns(old)
+    assert slots[0] == 0, car.decode_status(int(slots[0]))
+    assert np.array_equal(bits(out), want)
+    assert np.array_equal(bits(own), oracle_bits(segs[0]))
