@@ -129,20 +129,21 @@ def test_send_and_receive_waits_for_late_peers(proto, dt):
     assert np.array_equal(bits(own), oracle.ll_pack(proto, bits(src), 9))
 
 
+@pytest.mark.parametrize("proto", ["ll", "ll128"])
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
-def test_twoshot_ll128_share_waits_for_the_host_written_peer_segments(dt):
-    """Rank 0's two-shot under LL128 with the peers' segment wires in pinned
-    host memory, all flags 0 at launch: the all-gather polls the flags; the
-    host then writes every peer line's data and afterwards its flag.  The
-    output must be the oracle's all-reduce, and rank 0's own segment wire the
-    oracle's LL128 packing of its segment."""
+def test_twoshot_share_under_ll_waits_for_the_host_written_peer_segments(proto, dt):
+    """Rank 0's two-shot under LL or LL128 with the peers' segment wires in
+    pinned host memory, all flags 0 at launch: the all-gather polls the
+    flags; the host then writes every peer line's data and afterwards its
+    flag.  The output must be the oracle's all-reduce, and rank 0's own
+    segment wire the oracle's packing of its segment."""
     n, es = 4, 4 if dt == "f32" else 2
     m = (16 // es) * 150  # 150 vectors: 20 lines per segment, a partial last line
     numel = n * m
     host = synth.rank_inputs(n, numel, dt, "normal", config=311)
     segs, _ = oracle.twoshot(host, dt)
     want = oracle_bits(oracle.oneshot(host, dt))
-    W = car.ll_wire_bytes("ll128", m * es)
+    W = car.ll_wire_bytes(proto, m * es)
     ins = [to_dev(a) for a in host]
     own = torch.zeros(W, dtype=torch.uint8, device="cuda")
     bufs = [None] + [pinned_device_view(W) for _ in range(1, n)]
@@ -157,19 +158,19 @@ def test_twoshot_ll128_share_waits_for_the_host_written_peer_segments(dt):
     car.set_poll_timeout_ns(3_000_000_000)
     try:
         st = P(torch.cuda.current_stream().cuda_stream)
-        rc = car.lib.ar_twoshot_ll128(in_p, n, seg_p, numel, 0 if dt == "f32" else 1, 0, 1, flags.data_ptr(), 7,
-                                      out_p, st)
+        fn = car.lib.ar_twoshot_ll if proto == "ll" else car.lib.ar_twoshot_ll128
+        rc = fn(in_p, n, seg_p, numel, 0 if dt == "f32" else 1, 0, 1, flags.data_ptr(), 7, out_p, st)
         assert rc == 0
         time.sleep(0.05)  # the all-gather is polling now
         for j in range(1, n):
             t, off, _ = bufs[j]
-            write_lines(t.numpy()[off:], "ll128", segs[j], 7)
+            write_lines(t.numpy()[off:], proto, segs[j], 7)
         torch.cuda.synchronize()
     finally:
         car.set_poll_timeout_ns(old)
     assert car.read_status(flags)[0] == 0
     assert np.array_equal(bits(out), want)
-    assert np.array_equal(bits(own), oracle.ll_pack("ll128", segs[0], 7))
+    assert np.array_equal(bits(own), oracle.ll_pack(proto, segs[0], 7))
 
 
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
