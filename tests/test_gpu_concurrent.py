@@ -218,3 +218,42 @@ def test_slot_share_waits_for_host_published_peers(dt):
     assert slots[0] == 0, car.decode_status(int(slots[0]))
     assert np.array_equal(bits(out), want)
     assert np.array_equal(bits(own), oracle_bits(segs[0]))
+
+
+def test_copy_engine_all_gather_waits_for_host_published_slots():
+    """The copy-engine all-gather (one waiting workgroup, then one copy per
+    segment) launched while no peer has published: segments and slots are
+    pinned host memory that the host fills after a delay (segments first,
+    then slots).  Rank 0's output must be the oracle's all-reduce."""
+    n, dt, es = 4, "bf16", 2
+    m = 8 * 64 * 3
+    numel = n * m
+    host = synth.rank_inputs(n, numel, dt, "normal", config=314)
+    segs, _ = oracle.twoshot(host, dt)
+    want = oracle_bits(oracle.oneshot(host, dt))
+    bufs = [pinned_device_view(m * es) for _ in range(n)]
+    fl_t, fl_off, fl_dev = pinned_device_view(car.flag_bytes(n))
+    out = torch.empty(numel, dtype=torch.bfloat16, device="cuda")
+    torch.cuda.synchronize()
+    P = ctypes.c_void_p
+    seg_p = (P * n)(*[b[2] for b in bufs])
+    out_p = (P * n)(out.data_ptr(), *([None] * (n - 1)))
+    slots = fl_t.numpy()[fl_off:].view(np.uint32)
+    old = car.get_poll_timeout_ns()
+    car.set_poll_timeout_ns(3_000_000_000)
+    try:
+        st = P(torch.cuda.current_stream().cuda_stream)
+        rc = car.lib.ar_twoshot_ag_copy(seg_p, n, out_p, numel, 1, 0, 1, P(fl_dev), 9, st)
+        assert rc == 0
+        time.sleep(0.05)  # the wait kernel is polling now
+        for j in range(n):
+            t, off, _ = bufs[j]
+            t.numpy()[off:off + m * es] = segs[j].view(np.uint8)
+        for j in range(n):
+            base = 32 + j * car.AR_SLOTS_PER_RANK
+            slots[base:base + car.AR_SLOTS_PER_RANK] = 9
+        torch.cuda.synchronize()
+    finally:
+        car.set_poll_timeout_ns(old)
+    assert slots[0] == 0, car.decode_status(int(slots[0]))
+    assert np.array_equal(bits(out), want)
