@@ -1,17 +1,19 @@
-"""Receivers that start before their data exists.
+"""Consumers that start before their data exists.
 
-The LL / LL128 receiver is launched while every flag of its wire buffers is
-still 0; the wire buffers live in pinned host memory, and the host writes the
-lines (all data first, then the flags) after a delay while the kernel polls.
-This exercises the receivers' polling slow paths against a writer that is
-truly concurrent (two GPU streams may share one hardware queue, so a second
-stream would not guarantee that).  Only loads touch host memory; the status
-words stay in device memory.  Every wait is bounded, so a mistake shows up
-as a reported timeout, never as a hang.
+Each case launches a consumer while the producers it waits on have written
+nothing; their buffers (wire lines, segments, arrival slots) live in pinned
+host memory, and the host writes them (all data first, then the flags or
+slots) after a delay while the kernel polls: the LL / LL128 receivers, one
+GPU's LL / LL128 step in one launch, one rank's two-shot share with slots,
+under LL and under LL128, and the copy-engine all-gather.  This exercises the
+polling paths against a writer that is truly concurrent (two GPU streams may
+share one hardware queue, so a second stream would not guarantee that).
+Every wait is bounded, so a mistake shows up as a reported timeout, never as
+a hang.
 
-(The two-shot barrier's concurrent case -- consumers polling while producers
-of the same launch publish -- is the fused full-emulation launch exercised
-throughout test_gpu_twoshot.py.)"""
+(The two-shot barrier's case of consumers polling while producers of the
+same launch publish is the fused full-emulation launch exercised throughout
+test_gpu_twoshot.py.)"""
 from __future__ import annotations
 
 import ctypes
