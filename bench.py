@@ -459,6 +459,14 @@ def curve(args, torch, car, np):
 SWEEP_SIZES = [16 << 10, 256 << 10, 1 << 20, 8 << 20, 64 << 20]
 
 
+def nvlink_model_crossover(n, alpha=1.5e-6, beta=450e9):
+    """Bytes per rank where the pages' alpha-beta model of 8-GPU NVLink ("集合通信：
+    NCCL 的算法、协议与推理框架的定制 all-reduce", 算法 and 练习 2; alpha = 1.5 us,
+    beta = 450 GB/s) makes the two-shot (4 alpha + 2 (n-1)/n S / beta) as fast as
+    the one-shot (2 alpha + (n-1) S / beta): S* = 2 alpha beta / ((n-1)(1 - 2/n))."""
+    return 2 * alpha * beta / ((n - 1) * (1 - 2 / n))
+
+
 def sweep(args, torch, car, np, out_path):
     """Per-kernel GB/s and fraction of HBM peak vs bytes per rank, for n = 8
     and n = 16, fp32 and bf16 (cold caches, graph-replayed launches), for the
@@ -469,6 +477,7 @@ def sweep(args, torch, car, np, out_path):
 
     rows = []
     cross = {}
+    cross_hbm = {}
     for n in (8, 16):
         for dt_name in ("bf16", "f32"):
             es = 4 if dt_name == "f32" else 2
@@ -543,11 +552,20 @@ def sweep(args, torch, car, np, out_path):
             if xs is None and t_two[SWEEP_SIZES[0]] < t_one[SWEEP_SIZES[0]]:
                 xs = float(SWEEP_SIZES[0])
             cross[f"n{n}_{dt_name}"] = None if xs is None else round(xs)
+            # the same alpha-beta model on HBM: the two-shot's extra fixed cost at
+            # the smallest size over the one-shot's streaming rate at the largest,
+            # S* = alpha_gpu * B / (n - 2) (one-shot (n+1) S vs two-shot ~3 S bytes)
+            s0, s1 = SWEEP_SIZES[0], SWEEP_SIZES[-1]
+            alpha_us = t_two[s0] - t_one[s0]
+            b_per_us = (n + 1) * s1 / t_one[s1]
+            cross_hbm[f"n{n}_{dt_name}"] = round(max(alpha_us, 0.0) * b_per_us / (n - 2))
+    nvlink = {f"n{n}": round(nvlink_model_crossover(n)) for n in (8, 16)}
     with open(out_path, "w", encoding="utf-8") as f:
         for r in rows:
             f.write(json.dumps(r) + "\n")
-        f.write(json.dumps({"crossover_bytes_per_rank": cross}) + "\n")
-    return rows, cross
+        f.write(json.dumps({"crossover_bytes_per_rank": cross, "hbm_analogue_bytes_per_rank": cross_hbm,
+                            "nvlink_model_bytes_per_rank": nvlink}) + "\n")
+    return rows, {"measured": cross, "hbm_analogue": cross_hbm, "nvlink_model": nvlink}
 
 
 SELECT_SIZES = [16 << 10, 32 << 10, 64 << 10, 128 << 10, 256 << 10, 512 << 10, 1 << 20, 3 << 19, 2 << 20,

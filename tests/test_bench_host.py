@@ -104,3 +104,15 @@ def test_roofline_kernel_is_also_timed_per_call_and_in_batches():
     ev = inspect.getsource(bench.Rig.event_timings)
     assert "warm=20, calls=200, batch=20" in ev
     assert "statistics.median(per)" in ev and "statistics.median(bat)" in ev
+
+
+def test_nvlink_model_crossover_beside_the_measured_one():
+    """The sweep prints the pages' NVLink model crossover beside the measured
+    one; bench's formula agrees with the oracle's model (pinned against the
+    pages' ~257 KB at n = 8)."""
+    from oracle import model
+
+    for n in (8, 16):
+        assert abs(bench.nvlink_model_crossover(n) - model.crossover_oneshot_twoshot(n)) < 1e-6 * model.crossover_oneshot_twoshot(n)
+    assert round(bench.nvlink_model_crossover(8)) == 257143
+    assert round(bench.nvlink_model_crossover(16)) == 102857
