@@ -4,9 +4,10 @@ Each case draws a rank count, a size (ragged for the paths that accept any
 size, divisible for the two-shot), a dtype and a value mix -- N(0,1) scaled by
 a random power of two per rank, small integers, values near the overflow and
 subnormal ranges, and a sprinkling of inf, NaN and -0 -- then compares the
-one-shot, the fused two-shot (every rank; slots and LL segments), the
-reduce-broadcast, LL and LL128 (pack then receiver, and one rank's send and
-receive in one launch) with the CPU oracle bit for bit.  The cases are fixed
+one-shot, the fused two-shot (every rank, and one rank's share after its
+peers' reduce-scatters; slots, LL and LL128 segments; the allocation-free
+entry point), the reduce-broadcast, LL and LL128 (pack then receiver, and
+one rank's send and receive in one launch) with the CPU oracle bit for bit.  The cases are fixed
 by the seed."""
 from __future__ import annotations
 
@@ -93,6 +94,31 @@ def test_random_case_every_path(k):
         car.raise_on_status(flags, label)
         for r in range(n):
             assert np.array_equal(bits(outs[r]), want), label + f" two-shot under LL rank {r}"
+        segw128 = [torch.zeros(car.ll_wire_bytes("ll128", numel // n * es), dtype=torch.uint8, device="cuda")
+                   for _ in range(n)]
+        car.ar_twoshot_ll128(ins, segw128, flags, 1, outs=outs)
+        torch.cuda.synchronize()
+        car.raise_on_status(flags, label)
+        for r in range(n):
+            assert np.array_equal(bits(outs[r]), want), label + f" two-shot under LL128 rank {r}"
+        # one rank's share (the grid sized to the work) after the peers' reduce-scatters
+        me = k % n
+        for name, fn, seg in (("slots", car.ar_twoshot_rs, segs), ("LL", car.ar_twoshot_ll, segw),
+                              ("LL128", car.ar_twoshot_ll128, segw128)):
+            for r in range(n):
+                if r != me:
+                    fn(ins, seg, flags, 3, r0=r, r1=r + 1)
+            out.fill_(7)
+            fn(ins, seg, flags, 3, r0=me, r1=me + 1, outs=[out if r == me else None for r in range(n)])
+            torch.cuda.synchronize()
+            car.raise_on_status(flags, label)
+            assert np.array_equal(bits(out), want), label + f" two-shot share of rank {me} with {name}"
+        for o in outs:
+            o.fill_(7)
+        car.ar_twoshot_noalloc(ins, outs)
+        torch.cuda.synchronize()
+        for r in range(n):
+            assert np.array_equal(bits(outs[r]), want), label + f" allocation-free two-shot rank {r}"
 
     for proto in ("ll", "ll128"):
         W = car.ll_wire_bytes(proto, numel * es)
