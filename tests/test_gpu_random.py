@@ -5,8 +5,9 @@ size, divisible for the two-shot), a dtype and a value mix -- N(0,1) scaled by
 a random power of two per rank, small integers, values near the overflow and
 subnormal ranges, and a sprinkling of inf, NaN and -0 -- then compares the
 one-shot, the fused two-shot (every rank, and one rank's share after its
-peers' reduce-scatters; slots, LL and LL128 segments; the allocation-free
-entry point), the reduce-broadcast, LL and LL128 (pack then receiver, and
+peers' reduce-scatters; slots, LL and LL128 segments; split into a
+reduce-scatter and an all-gather on the compute units or on the copy
+engines; the allocation-free entry point), the reduce-broadcast, LL and LL128 (pack then receiver, and
 one rank's send and receive in one launch) with the CPU oracle bit for bit.  The cases are fixed
 by the seed."""
 from __future__ import annotations
@@ -113,6 +114,18 @@ def test_random_case_every_path(k):
             torch.cuda.synchronize()
             car.raise_on_status(flags, label)
             assert np.array_equal(bits(out), want), label + f" two-shot share of rank {me} with {name}"
+        # split: every rank's reduce-scatter, then the all-gather on the compute
+        # units, then again with the all-gather on the copy engines
+        for name, ag in (("all-gather", car.ar_twoshot_ag), ("copy-engine all-gather", car.ar_twoshot_ag_copy)):
+            step = 5 if ag is car.ar_twoshot_ag else 6
+            for o in outs:
+                o.fill_(7)
+            car.ar_twoshot_rs(ins, segs, flags, step)
+            ag(segs, outs, flags, step)
+            torch.cuda.synchronize()
+            car.raise_on_status(flags, label)
+            for r in range(n):
+                assert np.array_equal(bits(outs[r]), want), label + f" split two-shot ({name}) rank {r}"
         for o in outs:
             o.fill_(7)
         car.ar_twoshot_noalloc(ins, outs)
