@@ -3,13 +3,14 @@
 Each case draws a rank count, a size (ragged for the paths that accept any
 size, divisible for the two-shot), a dtype and a value mix -- N(0,1) scaled by
 a random power of two per rank, small integers, values near the overflow and
-subnormal ranges, and a sprinkling of inf, NaN and -0 -- then compares the
-one-shot, the fused two-shot (every rank, and one rank's share after its
-peers' reduce-scatters; slots, LL and LL128 segments; split into a
-reduce-scatter and an all-gather on the compute units or on the copy
-engines; the allocation-free entry point), the reduce-broadcast, LL and LL128 (pack then receiver, and
-one rank's send and receive in one launch) with the CPU oracle bit for bit.  The cases are fixed
-by the seed."""
+subnormal ranges, and a sprinkling of inf, NaN and -0 -- then compares with
+the CPU oracle, bit for bit: the one-shot; the fused two-shot (every rank,
+and one rank's share after its peers' reduce-scatters; slots, LL and LL128
+segments); the two-shot split into a reduce-scatter and an all-gather on the
+compute units or on the copy engines; the allocation-free entry point; the
+reduce-broadcast; the push and staging copies; LL and LL128 (pack then
+receiver, and one rank's send and receive in one launch).  The cases are
+fixed by the seed."""
 from __future__ import annotations
 
 import numpy as np
@@ -79,6 +80,17 @@ def test_random_case_every_path(k):
     torch.cuda.synchronize()
     for r in range(n):
         assert np.array_equal(bits(outs[r]), want), label + f" reduce-broadcast out[{r}]"
+
+    # push: one rank's message to every output (a bit copy); staging copy: to one
+    me = k % n
+    car.ar_push([ins[me]], [outs])
+    torch.cuda.synchronize()
+    for r in range(n):
+        assert np.array_equal(bits(outs[r]), oracle_bits(host[me])), label + f" push to out[{r}]"
+    out.fill_(7)
+    car.ar_push([ins[me]], [[out]])
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(out), oracle_bits(host[me])), label + " staging copy"
 
     flags = car.new_flags(n)
     if numel % n == 0 and (numel // n * es) % 16 == 0:
