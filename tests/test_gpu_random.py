@@ -25,7 +25,7 @@ pytestmark = pytest.mark.gpu
 
 car = pytest.importorskip("custom_all_reduce_amd")
 
-CASES = 40
+CASES = 100
 
 
 def case(k):
