@@ -1,6 +1,8 @@
 """Index arithmetic at large sizes: n = 2 ranks of 2^30 + 5 bf16 elements
 (2 GiB and a ragged tail per rank; 2^27 16-byte vectors, LL wires of 4 GiB,
-byte offsets past 2^32).  Small-integer inputs keep every sum exact, so a
+byte offsets past 2^32), through every path: one-shot, reduce-broadcast, LL
+and LL128 (receiver and one launch), and the two-shot (every rank with
+slots, LL and LL128 segments, and one rank's share).  Small-integer inputs keep every sum exact, so a
 wrong index anywhere shows as a wrong value.  Outputs are checked on samples
 around the power-of-two boundaries against the oracle run on the sampled
 columns."""
@@ -119,3 +121,23 @@ def test_two_shot_divisible_prefix(data):
     car.raise_on_status(flags)
     for r in range(N):
         check(outs[r], idx[keep], want[keep], f"two-shot under LL rank {r}")
+    # under LL128: 1 GiB segments as 1.07 GiB wires of 128-byte lines
+    del segw
+    segw = [torch.zeros(car.ll_wire_bytes("ll128", m // N * 2), dtype=torch.uint8, device="cuda") for _ in range(N)]
+    for o in outs:
+        o.zero_()
+    car.ar_twoshot_ll128(heads, segw, flags, 1, outs=outs)
+    torch.cuda.synchronize()
+    car.raise_on_status(flags)
+    for r in range(N):
+        check(outs[r], idx[keep], want[keep], f"two-shot under LL128 rank {r}")
+    del segw
+    # one rank's share with slots (the grid sized to the work) after its peer's
+    # reduce-scatter: rank 1, whose segment starts past byte 2^31 of every input
+    segs = [torch.empty(m // N, dtype=torch.bfloat16, device="cuda") for _ in range(N)]
+    car.ar_twoshot_rs(heads, segs, flags, 2, r0=0, r1=1)
+    outs[1].zero_()
+    car.ar_twoshot_rs(heads, segs, flags, 2, r0=1, r1=2, outs=[None, outs[1]])
+    torch.cuda.synchronize()
+    car.raise_on_status(flags)
+    check(outs[1], idx[keep], want[keep], "two-shot share of rank 1")
