@@ -55,10 +55,7 @@ __device__ __forceinline__ void st_coherent(__amdgpu_buffer_rsrc_t r, uint32_t b
 __device__ __forceinline__ u32x4 ld_coherent(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
     return __builtin_amdgcn_raw_buffer_load_b128(r, int(byte_off), 0, kCachePolicySc1);
 }
-// The same for 8 bytes (an LL128 line's flag, or its last 8 data bytes).
-__device__ __forceinline__ void st_coherent8(__amdgpu_buffer_rsrc_t r, uint32_t byte_off, u32x2 v) {
-    __builtin_amdgcn_raw_buffer_store_b64(v, r, int(byte_off), 0, kCachePolicySc1);
-}
+// An 8-byte load of the same kind (an LL128 line's flag).
 __device__ __forceinline__ u32x2 ld_coherent8(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
     return __builtin_amdgcn_raw_buffer_load_b64(r, int(byte_off), 0, kCachePolicySc1);
 }
@@ -189,7 +186,6 @@ __device__ __forceinline__ void flag_store_relaxed(uint32_t* p, uint32_t v) {
 __device__ __forceinline__ uint64_t line_load_relaxed(const uint64_t* p) {
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ void fence_release_agent() { __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent"); }
 __device__ __forceinline__ void fence_acquire_agent() { __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent"); }
 
 // Record the first asynchronous error of a launch in the flag region's
