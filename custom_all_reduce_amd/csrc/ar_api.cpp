@@ -25,9 +25,12 @@ std::mutex g_info_mu;
 DeviceInfo g_info[kMaxDevices];
 bool g_info_ok[kMaxDevices] = {};
 
-// Largest message accepted per rank (32 GiB): the kernels index 16-byte
-// vectors with 32-bit integers and keep headroom for a grid's last workgroup.
-constexpr size_t kMaxBytes = size_t(1) << 35;
+// Largest message accepted per rank (16 GiB).  A dispatch holds fewer than
+// 2^32 work-items, and the finest-grained launches take one work-item per
+// 8 bytes of the message (the one-shot's 8-byte lanes, the reduce-broadcast's
+// 8-byte halves, the LL reduction's pairs of lines), so 2^34 bytes keeps every
+// grid at 2^31 work-items or fewer; 16-byte vector indices then fit in 31 bits.
+constexpr size_t kMaxBytes = size_t(1) << 34;
 constexpr size_t kStatusBytes = size_t(kStatusWords) * 4;
 
 size_t elem_bytes(int dtype) { return dtype == AR_F32 ? 4 : 2; }

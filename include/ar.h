@@ -27,7 +27,7 @@
  *  - Every data pointer is device memory of the current HIP device, 16-byte
  *    aligned ([CAR] step 1: 128-bit accesses).  All memory is caller-owned;
  *    the library never allocates on these paths.
- *  - numel counts elements per rank, at most 2^35 bytes (32 GiB) per rank
+ *  - numel counts elements per rank, at most 2^34 bytes (16 GiB) per rank
  *    (else AR_ERR_ARG); dtype is an ar_dtype.  Sums are taken in
  *    fp32, rank 0 first, starting from +0.0, and rounded once to the output
  *    type with round-to-nearest-even ([CAR] step 4).  Results are therefore

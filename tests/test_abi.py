@@ -108,12 +108,12 @@ def test_oneshot_argument_errors():
     # touching but not overlapping is fine -> would launch; not called here
 
 
-def test_size_limit_is_32_GiB_per_rank():
+def test_size_limit_is_16_GiB_per_rank():
     ins = fake_ins(2, stride=1 << 40)
     out = A + (8 << 40)
-    # 2^35 bytes + one element is refused before anything else happens
-    assert L.ar_oneshot(ins, 2, out, (1 << 35) // 4 + 1, 0, NUL) == car.AR_ERR_ARG
-    assert L.ar_oneshot(ins, 2, out, (1 << 35) // 2 + 1, 1, NUL) == car.AR_ERR_ARG
+    # 2^34 bytes + one element is refused before anything else happens
+    assert L.ar_oneshot(ins, 2, out, (1 << 34) // 4 + 1, 0, NUL) == car.AR_ERR_ARG
+    assert L.ar_oneshot(ins, 2, out, (1 << 34) // 2 + 1, 1, NUL) == car.AR_ERR_ARG
 
 
 def test_reduce_bcast_argument_errors():
