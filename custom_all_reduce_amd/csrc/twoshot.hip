@@ -786,9 +786,13 @@ __device__ __forceinline__ void ll128_ag_chunk(const TwoShot128Params& p, uint8_
         *reinterpret_cast<u32x2*>(strip + d) = u32x2{x[c].x, x[c].y};
         if (part != 7u) *reinterpret_cast<u32x2*>(strip + d + 8) = u32x2{x[c].z, x[c].w};
         strip_sync();
-        const u32x4 v = *reinterpret_cast<const u32x4*>(strip + lane * 16);
+        // lanes 0..59 hold the unit's chunks (fewer in a segment's last unit);
+        // the others read nothing, so no lane reads past its 960-byte strip
+        const bool mine = uint32_t(lane) * 16u < ub;
+        u32x4 v = u32x4{0u, 0u, 0u, 0u};
+        if (mine) v = *reinterpret_cast<const u32x4*>(strip + lane * 16);
         strip_sync();  // the strip's next writes after these reads
-        if (uint32_t(lane) * 16u < ub) st_stream(reinterpret_cast<u32x4*>(o + ubase) + lane, v);
+        if (mine) st_stream(reinterpret_cast<u32x4*>(o + ubase) + lane, v);
     }
 }
 
