@@ -19,6 +19,9 @@ Parity status of each function:
   ll_pack / ll_unpack (O5, O6)     pinned: round trip, sizes, flag positions, efficiencies
   ll_reduce (O7)                   pinned: equals O2 of payloads; stale flag -> timeout
   FlagBarrier (O8)                 pinned: steps 1..1000, withheld flag, reset
+  oneshot_rmsnorm (O10)            pinned: residual_out against O2 + residual on integer
+                                   data; y by constant rows, a one-hot row, unit RMS
+                                   of the normalized row, scale invariance, eps
   model.* (O9)                     pinned: the printed alpha-beta table and exercises;
                                    hbm_bytes by a byte-counting walk of each operation's
                                    steps, the stated configuration values, and the pages'
@@ -46,7 +49,7 @@ GCC_FLAGS = ["-O2", "-ffp-contract=off", "-fno-fast-math", "-std=c11", "-shared"
 
 def build(src: str = _SRC, out: str = _LIB, extra=()) -> str:
     """Compile the C oracle with gcc (no FMA contraction, no fast-math)."""
-    cmd = ["gcc", *GCC_FLAGS, *extra, "-o", out + ".tmp", src]
+    cmd = ["gcc", *GCC_FLAGS, *extra, "-o", out + ".tmp", src, "-lm"]
     subprocess.run(cmd, check=True)
     os.replace(out + ".tmp", out)
     return out
@@ -77,6 +80,7 @@ def _setup(lib):
     lib.oracle_ll_unpack.restype = i32
     lib.oracle_ll_reduce.argtypes = [i32, vp, i32, vp, sz, i32, u32, c.POINTER(i32), c.POINTER(sz)]
     lib.oracle_ll_reduce.restype = i32
+    lib.oracle_oneshot_rmsnorm.argtypes = [vp, i32, vp, vp, vp, vp, sz, sz, c.c_double, i32]
     return lib
 
 
@@ -246,3 +250,23 @@ class FlagBarrier:
 
     def reset(self):
         self.flags = [0] * len(self.flags)
+
+
+# ---------------------------------------------------------------- O10 ------
+def oneshot_rmsnorm(ins, residual, weight, hidden: int, eps: float, dt, lib=None):
+    """One-shot all-reduce + residual add + RMSNorm (see ar_oracle.c, O10).
+
+    ``ins`` and ``residual`` hold rows * hidden elements each, ``weight``
+    hidden.  Returns (residual_out in the data type, y as float64 unrounded)."""
+    lib = lib or load()
+    n, numel = len(ins), ins[0].size
+    _check(list(ins) + [residual], dt, numel)
+    _check([weight], dt, hidden)
+    if hidden <= 0 or numel % hidden != 0:
+        raise ValueError("numel must be a multiple of hidden")
+    rows = numel // hidden
+    res_out = np.empty(numel, dtype=_np_dtype(dt))
+    y = np.empty(numel, dtype=np.float64)
+    lib.oracle_oneshot_rmsnorm(_ptrs(ins), n, residual.ctypes.data, weight.ctypes.data, res_out.ctypes.data,
+                               y.ctypes.data, rows, hidden, float(eps), _DT[dt])
+    return res_out, y

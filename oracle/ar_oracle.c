@@ -18,11 +18,15 @@
  *       (one-shot / two-shot), 协议 table (LL, LL128, Simple).
  *  [P4] "多 GPU 与 NCCL": 集合通信 table and identity all-reduce =
  *       reduce-scatter + all-gather; ring all-reduce section.
+ *  [P3] also names, in its 推理框架 section, an all-reduce fused with
+ *       RMSNorm (the FlashInfer kernel SGLang integrates) without defining
+ *       it; O10 below is this repository's reading of that op.
  *
  * Readings where the pages are silent are marked [reading].
  *
  * dtype codes: 0 = float32, 1 = bfloat16 (stored as raw uint16 patterns).
  */
+#include <math.h>
 #include <stdint.h>
 #include <stddef.h>
 #include <string.h>
@@ -299,4 +303,44 @@ int oracle_ll_reduce(int proto, const void* const* wire, int n, void* out, size_
         free(msgs[i]);
     free(msgs);
     return ok;
+}
+
+/* ----------------------------------------------------------------- O10 --- */
+/* One-shot all-reduce fused with a residual add and RMSNorm.  [P3] names the
+ * fused op only; the definition here is a [reading]: RMSNorm as usually
+ * defined (each element divided by the root mean square of its row, plus
+ * eps inside the root, times a per-column weight), applied to the residual
+ * stream after the all-reduced sum has been added to it.
+ * The data are rows x hidden, row-major.  For element (i, k):
+ *   h      = (O2's fold of the ranks' element, fp32, rank order, from +0)
+ *            + residual[i, k]                              (one more fp32 add)
+ *   residual_out[i, k] = h rounded once to the data type
+ *   ms_i   = (sum over k of h^2) / hidden                  (fp64, k ascending)
+ *   y[i, k] = h / sqrt(ms_i + eps) * weight[k]             (fp64, not rounded)
+ * h is an fp32 value and is carried into the fp64 steps exactly; y is left
+ * unrounded so a test can state its own tolerance for the device's fp32
+ * arithmetic.  weight holds hidden elements of the data type.                 */
+void oracle_oneshot_rmsnorm(const void* const* in, int n, const void* residual, const void* weight,
+                            void* residual_out, double* y, size_t rows, size_t hidden, double eps,
+                            int dtype)
+{
+    double* hrow = (double*)malloc(hidden * sizeof(double));
+    for (size_t i = 0; i < rows; ++i) {
+        double sumsq = 0.0;
+        for (size_t k = 0; k < hidden; ++k) {
+            size_t e = i * hidden + k;
+            float acc = 0.0f;
+            for (int r = 0; r < n; ++r)
+                acc = acc + load_elem(in[r], e, dtype);
+            float h = acc + load_elem(residual, e, dtype);
+            store_elem(residual_out, e, dtype, h);
+            hrow[k] = (double)h;
+            sumsq += (double)h * (double)h;
+        }
+        double ms = sumsq / (double)hidden;
+        double inv = 1.0 / sqrt(ms + eps);
+        for (size_t k = 0; k < hidden; ++k)
+            y[i * hidden + k] = hrow[k] * inv * (double)load_elem(weight, k, dtype);
+    }
+    free(hrow);
 }

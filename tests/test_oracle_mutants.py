@@ -40,6 +40,14 @@ MUTANTS = [
     ("ll128_payload_124", "return proto == OR_LL ? 4u : 120u;", "return proto == OR_LL ? 4u : 124u;"),
     ("flag_compare_equal", "if (line_flag(proto, line) < (uint64_t)step) {",
      "if (line_flag(proto, line) != (uint64_t)step) {"),
+    ("rms_over_hidden_minus_one", "double ms = sumsq / (double)hidden;", "double ms = sumsq / (double)(hidden - 1);"),
+    ("eps_outside_the_root", "double inv = 1.0 / sqrt(ms + eps);", "double inv = 1.0 / (sqrt(ms) + eps);"),
+    ("residual_added_first",
+     "            float acc = 0.0f;\n            for (int r = 0; r < n; ++r)\n                acc = acc + load_elem(in[r], e, dtype);\n            float h = acc + load_elem(residual, e, dtype);",
+     "            float acc = load_elem(residual, e, dtype);\n            for (int r = 0; r < n; ++r)\n                acc = acc + load_elem(in[r], e, dtype);\n            float h = acc;"),
+    ("weight_indexed_by_row", "(double)load_elem(weight, k, dtype)", "(double)load_elem(weight, i % hidden, dtype)"),
+    ("normalized_from_rounded_sum", "            hrow[k] = (double)h;",
+     "            hrow[k] = (double)load_elem(residual_out, e, dtype);"),
 ]
 
 
@@ -90,6 +98,30 @@ def _run_pins(lib):
             bad.append("layout_" + proto)
         if not oracle.ll_unpack(proto, w, 250, 8, lib)[1]:
             bad.append("ge_" + proto)
+    # O10: residual output = O2 fold + residual; unit RMS; eps in the root; weight per column;
+    # the row normalized from the unrounded fp32 sum
+    hidden, rows = 40, 3
+    ins = synth.rank_inputs(3, rows * hidden, "f32", "normal", config=80)
+    res = synth.rank_inputs(1, rows * hidden, "f32", "normal", config=81)[0]
+    ro, y = oracle.oneshot_rmsnorm(ins, res, np.ones(hidden, np.float32), hidden, 0.0, "f32", lib)
+    if not np.array_equal(ro, oracle.oneshot(ins, "f32", lib) + res):
+        bad.append("rmsnorm_residual")
+    if not np.allclose((y.reshape(rows, hidden) ** 2).mean(axis=1), 1.0, rtol=1e-12, atol=0):
+        bad.append("rmsnorm_unit_rms")
+    c = np.full(hidden, -2.0, np.float32)
+    zero = np.zeros(hidden, np.float32)
+    w = synth.rank_inputs(1, hidden, "f32", "normal", config=82)[0]
+    _, y = oracle.oneshot_rmsnorm([c, zero], zero, w, hidden, 4.0, "f32", lib)
+    if not np.allclose(y, -w.astype(np.float64) / np.sqrt(2.0), rtol=1e-15, atol=0):
+        bad.append("rmsnorm_eps_weight")
+    r0, r1 = np.zeros(8, np.float32), np.zeros(8, np.float32)
+    r0[0], r1[0], r0[3] = 1.0, 2.0**-10, 2.0
+    bz = oracle.f32_to_bf16(np.zeros(8, np.float32), lib)
+    _, y = oracle.oneshot_rmsnorm([oracle.f32_to_bf16(r0, lib), oracle.f32_to_bf16(r1, lib)], bz,
+                                  oracle.f32_to_bf16(np.ones(8, np.float32), lib), 8, 0.0, "bf16", lib)
+    a = 1.0 + 2.0**-10
+    if not np.isclose(y[0], a / np.sqrt((a * a + 4.0) / 8), rtol=1e-15, atol=0):
+        bad.append("rmsnorm_unrounded")
     return bad
 
 
