@@ -8,6 +8,8 @@ library is missing, importing this package raises.
 Functions mirror the C entry points and take ``torch.Tensor`` arguments:
 
     ar_oneshot(ins, out)                         one output = sum of ranks
+    ar_oneshot_rmsnorm(ins, residual, weight, residual_out, out, eps)
+                                                 the same, + residual, then RMSNorm of each row
     ar_twoshot_rs(ins, segs, flags, step, r0=0, r1=None, outs=None)
     ar_twoshot_ag(segs, outs, flags, step, r0=0, r1=None)
     ar_ll_pack(srcs, wires, proto, step)
@@ -74,6 +76,8 @@ def _load(path: str = LIB_PATH):
     lib.ar_get_poll_timeout_ns.argtypes, lib.ar_get_poll_timeout_ns.restype = [], u64
     lib.ar_status_string.argtypes, lib.ar_status_string.restype = [i32], ctypes.c_char_p
     lib.ar_oneshot.argtypes, lib.ar_oneshot.restype = [P, i32, vp, sz, i32, vp], i32
+    lib.ar_oneshot_rmsnorm.argtypes = [P, i32, vp, vp, vp, vp, sz, sz, ctypes.c_float, i32, vp]
+    lib.ar_oneshot_rmsnorm.restype = i32
     lib.ar_reduce_bcast.argtypes, lib.ar_reduce_bcast.restype = [P, i32, P, sz, i32, i32, i32, vp], i32
     lib.ar_push.argtypes, lib.ar_push.restype = [P, i32, P, i32, sz, i32, vp], i32
     lib.ar_twoshot_rs.argtypes, lib.ar_twoshot_rs.restype = [P, i32, P, sz, i32, i32, i32, vp, u32, P, vp], i32
@@ -287,6 +291,28 @@ def prepare_oneshot(ins, out: torch.Tensor) -> Prepared:
     return Prepared(_lib.ar_oneshot, args, None, "ar_oneshot", (ins, out))
 
 
+def prepare_oneshot_rmsnorm(ins, residual: torch.Tensor, weight: torch.Tensor, residual_out: torch.Tensor,
+                            out: torch.Tensor, eps: float = 1e-6) -> Prepared:
+    """One-shot all-reduce + residual add + RMSNorm over rows of
+    ``weight.numel()`` elements: every input, the residual, residual_out and
+    out hold rows * hidden elements (residual_out may be residual itself)."""
+    ins = [_dev_tensor(t, "input") for t in ins]
+    residual = _dev_tensor(residual, "residual")
+    weight = _dev_tensor(weight, "weight")
+    residual_out = _dev_tensor(residual_out, "residual_out")
+    out = _dev_tensor(out, "out")
+    dt = _dtype_code(out)
+    hidden = weight.numel()
+    if hidden == 0 or out.numel() % hidden != 0:
+        raise ValueError(f"out holds {out.numel()} elements, not whole rows of {hidden}")
+    _need_like(ins + [residual, residual_out], out.dtype, out.numel(), "every input, residual and residual_out")
+    _need_like([weight], out.dtype, hidden, "weight")
+    args = [_ptr_array([t.data_ptr() for t in ins]), len(ins), residual.data_ptr(), weight.data_ptr(),
+            residual_out.data_ptr(), out.data_ptr(), out.numel() // hidden, hidden, float(eps), dt, None]
+    return Prepared(_lib.ar_oneshot_rmsnorm, args, None, "ar_oneshot_rmsnorm",
+                    (ins, residual, weight, residual_out, out))
+
+
 def _same_shape(ts, ref, what):
     for t in ts:
         if t.dtype != ref.dtype or t.numel() != ref.numel():
@@ -449,6 +475,13 @@ def prepare_ll_allreduce(src, wires, out, flags, proto, me: int) -> Prepared:
 def ar_oneshot(ins, out: torch.Tensor, stream=None):
     """out = sum of ins (fp32 accumulation in rank order, one rounding)."""
     prepare_oneshot(ins, out)(stream=stream)
+    return out
+
+
+def ar_oneshot_rmsnorm(ins, residual, weight, residual_out, out, eps: float = 1e-6, stream=None):
+    """h = sum of ins + residual (fp32, rank order); residual_out = h rounded;
+    out = h / sqrt(mean of h^2 over its row + eps) * weight, rounded once."""
+    prepare_oneshot_rmsnorm(ins, residual, weight, residual_out, out, eps)(stream=stream)
     return out
 
 

@@ -18,7 +18,7 @@ ROOT = os.path.dirname(HERE)
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libar.so")
 
-SOURCES = ["ar_api.cpp", "oneshot.hip", "twoshot.hip", "ll.hip", "flags.hip", "bcast.hip", "noalloc.hip"]
+SOURCES = ["ar_api.cpp", "oneshot.hip", "twoshot.hip", "ll.hip", "flags.hip", "bcast.hip", "noalloc.hip", "rmsnorm.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

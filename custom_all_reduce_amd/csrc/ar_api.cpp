@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cfloat>
 #include <atomic>
 #include <mutex>
 #include <vector>
@@ -231,6 +232,39 @@ int ar_oneshot(const void* const* in, int n, void* out, size_t numel, int dtype,
     for (int i = 0; i < n; ++i) v.push_back(span(in[i], S, false));
     if (!spans_ok(v)) return AR_ERR_ALIAS;
     return hip_status(launch_oneshot(in, n, out, numel, dtype, static_cast<hipStream_t>(stream)));
+}
+
+int ar_oneshot_rmsnorm(const void* const* in, int n, const void* residual, const void* weight, void* residual_out,
+                       void* out, size_t rows, size_t hidden, float eps, int dtype, void* stream) {
+    if (!in || !residual || !weight || !residual_out || !out || !ranks_ok(n) || !dtype_ok(dtype) || rows == 0 ||
+        hidden == 0)
+        return AR_ERR_ARG;
+    if (!(eps >= 0.0f && eps <= FLT_MAX)) return AR_ERR_ARG;  // negative, NaN or infinite
+    const size_t es = elem_bytes(dtype);
+    if (hidden > kRmsMaxRowVecs * 16 / es || rows > kMaxBytes / es / hidden) return AR_ERR_ARG;
+    for (int i = 0; i < n; ++i) {
+        if (!in[i]) return AR_ERR_ARG;
+        if (!aligned16(in[i])) return AR_ERR_ALIGN;
+    }
+    if (!aligned16(residual) || !aligned16(weight) || !aligned16(residual_out) || !aligned16(out))
+        return AR_ERR_ALIGN;
+    if ((hidden * es) % 16 != 0) return AR_ERR_DIVISIBLE;
+    const size_t S = rows * hidden * es;
+    std::vector<Span> v;
+    v.push_back(span(out, S, true));
+    // residual_out may be residual itself (each element is read before the
+    // same lane writes it); any other overlap is refused
+    if (residual_out != residual) {
+        v.push_back(span(residual_out, S, true));
+        v.push_back(span(residual, S, false));
+    } else {
+        v.push_back(span(residual_out, S, true));
+    }
+    v.push_back(span(weight, hidden * es, false));
+    for (int i = 0; i < n; ++i) v.push_back(span(in[i], S, false));
+    if (!spans_ok(v)) return AR_ERR_ALIAS;
+    return hip_status(launch_oneshot_rmsnorm(in, n, residual, weight, residual_out, out, rows, hidden, eps, dtype,
+                                             static_cast<hipStream_t>(stream)));
 }
 
 int ar_reduce_bcast(const void* const* in, int n, void* const* out, size_t numel, int dtype, int r0, int r1,

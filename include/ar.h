@@ -124,6 +124,30 @@ const char* ar_status_string(int status);
  * Errors: AR_ERR_ARG, AR_ERR_ALIGN, AR_ERR_ALIAS, AR_ERR_HIP. */
 int ar_oneshot(const void* const* in, int n, void* out, size_t numel, int dtype, void* stream);
 
+/* One-shot all-reduce fused with a residual add and RMSNorm.  [NCCL] names
+ * such a fused kernel among the inference frameworks' paths (all-reduce +
+ * RMSNorm, the FlashInfer kernel SGLang integrates) without defining it; this
+ * library's reading, for rows x hidden elements stored row-major:
+ *   h[i][k] = (ar_oneshot's fp32 fold of the ranks' element, rank order)
+ *             + residual[i][k]                      (one more fp32 add)
+ *   residual_out[i][k] = h rounded once to dtype
+ *   out[i][k] = round(h * (1 / sqrt(sum over k of h^2 / hidden + eps))
+ *                     * weight[k]), in fp32.
+ *  in           : host array of n device pointers, rows * hidden elements each.
+ *  residual     : rows * hidden elements; residual_out may be the same buffer
+ *                 (updated in place) but may not otherwise overlap anything.
+ *  weight       : hidden elements, the same for every row.
+ *  out          : rows * hidden elements; may not overlap any other buffer.
+ *  hidden * element size must be a multiple of 16 and at most 64 KiB
+ *  (32768 bf16 / 16384 fp32 elements); eps >= 0 and finite.
+ * residual_out matches the oracle bit for bit; out is fp32 arithmetic whose
+ * sum of squares is taken in a tree, within one unit in the last place of
+ * the correctly rounded value.  Reads (n + 1) * S + hidden * element size
+ * bytes and writes 2 * S (S = rows * hidden * element size).
+ * Errors: AR_ERR_ARG, AR_ERR_ALIGN, AR_ERR_DIVISIBLE, AR_ERR_ALIAS, AR_ERR_HIP. */
+int ar_oneshot_rmsnorm(const void* const* in, int n, const void* residual, const void* weight, void* residual_out,
+                       void* out, size_t rows, size_t hidden, float eps, int dtype, void* stream);
+
 /* Reduce with a broadcast store: the kBroadcast store path of [CAR] step 5
  * -- each result written to every rank's output, not only the local one --
  * applied to one rank's share of the elements, which makes a two-shot whose

@@ -433,3 +433,34 @@ def test_size_checks_reject_undersized_buffers():
     assert car.ll_wire_bytes("ll128", m * 2) < car.ll_wire_bytes("ll", m * 2)
     with pytest.raises(ValueError):
         car._need_bytes([torch.zeros(127, dtype=torch.uint8)], car.STATUS_BYTES, "flags")
+
+
+def test_oneshot_rmsnorm_argument_errors():
+    f = L.ar_oneshot_rmsnorm
+    n, rows, hidden = 4, 8, 4096
+    ins = fake_ins(n)
+    res, w, ro, out = A + (64 << 30), A + (65 << 30), A + (66 << 30), A + (67 << 30)
+    assert f(ins, 1, res, w, ro, out, rows, hidden, 1e-6, 1, NUL) == car.AR_ERR_ARG  # n < 2
+    assert f(ins, n, res, w, ro, out, 0, hidden, 1e-6, 1, NUL) == car.AR_ERR_ARG  # no rows
+    assert f(ins, n, res, w, ro, out, rows, 0, 1e-6, 1, NUL) == car.AR_ERR_ARG  # no columns
+    assert f(ins, n, res, w, ro, out, rows, hidden, 1e-6, 2, NUL) == car.AR_ERR_ARG  # dtype
+    assert f(ins, n, None, w, ro, out, rows, hidden, 1e-6, 1, NUL) == car.AR_ERR_ARG
+    assert f(ins, n, res, None, ro, out, rows, hidden, 1e-6, 1, NUL) == car.AR_ERR_ARG
+    for eps in (-1e-6, float("nan"), float("inf")):
+        assert f(ins, n, res, w, ro, out, rows, hidden, eps, 1, NUL) == car.AR_ERR_ARG
+    # a row of at most 64 KiB: 32768 bf16 or 16384 fp32 elements
+    assert f(ins, n, res, w, ro, out, rows, 32768 + 8, 1e-6, 1, NUL) == car.AR_ERR_ARG
+    assert f(ins, n, res, w, ro, out, rows, 16384 + 4, 1e-6, 0, NUL) == car.AR_ERR_ARG
+    # the 16 GiB per rank limit
+    assert f(ins, n, res, w, ro, out, (1 << 34) // (2 * 8) + 1, 8, 1e-6, 1, NUL) == car.AR_ERR_ARG
+    assert f(ins, n, res + 8, w, ro, out, rows, hidden, 1e-6, 1, NUL) == car.AR_ERR_ALIGN
+    assert f(ins, n, res, w + 8, ro, out, rows, hidden, 1e-6, 1, NUL) == car.AR_ERR_ALIGN
+    # a row must be whole 16-byte vectors
+    assert f(ins, n, res, w, ro, out, rows, 4100, 1e-6, 1, NUL) == car.AR_ERR_DIVISIBLE
+    assert f(ins, n, res, w, ro, out, rows, 4098, 1e-6, 0, NUL) == car.AR_ERR_DIVISIBLE
+    # out overlapping an input, the weight or residual_out; residual_out partly over the residual
+    assert f(ins, n, res, w, ro, A + 16, rows, hidden, 1e-6, 1, NUL) == car.AR_ERR_ALIAS
+    assert f(ins, n, res, w, ro, w + 64, rows, hidden, 1e-6, 1, NUL) == car.AR_ERR_ALIAS
+    assert f(ins, n, res, w, ro, ro + 1024, rows, hidden, 1e-6, 1, NUL) == car.AR_ERR_ALIAS
+    assert f(ins, n, res, w, res + 1024, out, rows, hidden, 1e-6, 1, NUL) == car.AR_ERR_ALIAS
+    assert f(ins, n, res, w, A + (1 << 30), out, rows, hidden, 1e-6, 1, NUL) == car.AR_ERR_ALIAS
