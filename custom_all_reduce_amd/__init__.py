@@ -8,7 +8,7 @@ library is missing, importing this package raises.
 Functions mirror the C entry points and take ``torch.Tensor`` arguments:
 
     ar_oneshot(ins, out)                         one output = sum of ranks
-    ar_oneshot_rmsnorm(ins, residual, weight, residual_out, out, eps)
+    ar_oneshot_rmsnorm(ins, residual, weight, residual_out, out, eps, workspace=None)
                                                  the same, + residual, then RMSNorm of each row
     ar_twoshot_rs(ins, segs, flags, step, r0=0, r1=None, outs=None)
     ar_twoshot_ag(segs, outs, flags, step, r0=0, r1=None)
@@ -48,7 +48,7 @@ AR_PROTO_LL, AR_PROTO_LL128 = 0, 1
 AR_MAX_RANKS = 16
 AR_SLOTS_PER_RANK = 1024
 AR_EPOCH_COPIES = 4096
-PHASE_TWOSHOT_AG, PHASE_LL, PHASE_LL128 = 1, 2, 3
+PHASE_TWOSHOT_AG, PHASE_LL, PHASE_LL128, PHASE_RMSNORM = 1, 2, 3, 4
 
 _DTYPES = {torch.float32: AR_F32, torch.bfloat16: AR_BF16}
 _PROTOS = {"ll": AR_PROTO_LL, "ll128": AR_PROTO_LL128, AR_PROTO_LL: AR_PROTO_LL, AR_PROTO_LL128: AR_PROTO_LL128}
@@ -76,8 +76,9 @@ def _load(path: str = LIB_PATH):
     lib.ar_get_poll_timeout_ns.argtypes, lib.ar_get_poll_timeout_ns.restype = [], u64
     lib.ar_status_string.argtypes, lib.ar_status_string.restype = [i32], ctypes.c_char_p
     lib.ar_oneshot.argtypes, lib.ar_oneshot.restype = [P, i32, vp, sz, i32, vp], i32
-    lib.ar_oneshot_rmsnorm.argtypes = [P, i32, vp, vp, vp, vp, sz, sz, ctypes.c_float, i32, vp]
+    lib.ar_oneshot_rmsnorm.argtypes = [P, i32, vp, vp, vp, vp, sz, sz, ctypes.c_float, i32, vp, vp]
     lib.ar_oneshot_rmsnorm.restype = i32
+    lib.ar_rmsnorm_workspace_bytes.argtypes, lib.ar_rmsnorm_workspace_bytes.restype = [], sz
     lib.ar_reduce_bcast.argtypes, lib.ar_reduce_bcast.restype = [P, i32, P, sz, i32, i32, i32, vp], i32
     lib.ar_push.argtypes, lib.ar_push.restype = [P, i32, P, i32, sz, i32, vp], i32
     lib.ar_twoshot_rs.argtypes, lib.ar_twoshot_rs.restype = [P, i32, P, sz, i32, i32, i32, vp, u32, P, vp], i32
@@ -291,11 +292,23 @@ def prepare_oneshot(ins, out: torch.Tensor) -> Prepared:
     return Prepared(_lib.ar_oneshot, args, None, "ar_oneshot", (ins, out))
 
 
+def rmsnorm_workspace_bytes() -> int:
+    return int(_lib.ar_rmsnorm_workspace_bytes())
+
+
+def new_rmsnorm_workspace(device=None) -> torch.Tensor:
+    """A zeroed workspace for ar_oneshot_rmsnorm's few-rows path (one per call
+    site; calls sharing it must be ordered on one stream)."""
+    return torch.zeros(rmsnorm_workspace_bytes() // 4, dtype=torch.int32, device=device or "cuda")
+
+
 def prepare_oneshot_rmsnorm(ins, residual: torch.Tensor, weight: torch.Tensor, residual_out: torch.Tensor,
-                            out: torch.Tensor, eps: float = 1e-6) -> Prepared:
+                            out: torch.Tensor, eps: float = 1e-6, workspace=None) -> Prepared:
     """One-shot all-reduce + residual add + RMSNorm over rows of
     ``weight.numel()`` elements: every input, the residual, residual_out and
-    out hold rows * hidden elements (residual_out may be residual itself)."""
+    out hold rows * hidden elements (residual_out may be residual itself).
+    ``workspace`` (from :func:`new_rmsnorm_workspace`, or None) lets few rows
+    spread over the whole device."""
     ins = [_dev_tensor(t, "input") for t in ins]
     residual = _dev_tensor(residual, "residual")
     weight = _dev_tensor(weight, "weight")
@@ -307,10 +320,15 @@ def prepare_oneshot_rmsnorm(ins, residual: torch.Tensor, weight: torch.Tensor, r
         raise ValueError(f"out holds {out.numel()} elements, not whole rows of {hidden}")
     _need_like(ins + [residual, residual_out], out.dtype, out.numel(), "every input, residual and residual_out")
     _need_like([weight], out.dtype, hidden, "weight")
+    ws = None
+    if workspace is not None:
+        workspace = _dev_tensor(workspace, "workspace")
+        _need_bytes([workspace], rmsnorm_workspace_bytes(), "the workspace")
+        ws = workspace.data_ptr()
     args = [_ptr_array([t.data_ptr() for t in ins]), len(ins), residual.data_ptr(), weight.data_ptr(),
-            residual_out.data_ptr(), out.data_ptr(), out.numel() // hidden, hidden, float(eps), dt, None]
+            residual_out.data_ptr(), out.data_ptr(), out.numel() // hidden, hidden, float(eps), dt, ws, None]
     return Prepared(_lib.ar_oneshot_rmsnorm, args, None, "ar_oneshot_rmsnorm",
-                    (ins, residual, weight, residual_out, out))
+                    (ins, residual, weight, residual_out, out, workspace))
 
 
 def _same_shape(ts, ref, what):
@@ -478,10 +496,10 @@ def ar_oneshot(ins, out: torch.Tensor, stream=None):
     return out
 
 
-def ar_oneshot_rmsnorm(ins, residual, weight, residual_out, out, eps: float = 1e-6, stream=None):
+def ar_oneshot_rmsnorm(ins, residual, weight, residual_out, out, eps: float = 1e-6, workspace=None, stream=None):
     """h = sum of ins + residual (fp32, rank order); residual_out = h rounded;
     out = h / sqrt(mean of h^2 over its row + eps) * weight, rounded once."""
-    prepare_oneshot_rmsnorm(ins, residual, weight, residual_out, out, eps)(stream=stream)
+    prepare_oneshot_rmsnorm(ins, residual, weight, residual_out, out, eps, workspace)(stream=stream)
     return out
 
 

@@ -234,8 +234,11 @@ int ar_oneshot(const void* const* in, int n, void* out, size_t numel, int dtype,
     return hip_status(launch_oneshot(in, n, out, numel, dtype, static_cast<hipStream_t>(stream)));
 }
 
+size_t ar_rmsnorm_workspace_bytes(void) { return kRmsWorkspaceBytes; }
+
 int ar_oneshot_rmsnorm(const void* const* in, int n, const void* residual, const void* weight, void* residual_out,
-                       void* out, size_t rows, size_t hidden, float eps, int dtype, void* stream) {
+                       void* out, size_t rows, size_t hidden, float eps, int dtype, uint32_t* workspace,
+                       void* stream) {
     if (!in || !residual || !weight || !residual_out || !out || !ranks_ok(n) || !dtype_ok(dtype) || rows == 0 ||
         hidden == 0)
         return AR_ERR_ARG;
@@ -246,7 +249,8 @@ int ar_oneshot_rmsnorm(const void* const* in, int n, const void* residual, const
         if (!in[i]) return AR_ERR_ARG;
         if (!aligned16(in[i])) return AR_ERR_ALIGN;
     }
-    if (!aligned16(residual) || !aligned16(weight) || !aligned16(residual_out) || !aligned16(out))
+    if (!aligned16(residual) || !aligned16(weight) || !aligned16(residual_out) || !aligned16(out) ||
+        !aligned16(workspace))
         return AR_ERR_ALIGN;
     if ((hidden * es) % 16 != 0) return AR_ERR_DIVISIBLE;
     const size_t S = rows * hidden * es;
@@ -262,9 +266,10 @@ int ar_oneshot_rmsnorm(const void* const* in, int n, const void* residual, const
     }
     v.push_back(span(weight, hidden * es, false));
     for (int i = 0; i < n; ++i) v.push_back(span(in[i], S, false));
+    if (workspace) v.push_back(span(workspace, kRmsWorkspaceBytes, true));
     if (!spans_ok(v)) return AR_ERR_ALIAS;
     return hip_status(launch_oneshot_rmsnorm(in, n, residual, weight, residual_out, out, rows, hidden, eps, dtype,
-                                             static_cast<hipStream_t>(stream)));
+                                             workspace, timeout_ticks(), static_cast<hipStream_t>(stream)));
 }
 
 int ar_reduce_bcast(const void* const* in, int n, void* const* out, size_t numel, int dtype, int r0, int r1,

@@ -77,11 +77,14 @@ hipError_t launch_flag_reset(uint32_t* flags, size_t words, hipStream_t s);
 
 // One-shot all-reduce + residual add + RMSNorm over rows of `hidden`
 // elements (hidden * element size a multiple of 16, at most 4096 16-byte
-// vectors per row).
+// vectors per row).  ws (may be null): the workspace of the cooperative
+// few-rows path, kRmsWorkspaceBytes, zeroed before first use.
 constexpr size_t kRmsMaxRowVecs = 4096;
+constexpr uint32_t kCoopGrid = 1024;
+constexpr size_t kRmsWorkspaceBytes = (size_t(kStatusWords) + kCoopGrid + 2 * size_t(kCoopGrid)) * 4;
 hipError_t launch_oneshot_rmsnorm(const void* const* in, int n, const void* residual, const void* weight,
                                   void* residual_out, void* out, size_t rows, size_t hidden, float eps, int dtype,
-                                  hipStream_t s);
+                                  uint32_t* ws, uint64_t timeout_ticks, hipStream_t s);
 
 // Allocation-free two-shot: a device array holding the arrival slots of up to
 // kMaxRanks ranks (the flag region without its epoch area, padded to 256

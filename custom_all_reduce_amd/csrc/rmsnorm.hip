@@ -16,10 +16,24 @@
 // ranks' vectors and the residual's with nontemporal loads, folds them,
 // stores residual_out and keeps h in registers.  The row's sum of h^2 goes
 // lane -> wavefront (xor shuffles) -> workgroup (LDS), then every lane
-// scales its h by the row's factor and the weight (plain loads: the same
-// hidden-length vector for every row, so it stays in the caches) and stores
-// the output.  One pass over HBM: the inputs and the residual are read
+// scales its h by the row's factor and the weight (plain loads, issued with
+// the data: the same hidden-length vector for every row, so it stays in the
+// caches) and stores the output.  One pass over HBM: the inputs and the residual are read
 // once, residual_out and the output written once.
+//
+// Few rows (a decode step's handful of tokens) would leave most compute
+// units idle with a workgroup per row, so with a workspace a fixed grid of
+// kCoopGrid one-wavefront workgroups splits every row into parts of 64
+// vectors: each part folds its vectors, stores residual_out, and publishes
+// the partial sum of its h^2 to its own slot as one 8-byte store of the
+// value and the call's step id (written together, so a reader that sees the
+// step sees the value, with no store wait, as in an LL line).  The parts of
+// a row poll their siblings' slots (bounded; a timeout is reported in the
+// workspace's status words), add the partials in slot order with the same
+// shuffle tree, so every part gets the same factor, and scale their own h.
+// The step id is the workgroup's epoch in the workspace plus one, stored
+// back at the end: every call advances every workgroup's epoch by one, so
+// all epochs agree and calls captured once into a graph need no host step.
 #include "ar_device.hpp"
 #include "ar_launch.hpp"
 
@@ -96,12 +110,14 @@ __device__ __forceinline__ void rmsnorm_row(const RmsParams& p, size_t row, floa
     const size_t base = row * p.vecs;
     const uint32_t row_bytes = p.vecs * 16u;
     float h[VPT][E];
+    u32x4 wv[VPT];  // the weight, loaded with the data: it does not wait for the row's factor
     float ss = 0.0f;
 #pragma unroll
     for (int j = 0; j < VPT; ++j) {
         const uint32_t v = tid + uint32_t(j) * blockDim.x;
         const bool valid = v < p.vecs;
         const uint32_t off = (valid ? v : 0u) * 16u;  // lanes past the row re-read its first vector
+        wv[j] = row_load<0>(buffer_range(p.weight, row_bytes), off);
         const u32x4 rv = row_load<kCachePolicyNt>(buffer_range(p.residual + base, row_bytes), off);
         // the ranks in batches of RB loads, each folded (rank order) before
         // the next is issued: with several vectors per lane all n loads at
@@ -143,7 +159,7 @@ __device__ __forceinline__ void rmsnorm_row(const RmsParams& p, size_t row, floa
         const uint32_t v = tid + uint32_t(j) * blockDim.x;
         if (v < p.vecs) {
             float w[E];
-            Vec<T>::widen(row_load<0>(buffer_range(p.weight, row_bytes), v * 16u), w);
+            Vec<T>::widen(wv[j], w);
             float y[E];
 #pragma unroll
             for (int e = 0; e < E; ++e) y[e] = (h[j][e] * f) * w[e];
@@ -168,14 +184,113 @@ __global__ __launch_bounds__(kMaxBlock) void oneshot_rmsnorm_kernel(RmsParams p)
     }
 }
 
+// Cooperative path (few rows): workspace layout in 32-bit words, after the
+// 32 status words: kCoopGrid epochs, then kCoopGrid 8-byte slots {partial
+// sum of h^2 as fp32 bits, step id}.
+constexpr uint32_t kEpochBase = kStatusWords;
+constexpr uint32_t kSlotBase = kStatusWords + kCoopGrid;  // word index of slot 0 (8-byte aligned)
+
+template <typename T, int NR>
+__global__ __launch_bounds__(kWave) void oneshot_rmsnorm_coop_kernel(RmsParams p, uint32_t* ws, uint32_t parts,
+                                                                     uint64_t timeout_ticks) {
+    constexpr int E = Vec<T>::E;
+    const uint32_t lane = threadIdx.x;
+    const uint32_t g = blockIdx.x;
+    // the epoch load goes out first and is used only after the data loads
+    // are issued, so its round trip overlaps theirs
+    const uint32_t epoch = flag_load_relaxed(ws + kEpochBase + g);
+    const uint32_t row = g / parts, part = g - row * parts;
+    uint32_t step = 0;
+    if (row < p.rows) {
+        const size_t base = size_t(row) * p.vecs;
+        const uint32_t row_bytes = p.vecs * 16u;
+        const uint32_t v = part * kWave + lane;
+        const bool valid = v < p.vecs;
+        const uint32_t off = (valid ? v : 0u) * 16u;
+        const u32x4 wv = row_load<0>(buffer_range(p.weight, row_bytes), off);
+        const u32x4 rv = row_load<kCachePolicyNt>(buffer_range(p.residual + base, row_bytes), off);
+        u32x4 x[NR];
+#pragma unroll
+        for (int r = 0; r < NR; ++r) x[r] = row_load<kCachePolicyNt>(buffer_range(p.in[r] + base, row_bytes), off);
+        Acc<T> acc;
+#pragma unroll
+        for (int r = 0; r < NR; ++r) acc.add(x[r]);
+        step = __builtin_amdgcn_readfirstlane(epoch) + 1u;
+        float res[E], h[E];
+        Vec<T>::widen(rv, res);
+        float ss = 0.0f;
+#pragma unroll
+        for (int e = 0; e < E; ++e) h[e] = acc.a[e] + res[e];
+        if (valid) {
+            row_store(buffer_range(p.residual_out + base, row_bytes), off, Vec<T>::narrow(h));
+#pragma unroll
+            for (int e = 0; e < E; ++e) ss += h[e] * h[e];
+        }
+        ss = wave_sum(ss);
+        // this part's slot: the value and the step in one 8-byte store
+        const __amdgpu_buffer_rsrc_t slots = buffer_range(ws + kSlotBase, kCoopGrid * 8u);
+        if (lane == 0)
+            __builtin_amdgcn_raw_buffer_store_b64(u32x2{__float_as_uint(ss), step}, slots, int(g * 8u), 0,
+                                                  kCachePolicySc1);
+        // the row's parts: lane q < parts polls slot row * parts + q
+        const bool mine = lane < parts;
+        const uint32_t soff = (row * parts + (mine ? lane : 0u)) * 8u;
+        u32x2 sl = __builtin_amdgcn_raw_buffer_load_b64(slots, int(soff), 0, kCachePolicySc1);
+        const uint64_t t0 = now_ticks();
+        bool timed_out = false;
+        while (true) {
+            const uint64_t missing = ~wave_ballot(!mine || sl.y >= step) & wave_exec();
+            if (missing == 0) break;
+            if (now_ticks() - t0 > timeout_ticks) {
+                if (lane == 0) report_timeout(ws, 4u, 0u, row);
+                timed_out = true;
+                break;
+            }
+            __builtin_amdgcn_s_sleep(1);
+            if (mine && sl.y < step) sl = __builtin_amdgcn_raw_buffer_load_b64(slots, int(soff), 0, kCachePolicySc1);
+        }
+        if (!timed_out) {
+            // the same values in the same lanes in every part of the row: the
+            // same total, the same factor
+            const float total = wave_sum(mine ? __uint_as_float(sl.x) : 0.0f);
+            const float f = 1.0f / sqrtf(total / p.hidden + p.eps);
+            if (valid) {
+                float w[E], y[E];
+                Vec<T>::widen(wv, w);
+#pragma unroll
+                for (int e = 0; e < E; ++e) y[e] = (h[e] * f) * w[e];
+                row_store(buffer_range(p.out + base, row_bytes), off, Vec<T>::narrow(y));
+            }
+        }
+    }
+    if (row >= p.rows) step = __builtin_amdgcn_readfirstlane(epoch) + 1u;
+    if (lane == 0) flag_store_relaxed(ws + kEpochBase + g, step);
+}
+
 // Rows up to this many get a workgroup each; beyond, the grid strides.
 constexpr size_t kRmsMaxGrid = size_t(1) << 20;
 
+// The cooperative path where it measured faster than a workgroup per row:
+// rows whose n + 1 input streams hold at least kCoopMinRowBytes (one
+// compute unit pulling that much is the bottleneck; below it the slot
+// exchange costs more than it saves) and at most kCoopMaxParts parts in all
+// (n = 8 bf16, hidden 8192: 4.8 against 5.1 us at 1 row, 5.2 against 5.6 at
+// 8, equal at 32, slower at 64; n = 16, 8 rows: 5.6 against 7.8; n = 2 and
+// hidden 4096 at n = 8: slower).
+constexpr uint32_t kCoopMinRowBytes = 128u << 10;
+constexpr uint32_t kCoopMaxParts = 512;
+
 template <typename T, int NR>
-hipError_t launch_t(const RmsParams& p, hipStream_t s) {
+hipError_t launch_t(const RmsParams& p, uint32_t* ws, uint64_t timeout_ticks, hipStream_t s) {
+    const uint32_t V = p.vecs;
+    const uint32_t parts = (V + kWave - 1) / kWave;
+    if (ws && p.rows * parts <= kCoopMaxParts && uint32_t(NR + 1) * V * 16u >= kCoopMinRowBytes) {
+        hipLaunchKernelGGL((oneshot_rmsnorm_coop_kernel<T, NR>), dim3(kCoopGrid), dim3(kWave), 0, s, p, ws, parts,
+                           timeout_ticks);
+        return hipGetLastError();
+    }
     // vectors per lane and workgroup size: every row fits one workgroup of
     // at most 1024 lanes with 1, 2 or 4 vectors each
-    const uint32_t V = p.vecs;
     const int vpt = V <= 1024u ? 1 : (V <= 2048u ? 2 : 4);
     uint32_t block = (V + uint32_t(vpt) - 1) / uint32_t(vpt);
     block = (block + kWave - 1) / kWave * kWave;
@@ -199,7 +314,7 @@ hipError_t launch_t(const RmsParams& p, hipStream_t s) {
 
 hipError_t launch_oneshot_rmsnorm(const void* const* in, int n, const void* residual, const void* weight,
                                   void* residual_out, void* out, size_t rows, size_t hidden, float eps, int dtype,
-                                  hipStream_t s) {
+                                  uint32_t* ws, uint64_t timeout_ticks, hipStream_t s) {
     RmsParams p{};
     for (int r = 0; r < n; ++r) p.in[r] = static_cast<const u32x4*>(in[r]);
     p.residual = static_cast<const u32x4*>(residual);
@@ -212,7 +327,7 @@ hipError_t launch_oneshot_rmsnorm(const void* const* in, int n, const void* resi
     p.eps = eps;
     return dispatch_ranks(n, [&](auto nr) {
         constexpr int NR = decltype(nr)::value;
-        return dtype == 0 ? launch_t<float, NR>(p, s) : launch_t<bf16_t, NR>(p, s);
+        return dtype == 0 ? launch_t<float, NR>(p, ws, timeout_ticks, s) : launch_t<bf16_t, NR>(p, ws, timeout_ticks, s);
     });
 }
 

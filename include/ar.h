@@ -88,6 +88,7 @@ typedef enum { AR_PROTO_LL = 0, AR_PROTO_LL128 = 1 } ar_proto;
 #define AR_PHASE_TWOSHOT_AG 1
 #define AR_PHASE_LL 2
 #define AR_PHASE_LL128 3
+#define AR_PHASE_RMSNORM 4
 
 /* Bytes of the flag region used by the two-shot barrier and the LL status
  * word for up to n ranks: a 128-byte status line (word 0 status, word 1
@@ -138,6 +139,18 @@ int ar_oneshot(const void* const* in, int n, void* out, size_t numel, int dtype,
  *                 (updated in place) but may not otherwise overlap anything.
  *  weight       : hidden elements, the same for every row.
  *  out          : rows * hidden elements; may not overlap any other buffer.
+ *  workspace    : NULL, or ar_rmsnorm_workspace_bytes() bytes, 16-byte
+ *                 aligned and zeroed before its first use, owned by one call
+ *                 site (calls sharing it must be ordered).  With it, few
+ *                 heavy rows (rows * ceil(vectors per row / 64) <= 512 and
+ *                 (n + 1) * hidden * element size >= 128 KiB: a decode
+ *                 step's tokens) are split over a fixed grid of one-wavefront
+ *                 workgroups that exchange their partial sums of squares
+ *                 through it; its step ids advance by themselves, so the call
+ *                 may be captured once into a graph.
+ *                 A part that waits longer than the poll budget writes
+ *                 AR_ERR_TIMEOUT | AR_PHASE_RMSNORM << 8 to its first word
+ *                 (detail word: the row) and leaves that part of out unwritten.
  *  hidden * element size must be a multiple of 16 and at most 64 KiB
  *  (32768 bf16 / 16384 fp32 elements); eps >= 0 and finite.
  * residual_out matches the oracle bit for bit; out is fp32 arithmetic whose
@@ -145,8 +158,10 @@ int ar_oneshot(const void* const* in, int n, void* out, size_t numel, int dtype,
  * the correctly rounded value.  Reads (n + 1) * S + hidden * element size
  * bytes and writes 2 * S (S = rows * hidden * element size).
  * Errors: AR_ERR_ARG, AR_ERR_ALIGN, AR_ERR_DIVISIBLE, AR_ERR_ALIAS, AR_ERR_HIP. */
+size_t ar_rmsnorm_workspace_bytes(void);
 int ar_oneshot_rmsnorm(const void* const* in, int n, const void* residual, const void* weight, void* residual_out,
-                       void* out, size_t rows, size_t hidden, float eps, int dtype, void* stream);
+                       void* out, size_t rows, size_t hidden, float eps, int dtype, uint32_t* workspace,
+                       void* stream);
 
 /* Reduce with a broadcast store: the kBroadcast store path of [CAR] step 5
  * -- each result written to every rank's output, not only the local one --

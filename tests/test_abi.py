@@ -436,7 +436,11 @@ def test_size_checks_reject_undersized_buffers():
 
 
 def test_oneshot_rmsnorm_argument_errors():
-    f = L.ar_oneshot_rmsnorm
+    f0 = L.ar_oneshot_rmsnorm
+
+    def f(*a):  # without a workspace (its checks are below)
+        return f0(*a[:-1], None, a[-1])
+
     n, rows, hidden = 4, 8, 4096
     ins = fake_ins(n)
     res, w, ro, out = A + (64 << 30), A + (65 << 30), A + (66 << 30), A + (67 << 30)
@@ -464,3 +468,13 @@ def test_oneshot_rmsnorm_argument_errors():
     assert f(ins, n, res, w, ro, ro + 1024, rows, hidden, 1e-6, 1, NUL) == car.AR_ERR_ALIAS
     assert f(ins, n, res, w, res + 1024, out, rows, hidden, 1e-6, 1, NUL) == car.AR_ERR_ALIAS
     assert f(ins, n, res, w, A + (1 << 30), out, rows, hidden, 1e-6, 1, NUL) == car.AR_ERR_ALIAS
+    # the workspace: aligned, and not overlapping any other buffer
+    ws = A + (68 << 30)
+    assert f0(ins, n, res, w, ro, out, rows, hidden, 1e-6, 1, ws + 4, NUL) == car.AR_ERR_ALIGN
+    assert f0(ins, n, res, w, ro, out, rows, hidden, 1e-6, 1, out + 64, NUL) == car.AR_ERR_ALIAS
+    assert f0(ins, n, res, w, ro, out, rows, hidden, 1e-6, 1, w, NUL) == car.AR_ERR_ALIAS
+
+
+def test_rmsnorm_workspace_size():
+    # 32 status words, 1024 epochs and 1024 8-byte slots
+    assert car.rmsnorm_workspace_bytes() == (32 + 1024 + 2 * 1024) * 4
