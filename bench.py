@@ -486,8 +486,17 @@ def sweep(args, torch, car, np, out_path):
                 rig = Rig(torch, car, np, n, dt_name, S // es, args.rotate_gib * (1 << 30), full=True)
                 fl = rig.flags
                 extra = {}
+                # the fused all-reduce + RMSNorm over rows of 16 KiB, with a workspace (its
+                # few-rows path where that applies); residual, residual_out and output are
+                # three of the set's other output buffers
+                rms_row = 16 << 10
+                rms_w = torch.ones(rms_row // es, dtype=rig.dt, device="cuda")
+                rms_ws = car.new_rmsnorm_workspace()
                 for i, b in enumerate(rig.sets):
                     c = rig.calls[i]
+                    rn = car.prepare_oneshot_rmsnorm(b.ins, b.outs[1], rms_w, b.outs[2], b.outs[3], 1e-6,
+                                                     workspace=rms_ws)
+                    c["oneshot_rmsnorm"] = lambda s, f=rn: f()
                     c["ll_pack"] = car.prepare_ll_pack([b.ins[ME]], [b.w_ll[ME]], "ll")
                     c["ll_reduce"] = car.prepare_ll_reduce(b.w_ll, b.out_ll, fl, "ll")
                     c["ll128_pack"] = car.prepare_ll_pack([b.ins[ME]], [b.w_128[ME]], "ll128")
@@ -521,6 +530,7 @@ def sweep(args, torch, car, np, out_path):
                     ("bcast", acc.reduce_bcast(n, S, 1)), ("bcast_full", acc.reduce_bcast(n, S, n)),
                     ("push", acc.push(S, n)), ("stage", acc.push(S, 1)), ("ag_copy", acc.twoshot_ag(n, S, 1)),
                     ("twoshot_auto", acc.twoshot(n, S, 1)),
+                    ("oneshot_rmsnorm", acc.oneshot_rmsnorm(n, S, rms_row)),
                     # the all-rank launches last: they rewrite every rank's segments
                     ("twoshot_full", acc.twoshot(n, S, n)), ("twoshot_ll_full", acc.twoshot_ll(n, S, n, "ll")),
                     ("twoshot_ll128_full", acc.twoshot_ll(n, S, n, "ll128"))]

@@ -19,6 +19,8 @@ and every write, each byte once.  S = numel * element size (bytes per rank).
   LL / LL128 reduce       reads n*W(S)            writes S
   LL / LL128 send and     reads S (own message) + (n-1)*W(S) (the peers' wires)
     receive, one launch   writes W(S) (own wire) + S
+  one-shot + residual +   reads n*S + S (residual) + one row (the weight)
+    RMSNorm               writes S (residual_out) + S (output)
 
 The fused two-shot kernel writes rank r's own segment of its output straight
 from the reduce-scatter's registers and never reads it back, so it moves
@@ -44,6 +46,13 @@ def wire_bytes(proto: str, S: int) -> int:
 
 def oneshot(n: int, S: int):
     return n * S, S
+
+
+def oneshot_rmsnorm(n: int, S: int, row_bytes: int):
+    """One-shot all-reduce + residual add + RMSNorm over rows of row_bytes:
+    the n inputs and the residual once, the weight (one row) once; residual_out
+    and the output once."""
+    return n * S + S + row_bytes, 2 * S
 
 
 def twoshot(n: int, S: int, ranks: int):
