@@ -5,6 +5,7 @@
  * Test infrastructure: it links the oracle (liboracle.so) to check the
  * library (libar.so).  Exit status 0 when every case matches.
  */
+#include <math.h>
 #include <stdint.h>
 #include <stdio.h>
 #include <stdlib.h>
@@ -17,6 +18,8 @@
 /* the oracle's entry points (oracle/ar_oracle.c) */
 void oracle_oneshot(const void* const* in, int n, void* out, size_t numel, int dtype);
 size_t oracle_ll_wire_bytes(int proto, size_t nbytes);
+void oracle_oneshot_rmsnorm(const void* const* in, int n, const void* residual, const void* weight,
+                            void* residual_out, double* y, size_t rows, size_t hidden, double eps, int dtype);
 
 #define CHECK_HIP(x)                                                              \
     do {                                                                          \
@@ -166,6 +169,53 @@ int main(void) {
     CHECK_HIP(hipFree(out));
     CHECK_HIP(hipFree(flags));
     teardown(&c);
+
+    /* the fused all-reduce + residual add + RMSNorm, fp32, with a workspace: residual_out bit
+     * for bit, out within 4e-6 of the oracle's fp64 value (the bound derived for the device's
+     * fp32 sum of squares) */
+    {
+        const size_t rows = 6, hidden = 4096;
+        setup(&c, 8, rows * hidden, AR_F32);
+        float* res = malloc(c.bytes);
+        float* w = malloc(hidden * 4);
+        float* ro_want = malloc(c.bytes);
+        float* got = malloc(c.bytes);
+        double* y = malloc(c.numel * sizeof(double));
+        fill(res, c.numel, AR_F32);
+        fill(w, hidden, AR_F32);
+        oracle_oneshot_rmsnorm((const void* const*)c.host, c.n, res, w, ro_want, y, rows, hidden, 1e-6, AR_F32);
+        void *d_res, *d_w, *d_ro, *d_out, *d_ws;
+        CHECK_HIP(hipMalloc(&d_res, c.bytes));
+        CHECK_HIP(hipMalloc(&d_w, hidden * 4));
+        CHECK_HIP(hipMalloc(&d_ro, c.bytes));
+        CHECK_HIP(hipMalloc(&d_out, c.bytes));
+        CHECK_HIP(hipMalloc(&d_ws, ar_rmsnorm_workspace_bytes()));
+        CHECK_HIP(hipMemset(d_ws, 0, ar_rmsnorm_workspace_bytes()));
+        CHECK_HIP(hipMemcpy(d_res, res, c.bytes, hipMemcpyHostToDevice));
+        CHECK_HIP(hipMemcpy(d_w, w, hidden * 4, hipMemcpyHostToDevice));
+        ok &= ar_oneshot_rmsnorm((const void* const*)c.dev, c.n, d_res, d_w, d_ro, d_out, rows, hidden, 1e-6f,
+                                 AR_F32, (uint32_t*)d_ws, NULL) == AR_OK;
+        CHECK_HIP(hipDeviceSynchronize());
+        CHECK_HIP(hipMemcpy(got, d_ro, c.bytes, hipMemcpyDeviceToHost));
+        int good = memcmp(got, ro_want, c.bytes) == 0;
+        CHECK_HIP(hipMemcpy(got, d_out, c.bytes, hipMemcpyDeviceToHost));
+        for (size_t i = 0; i < c.numel; ++i) good &= fabs((double)got[i] - y[i]) <= 4e-6 * fabs(y[i]);
+        CHECK_HIP(hipMemcpy(&status, d_ws, 4, hipMemcpyDeviceToHost));
+        good &= status == 0;
+        printf("%-40s n=%2d numel=%8zu f32 : %s\n", "ar_oneshot_rmsnorm", c.n, c.numel, good ? "ok" : "MISMATCH");
+        ok &= good;
+        CHECK_HIP(hipFree(d_res));
+        CHECK_HIP(hipFree(d_w));
+        CHECK_HIP(hipFree(d_ro));
+        CHECK_HIP(hipFree(d_out));
+        CHECK_HIP(hipFree(d_ws));
+        free(res);
+        free(w);
+        free(ro_want);
+        free(got);
+        free(y);
+        teardown(&c);
+    }
 
     printf(ok ? "c abi ok\n" : "c abi FAILED\n");
     return ok ? 0 : 1;
