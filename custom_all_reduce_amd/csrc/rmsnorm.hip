@@ -11,20 +11,22 @@
 //            computed in fp32 and rounded once to the data type.
 // residual_out may be the residual buffer itself (updated in place).
 //
-// Work.  A workgroup owns a row (grid-stride over rows): each lane takes
-// 16-byte vectors v = lane + j * blockDim (j < VPT) of the row, loads the
-// ranks' vectors and the residual's with nontemporal loads, folds them,
-// stores residual_out and keeps h in registers.  The row's sum of h^2 goes
-// lane -> wavefront (xor shuffles) -> workgroup (LDS), then every lane
-// scales its h by the row's factor and the weight (plain loads, issued with
-// the data: the same hidden-length vector for every row, so it stays in the
-// caches) and stores the output.  One pass over HBM: the inputs and the residual are read
-// once, residual_out and the output written once.
+// Work.  A workgroup owns a row (above 2^20 rows the workgroups stride over
+// the rows): each lane takes 16-byte vectors v = lane + j * blockDim
+// (j < VPT) of the row, loads the ranks' vectors and the residual's with
+// nontemporal loads, folds them, stores residual_out and keeps h in
+// registers.  The row's sum of h^2 goes lane -> wavefront (xor shuffles) ->
+// workgroup (LDS), then every lane scales its h by the row's factor and the
+// weight (plain loads, issued with the data: the same hidden-length vector
+// for every row, so it stays in the caches) and stores the output.  One pass
+// over HBM: the inputs and the residual are read once, residual_out and the
+// output written once.
 //
-// Few rows (a decode step's handful of tokens) would leave most compute
-// units idle with a workgroup per row, so with a workspace a fixed grid of
-// kCoopGrid one-wavefront workgroups splits every row into parts of 64
-// vectors: each part folds its vectors, stores residual_out, and publishes
+// Few heavy rows (a decode step's handful of tokens) put a whole row's
+// n + 1 streams through one compute unit with a workgroup per row, so with a
+// workspace a fixed grid of kCoopGrid one-wavefront workgroups splits such
+// rows into parts of 64 vectors: each part folds its vectors, stores
+// residual_out, and publishes
 // the partial sum of its h^2 to its own slot as one 8-byte store of the
 // value and the call's step id (written together, so a reader that sees the
 // step sees the value, with no store wait, as in an LL line).  The parts of
