@@ -10,6 +10,8 @@ Functions mirror the C entry points and take ``torch.Tensor`` arguments:
     ar_oneshot(ins, out)                         one output = sum of ranks
     ar_oneshot_rmsnorm(ins, residual, weight, residual_out, out, eps, workspace=None)
                                                  the same, + residual, then RMSNorm of each row
+    ar_twoshot_rmsnorm(ins, residuals, weight, segs, flags, step, r0=0, r1=None,
+                       residual_outs=None, outs=None, eps=1e-6)   its two-shot form (rows split by rank)
     ar_twoshot_rs(ins, segs, flags, step, r0=0, r1=None, outs=None)
     ar_twoshot_ag(segs, outs, flags, step, r0=0, r1=None)
     ar_ll_pack(srcs, wires, proto, step)
@@ -79,6 +81,8 @@ def _load(path: str = LIB_PATH):
     lib.ar_oneshot_rmsnorm.argtypes = [P, i32, vp, vp, vp, vp, sz, sz, ctypes.c_float, i32, vp, vp]
     lib.ar_oneshot_rmsnorm.restype = i32
     lib.ar_rmsnorm_workspace_bytes.argtypes, lib.ar_rmsnorm_workspace_bytes.restype = [], sz
+    lib.ar_twoshot_rmsnorm.argtypes = [P, i32, P, vp, P, P, P, sz, sz, ctypes.c_float, i32, i32, i32, vp, u32, vp]
+    lib.ar_twoshot_rmsnorm.restype = i32
     lib.ar_reduce_bcast.argtypes, lib.ar_reduce_bcast.restype = [P, i32, P, sz, i32, i32, i32, vp], i32
     lib.ar_push.argtypes, lib.ar_push.restype = [P, i32, P, i32, sz, i32, vp], i32
     lib.ar_twoshot_rs.argtypes, lib.ar_twoshot_rs.restype = [P, i32, P, sz, i32, i32, i32, vp, u32, P, vp], i32
@@ -329,6 +333,64 @@ def prepare_oneshot_rmsnorm(ins, residual: torch.Tensor, weight: torch.Tensor, r
             residual_out.data_ptr(), out.data_ptr(), out.numel() // hidden, hidden, float(eps), dt, ws, None]
     return Prepared(_lib.ar_oneshot_rmsnorm, args, None, "ar_oneshot_rmsnorm",
                     (ins, residual, weight, residual_out, out, workspace))
+
+
+def rmsnorm_segment_elems(n: int, rows: int, hidden: int) -> int:
+    """Elements of one rank's segment in ar_twoshot_rmsnorm: its rows of out, then of residual_out."""
+    return 2 * (rows // n) * hidden
+
+
+def prepare_twoshot_rmsnorm(ins, residuals, weight: torch.Tensor, segs, flags: torch.Tensor, r0: int = 0,
+                            r1=None, residual_outs=None, outs=None, eps: float = 1e-6) -> Prepared:
+    """The fused all-reduce + residual add + RMSNorm in two-shot form (see
+    ar_twoshot_rmsnorm in include/ar.h).  outs / residual_outs None: the
+    reduce-scatter of ranks [r0, r1) alone; else one rank's share (r1 = r0 + 1),
+    with n entries each (None outside [r0, r1)).  Called with the step id."""
+    n = len(ins)
+    r1 = r0 + 1 if r1 is None else r1
+    ins = [_dev_tensor(t, "input") for t in ins]
+    ref = ins[0]
+    weight = _dev_tensor(weight, "weight")
+    hidden = weight.numel()
+    dt = _dtype_code(ref)
+    if hidden == 0 or ref.numel() % hidden != 0:
+        raise ValueError(f"inputs hold {ref.numel()} elements, not whole rows of {hidden}")
+    rows = ref.numel() // hidden
+    _need_like(ins, ref.dtype, ref.numel(), "every input")
+    _need_like([weight], ref.dtype, hidden, "weight")
+    if len(residuals) != n or len(segs) != n:
+        raise ValueError("residuals and segs need one entry per rank")
+    mine = range(r0, r1)
+    for r in mine:
+        _need_like([_dev_tensor(residuals[r], "residual")], ref.dtype, ref.numel(), "every residual in [r0, r1)")
+    segs = [_dev_tensor(t, "segment") for t in segs]
+    if rows % n == 0:
+        _need_like(segs, ref.dtype, rmsnorm_segment_elems(n, rows, hidden), "every segment")
+    _need_bytes([_dev_tensor(flags, "flags")], flag_bytes(n), "the flag region")
+    ro_arr = o_arr = None
+    if (outs is None) != (residual_outs is None):
+        raise ValueError("pass both outs and residual_outs, or neither")
+    if outs is not None:
+        if len(outs) != n or len(residual_outs) != n:
+            raise ValueError("outs and residual_outs need n entries (None outside [r0, r1))")
+        for r in mine:
+            _need_like([_dev_tensor(outs[r], "out"), _dev_tensor(residual_outs[r], "residual_out")], ref.dtype,
+                       ref.numel(), "every output in [r0, r1)")
+        o_arr = _ptr_array([outs[r].data_ptr() if r in mine else 0 for r in range(n)])
+        ro_arr = _ptr_array([residual_outs[r].data_ptr() if r in mine else 0 for r in range(n)])
+    res_arr = _ptr_array([residuals[r].data_ptr() if r in mine else 0 for r in range(n)])
+    args = [_ptr_array([t.data_ptr() for t in ins]), n, res_arr, weight.data_ptr(),
+            _ptr_array([t.data_ptr() for t in segs]), ro_arr, o_arr, rows, hidden, float(eps), dt, r0, r1,
+            flags.data_ptr(), 0, None]
+    return Prepared(_lib.ar_twoshot_rmsnorm, args, 14, "ar_twoshot_rmsnorm",
+                    (ins, residuals, weight, segs, flags, outs, residual_outs))
+
+
+def ar_twoshot_rmsnorm(ins, residuals, weight, segs, flags, step: int, r0: int = 0, r1=None, residual_outs=None,
+                       outs=None, eps: float = 1e-6, stream=None):
+    """ar_twoshot_rmsnorm: the reduce-scatter of ranks [r0, r1) (outs None), or
+    one rank's share with the all-gather of its peers' rows."""
+    prepare_twoshot_rmsnorm(ins, residuals, weight, segs, flags, r0, r1, residual_outs, outs, eps)(step, stream)
 
 
 def _same_shape(ts, ref, what):

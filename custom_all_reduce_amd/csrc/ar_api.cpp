@@ -272,6 +272,52 @@ int ar_oneshot_rmsnorm(const void* const* in, int n, const void* residual, const
                                              workspace, timeout_ticks(), static_cast<hipStream_t>(stream)));
 }
 
+int ar_twoshot_rmsnorm(const void* const* in, int n, const void* const* residual, const void* weight,
+                       void* const* seg, void* const* residual_out, void* const* out, size_t rows, size_t hidden,
+                       float eps, int dtype, int r0, int r1, uint32_t* flags, uint32_t step, void* stream) {
+    if (!in || !residual || !weight || !seg || !flags || !ranks_ok(n) || !dtype_ok(dtype) || rows == 0 ||
+        hidden == 0 || step == 0)
+        return AR_ERR_ARG;
+    if (r0 < 0 || r1 > n || r0 >= r1) return AR_ERR_ARG;
+    const bool fused = out != nullptr;
+    if (fused != (residual_out != nullptr)) return AR_ERR_ARG;
+    if (fused && r1 != r0 + 1) return AR_ERR_ARG;  // the all-gather: one rank's share per launch
+    if (!(eps >= 0.0f && eps <= FLT_MAX)) return AR_ERR_ARG;
+    const size_t es = elem_bytes(dtype);
+    if (hidden > kRmsMaxRowVecs * 16 / es || rows > kMaxBytes / es / hidden) return AR_ERR_ARG;
+    for (int i = 0; i < n; ++i) {
+        if (!in[i] || !seg[i]) return AR_ERR_ARG;
+        if (!aligned16(in[i]) || !aligned16(seg[i])) return AR_ERR_ALIGN;
+    }
+    for (int r = r0; r < r1; ++r) {
+        if (!residual[r] || (fused && (!residual_out[r] || !out[r]))) return AR_ERR_ARG;
+        if (!aligned16(residual[r]) || (fused && (!aligned16(residual_out[r]) || !aligned16(out[r]))))
+            return AR_ERR_ALIGN;
+    }
+    if (!aligned16(weight) || !aligned16(flags)) return AR_ERR_ALIGN;
+    if ((hidden * es) % 16 != 0 || rows % size_t(n) != 0) return AR_ERR_DIVISIBLE;
+    const size_t S = rows * hidden * es, seg_bytes = 2 * (rows / size_t(n)) * hidden * es;
+    std::vector<Span> v;
+    v.push_back(span(flags, ar_flag_bytes(n), true));
+    v.push_back(span(weight, hidden * es, false));
+    for (int i = 0; i < n; ++i) {
+        v.push_back(span(in[i], S, false));
+        const bool mine = i >= r0 && i < r1;
+        if (mine || fused) v.push_back(span(seg[i], seg_bytes, mine));
+    }
+    for (int r = r0; r < r1; ++r) {
+        v.push_back(span(residual[r], S, false));
+        if (fused) {
+            v.push_back(span(residual_out[r], S, true));
+            v.push_back(span(out[r], S, true));
+        }
+    }
+    if (!spans_ok(v)) return AR_ERR_ALIAS;
+    return hip_status(launch_twoshot_rmsnorm(in, n, residual, weight, seg, residual_out, out, rows, hidden, eps,
+                                             dtype, r0, r1, flags, step, timeout_ticks(),
+                                             static_cast<hipStream_t>(stream)));
+}
+
 int ar_reduce_bcast(const void* const* in, int n, void* const* out, size_t numel, int dtype, int r0, int r1,
                     void* stream) {
     if (!in || !out || !ranks_ok(n) || !dtype_ok(dtype) || numel == 0) return AR_ERR_ARG;

@@ -85,6 +85,15 @@ constexpr size_t kRmsWorkspaceBytes = (size_t(kStatusWords) + kCoopGrid + 2 * si
 hipError_t launch_oneshot_rmsnorm(const void* const* in, int n, const void* residual, const void* weight,
                                   void* residual_out, void* out, size_t rows, size_t hidden, float eps, int dtype,
                                   uint32_t* ws, uint64_t timeout_ticks, hipStream_t s);
+// Its two-shot form: rank r's reduce-scatter owns rows [r G, (r+1) G),
+// G = rows / n, and writes them (out rows, then residual_out rows) to seg[r]
+// with an arrival slot per tile; out == null: the reduce-scatter of ranks
+// [r0, r1) alone; else one rank's share (r1 == r0 + 1), the all-gather of
+// the peers' rows included.
+hipError_t launch_twoshot_rmsnorm(const void* const* in, int n, const void* const* residual, const void* weight,
+                                  void* const* seg, void* const* residual_out, void* const* out, size_t rows,
+                                  size_t hidden, float eps, int dtype, int r0, int r1, uint32_t* flags,
+                                  uint32_t step, uint64_t timeout_ticks, hipStream_t s);
 
 // Allocation-free two-shot: a device array holding the arrival slots of up to
 // kMaxRanks ranks (the flag region without its epoch area, padded to 256

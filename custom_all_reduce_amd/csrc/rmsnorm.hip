@@ -100,16 +100,32 @@ __device__ __forceinline__ void row_store(__amdgpu_buffer_rsrc_t r, uint32_t off
     __builtin_amdgcn_raw_buffer_store_b128(v, r, int(off), 0, kCachePolicyNt);
 }
 
+// Where one row's results go: residual_out and out (nontemporal stores),
+// and, in the two-shot's reduce-scatter, the row's copies in the rank's
+// segment (device-coherent stores: the peers' all-gathers read them).  A
+// null pointer is not written.  Each is the row's first vector.
+struct RowDst {
+    u32x4* res_out;
+    u32x4* out;
+    u32x4* seg_res;
+    u32x4* seg_out;
+};
+
+__device__ __forceinline__ void row_store_coherent(u32x4* row, uint32_t row_bytes, uint32_t off, u32x4 v) {
+    st_coherent(buffer_range(row, row_bytes), off, v);
+}
+
+// One row: base = the row's first vector in the ranks' inputs, residual =
+// the row's first vector of the residual.
 template <typename T, int NR, int VPT>
-__device__ __forceinline__ void rmsnorm_row(const RmsParams& p, size_t row, float (&part)[kMaxWaves],
-                                            float& factor) {
+__device__ __forceinline__ void rmsnorm_row(const RmsParams& p, size_t base, const u32x4* residual, RowDst d,
+                                            float (&part)[kMaxWaves], float& factor) {
     constexpr int E = Vec<T>::E;
     constexpr int RB = VPT == 1 || NR <= 8 ? NR : 8;  // loads in flight per vector
     const uint32_t tid = threadIdx.x;
     const uint32_t lane = tid & (kWave - 1);
     const uint32_t wave = tid / kWave;
     const uint32_t nwaves = blockDim.x / kWave;
-    const size_t base = row * p.vecs;
     const uint32_t row_bytes = p.vecs * 16u;
     float h[VPT][E];
     u32x4 wv[VPT];  // the weight, loaded with the data: it does not wait for the row's factor
@@ -120,7 +136,7 @@ __device__ __forceinline__ void rmsnorm_row(const RmsParams& p, size_t row, floa
         const bool valid = v < p.vecs;
         const uint32_t off = (valid ? v : 0u) * 16u;  // lanes past the row re-read its first vector
         wv[j] = row_load<0>(buffer_range(p.weight, row_bytes), off);
-        const u32x4 rv = row_load<kCachePolicyNt>(buffer_range(p.residual + base, row_bytes), off);
+        const u32x4 rv = row_load<kCachePolicyNt>(buffer_range(residual, row_bytes), off);
         // the ranks in batches of RB loads, each folded (rank order) before
         // the next is issued: with several vectors per lane all n loads at
         // once would not fit in registers beside the kept h
@@ -141,7 +157,9 @@ __device__ __forceinline__ void rmsnorm_row(const RmsParams& p, size_t row, floa
 #pragma unroll
         for (int e = 0; e < E; ++e) h[j][e] = acc.a[e] + res[e];
         if (valid) {
-            row_store(buffer_range(p.residual_out + base, row_bytes), off, Vec<T>::narrow(h[j]));
+            const u32x4 hv = Vec<T>::narrow(h[j]);
+            if (d.res_out) row_store(buffer_range(d.res_out, row_bytes), off, hv);
+            if (d.seg_res) row_store_coherent(d.seg_res, row_bytes, off, hv);
 #pragma unroll
             for (int e = 0; e < E; ++e) ss += h[j][e] * h[j][e];
         }
@@ -165,7 +183,9 @@ __device__ __forceinline__ void rmsnorm_row(const RmsParams& p, size_t row, floa
             float y[E];
 #pragma unroll
             for (int e = 0; e < E; ++e) y[e] = (h[j][e] * f) * w[e];
-            row_store(buffer_range(p.out + base, row_bytes), v * 16u, Vec<T>::narrow(y));
+            const u32x4 yv = Vec<T>::narrow(y);
+            if (d.out) row_store(buffer_range(d.out, row_bytes), v * 16u, yv);
+            if (d.seg_out) row_store_coherent(d.seg_out, row_bytes, v * 16u, yv);
         }
     }
 }
@@ -178,12 +198,125 @@ __global__ __launch_bounds__(kMaxBlock) void oneshot_rmsnorm_kernel(RmsParams p)
     __shared__ float factor;
     if constexpr (kLoop) {
         for (size_t row = blockIdx.x; row < p.rows; row += gridDim.x) {
-            rmsnorm_row<T, NR, VPT>(p, row, part, factor);
+            const size_t base = row * p.vecs;
+            rmsnorm_row<T, NR, VPT>(p, base, p.residual + base,
+                                    RowDst{p.residual_out + base, p.out + base, nullptr, nullptr}, part, factor);
             __syncthreads();  // part and factor are rewritten by the next row
         }
     } else {
-        rmsnorm_row<T, NR, VPT>(p, blockIdx.x, part, factor);
+        const size_t base = size_t(blockIdx.x) * p.vecs;
+        rmsnorm_row<T, NR, VPT>(p, base, p.residual + base,
+                                RowDst{p.residual_out + base, p.out + base, nullptr, nullptr}, part, factor);
     }
+}
+
+// ---------------------------------------------------------------------------
+// The two-shot form.  The reduce-scatter owns whole rows: rank r's group is
+// rows [r G, (r + 1) G), G = rows / n, so a rank finishes the norm of its
+// rows alone (a workgroup per row, the same per-row code as above, so the
+// same bits).  It writes its own outputs' rows and copies both results of
+// its rows into its segment (out rows, then residual_out rows) with
+// device-coherent stores; each tile of rows is published with an arrival
+// slot in the flag region once every store of the tile is complete.  The
+// all-gather of one rank's share polls a peer tile's slot and copies that
+// tile's out and residual_out rows into its outputs.  One rank's share is
+// one launch (no workgroup waits on another of the same launch); every
+// rank's reduce-scatter alone is another (for the peers, or for all ranks
+// before their shares).
+struct TsRmsParams {
+    RmsParams p;  // inputs, weight, row size, eps (residual and outputs unused)
+    const u32x4* residual[kMaxRanks];
+    u32x4* seg[kMaxRanks];
+    u32x4* res_out[kMaxRanks];
+    u32x4* out[kMaxRanks];
+    uint32_t* flags;
+    uint64_t timeout_ticks;
+    uint32_t step;
+    int r0, r1;
+    uint32_t group;   // rows per rank
+    uint32_t tile;    // rows per arrival slot
+    uint32_t ntiles;  // slots per rank
+    int do_ag;
+};
+
+template <typename T, int NR, int VPT>
+__global__ __launch_bounds__(kMaxBlock) void twoshot_rmsnorm_kernel(TsRmsParams q) {
+    __shared__ float part[kMaxWaves];
+    __shared__ float factor;
+    const RmsParams& p = q.p;
+    const uint32_t R = uint32_t(q.r1 - q.r0);
+    const uint32_t rs_items = R * q.ntiles;
+    uint32_t* slots = q.flags + kStatusWords;
+    const uint32_t b = blockIdx.x;
+    if (b < rs_items) {
+        const uint32_t rr = b / q.ntiles, t = b - rr * q.ntiles;
+        const uint32_t r = uint32_t(q.r0) + rr;
+        const uint32_t k1 = min((t + 1u) * q.tile, q.group);
+        for (uint32_t k = t * q.tile; k < k1; ++k) {
+            const size_t base = (size_t(r) * q.group + k) * p.vecs;
+            RowDst d{q.do_ag ? q.res_out[r] + base : nullptr, q.do_ag ? q.out[r] + base : nullptr,
+                     q.seg[r] + (size_t(q.group) + k) * p.vecs, q.seg[r] + size_t(k) * p.vecs};
+            rmsnorm_row<T, NR, VPT>(p, base, q.residual[r] + base, d, part, factor);
+            __syncthreads();  // part and factor are rewritten by the next row
+        }
+        // publish the tile once every wavefront's stores are complete
+        wait_stores();
+        __syncthreads();
+        if (threadIdx.x == 0) flag_store_relaxed(slots + r * kSlotsPerRank + t, q.step);
+        return;
+    }
+    // all-gather item: (output rank, peer, tile)
+    const uint32_t c = b - rs_items;
+    const uint32_t per_out = uint32_t(NR - 1) * q.ntiles;
+    const uint32_t oo = c / per_out;
+    if (oo >= R) return;
+    const uint32_t rem = c - oo * per_out;
+    const uint32_t r = uint32_t(q.r0) + oo;
+    const uint32_t jj = rem / q.ntiles, t = rem - jj * q.ntiles;
+    const uint32_t j = jj < r ? jj : jj + 1u;  // every rank but r
+    const uint32_t lane = threadIdx.x & (kWave - 1);
+    // every wavefront polls the tile's slot itself (bounded)
+    uint32_t seen = flag_load_relaxed(slots + j * kSlotsPerRank + t);
+    const uint64_t t0 = now_ticks();
+    while (__builtin_amdgcn_readfirstlane(seen) < q.step) {
+        if (now_ticks() - t0 > q.timeout_ticks) {
+            if (lane == 0) report_timeout(q.flags, 1u, j, t);
+            return;
+        }
+        __builtin_amdgcn_s_sleep(1);
+        seen = flag_load_relaxed(slots + j * kSlotsPerRank + t);
+    }
+    // the tile's rows of both results: out rows k, then residual_out rows
+    const uint32_t k0 = t * q.tile, k1 = min(k0 + q.tile, q.group);
+    const uint32_t tv = (k1 - k0) * p.vecs;  // vectors per result in this tile
+    const __amdgpu_buffer_rsrc_t so = buffer_range(q.seg[j] + size_t(k0) * p.vecs, tv * 16u);
+    const __amdgpu_buffer_rsrc_t sr = buffer_range(q.seg[j] + (size_t(q.group) + k0) * p.vecs, tv * 16u);
+    u32x4* o = q.out[r] + (size_t(j) * q.group + k0) * p.vecs;
+    u32x4* ro = q.res_out[r] + (size_t(j) * q.group + k0) * p.vecs;
+    for (uint32_t v = threadIdx.x; v < tv; v += blockDim.x) {
+        const u32x4 a = ld_coherent(so, v * 16u);
+        const u32x4 e = ld_coherent(sr, v * 16u);
+        st_stream(o + v, a);
+        st_stream(ro + v, e);
+    }
+}
+
+template <typename T, int NR>
+hipError_t launch_ts_t(const TsRmsParams& q, hipStream_t s) {
+    const uint32_t V = q.p.vecs;
+    const int vpt = V <= 1024u ? 1 : (V <= 2048u ? 2 : 4);
+    uint32_t block = (V + uint32_t(vpt) - 1) / uint32_t(vpt);
+    block = (block + kWave - 1) / kWave * kWave;
+    const uint32_t R = uint32_t(q.r1 - q.r0);
+    const uint64_t items = uint64_t(R) * q.ntiles + (q.do_ag ? uint64_t(R) * (NR - 1) * q.ntiles : 0u);
+    const dim3 grid = dim3(uint32_t(items)), blk = dim3(block);
+    if (vpt == 1)
+        hipLaunchKernelGGL((twoshot_rmsnorm_kernel<T, NR, 1>), grid, blk, 0, s, q);
+    else if (vpt == 2)
+        hipLaunchKernelGGL((twoshot_rmsnorm_kernel<T, NR, 2>), grid, blk, 0, s, q);
+    else
+        hipLaunchKernelGGL((twoshot_rmsnorm_kernel<T, NR, 4>), grid, blk, 0, s, q);
+    return hipGetLastError();
 }
 
 // Cooperative path (few rows): workspace layout in 32-bit words, after the
@@ -313,6 +446,42 @@ hipError_t launch_t(const RmsParams& p, uint32_t* ws, uint64_t timeout_ticks, hi
 }
 
 }  // namespace
+
+hipError_t launch_twoshot_rmsnorm(const void* const* in, int n, const void* const* residual, const void* weight,
+                                  void* const* seg, void* const* residual_out, void* const* out, size_t rows,
+                                  size_t hidden, float eps, int dtype, int r0, int r1, uint32_t* flags,
+                                  uint32_t step, uint64_t timeout_ticks, hipStream_t s) {
+    TsRmsParams q{};
+    for (int r = 0; r < n; ++r) {
+        q.p.in[r] = static_cast<const u32x4*>(in[r]);
+        q.seg[r] = static_cast<u32x4*>(seg[r]);
+        if (r >= r0 && r < r1) {
+            q.residual[r] = static_cast<const u32x4*>(residual[r]);
+            if (out) {
+                q.res_out[r] = static_cast<u32x4*>(residual_out[r]);
+                q.out[r] = static_cast<u32x4*>(out[r]);
+            }
+        }
+    }
+    q.p.weight = static_cast<const u32x4*>(weight);
+    q.p.rows = rows;
+    q.p.vecs = uint32_t(hidden * (dtype == 0 ? 4u : 2u) / 16u);
+    q.p.hidden = float(hidden);
+    q.p.eps = eps;
+    q.flags = flags;
+    q.timeout_ticks = timeout_ticks;
+    q.step = step;
+    q.r0 = r0;
+    q.r1 = r1;
+    q.group = uint32_t(rows / size_t(n));
+    q.tile = (q.group + uint32_t(kSlotsPerRank) - 1) / uint32_t(kSlotsPerRank);
+    q.ntiles = (q.group + q.tile - 1) / q.tile;
+    q.do_ag = out != nullptr;
+    return dispatch_ranks(n, [&](auto nr) {
+        constexpr int NR = decltype(nr)::value;
+        return dtype == 0 ? launch_ts_t<float, NR>(q, s) : launch_ts_t<bf16_t, NR>(q, s);
+    });
+}
 
 hipError_t launch_oneshot_rmsnorm(const void* const* in, int n, const void* residual, const void* weight,
                                   void* residual_out, void* out, size_t rows, size_t hidden, float eps, int dtype,

@@ -163,6 +163,38 @@ int ar_oneshot_rmsnorm(const void* const* in, int n, const void* residual, const
                        void* out, size_t rows, size_t hidden, float eps, int dtype, uint32_t* workspace,
                        void* stream);
 
+/* The same op in two-shot form ([NCCL] 算法, two-shot; the fused op as read
+ * for ar_oneshot_rmsnorm).  The reduce-scatter owns whole rows: rank r's
+ * group is rows [r G, (r+1) G), G = rows / n, so the rank finishes the norm
+ * of its rows alone (with the same per-row arithmetic as ar_oneshot_rmsnorm
+ * without a workspace: the same bits).  It writes them to seg[r] -- G out
+ * rows, then G residual_out rows -- and publishes each tile of rows with an
+ * arrival slot in the flag region (as ar_twoshot_rs); the all-gather copies
+ * the peers' rows of both results once their slots hold step.
+ *  in           : n device pointers, rows * hidden elements each.
+ *  residual     : n device pointers, rank r's copy of the residual stream
+ *                 (rows * hidden elements); only ranks [r0, r1) are read.
+ *  weight       : hidden elements.
+ *  seg          : n device pointers, 2 * G * hidden elements each; seg[r]
+ *                 for r in [r0, r1) written, the peers' read when fused.
+ *  residual_out, out : NULL (the reduce-scatter of ranks [r0, r1) alone),
+ *                 or n device pointers of rows * hidden elements, entries in
+ *                 [r0, r1) used, and then r1 = r0 + 1: one rank's share in
+ *                 one launch (its own rows straight from the reduce-scatter,
+ *                 the peers' through the all-gather).
+ *  flags, step  : a flag region of ar_flag_bytes(n) and the step id (>= 1;
+ *                 the peers' reduce-scatters of this step publish it).
+ * A wait that runs out writes AR_ERR_TIMEOUT | AR_PHASE_TWOSHOT_AG << 8 |
+ * peer << 16 to the flag region's status word (detail: the tile).
+ * rows must be a multiple of n, hidden as for ar_oneshot_rmsnorm.  One
+ * rank's share reads S + S/n + (one row) + 2 (n-1) S/n bytes and writes
+ * 2 S/n (own rows) + 2 S/n (segment) + 2 (n-1) S/n (S = rows * hidden *
+ * element size).
+ * Errors: AR_ERR_ARG, AR_ERR_ALIGN, AR_ERR_DIVISIBLE, AR_ERR_ALIAS, AR_ERR_HIP. */
+int ar_twoshot_rmsnorm(const void* const* in, int n, const void* const* residual, const void* weight,
+                       void* const* seg, void* const* residual_out, void* const* out, size_t rows, size_t hidden,
+                       float eps, int dtype, int r0, int r1, uint32_t* flags, uint32_t step, void* stream);
+
 /* Reduce with a broadcast store: the kBroadcast store path of [CAR] step 5
  * -- each result written to every rank's output, not only the local one --
  * applied to one rank's share of the elements, which makes a two-shot whose

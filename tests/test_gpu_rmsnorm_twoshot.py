@@ -1,0 +1,147 @@
+"""The fused all-reduce + residual add + RMSNorm in two-shot form
+(ar_twoshot_rmsnorm): every rank's reduce-scatter publishes its rows, then
+each rank's share (its own rows and the all-gather of its peers') is checked
+against the oracle (O10: residual_out bit for bit, out within the bound
+derived in test_gpu_rmsnorm.py) and against the one-shot form without a
+workspace, bit for bit (the same per-row arithmetic)."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from devtensors import bits, oracle_bits, to_dev
+from test_gpu_rmsnorm import check_out, host_values
+
+pytestmark = pytest.mark.gpu
+
+car = pytest.importorskip("custom_all_reduce_amd")
+
+
+class Setup:
+    def __init__(self, n, dt, rows, hidden, config, eps=1e-6):
+        self.n, self.dt, self.rows, self.hidden, self.eps = n, dt, rows, hidden, eps
+        numel = rows * hidden
+        self.host = synth.rank_inputs(n, numel, dt, "normal", config=config)
+        self.res = synth.rank_inputs(1, numel, dt, "normal", config=config + 1000)[0]
+        self.w = synth.rank_inputs(1, hidden, dt, "normal", config=config + 2000)[0]
+        self.ins = [to_dev(a) for a in self.host]
+        self.residuals = [to_dev(self.res) for _ in range(n)]  # every rank's copy of the residual stream
+        self.weight = to_dev(self.w)
+        tdt = self.ins[0].dtype
+        self.segs = [torch.empty(car.rmsnorm_segment_elems(n, rows, hidden), dtype=tdt, device="cuda")
+                     for _ in range(n)]
+        self.outs = [torch.empty(numel, dtype=tdt, device="cuda") for _ in range(n)]
+        self.ros = [torch.empty(numel, dtype=tdt, device="cuda") for _ in range(n)]
+        self.flags = car.new_flags(n)
+
+    def want(self):
+        return oracle.oneshot_rmsnorm(self.host, self.res, self.w, self.hidden, self.eps, self.dt)
+
+    def oneshot_bits(self):
+        ro, out = torch.empty_like(self.outs[0]), torch.empty_like(self.outs[0])
+        car.ar_oneshot_rmsnorm(self.ins, self.residuals[0], self.weight, ro, out, self.eps)
+        torch.cuda.synchronize()
+        return bits(ro), bits(out)
+
+    def reduce_scatter(self, step, ranks=None):
+        ranks = range(self.n) if ranks is None else ranks
+        for r in ranks:
+            car.ar_twoshot_rmsnorm(self.ins, self.residuals, self.weight, self.segs, self.flags, step, r0=r,
+                                   r1=r + 1, eps=self.eps)
+
+    def share(self, me, step):
+        outs = [self.outs[r] if r == me else None for r in range(self.n)]
+        ros = [self.ros[r] if r == me else None for r in range(self.n)]
+        car.ar_twoshot_rmsnorm(self.ins, self.residuals, self.weight, self.segs, self.flags, step, r0=me,
+                               r1=me + 1, residual_outs=ros, outs=outs, eps=self.eps)
+
+
+def check_rank(s: Setup, me, want_ro, y, one_ro, one_out, what):
+    assert np.array_equal(bits(s.ros[me]), oracle_bits(want_ro)), f"{what}: residual_out differs from the oracle"
+    check_out(host_values(s.outs[me], s.dt), y, s.dt, what)
+    assert np.array_equal(bits(s.ros[me]), one_ro), f"{what}: residual_out differs from the one-shot form"
+    assert np.array_equal(bits(s.outs[me]), one_out), f"{what}: out differs from the one-shot form"
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("n", [2, 3, 8, 16])
+@pytest.mark.parametrize("groups, hidden", [(1, 8), (3, 264), (2, 1000), (4, 8192), (2, 16384)])
+def test_every_rank_matches_the_oracle_and_the_one_shot(n, dt, groups, hidden):
+    if dt == "f32" and hidden == 16384 and n == 16:
+        hidden = 8192  # keep the case small
+    s = Setup(n, dt, n * groups, hidden, config=400 + n)
+    want_ro, y = s.want()
+    one_ro, one_out = s.oneshot_bits()
+    s.reduce_scatter(1)  # every rank's rows published (split launches)
+    car.ar_twoshot_rmsnorm(s.ins, s.residuals, s.weight, s.segs, s.flags, 1, r0=0, r1=n, eps=s.eps)  # one launch
+    for me in range(n):
+        s.share(me, 1)
+    torch.cuda.synchronize()
+    car.raise_on_status(s.flags, "two-shot rmsnorm")
+    for me in range(n):
+        check_rank(s, me, want_ro, y, one_ro, one_out, f"n={n} {dt} rows={s.rows} hidden={hidden} rank {me}")
+
+
+def test_more_rows_per_rank_than_slots():
+    # 1030 rows per rank: two rows per arrival slot
+    s = Setup(2, "bf16", 2 * 1030, 8, config=420)
+    want_ro, y = s.want()
+    one_ro, one_out = s.oneshot_bits()
+    s.reduce_scatter(1)
+    s.share(0, 1)
+    s.share(1, 1)
+    torch.cuda.synchronize()
+    car.raise_on_status(s.flags, "two-shot rmsnorm")
+    for me in range(2):
+        check_rank(s, me, want_ro, y, one_ro, one_out, f"rank {me}")
+
+
+def test_steps_in_a_row_with_changing_data():
+    n, rows, hidden = 8, 16, 4096
+    s = Setup(n, "bf16", rows, hidden, config=430)
+    for step in range(1, 6):
+        host = synth.rank_inputs(n, rows * hidden, "bf16", "normal", config=431 + step)
+        for t, a in zip(s.ins, host):
+            t.copy_(to_dev(a))
+        s.host = host
+        want_ro, y = s.want()
+        s.reduce_scatter(step, ranks=[r for r in range(n) if r != 3])
+        s.share(3, step)  # rank 3's share publishes its own rows too
+        torch.cuda.synchronize()
+        car.raise_on_status(s.flags, f"step {step}")
+        assert np.array_equal(bits(s.ros[3]), oracle_bits(want_ro)), f"step {step}"
+        check_out(host_values(s.outs[3], "bf16"), y, "bf16", f"step {step}")
+
+
+def test_a_missing_peer_is_reported_as_a_timeout():
+    n, rows, hidden = 4, 8, 1024
+    s = Setup(n, "bf16", rows, hidden, config=440)
+    s.reduce_scatter(1, ranks=[0, 2, 3])  # rank 1 never publishes
+    old = car.get_poll_timeout_ns()
+    car.set_poll_timeout_ns(1_000_000)
+    try:
+        s.share(0, 1)
+        torch.cuda.synchronize()
+    finally:
+        car.set_poll_timeout_ns(old)
+    word, _ = car.read_status(s.flags)
+    code, phase, rank = car.decode_status(word)
+    assert (code, phase, rank) == (car.AR_ERR_TIMEOUT, car.PHASE_TWOSHOT_AG, 1)
+
+
+def test_argument_errors():
+    s = Setup(4, "bf16", 8, 64, config=450)
+    f = car.ar_twoshot_rmsnorm
+    with pytest.raises(car.ArError):  # step 0
+        f(s.ins, s.residuals, s.weight, s.segs, s.flags, 0, r0=0, r1=1)
+    with pytest.raises(car.ArError):  # the all-gather for two ranks in one launch
+        f(s.ins, s.residuals, s.weight, s.segs, s.flags, 1, r0=0, r1=2, residual_outs=s.ros, outs=s.outs)
+    with pytest.raises(ValueError):  # residual_outs without outs
+        f(s.ins, s.residuals, s.weight, s.segs, s.flags, 1, r0=0, r1=1, residual_outs=s.ros)
+    t = Setup(4, "bf16", 6, 64, config=451)  # 6 rows over 4 ranks
+    with pytest.raises(car.ArError) as e:
+        f(t.ins, t.residuals, t.weight, [torch.empty(64, dtype=torch.bfloat16, device="cuda")] * 4, t.flags, 1)
+    assert e.value.code == car.AR_ERR_DIVISIBLE
