@@ -83,6 +83,7 @@ def _load(path: str = LIB_PATH):
     lib.ar_rmsnorm_workspace_bytes.argtypes, lib.ar_rmsnorm_workspace_bytes.restype = [], sz
     lib.ar_twoshot_rmsnorm.argtypes = [P, i32, P, vp, P, P, P, sz, sz, ctypes.c_float, i32, i32, i32, vp, u32, vp]
     lib.ar_twoshot_rmsnorm.restype = i32
+    lib.ar_rmsnorm_segment_bytes.argtypes, lib.ar_rmsnorm_segment_bytes.restype = [i32, sz, sz, i32], sz
     lib.ar_reduce_bcast.argtypes, lib.ar_reduce_bcast.restype = [P, i32, P, sz, i32, i32, i32, vp], i32
     lib.ar_push.argtypes, lib.ar_push.restype = [P, i32, P, i32, sz, i32, vp], i32
     lib.ar_twoshot_rs.argtypes, lib.ar_twoshot_rs.restype = [P, i32, P, sz, i32, i32, i32, vp, u32, P, vp], i32
@@ -335,9 +336,18 @@ def prepare_oneshot_rmsnorm(ins, residual: torch.Tensor, weight: torch.Tensor, r
                     (ins, residual, weight, residual_out, out, workspace))
 
 
-def rmsnorm_segment_elems(n: int, rows: int, hidden: int) -> int:
-    """Elements of one rank's segment in ar_twoshot_rmsnorm: its rows of out, then of residual_out."""
-    return 2 * (rows // n) * hidden
+def rmsnorm_segment_bytes(n: int, rows: int, hidden: int, dtype) -> int:
+    """Bytes of one rank's segment in ar_twoshot_rmsnorm (its rows of out and of
+    residual_out, then the parts' slots and flags); 0 if rows is not a multiple of n."""
+    return int(_lib.ar_rmsnorm_segment_bytes(int(n), int(rows), int(hidden), _dtype_arg(dtype)))
+
+
+def new_rmsnorm_segments(n: int, rows: int, hidden: int, dtype, device=None):
+    """n zeroed segments for ar_twoshot_rmsnorm (uint8 tensors)."""
+    nb = rmsnorm_segment_bytes(n, rows, hidden, dtype)
+    if nb == 0:
+        raise ValueError(f"{rows} rows do not split over {n} ranks")
+    return [torch.zeros(nb, dtype=torch.uint8, device=device or "cuda") for _ in range(n)]
 
 
 def prepare_twoshot_rmsnorm(ins, residuals, weight: torch.Tensor, segs, flags: torch.Tensor, r0: int = 0,
@@ -365,7 +375,7 @@ def prepare_twoshot_rmsnorm(ins, residuals, weight: torch.Tensor, segs, flags: t
         _need_like([_dev_tensor(residuals[r], "residual")], ref.dtype, ref.numel(), "every residual in [r0, r1)")
     segs = [_dev_tensor(t, "segment") for t in segs]
     if rows % n == 0:
-        _need_like(segs, ref.dtype, rmsnorm_segment_elems(n, rows, hidden), "every segment")
+        _need_bytes(segs, rmsnorm_segment_bytes(n, rows, hidden, ref.dtype), "every segment")
     _need_bytes([_dev_tensor(flags, "flags")], flag_bytes(n), "the flag region")
     ro_arr = o_arr = None
     if (outs is None) != (residual_outs is None):

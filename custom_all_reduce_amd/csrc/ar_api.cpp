@@ -272,6 +272,11 @@ int ar_oneshot_rmsnorm(const void* const* in, int n, const void* residual, const
                                              workspace, timeout_ticks(), static_cast<hipStream_t>(stream)));
 }
 
+size_t ar_rmsnorm_segment_bytes(int n, size_t rows, size_t hidden, int dtype) {
+    if (!ranks_ok(n) || !dtype_ok(dtype) || rows % size_t(n) != 0) return 0;
+    return twoshot_rmsnorm_segment_bytes(n, rows, hidden, dtype);
+}
+
 int ar_twoshot_rmsnorm(const void* const* in, int n, const void* const* residual, const void* weight,
                        void* const* seg, void* const* residual_out, void* const* out, size_t rows, size_t hidden,
                        float eps, int dtype, int r0, int r1, uint32_t* flags, uint32_t step, void* stream) {
@@ -296,7 +301,7 @@ int ar_twoshot_rmsnorm(const void* const* in, int n, const void* const* residual
     }
     if (!aligned16(weight) || !aligned16(flags)) return AR_ERR_ALIGN;
     if ((hidden * es) % 16 != 0 || rows % size_t(n) != 0) return AR_ERR_DIVISIBLE;
-    const size_t S = rows * hidden * es, seg_bytes = 2 * (rows / size_t(n)) * hidden * es;
+    const size_t S = rows * hidden * es, seg_bytes = twoshot_rmsnorm_segment_bytes(n, rows, hidden, dtype);
     std::vector<Span> v;
     v.push_back(span(flags, ar_flag_bytes(n), true));
     v.push_back(span(weight, hidden * es, false));

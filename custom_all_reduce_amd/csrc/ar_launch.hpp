@@ -90,6 +90,7 @@ hipError_t launch_oneshot_rmsnorm(const void* const* in, int n, const void* resi
 // with an arrival slot per tile; out == null: the reduce-scatter of ranks
 // [r0, r1) alone; else one rank's share (r1 == r0 + 1), the all-gather of
 // the peers' rows included.
+size_t twoshot_rmsnorm_segment_bytes(int n, size_t rows, size_t hidden, int dtype);
 hipError_t launch_twoshot_rmsnorm(const void* const* in, int n, const void* const* residual, const void* weight,
                                   void* const* seg, void* const* residual_out, void* const* out, size_t rows,
                                   size_t hidden, float eps, int dtype, int r0, int r1, uint32_t* flags,

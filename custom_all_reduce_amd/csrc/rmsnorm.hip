@@ -44,6 +44,10 @@ namespace {
 
 constexpr int kMaxBlock = 1024;
 constexpr int kMaxWaves = kMaxBlock / kWave;
+// Rows whose n + 1 input streams hold at least this many bytes are split
+// into parts (one compute unit pulling such a row is the bottleneck; below
+// it the parts' exchange costs more than it saves); see the launch rules.
+constexpr uint32_t kCoopMinRowBytes = 128u << 10;
 
 struct RmsParams {
     const u32x4* in[kMaxRanks];
@@ -236,8 +240,135 @@ struct TsRmsParams {
     uint32_t group;   // rows per rank
     uint32_t tile;    // rows per arrival slot
     uint32_t ntiles;  // slots per rank
+    uint32_t parts;   // 64-vector parts per row
     int do_ag;
 };
+
+// Parts of rows.  A rank's 64 rows of the prefill message would put each
+// row's n + 1 streams through one compute unit (the workgroup-per-row form
+// above), so here every row is cut into parts of 64 vectors, one wavefront
+// each, as in the one-shot form's few-rows path: a part folds its vectors,
+// stores residual_out (its own and its segment's copy), publishes its
+// partial sum of h^2 with the step id as one 8-byte store in the segment,
+// polls its siblings' (bounded), scales its h by the row's factor and stores
+// out; once all its stores are complete it sets its done flag (the step id)
+// in the segment.  An all-gather item is a part of a peer's row: it polls
+// that part's done flag and copies its vectors of both results.  Segment of
+// a rank, in bytes: G out rows and G residual_out rows (16 V each), then
+// G P partial slots of 8 bytes, then G P done flags of 4 bytes.
+__host__ __device__ constexpr size_t ts_partial_off(size_t G, size_t V) { return 32 * G * V; }
+__host__ __device__ constexpr size_t ts_done_off(size_t G, size_t V, size_t P) { return 32 * G * V + 8 * G * P; }
+
+template <typename T, int NR>
+__global__ __launch_bounds__(kWave) void twoshot_rmsnorm_parts_kernel(TsRmsParams q) {
+    constexpr int E = Vec<T>::E;
+    const RmsParams& p = q.p;
+    const uint32_t lane = threadIdx.x;
+    const uint32_t b = blockIdx.x;
+    const uint32_t R = uint32_t(q.r1 - q.r0);
+    const uint32_t G = q.group, P = q.parts, V = p.vecs;
+    const uint32_t row_bytes = V * 16u;
+    const uint32_t rs_items = R * G * P;
+    if (b < rs_items) {
+        const uint32_t rr = b / (G * P), rem = b - rr * (G * P);
+        const uint32_t k = rem / P, pp = rem - k * P;
+        const uint32_t r = uint32_t(q.r0) + rr;
+        const size_t base = (size_t(r) * G + k) * V;
+        const uint32_t v = pp * kWave + lane;
+        const bool valid = v < V;
+        const uint32_t off = (valid ? v : 0u) * 16u;
+        const u32x4 wv = row_load<0>(buffer_range(p.weight, row_bytes), off);
+        const u32x4 rv = row_load<kCachePolicyNt>(buffer_range(q.residual[r] + base, row_bytes), off);
+        u32x4 x[NR];
+#pragma unroll
+        for (int i = 0; i < NR; ++i) x[i] = row_load<kCachePolicyNt>(buffer_range(p.in[i] + base, row_bytes), off);
+        Acc<T> acc;
+#pragma unroll
+        for (int i = 0; i < NR; ++i) acc.add(x[i]);
+        float res[E], h[E];
+        Vec<T>::widen(rv, res);
+        float ss = 0.0f;
+#pragma unroll
+        for (int e = 0; e < E; ++e) h[e] = acc.a[e] + res[e];
+        u32x4* seg = q.seg[r];
+        if (valid) {
+            const u32x4 hv = Vec<T>::narrow(h);
+            if (q.do_ag) row_store(buffer_range(q.res_out[r] + base, row_bytes), off, hv);
+            row_store_coherent(seg + (size_t(G) + k) * V, row_bytes, off, hv);
+#pragma unroll
+            for (int e = 0; e < E; ++e) ss += h[e] * h[e];
+        }
+        ss = wave_sum(ss);
+        uint8_t* segb = reinterpret_cast<uint8_t*>(seg);
+        const __amdgpu_buffer_rsrc_t slots = buffer_range(segb + ts_partial_off(G, V) + size_t(k) * P * 8u, P * 8u);
+        if (lane == 0)
+            __builtin_amdgcn_raw_buffer_store_b64(u32x2{__float_as_uint(ss), q.step}, slots, int(pp * 8u), 0,
+                                                  kCachePolicySc1);
+        const bool mine = lane < P;
+        const uint32_t soff = (mine ? lane : 0u) * 8u;
+        u32x2 sl = __builtin_amdgcn_raw_buffer_load_b64(slots, int(soff), 0, kCachePolicySc1);
+        const uint64_t t0 = now_ticks();
+        while (true) {
+            const uint64_t missing = ~wave_ballot(!mine || sl.y >= q.step) & wave_exec();
+            if (missing == 0) break;
+            if (now_ticks() - t0 > q.timeout_ticks) {
+                if (lane == 0) report_timeout(q.flags, 4u, r, k);
+                return;  // no output, no done flag
+            }
+            __builtin_amdgcn_s_sleep(1);
+            if (mine && sl.y < q.step) sl = __builtin_amdgcn_raw_buffer_load_b64(slots, int(soff), 0, kCachePolicySc1);
+        }
+        // the same values in the same lanes in every part of the row
+        const float total = wave_sum(mine ? __uint_as_float(sl.x) : 0.0f);
+        const float f = 1.0f / sqrtf(total / p.hidden + p.eps);
+        if (valid) {
+            float w[E], y[E];
+            Vec<T>::widen(wv, w);
+#pragma unroll
+            for (int e = 0; e < E; ++e) y[e] = (h[e] * f) * w[e];
+            const u32x4 yv = Vec<T>::narrow(y);
+            if (q.do_ag) row_store(buffer_range(q.out[r] + base, row_bytes), off, yv);
+            row_store_coherent(seg + size_t(k) * V, row_bytes, off, yv);
+        }
+        // done: every store of this part complete, then its flag
+        wait_stores();
+        if (lane == 0)
+            __builtin_amdgcn_raw_buffer_store_b32(q.step, buffer_range(segb + ts_done_off(G, V, P), G * P * 4u),
+                                                  int((k * P + pp) * 4u), 0, kCachePolicySc1);
+        return;
+    }
+    // all-gather item: (output rank, peer, row, part)
+    const uint32_t c = b - rs_items;
+    const uint32_t per_out = uint32_t(NR - 1) * G * P;
+    const uint32_t oo = c / per_out;
+    if (oo >= R) return;
+    const uint32_t rem = c - oo * per_out;
+    const uint32_t r = uint32_t(q.r0) + oo;
+    const uint32_t jj = rem / (G * P), rem2 = rem - jj * (G * P);
+    const uint32_t j = jj < r ? jj : jj + 1u;  // every rank but r
+    const uint32_t k = rem2 / P, pp = rem2 - k * P;
+    uint8_t* segb = reinterpret_cast<uint8_t*>(q.seg[j]);
+    const __amdgpu_buffer_rsrc_t done = buffer_range(segb + ts_done_off(G, V, P), G * P * 4u);
+    const uint32_t doff = (k * P + pp) * 4u;
+    uint32_t seen = __builtin_amdgcn_raw_buffer_load_b32(done, int(doff), 0, kCachePolicySc1);
+    const uint64_t t0 = now_ticks();
+    while (__builtin_amdgcn_readfirstlane(seen) < q.step) {
+        if (now_ticks() - t0 > q.timeout_ticks) {
+            if (lane == 0) report_timeout(q.flags, 1u, j, k);
+            return;
+        }
+        __builtin_amdgcn_s_sleep(1);
+        seen = __builtin_amdgcn_raw_buffer_load_b32(done, int(doff), 0, kCachePolicySc1);
+    }
+    const uint32_t v = pp * kWave + lane;
+    if (v < V) {
+        const u32x4 yv = ld_coherent(buffer_range(q.seg[j] + size_t(k) * V, row_bytes), v * 16u);
+        const u32x4 hv = ld_coherent(buffer_range(q.seg[j] + (size_t(G) + k) * V, row_bytes), v * 16u);
+        const size_t dst = (size_t(j) * G + k) * V + v;
+        st_stream(q.out[r] + dst, yv);
+        st_stream(q.res_out[r] + dst, hv);
+    }
+}
 
 template <typename T, int NR, int VPT>
 __global__ __launch_bounds__(kMaxBlock) void twoshot_rmsnorm_kernel(TsRmsParams q) {
@@ -301,9 +432,30 @@ __global__ __launch_bounds__(kMaxBlock) void twoshot_rmsnorm_kernel(TsRmsParams 
     }
 }
 
+// Which two-shot form runs, by rank count and size (the same for every
+// rank's launch of a step, so a share and its peers' reduce-scatters agree):
+// parts where a row's n + 1 streams hold at least kCoopMinRowBytes and a
+// rank owns fewer than kTsPartsMaxRows rows.  Measured, one rank's share,
+// bf16, rows of 8192: n = 8 at 8 MiB per rank 9.3 against 12.1 us (parts
+// against a workgroup per row), at 1 MiB 5.6 against 7.8, 1 row per rank
+// 5.1 against 7.2; n = 16 at 8 MiB 9.5 against 14.0; but n = 8 at 64 MiB
+// (512 rows per rank) 55.4 against 52.5, and n = 2 at 8 MiB 13.2 against
+// 10.3 (light rows).
+constexpr uint32_t kTsPartsMaxRows = 256;
+inline bool ts_parts(int nr, uint32_t group, uint32_t vecs) {
+    return group < kTsPartsMaxRows && uint32_t(nr + 1) * vecs * 16u >= kCoopMinRowBytes;
+}
+
 template <typename T, int NR>
 hipError_t launch_ts_t(const TsRmsParams& q, hipStream_t s) {
     const uint32_t V = q.p.vecs;
+    if (ts_parts(NR, q.group, V)) {
+        const uint32_t R = uint32_t(q.r1 - q.r0);
+        const uint64_t per = uint64_t(q.group) * q.parts;
+        const uint64_t items = uint64_t(R) * per + (q.do_ag ? uint64_t(R) * (NR - 1) * per : 0u);
+        hipLaunchKernelGGL((twoshot_rmsnorm_parts_kernel<T, NR>), dim3(uint32_t(items)), dim3(kWave), 0, s, q);
+        return hipGetLastError();
+    }
     const int vpt = V <= 1024u ? 1 : (V <= 2048u ? 2 : 4);
     uint32_t block = (V + uint32_t(vpt) - 1) / uint32_t(vpt);
     block = (block + kWave - 1) / kWave * kWave;
@@ -412,7 +564,6 @@ constexpr size_t kRmsMaxGrid = size_t(1) << 20;
 // (n = 8 bf16, hidden 8192: 4.8 against 5.1 us at 1 row, 5.2 against 5.6 at
 // 8, equal at 32, slower at 64; n = 16, 8 rows: 5.6 against 7.8; n = 2 and
 // hidden 4096 at n = 8: slower).
-constexpr uint32_t kCoopMinRowBytes = 128u << 10;
 constexpr uint32_t kCoopMaxParts = 512;
 
 template <typename T, int NR>
@@ -447,6 +598,11 @@ hipError_t launch_t(const RmsParams& p, uint32_t* ws, uint64_t timeout_ticks, hi
 
 }  // namespace
 
+size_t twoshot_rmsnorm_segment_bytes(int n, size_t rows, size_t hidden, int dtype) {
+    const size_t G = rows / size_t(n), V = hidden * (dtype == 0 ? 4u : 2u) / 16u, P = (V + kWave - 1) / kWave;
+    return (ts_done_off(G, V, P) + 4 * G * P + 15) / 16 * 16;
+}
+
 hipError_t launch_twoshot_rmsnorm(const void* const* in, int n, const void* const* residual, const void* weight,
                                   void* const* seg, void* const* residual_out, void* const* out, size_t rows,
                                   size_t hidden, float eps, int dtype, int r0, int r1, uint32_t* flags,
@@ -476,6 +632,7 @@ hipError_t launch_twoshot_rmsnorm(const void* const* in, int n, const void* cons
     q.group = uint32_t(rows / size_t(n));
     q.tile = (q.group + uint32_t(kSlotsPerRank) - 1) / uint32_t(kSlotsPerRank);
     q.ntiles = (q.group + q.tile - 1) / q.tile;
+    q.parts = (q.p.vecs + kWave - 1) / kWave;
     q.do_ag = out != nullptr;
     return dispatch_ranks(n, [&](auto nr) {
         constexpr int NR = decltype(nr)::value;

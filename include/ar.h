@@ -166,31 +166,47 @@ int ar_oneshot_rmsnorm(const void* const* in, int n, const void* residual, const
 /* The same op in two-shot form ([NCCL] 算法, two-shot; the fused op as read
  * for ar_oneshot_rmsnorm).  The reduce-scatter owns whole rows: rank r's
  * group is rows [r G, (r+1) G), G = rows / n, so the rank finishes the norm
- * of its rows alone (with the same per-row arithmetic as ar_oneshot_rmsnorm
- * without a workspace: the same bits).  It writes them to seg[r] -- G out
- * rows, then G residual_out rows -- and publishes each tile of rows with an
- * arrival slot in the flag region (as ar_twoshot_rs); the all-gather copies
- * the peers' rows of both results once their slots hold step.
+ * of its rows alone.  Two forms, chosen by size (the same for every rank's
+ * launch of a step):
+ *  - heavy rows, few per rank (n + 1 streams of at least 128 KiB a row,
+ *    G < 256): each row is cut into parts of 64 16-byte vectors, one
+ *    wavefront each, that exchange their partial sums of squares through
+ *    8-byte {value, step id} slots in the rank's segment; a part writes its
+ *    results (its own outputs and the segment's copies), then, once those
+ *    stores are complete, its done flag (the step id) in the segment; the
+ *    all-gather copies a peer's part once its done flag holds the step;
+ *  - otherwise a workgroup per row (the code of ar_oneshot_rmsnorm's
+ *    workgroup-per-row path), each tile of rows published with an arrival
+ *    slot in the flag region; the all-gather copies a tile once its slot
+ *    holds the step.
+ * Each form's results are identical to ar_oneshot_rmsnorm's on the same kind
+ * of path.
  *  in           : n device pointers, rows * hidden elements each.
  *  residual     : n device pointers, rank r's copy of the residual stream
  *                 (rows * hidden elements); only ranks [r0, r1) are read.
  *  weight       : hidden elements.
- *  seg          : n device pointers, 2 * G * hidden elements each; seg[r]
- *                 for r in [r0, r1) written, the peers' read when fused.
+ *  seg          : n device pointers, ar_rmsnorm_segment_bytes(n, rows,
+ *                 hidden, dtype) bytes each, zeroed before their first use
+ *                 (their slots and flags carry step ids); seg[r] for r in
+ *                 [r0, r1) written, the peers' read when fused.
  *  residual_out, out : NULL (the reduce-scatter of ranks [r0, r1) alone),
  *                 or n device pointers of rows * hidden elements, entries in
  *                 [r0, r1) used, and then r1 = r0 + 1: one rank's share in
  *                 one launch (its own rows straight from the reduce-scatter,
  *                 the peers' through the all-gather).
- *  flags, step  : a flag region of ar_flag_bytes(n) and the step id (>= 1;
- *                 the peers' reduce-scatters of this step publish it).
- * A wait that runs out writes AR_ERR_TIMEOUT | AR_PHASE_TWOSHOT_AG << 8 |
- * peer << 16 to the flag region's status word (detail: the tile).
+ *  flags, step  : a flag region of ar_flag_bytes(n) and the step id, >= 1
+ *                 and above every earlier call's on these segments and flags
+ *                 (the peers' reduce-scatters of this step publish it).
+ * A wait that runs out writes AR_ERR_TIMEOUT | phase << 8 | rank << 16 to the
+ * flag region's status word: AR_PHASE_TWOSHOT_AG with the peer (all-gather),
+ * AR_PHASE_RMSNORM with the rank (a row's parts); detail: the row in the
+ * rank's group.
  * rows must be a multiple of n, hidden as for ar_oneshot_rmsnorm.  One
  * rank's share reads S + S/n + (one row) + 2 (n-1) S/n bytes and writes
  * 2 S/n (own rows) + 2 S/n (segment) + 2 (n-1) S/n (S = rows * hidden *
- * element size).
+ * element size), besides the slots and flags.
  * Errors: AR_ERR_ARG, AR_ERR_ALIGN, AR_ERR_DIVISIBLE, AR_ERR_ALIAS, AR_ERR_HIP. */
+size_t ar_rmsnorm_segment_bytes(int n, size_t rows, size_t hidden, int dtype);
 int ar_twoshot_rmsnorm(const void* const* in, int n, const void* const* residual, const void* weight,
                        void* const* seg, void* const* residual_out, void* const* out, size_t rows, size_t hidden,
                        float eps, int dtype, int r0, int r1, uint32_t* flags, uint32_t step, void* stream);
