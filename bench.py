@@ -492,11 +492,24 @@ def sweep(args, torch, car, np, out_path):
                 rms_row = 16 << 10
                 rms_w = torch.ones(rms_row // es, dtype=rig.dt, device="cuda")
                 rms_ws = car.new_rmsnorm_workspace()
+                # its two-shot form: rank 0's share, the peers' reduce-scatters published
+                # once beforehand (on a flag region of its own), where the rows split
+                rms_rows = S // rms_row
+                rms_ts = rms_rows > 0 and rms_rows % n == 0
+                rms_fl = car.new_flags(n)
                 for i, b in enumerate(rig.sets):
                     c = rig.calls[i]
                     rn = car.prepare_oneshot_rmsnorm(b.ins, b.outs[1], rms_w, b.outs[2], b.outs[3], 1e-6,
                                                      workspace=rms_ws)
                     c["oneshot_rmsnorm"] = lambda s, f=rn: f()
+                    if rms_ts:
+                        segs = car.new_rmsnorm_segments(n, rms_rows, rms_row // es, rig.dt)
+                        resid = [b.outs[1]] * n
+                        car.ar_twoshot_rmsnorm(b.ins, resid, rms_w, segs, rms_fl, PEER_STEP, r0=1, r1=n)
+                        tr = car.prepare_twoshot_rmsnorm(b.ins, resid, rms_w, segs, rms_fl, ME, ME + 1,
+                                                         only_me(b, b.outs[2:3] * n), only_me(b, b.outs[3:4] * n))
+                        c["twoshot_rmsnorm"] = lambda s, f=tr: f(s)
+                        extra[i] = segs
                     c["ll_pack"] = car.prepare_ll_pack([b.ins[ME]], [b.w_ll[ME]], "ll")
                     c["ll_reduce"] = car.prepare_ll_reduce(b.w_ll, b.out_ll, fl, "ll")
                     c["ll128_pack"] = car.prepare_ll_pack([b.ins[ME]], [b.w_128[ME]], "ll128")
@@ -531,6 +544,7 @@ def sweep(args, torch, car, np, out_path):
                     ("push", acc.push(S, n)), ("stage", acc.push(S, 1)), ("ag_copy", acc.twoshot_ag(n, S, 1)),
                     ("twoshot_auto", acc.twoshot(n, S, 1)),
                     ("oneshot_rmsnorm", acc.oneshot_rmsnorm(n, S, rms_row)),
+                    *([("twoshot_rmsnorm", acc.twoshot_rmsnorm(n, S, rms_row))] if rms_ts else []),
                     # the all-rank launches last: they rewrite every rank's segments
                     ("twoshot_full", acc.twoshot(n, S, n)), ("twoshot_ll_full", acc.twoshot_ll(n, S, n, "ll")),
                     ("twoshot_ll128_full", acc.twoshot_ll(n, S, n, "ll128"))]

@@ -21,6 +21,9 @@ and every write, each byte once.  S = numel * element size (bytes per rank).
     receive, one launch   writes W(S) (own wire) + S
   one-shot + residual +   reads n*S + S (residual) + one row (the weight)
     RMSNorm               writes S (residual_out) + S (output)
+  two-shot + residual +   reads S (its rows of n inputs) + S/n (residual) + one row
+    RMSNorm, one rank       + 2(n-1)S/n (the peers' rows of both results)
+                          writes 2S/n (own rows) + 2S/n (segment) + 2(n-1)S/n
 
 The fused two-shot kernel writes rank r's own segment of its output straight
 from the reduce-scatter's registers and never reads it back, so it moves
@@ -53,6 +56,12 @@ def oneshot_rmsnorm(n: int, S: int, row_bytes: int):
     the n inputs and the residual once, the weight (one row) once; residual_out
     and the output once."""
     return n * S + S + row_bytes, 2 * S
+
+
+def twoshot_rmsnorm(n: int, S: int, row_bytes: int):
+    """One rank's share of the two-shot fused all-reduce + RMSNorm."""
+    peers = 2 * (n - 1) * (S // n)
+    return S + S // n + row_bytes + peers, 4 * (S // n) + peers
 
 
 def twoshot(n: int, S: int, ranks: int):
