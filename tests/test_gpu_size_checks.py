@@ -44,8 +44,34 @@ def test_undersized_buffers_raise_before_launch():
                                                                     proto, 0, 1))
         cases.append(lambda proto=proto, mw=mw: car.ar_ll_allreduce(ins[0], mw, out, flags[:31], proto, 0, 1))
         cases.append(lambda proto=proto, mw=mw: car.ar_ll_pack([ins[0], ins[1][:-8]], mw[:2], proto, 1))
+    # the fused all-reduce + RMSNorm: rows of 64, one-shot and two-shot forms
+    hidden = 64
+    w = torch.ones(hidden, dtype=bf, device="cuda")
+    res = torch.zeros(numel, dtype=bf, device="cuda")
+    ws = car.new_rmsnorm_workspace()
+    rsegs = car.new_rmsnorm_segments(n, numel // hidden, hidden, bf)
+    resid = [res] * n
+    cases += [
+        lambda: car.ar_oneshot_rmsnorm(ins, res[:-hidden], w, out, out),
+        lambda: car.ar_oneshot_rmsnorm(ins, res, w, out[:-hidden], out),
+        lambda: car.ar_oneshot_rmsnorm(ins, res, w, out, out[:-8]),
+        lambda: car.ar_oneshot_rmsnorm(ins[:-1] + [ins[-1][:-hidden]], res, w, out, out),
+        lambda: car.ar_oneshot_rmsnorm(ins, res, w, out, out, workspace=ws[:-1]),
+        lambda: car.ar_oneshot_rmsnorm(ins, res, torch.ones(hidden - 8, dtype=bf, device="cuda"), out, out),
+        lambda: car.ar_twoshot_rmsnorm(ins, resid, w, rsegs[:-1] + [rsegs[-1][:-16]], flags, 1),
+        lambda: car.ar_twoshot_rmsnorm(ins, resid, w, rsegs, flags[:-1], 1),
+        lambda: car.ar_twoshot_rmsnorm(ins, [res[:-hidden]] + resid[1:], w, rsegs, flags, 1, 0, 1),
+        lambda: car.ar_twoshot_rmsnorm(ins, resid, w, rsegs, flags, 1, 0, 1, residual_outs=outs,
+                                       outs=[out[:-hidden]] + outs[1:]),
+        lambda: car.ar_twoshot_rmsnorm(ins, resid, w, rsegs, flags, 1, 0, 1, residual_outs=[out[:-hidden]] + outs[1:],
+                                       outs=outs),
+        lambda: car.ar_twoshot_rmsnorm(ins, resid, w, rsegs, flags, 1, 0, 1, residual_outs=outs),
+    ]
+    ws_before = ws.clone()
+    seg_before = [t.clone() for t in rsegs]
     for k, c in enumerate(cases):
         with pytest.raises(ValueError):
             c()
     torch.cuda.synchronize()
     assert torch.equal(out, before[0]) and torch.equal(flags, before[1])
+    assert torch.equal(ws, ws_before) and all(torch.equal(a, b) for a, b in zip(rsegs, seg_before))
