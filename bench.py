@@ -65,7 +65,10 @@ WORKLOADS = {
     "ll1m": (8, "f32", 262144, "ll128", "LL / LL128 message: n=8 ranks, fp32 1 MiB per rank"),
 }
 KERNELS = ["oneshot", "twoshot", "twoshot_ll", "twoshot_ll128", "ll", "ll128"]
+FUSED_KERNELS = ["oneshot_rmsnorm", "twoshot_rmsnorm"]  # the fused all-reduce + RMSNorm, both forms
 KERNEL_SOURCES = {
+    "oneshot_rmsnorm": ["rmsnorm.hip"],
+    "twoshot_rmsnorm": ["rmsnorm.hip"],
     "oneshot": ["oneshot.hip"],
     "twoshot": ["twoshot.hip", "fastdiv.hpp"],
     "twoshot_ll": ["twoshot.hip", "fastdiv.hpp"],
@@ -459,6 +462,43 @@ def curve(args, torch, car, np):
 SWEEP_SIZES = [16 << 10, 256 << 10, 1 << 20, 8 << 20, 64 << 20]
 
 
+RMS_ROW = 16 << 10  # row bytes of the fused all-reduce + RMSNorm in the sweep and its profile
+
+
+def add_rmsnorm_calls(torch, car, rig):
+    """Add the fused all-reduce + RMSNorm over rows of RMS_ROW bytes to every
+    buffer set of a full rig (one with n + 1 outputs per set): the one-shot
+    form with a workspace (its few-rows path where that applies), residual,
+    residual_out and output in three of the set's other output buffers; where
+    the rows split over the ranks, also its two-shot form, rank 0's share, the
+    peers' reduce-scatters published once beforehand on a flag region of its
+    own.  Returns (whether the two-shot form was added, the segments to keep
+    alive)."""
+    n, es, S = rig.n, rig.es, rig.S
+    w = torch.ones(RMS_ROW // es, dtype=rig.dt, device="cuda")
+    ws = car.new_rmsnorm_workspace()
+    rows = S // RMS_ROW
+    two = rows > 0 and rows % n == 0
+    fl = car.new_flags(n)
+    keep = {}
+    for i, b in enumerate(rig.sets):
+        c = rig.calls[i]
+        rn = car.prepare_oneshot_rmsnorm(b.ins, b.outs[1], w, b.outs[2], b.outs[3], 1e-6, workspace=ws)
+        c["oneshot_rmsnorm"] = lambda s, f=rn: f()
+        if two:
+            segs = car.new_rmsnorm_segments(n, rows, RMS_ROW // es, rig.dt)
+            resid = [b.outs[1]] * n
+            car.ar_twoshot_rmsnorm(b.ins, resid, w, segs, fl, PEER_STEP, r0=1, r1=n)
+            tr = car.prepare_twoshot_rmsnorm(b.ins, resid, w, segs, fl, ME, ME + 1,
+                                             only_me(b, b.outs[2:3] * n), only_me(b, b.outs[3:4] * n))
+            c["twoshot_rmsnorm"] = lambda s, f=tr: f(s)
+            keep[i] = segs
+    torch.cuda.synchronize()
+    car.raise_on_status(fl, "publishing the peers' fused reduce-scatters")
+    keep["flags"], keep["weight"], keep["workspace"] = fl, w, ws
+    return two, keep
+
+
 def nvlink_model_crossover(n, alpha=1.5e-6, beta=450e9):
     """Bytes per rank where the pages' alpha-beta model of 8-GPU NVLink ("集合通信：
     NCCL 的算法、协议与推理框架的定制 all-reduce", 算法 and 练习 2; alpha = 1.5 us,
@@ -485,31 +525,9 @@ def sweep(args, torch, car, np, out_path):
             for S in SWEEP_SIZES:
                 rig = Rig(torch, car, np, n, dt_name, S // es, args.rotate_gib * (1 << 30), full=True)
                 fl = rig.flags
-                extra = {}
-                # the fused all-reduce + RMSNorm over rows of 16 KiB, with a workspace (its
-                # few-rows path where that applies); residual, residual_out and output are
-                # three of the set's other output buffers
-                rms_row = 16 << 10
-                rms_w = torch.ones(rms_row // es, dtype=rig.dt, device="cuda")
-                rms_ws = car.new_rmsnorm_workspace()
-                # its two-shot form: rank 0's share, the peers' reduce-scatters published
-                # once beforehand (on a flag region of its own), where the rows split
-                rms_rows = S // rms_row
-                rms_ts = rms_rows > 0 and rms_rows % n == 0
-                rms_fl = car.new_flags(n)
+                rms_ts, extra = add_rmsnorm_calls(torch, car, rig)
                 for i, b in enumerate(rig.sets):
                     c = rig.calls[i]
-                    rn = car.prepare_oneshot_rmsnorm(b.ins, b.outs[1], rms_w, b.outs[2], b.outs[3], 1e-6,
-                                                     workspace=rms_ws)
-                    c["oneshot_rmsnorm"] = lambda s, f=rn: f()
-                    if rms_ts:
-                        segs = car.new_rmsnorm_segments(n, rms_rows, rms_row // es, rig.dt)
-                        resid = [b.outs[1]] * n
-                        car.ar_twoshot_rmsnorm(b.ins, resid, rms_w, segs, rms_fl, PEER_STEP, r0=1, r1=n)
-                        tr = car.prepare_twoshot_rmsnorm(b.ins, resid, rms_w, segs, rms_fl, ME, ME + 1,
-                                                         only_me(b, b.outs[2:3] * n), only_me(b, b.outs[3:4] * n))
-                        c["twoshot_rmsnorm"] = lambda s, f=tr: f(s)
-                        extra[i] = segs
                     c["ll_pack"] = car.prepare_ll_pack([b.ins[ME]], [b.w_ll[ME]], "ll")
                     c["ll_reduce"] = car.prepare_ll_reduce(b.w_ll, b.out_ll, fl, "ll")
                     c["ll128_pack"] = car.prepare_ll_pack([b.ins[ME]], [b.w_128[ME]], "ll128")
@@ -543,8 +561,8 @@ def sweep(args, torch, car, np, out_path):
                     ("bcast", acc.reduce_bcast(n, S, 1)), ("bcast_full", acc.reduce_bcast(n, S, n)),
                     ("push", acc.push(S, n)), ("stage", acc.push(S, 1)), ("ag_copy", acc.twoshot_ag(n, S, 1)),
                     ("twoshot_auto", acc.twoshot(n, S, 1)),
-                    ("oneshot_rmsnorm", acc.oneshot_rmsnorm(n, S, rms_row)),
-                    *([("twoshot_rmsnorm", acc.twoshot_rmsnorm(n, S, rms_row))] if rms_ts else []),
+                    ("oneshot_rmsnorm", acc.oneshot_rmsnorm(n, S, RMS_ROW)),
+                    *([("twoshot_rmsnorm", acc.twoshot_rmsnorm(n, S, RMS_ROW))] if rms_ts else []),
                     # the all-rank launches last: they rewrite every rank's segments
                     ("twoshot_full", acc.twoshot(n, S, n)), ("twoshot_ll_full", acc.twoshot_ll(n, S, n, "ll")),
                     ("twoshot_ll128_full", acc.twoshot_ll(n, S, n, "ll128"))]
@@ -663,8 +681,9 @@ def main(argv=None):
                     help="only time one GPU's share by each algorithm for n = 2..16 over a size grid, then exit")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run ten 256 MiB device-to-device copies (reference for HBM byte counters), then exit")
-    ap.add_argument("--profile-kernel", choices=KERNELS,
-                    help="only launch this kernel 20 times on the workload (for counter runs), then exit")
+    ap.add_argument("--profile-kernel", choices=KERNELS + FUSED_KERNELS,
+                    help="only launch this kernel 20 times on the workload (for counter runs), then exit; "
+                         "the fused all-reduce + RMSNorm kernels run over rows of 16 KiB")
     args = ap.parse_args(argv)
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -711,12 +730,21 @@ def main(argv=None):
         src = [torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda() for a in host]
 
     if args.profile_kernel:
-        rig = Rig(torch, car, np, n, dt_name, numel, args.rotate_gib * (1 << 30), src=src)
+        fused = args.profile_kernel in FUSED_KERNELS
+        rig = Rig(torch, car, np, n, dt_name, numel, args.rotate_gib * (1 << 30), src=src, full=fused)
+        if fused:
+            two, keep = add_rmsnorm_calls(torch, car, rig)
+            if args.profile_kernel == "twoshot_rmsnorm" and not two:
+                print(f"the rows of {RMS_ROW} bytes of workload {args.workload} do not split over {n} ranks",
+                      file=sys.stderr)
+                return 2
         s0 = rig.next_steps(20)
         for i in range(20):
             rig.calls[i % rig.nsets][args.profile_kernel](s0 + i)
         torch.cuda.synchronize()
         car.raise_on_status(rig.flags, "profile")
+        if fused:
+            car.raise_on_status(keep["flags"], "profile")
         print(json.dumps({"profiled_kernel": args.profile_kernel, "launches": 20, "workload": args.workload}),
               flush=True)
         return 0
