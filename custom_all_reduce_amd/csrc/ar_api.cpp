@@ -13,6 +13,10 @@
 #include "ar_launch.hpp"
 
 static_assert(ar::kNoAllocMaxBytes == AR_NOALLOC_MAX_BYTES, "the header states the scratch limit");
+static_assert(ar::kTimeoutCode == AR_ERR_TIMEOUT && ar::kPhaseTwoshotAg == AR_PHASE_TWOSHOT_AG &&
+                  ar::kPhaseLl == AR_PHASE_LL && ar::kPhaseLl128 == AR_PHASE_LL128 &&
+                  ar::kPhaseRmsnorm == AR_PHASE_RMSNORM,
+              "the kernels report the header's status codes");
 
 namespace ar {
 

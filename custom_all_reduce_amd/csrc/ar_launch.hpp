@@ -21,6 +21,13 @@ constexpr int kSlotsPerRank = 1024;
 constexpr int kEpochCopies = 4096;
 constexpr int kStatusWords = 32;
 constexpr uint32_t kTimeoutCode = 5;  // AR_ERR_TIMEOUT
+// Phase of a reported timeout (the status word's bits 8..15), one per kind
+// of bounded wait: a two-shot all-gather's slot or done flag, an LL line,
+// an LL128 line, a fused RMSNorm row's sibling partial sums.
+constexpr uint32_t kPhaseTwoshotAg = 1;  // AR_PHASE_TWOSHOT_AG
+constexpr uint32_t kPhaseLl = 2;         // AR_PHASE_LL
+constexpr uint32_t kPhaseLl128 = 3;      // AR_PHASE_LL128
+constexpr uint32_t kPhaseRmsnorm = 4;    // AR_PHASE_RMSNORM
 
 struct DeviceInfo {
     int cu_count;

@@ -165,7 +165,7 @@ __device__ bool ll_slow_wait(const ReduceParams& p, size_t c, uint32_t nl, u32x4
         if (missing == 0) return true;
         if (now_ticks() - t0 > p.timeout_ticks) {
             const int bl = __ffsll((unsigned long long)missing) - 1;
-            if (lane == bl) report_timeout(p.flags, 2u, uint32_t(bad_r), uint32_t(2 * c + bad_l));
+            if (lane == bl) report_timeout(p.flags, kPhaseLl, uint32_t(bad_r), uint32_t(2 * c + bad_l));
             return false;
         }
         __builtin_amdgcn_s_sleep(1);
@@ -345,7 +345,7 @@ __global__ __launch_bounds__(kBlockLL) void ll_reduce_kernel(ReduceParams p) {
                     }
                 }
                 if (!ok && now_ticks() - t0 > p.timeout_ticks) {
-                    report_timeout(p.flags, 2u, uint32_t(bad_r), uint32_t(2 * nfull));
+                    report_timeout(p.flags, kPhaseLl, uint32_t(bad_r), uint32_t(2 * nfull));
                     return;
                 }
                 if (!ok) __builtin_amdgcn_s_sleep(1);
@@ -452,7 +452,7 @@ __global__ __launch_bounds__(kBlockLL) void ll_reduce1_kernel(ReduceParams p) {
             if (missing == 0) break;
             if (now_ticks() - t0 > p.timeout_ticks) {
                 const int bl = __ffsll((unsigned long long)missing) - 1;
-                if (lane == bl) report_timeout(p.flags, 2u, uint32_t(bad_r), uint32_t(c));
+                if (lane == bl) report_timeout(p.flags, kPhaseLl, uint32_t(bad_r), uint32_t(c));
                 return;
             }
             __builtin_amdgcn_s_sleep(1);
@@ -621,7 +621,7 @@ __global__ __launch_bounds__(kBlock128) void ll128_reduce_kernel(ReduceParams p)
                 const int bl = __ffsll((unsigned long long)missing) - 1;
                 const int rr = __shfl(bad_r, bl);
                 const uint32_t ll = uint32_t(__shfl(uint32_t(bad_line), bl));
-                if (lane == bl) report_timeout(p.flags, 3u, uint32_t(rr), ll);
+                if (lane == bl) report_timeout(p.flags, kPhaseLl128, uint32_t(rr), ll);
                 return;
             }
             __builtin_amdgcn_s_sleep(1);

@@ -1,4 +1,6 @@
-// One-shot all-reduce fused with a residual add and RMSNorm, for gfx950.
+// All-reduce fused with a residual add and RMSNorm, for gfx950: a one-shot
+// form (every rank's launch reduces and norms every row) and a two-shot
+// form (each rank reduces and norms its own rows, then gathers its peers').
 //
 // "集合通信：NCCL 的算法、协议与推理框架的定制 all-reduce" names, among the
 // inference frameworks' communication paths, an all-reduce fused with
@@ -11,7 +13,7 @@
 //            computed in fp32 and rounded once to the data type.
 // residual_out may be the residual buffer itself (updated in place).
 //
-// Work.  A workgroup owns a row (above 2^20 rows the workgroups stride over
+// One-shot form.  A workgroup owns a row (above 2^20 rows the workgroups stride over
 // the rows): each lane takes 16-byte vectors v = lane + j * blockDim
 // (j < VPT) of the row, loads the ranks' vectors and the residual's with
 // nontemporal loads, folds them, stores residual_out and keeps h in
@@ -312,7 +314,7 @@ __global__ __launch_bounds__(kWave) void twoshot_rmsnorm_parts_kernel(TsRmsParam
             const uint64_t missing = ~wave_ballot(!mine || sl.y >= q.step) & wave_exec();
             if (missing == 0) break;
             if (now_ticks() - t0 > q.timeout_ticks) {
-                if (lane == 0) report_timeout(q.flags, 4u, r, k);
+                if (lane == 0) report_timeout(q.flags, kPhaseRmsnorm, r, k);
                 return;  // no output, no done flag
             }
             __builtin_amdgcn_s_sleep(1);
@@ -354,7 +356,7 @@ __global__ __launch_bounds__(kWave) void twoshot_rmsnorm_parts_kernel(TsRmsParam
     const uint64_t t0 = now_ticks();
     while (__builtin_amdgcn_readfirstlane(seen) < q.step) {
         if (now_ticks() - t0 > q.timeout_ticks) {
-            if (lane == 0) report_timeout(q.flags, 1u, j, k);
+            if (lane == 0) report_timeout(q.flags, kPhaseTwoshotAg, j, k);
             return;
         }
         __builtin_amdgcn_s_sleep(1);
@@ -411,7 +413,7 @@ __global__ __launch_bounds__(kMaxBlock) void twoshot_rmsnorm_kernel(TsRmsParams 
     const uint64_t t0 = now_ticks();
     while (__builtin_amdgcn_readfirstlane(seen) < q.step) {
         if (now_ticks() - t0 > q.timeout_ticks) {
-            if (lane == 0) report_timeout(q.flags, 1u, j, t);
+            if (lane == 0) report_timeout(q.flags, kPhaseTwoshotAg, j, t);
             return;
         }
         __builtin_amdgcn_s_sleep(1);
@@ -529,7 +531,7 @@ __global__ __launch_bounds__(kWave) void oneshot_rmsnorm_coop_kernel(RmsParams p
             const uint64_t missing = ~wave_ballot(!mine || sl.y >= step) & wave_exec();
             if (missing == 0) break;
             if (now_ticks() - t0 > timeout_ticks) {
-                if (lane == 0) report_timeout(ws, 4u, 0u, row);
+                if (lane == 0) report_timeout(ws, kPhaseRmsnorm, 0u, row);
                 timed_out = true;
                 break;
             }

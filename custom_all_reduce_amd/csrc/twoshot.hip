@@ -273,7 +273,7 @@ __device__ __forceinline__ void all_gather_phase(const TwoShotParams& p, const u
                 const int bad_lane = __ffsll((unsigned long long)missing) - 1;
                 const uint32_t bj = __shfl(j, bad_lane);
                 const uint32_t bt = __shfl(t, bad_lane);
-                if (lane == 0) report_timeout(p.flags, 1u, bj, bt);
+                if (lane == 0) report_timeout(p.flags, kPhaseTwoshotAg, bj, bt);
                 return;  // skip every copy of this wavefront
             }
             __builtin_amdgcn_s_sleep(1);
@@ -380,7 +380,7 @@ __device__ __forceinline__ void all_gather_ll_phase(const TwoShotParams& p, cons
                 if (missing == 0) break;
                 if (now_ticks() - t_start > p.timeout_ticks) {
                     const int bl = __ffsll((unsigned long long)missing) - 1;
-                    if (lane == bl) report_timeout(p.flags, 1u, bad_j, bad_t);
+                    if (lane == bl) report_timeout(p.flags, kPhaseTwoshotAg, bad_j, bad_t);
                     return;  // skip every remaining copy of this wavefront
                 }
                 __builtin_amdgcn_s_sleep(1);
@@ -572,7 +572,7 @@ __global__ __launch_bounds__(kWave * WB) void twoshot_share_kernel(TwoShotParams
                 if (missing == 0) break;
                 if (now_ticks() - t_start > p.timeout_ticks) {
                     const int bl = __ffsll((unsigned long long)missing) - 1;
-                    if (lane == bl) report_timeout(p.flags, 1u, j, fdiv(k * uint32_t(C) + bad_u, p.div_upt));
+                    if (lane == bl) report_timeout(p.flags, kPhaseTwoshotAg, j, fdiv(k * uint32_t(C) + bad_u, p.div_upt));
                     return;  // skip the chunk's copies
                 }
                 __builtin_amdgcn_s_sleep(1);
@@ -594,7 +594,7 @@ __global__ __launch_bounds__(kWave * WB) void twoshot_share_kernel(TwoShotParams
             if (missing == 0) break;
             if (now_ticks() - t_start > p.timeout_ticks) {
                 const int bad_lane = __ffsll((unsigned long long)missing) - 1;
-                if (lane == 0) report_timeout(p.flags, 1u, j, tf + uint32_t(bad_lane));
+                if (lane == 0) report_timeout(p.flags, kPhaseTwoshotAg, j, tf + uint32_t(bad_lane));
                 return;  // skip the chunk's copies
             }
             __builtin_amdgcn_s_sleep(1);
@@ -764,7 +764,7 @@ __device__ __forceinline__ void ll128_ag_chunk(const TwoShot128Params& p, uint8_
         if (missing == 0) break;
         if (now_ticks() - t_start > p.timeout_ticks) {
             const int bad = __ffsll((unsigned long long)missing) - 1;
-            if (lane == 0) report_timeout(p.flags, 1u, j, line0 + uint32_t(bad));
+            if (lane == 0) report_timeout(p.flags, kPhaseTwoshotAg, j, line0 + uint32_t(bad));
             return;  // skip the chunk's copies
         }
         __builtin_amdgcn_s_sleep(1);
@@ -957,7 +957,7 @@ __global__ __launch_bounds__(kBlock) void ag_wait_kernel(TwoShotParams p) {
                 const int bad_lane = __ffsll((unsigned long long)missing) - 1;
                 const uint32_t bj = __shfl(j, bad_lane);
                 const uint32_t bt = __shfl(t, bad_lane);
-                if (lane == 0) report_timeout(p.flags, 1u, bj, bt);
+                if (lane == 0) report_timeout(p.flags, kPhaseTwoshotAg, bj, bt);
                 return;
             }
             __builtin_amdgcn_s_sleep(1);
