@@ -370,6 +370,8 @@ def prepare_twoshot_rmsnorm(ins, residuals, weight: torch.Tensor, segs, flags: t
     _need_like([weight], ref.dtype, hidden, "weight")
     if len(residuals) != n or len(segs) != n:
         raise ValueError("residuals and segs need one entry per rank")
+    if not 0 <= r0 < r1 <= n:
+        raise ValueError(f"ranks [{r0}, {r1}) are not a range within [0, {n})")
     mine = range(r0, r1)
     for r in mine:
         _need_like([_dev_tensor(residuals[r], "residual")], ref.dtype, ref.numel(), "every residual in [r0, r1)")
@@ -399,7 +401,8 @@ def prepare_twoshot_rmsnorm(ins, residuals, weight: torch.Tensor, segs, flags: t
 def ar_twoshot_rmsnorm(ins, residuals, weight, segs, flags, step: int, r0: int = 0, r1=None, residual_outs=None,
                        outs=None, eps: float = 1e-6, stream=None):
     """ar_twoshot_rmsnorm: the reduce-scatter of ranks [r0, r1) (outs None), or
-    one rank's share with the all-gather of its peers' rows."""
+    one rank's share with the all-gather of its peers' rows.  step 0: ids
+    kept in the segments (one auto call per rank per step)."""
     prepare_twoshot_rmsnorm(ins, residuals, weight, segs, flags, r0, r1, residual_outs, outs, eps)(step, stream)
 
 

@@ -285,7 +285,7 @@ int ar_twoshot_rmsnorm(const void* const* in, int n, const void* const* residual
                        void* const* seg, void* const* residual_out, void* const* out, size_t rows, size_t hidden,
                        float eps, int dtype, int r0, int r1, uint32_t* flags, uint32_t step, void* stream) {
     if (!in || !residual || !weight || !seg || !flags || !ranks_ok(n) || !dtype_ok(dtype) || rows == 0 ||
-        hidden == 0 || step == 0)
+        hidden == 0)
         return AR_ERR_ARG;
     if (r0 < 0 || r1 > n || r0 >= r1) return AR_ERR_ARG;
     const bool fused = out != nullptr;

@@ -237,14 +237,47 @@ struct TsRmsParams {
     u32x4* out[kMaxRanks];
     uint32_t* flags;
     uint64_t timeout_ticks;
-    uint32_t step;
+    uint32_t step;    // 0: auto, each wavefront's epoch (in a segment) + 1
     int r0, r1;
     uint32_t group;   // rows per rank
     uint32_t tile;    // rows per arrival slot
     uint32_t ntiles;  // slots per rank
     uint32_t parts;   // 64-vector parts per row
     int do_ag;
+    size_t ep_off;    // byte offset of a segment's epoch words (auto ids)
+    uint32_t wpb;     // wavefronts per workgroup
 };
+
+// Auto step ids.  A segment ends with one epoch word per wavefront of its
+// rank's work in either role: first its reduce-scatter items, then the
+// items of its all-gather (for the peers' n - 1 groups, in order), a word
+// per wavefront of each.  A wavefront takes its word + 1 as the step id
+// when it starts and stores that id back when it ends, so every launch
+// advances every word it owns by one: the words of a rank's reduce-scatter
+// advance once per step whether the rank's share or a reduce-scatter-only
+// launch runs them, those of its all-gather with its share, and all agree
+// with no wavefront waiting on another.  A call captured once into a graph
+// takes a new id on every replay.  The words sit beside the done flags and
+// partial sums they must stay above, so zeroing the segments restarts both.
+struct AutoId {
+    uint32_t* word = nullptr;  // this wavefront's epoch word, null for explicit ids
+    uint32_t step = 0;
+};
+// The word's load goes out before the wavefront's first data load and its
+// value is taken only where the step is first needed, so its round trip
+// overlaps theirs.
+__device__ __forceinline__ uint32_t ts_epoch_load(const TsRmsParams& q, uint32_t r, uint32_t index, AutoId& id) {
+    if (q.step != 0) return 0u;
+    id.word = reinterpret_cast<uint32_t*>(reinterpret_cast<uint8_t*>(q.seg[r]) + q.ep_off) + index;
+    return flag_load_relaxed(id.word);
+}
+__device__ __forceinline__ uint32_t ts_take_step(const TsRmsParams& q, uint32_t epoch, AutoId& id) {
+    id.step = q.step != 0 ? q.step : __builtin_amdgcn_readfirstlane(epoch) + 1u;
+    return id.step;
+}
+__device__ __forceinline__ void ts_finish(const AutoId& id) {
+    if (id.word && id.step != 0 && (threadIdx.x & (kWave - 1)) == 0) flag_store_relaxed(id.word, id.step);
+}
 
 // Parts of rows.  A rank's 64 rows of the prefill message would put each
 // row's n + 1 streams through one compute unit (the workgroup-per-row form
@@ -262,7 +295,7 @@ __host__ __device__ constexpr size_t ts_partial_off(size_t G, size_t V) { return
 __host__ __device__ constexpr size_t ts_done_off(size_t G, size_t V, size_t P) { return 32 * G * V + 8 * G * P; }
 
 template <typename T, int NR>
-__global__ __launch_bounds__(kWave) void twoshot_rmsnorm_parts_kernel(TsRmsParams q) {
+__device__ __forceinline__ void twoshot_rmsnorm_parts(const TsRmsParams& q, AutoId& id) {
     constexpr int E = Vec<T>::E;
     const RmsParams& p = q.p;
     const uint32_t lane = threadIdx.x;
@@ -275,6 +308,7 @@ __global__ __launch_bounds__(kWave) void twoshot_rmsnorm_parts_kernel(TsRmsParam
         const uint32_t rr = b / (G * P), rem = b - rr * (G * P);
         const uint32_t k = rem / P, pp = rem - k * P;
         const uint32_t r = uint32_t(q.r0) + rr;
+        const uint32_t epoch = ts_epoch_load(q, r, rem, id);  // word k P + pp of rank r's
         const size_t base = (size_t(r) * G + k) * V;
         const uint32_t v = pp * kWave + lane;
         const bool valid = v < V;
@@ -287,6 +321,7 @@ __global__ __launch_bounds__(kWave) void twoshot_rmsnorm_parts_kernel(TsRmsParam
         Acc<T> acc;
 #pragma unroll
         for (int i = 0; i < NR; ++i) acc.add(x[i]);
+        const uint32_t step = ts_take_step(q, epoch, id);
         float res[E], h[E];
         Vec<T>::widen(rv, res);
         float ss = 0.0f;
@@ -304,21 +339,21 @@ __global__ __launch_bounds__(kWave) void twoshot_rmsnorm_parts_kernel(TsRmsParam
         uint8_t* segb = reinterpret_cast<uint8_t*>(seg);
         const __amdgpu_buffer_rsrc_t slots = buffer_range(segb + ts_partial_off(G, V) + size_t(k) * P * 8u, P * 8u);
         if (lane == 0)
-            __builtin_amdgcn_raw_buffer_store_b64(u32x2{__float_as_uint(ss), q.step}, slots, int(pp * 8u), 0,
+            __builtin_amdgcn_raw_buffer_store_b64(u32x2{__float_as_uint(ss), step}, slots, int(pp * 8u), 0,
                                                   kCachePolicySc1);
         const bool mine = lane < P;
         const uint32_t soff = (mine ? lane : 0u) * 8u;
         u32x2 sl = __builtin_amdgcn_raw_buffer_load_b64(slots, int(soff), 0, kCachePolicySc1);
         const uint64_t t0 = now_ticks();
         while (true) {
-            const uint64_t missing = ~wave_ballot(!mine || sl.y >= q.step) & wave_exec();
+            const uint64_t missing = ~wave_ballot(!mine || sl.y >= step) & wave_exec();
             if (missing == 0) break;
             if (now_ticks() - t0 > q.timeout_ticks) {
                 if (lane == 0) report_timeout(q.flags, kPhaseRmsnorm, r, k);
                 return;  // no output, no done flag
             }
             __builtin_amdgcn_s_sleep(1);
-            if (mine && sl.y < q.step) sl = __builtin_amdgcn_raw_buffer_load_b64(slots, int(soff), 0, kCachePolicySc1);
+            if (mine && sl.y < step) sl = __builtin_amdgcn_raw_buffer_load_b64(slots, int(soff), 0, kCachePolicySc1);
         }
         // the same values in the same lanes in every part of the row
         const float total = wave_sum(mine ? __uint_as_float(sl.x) : 0.0f);
@@ -335,7 +370,7 @@ __global__ __launch_bounds__(kWave) void twoshot_rmsnorm_parts_kernel(TsRmsParam
         // done: every store of this part complete, then its flag
         wait_stores();
         if (lane == 0)
-            __builtin_amdgcn_raw_buffer_store_b32(q.step, buffer_range(segb + ts_done_off(G, V, P), G * P * 4u),
+            __builtin_amdgcn_raw_buffer_store_b32(step, buffer_range(segb + ts_done_off(G, V, P), G * P * 4u),
                                                   int((k * P + pp) * 4u), 0, kCachePolicySc1);
         return;
     }
@@ -346,6 +381,7 @@ __global__ __launch_bounds__(kWave) void twoshot_rmsnorm_parts_kernel(TsRmsParam
     if (oo >= R) return;
     const uint32_t rem = c - oo * per_out;
     const uint32_t r = uint32_t(q.r0) + oo;
+    const uint32_t epoch = ts_epoch_load(q, r, G * P + rem, id);  // after the G P words of its reduce-scatter
     const uint32_t jj = rem / (G * P), rem2 = rem - jj * (G * P);
     const uint32_t j = jj < r ? jj : jj + 1u;  // every rank but r
     const uint32_t k = rem2 / P, pp = rem2 - k * P;
@@ -353,8 +389,9 @@ __global__ __launch_bounds__(kWave) void twoshot_rmsnorm_parts_kernel(TsRmsParam
     const __amdgpu_buffer_rsrc_t done = buffer_range(segb + ts_done_off(G, V, P), G * P * 4u);
     const uint32_t doff = (k * P + pp) * 4u;
     uint32_t seen = __builtin_amdgcn_raw_buffer_load_b32(done, int(doff), 0, kCachePolicySc1);
+    const uint32_t step = ts_take_step(q, epoch, id);
     const uint64_t t0 = now_ticks();
-    while (__builtin_amdgcn_readfirstlane(seen) < q.step) {
+    while (__builtin_amdgcn_readfirstlane(seen) < step) {
         if (now_ticks() - t0 > q.timeout_ticks) {
             if (lane == 0) report_timeout(q.flags, kPhaseTwoshotAg, j, k);
             return;
@@ -372,10 +409,16 @@ __global__ __launch_bounds__(kWave) void twoshot_rmsnorm_parts_kernel(TsRmsParam
     }
 }
 
+template <typename T, int NR>
+__global__ __launch_bounds__(kWave) void twoshot_rmsnorm_parts_kernel(TsRmsParams q) {
+    AutoId id;
+    twoshot_rmsnorm_parts<T, NR>(q, id);
+    ts_finish(id);
+}
+
 template <typename T, int NR, int VPT>
-__global__ __launch_bounds__(kMaxBlock) void twoshot_rmsnorm_kernel(TsRmsParams q) {
-    __shared__ float part[kMaxWaves];
-    __shared__ float factor;
+__device__ __forceinline__ void twoshot_rmsnorm_rows(const TsRmsParams& q, float (&part)[kMaxWaves],
+                                                     float& factor, AutoId& id) {
     const RmsParams& p = q.p;
     const uint32_t R = uint32_t(q.r1 - q.r0);
     const uint32_t rs_items = R * q.ntiles;
@@ -384,6 +427,7 @@ __global__ __launch_bounds__(kMaxBlock) void twoshot_rmsnorm_kernel(TsRmsParams 
     if (b < rs_items) {
         const uint32_t rr = b / q.ntiles, t = b - rr * q.ntiles;
         const uint32_t r = uint32_t(q.r0) + rr;
+        const uint32_t epoch = ts_epoch_load(q, r, t * q.wpb + threadIdx.x / kWave, id);
         const uint32_t k1 = min((t + 1u) * q.tile, q.group);
         for (uint32_t k = t * q.tile; k < k1; ++k) {
             const size_t base = (size_t(r) * q.group + k) * p.vecs;
@@ -392,10 +436,11 @@ __global__ __launch_bounds__(kMaxBlock) void twoshot_rmsnorm_kernel(TsRmsParams 
             rmsnorm_row<T, NR, VPT>(p, base, q.residual[r] + base, d, part, factor);
             __syncthreads();  // part and factor are rewritten by the next row
         }
+        const uint32_t step = ts_take_step(q, epoch, id);
         // publish the tile once every wavefront's stores are complete
         wait_stores();
         __syncthreads();
-        if (threadIdx.x == 0) flag_store_relaxed(slots + r * kSlotsPerRank + t, q.step);
+        if (threadIdx.x == 0) flag_store_relaxed(slots + r * kSlotsPerRank + t, step);
         return;
     }
     // all-gather item: (output rank, peer, tile)
@@ -408,10 +453,12 @@ __global__ __launch_bounds__(kMaxBlock) void twoshot_rmsnorm_kernel(TsRmsParams 
     const uint32_t jj = rem / q.ntiles, t = rem - jj * q.ntiles;
     const uint32_t j = jj < r ? jj : jj + 1u;  // every rank but r
     const uint32_t lane = threadIdx.x & (kWave - 1);
+    const uint32_t epoch = ts_epoch_load(q, r, (q.ntiles + rem) * q.wpb + threadIdx.x / kWave, id);
     // every wavefront polls the tile's slot itself (bounded)
     uint32_t seen = flag_load_relaxed(slots + j * kSlotsPerRank + t);
+    const uint32_t step = ts_take_step(q, epoch, id);
     const uint64_t t0 = now_ticks();
-    while (__builtin_amdgcn_readfirstlane(seen) < q.step) {
+    while (__builtin_amdgcn_readfirstlane(seen) < step) {
         if (now_ticks() - t0 > q.timeout_ticks) {
             if (lane == 0) report_timeout(q.flags, kPhaseTwoshotAg, j, t);
             return;
@@ -434,6 +481,15 @@ __global__ __launch_bounds__(kMaxBlock) void twoshot_rmsnorm_kernel(TsRmsParams 
     }
 }
 
+template <typename T, int NR, int VPT>
+__global__ __launch_bounds__(kMaxBlock) void twoshot_rmsnorm_kernel(TsRmsParams q) {
+    __shared__ float part[kMaxWaves];
+    __shared__ float factor;
+    AutoId id;
+    twoshot_rmsnorm_rows<T, NR, VPT>(q, part, factor, id);
+    ts_finish(id);
+}
+
 // Which two-shot form runs, by rank count and size (the same for every
 // rank's launch of a step, so a share and its peers' reduce-scatters agree):
 // parts where a row's n + 1 streams hold at least kCoopMinRowBytes and a
@@ -447,6 +503,17 @@ constexpr uint32_t kTsPartsMaxRows = 256;
 inline bool ts_parts(int nr, uint32_t group, uint32_t vecs) {
     return group < kTsPartsMaxRows && uint32_t(nr + 1) * vecs * 16u >= kCoopMinRowBytes;
 }
+// A workgroup per row: vectors per lane, wavefronts per workgroup (every row
+// fits one workgroup of at most 1024 lanes with 1, 2 or 4 vectors each).
+inline int ts_vpt(uint32_t vecs) { return vecs <= 1024u ? 1 : (vecs <= 2048u ? 2 : 4); }
+inline uint32_t ts_wpb(uint32_t vecs) {
+    const uint32_t v = uint32_t(ts_vpt(vecs));
+    return ((vecs + v - 1) / v + kWave - 1) / kWave;
+}
+inline uint32_t ts_tiles(uint32_t group) {
+    const uint32_t tile = (group + uint32_t(kSlotsPerRank) - 1) / uint32_t(kSlotsPerRank);
+    return (group + tile - 1) / tile;
+}
 
 template <typename T, int NR>
 hipError_t launch_ts_t(const TsRmsParams& q, hipStream_t s) {
@@ -458,18 +525,18 @@ hipError_t launch_ts_t(const TsRmsParams& q, hipStream_t s) {
         hipLaunchKernelGGL((twoshot_rmsnorm_parts_kernel<T, NR>), dim3(uint32_t(items)), dim3(kWave), 0, s, q);
         return hipGetLastError();
     }
-    const int vpt = V <= 1024u ? 1 : (V <= 2048u ? 2 : 4);
-    uint32_t block = (V + uint32_t(vpt) - 1) / uint32_t(vpt);
-    block = (block + kWave - 1) / kWave * kWave;
+    const int vpt = ts_vpt(V);
+    const uint32_t block = q.wpb * kWave;
     const uint32_t R = uint32_t(q.r1 - q.r0);
     const uint64_t items = uint64_t(R) * q.ntiles + (q.do_ag ? uint64_t(R) * (NR - 1) * q.ntiles : 0u);
     const dim3 grid = dim3(uint32_t(items)), blk = dim3(block);
+    const TsRmsParams& qa = q;
     if (vpt == 1)
-        hipLaunchKernelGGL((twoshot_rmsnorm_kernel<T, NR, 1>), grid, blk, 0, s, q);
+        hipLaunchKernelGGL((twoshot_rmsnorm_kernel<T, NR, 1>), grid, blk, 0, s, qa);
     else if (vpt == 2)
-        hipLaunchKernelGGL((twoshot_rmsnorm_kernel<T, NR, 2>), grid, blk, 0, s, q);
+        hipLaunchKernelGGL((twoshot_rmsnorm_kernel<T, NR, 2>), grid, blk, 0, s, qa);
     else
-        hipLaunchKernelGGL((twoshot_rmsnorm_kernel<T, NR, 4>), grid, blk, 0, s, q);
+        hipLaunchKernelGGL((twoshot_rmsnorm_kernel<T, NR, 4>), grid, blk, 0, s, qa);
     return hipGetLastError();
 }
 
@@ -600,9 +667,18 @@ hipError_t launch_t(const RmsParams& p, uint32_t* ws, uint64_t timeout_ticks, hi
 
 }  // namespace
 
-size_t twoshot_rmsnorm_segment_bytes(int n, size_t rows, size_t hidden, int dtype) {
+// Segment: the parts' layout above, then the epoch words: n G P for parts
+// of rows, n (tiles) (wavefronts per workgroup) for a workgroup per row.
+static size_t ts_ep_off(int n, size_t rows, size_t hidden, int dtype) {
     const size_t G = rows / size_t(n), V = hidden * (dtype == 0 ? 4u : 2u) / 16u, P = (V + kWave - 1) / kWave;
     return (ts_done_off(G, V, P) + 4 * G * P + 15) / 16 * 16;
+}
+
+size_t twoshot_rmsnorm_segment_bytes(int n, size_t rows, size_t hidden, int dtype) {
+    const uint32_t G = uint32_t(rows / size_t(n)), V = uint32_t(hidden * (dtype == 0 ? 4u : 2u) / 16u);
+    const size_t words = ts_parts(n, G, V) ? size_t(n) * G * ((V + kWave - 1) / kWave)
+                                           : size_t(n) * ts_tiles(G) * ts_wpb(V);
+    return (ts_ep_off(n, rows, hidden, dtype) + 4 * words + 15) / 16 * 16;
 }
 
 hipError_t launch_twoshot_rmsnorm(const void* const* in, int n, const void* const* residual, const void* weight,
@@ -633,9 +709,11 @@ hipError_t launch_twoshot_rmsnorm(const void* const* in, int n, const void* cons
     q.r1 = r1;
     q.group = uint32_t(rows / size_t(n));
     q.tile = (q.group + uint32_t(kSlotsPerRank) - 1) / uint32_t(kSlotsPerRank);
-    q.ntiles = (q.group + q.tile - 1) / q.tile;
+    q.ntiles = ts_tiles(q.group);
     q.parts = (q.p.vecs + kWave - 1) / kWave;
     q.do_ag = out != nullptr;
+    q.ep_off = ts_ep_off(n, rows, hidden, dtype);
+    q.wpb = ts_wpb(q.p.vecs);
     return dispatch_ranks(n, [&](auto nr) {
         constexpr int NR = decltype(nr)::value;
         return dtype == 0 ? launch_ts_t<float, NR>(q, s) : launch_ts_t<bf16_t, NR>(q, s);

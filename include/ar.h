@@ -187,7 +187,8 @@ int ar_oneshot_rmsnorm(const void* const* in, int n, const void* residual, const
  *  weight       : hidden elements.
  *  seg          : n device pointers, ar_rmsnorm_segment_bytes(n, rows,
  *                 hidden, dtype) bytes each, zeroed before their first use
- *                 (their slots and flags carry step ids); seg[r] for r in
+ *                 (their slots and flags carry step ids; the last 16 bytes
+ *                 hold the rank's epoch for auto ids); seg[r] for r in
  *                 [r0, r1) written, the peers' read when fused.
  *  residual_out, out : NULL (the reduce-scatter of ranks [r0, r1) alone),
  *                 or n device pointers of rows * hidden elements, entries in
@@ -196,7 +197,17 @@ int ar_oneshot_rmsnorm(const void* const* in, int n, const void* residual, const
  *                 the peers' through the all-gather).
  *  flags, step  : a flag region of ar_flag_bytes(n) and the step id, >= 1
  *                 and above every earlier call's on these segments and flags
- *                 (the peers' reduce-scatters of this step publish it).
+ *                 (the peers' reduce-scatters of this step publish it); or 0
+ *                 (auto): rank r's id is its epoch, kept in seg[r], plus
+ *                 one, and the launch advances the epochs of ranks [r0, r1)
+ *                 once all its wavefronts have finished (they count
+ *                 themselves out in seg[r0]).  Every rank's launch of a step
+ *                 takes the same id as long as each rank makes one auto call
+ *                 per step, so a call captured once into a HIP graph takes a
+ *                 new id on every replay ([CAR] 实现: the graph path keeps
+ *                 fixed registered addresses).  Zeroing the segments restarts
+ *                 the epochs; do not mix explicit and auto ids between
+ *                 zeroings, and zero them before 2^32 - 1 calls.
  * A wait that runs out writes AR_ERR_TIMEOUT | phase << 8 | rank << 16 to the
  * flag region's status word: AR_PHASE_TWOSHOT_AG with the peer (all-gather),
  * AR_PHASE_RMSNORM with the rank (a row's parts); detail: the row in the

@@ -154,8 +154,8 @@ def test_a_missing_peer_is_reported_as_a_timeout():
 def test_argument_errors():
     s = Setup(4, "bf16", 8, 64, config=450)
     f = car.ar_twoshot_rmsnorm
-    with pytest.raises(car.ArError):  # step 0
-        f(s.ins, s.residuals, s.weight, s.segs, s.flags, 0, r0=0, r1=1)
+    with pytest.raises(ValueError):  # a rank range past n
+        f(s.ins, s.residuals, s.weight, s.segs, s.flags, 1, r0=3, r1=5)
     with pytest.raises(car.ArError):  # the all-gather for two ranks in one launch
         f(s.ins, s.residuals, s.weight, s.segs, s.flags, 1, r0=0, r1=2, residual_outs=s.ros, outs=s.outs)
     with pytest.raises(ValueError):  # residual_outs without outs
@@ -164,3 +164,99 @@ def test_argument_errors():
     with pytest.raises(car.ArError) as e:
         f(x, x, s.weight, [torch.zeros(1 << 16, dtype=torch.uint8, device="cuda")] * 4, s.flags, 1)
     assert e.value.code == car.AR_ERR_DIVISIBLE
+
+
+# ---- auto step ids (step 0): each rank's epoch kept in its segment ----------
+def epoch_words(s: Setup, r):
+    """Rank r's epoch words: (those of its reduce-scatter, those of its
+    all-gather).  A segment holds G out rows and G residual_out rows, G P
+    partial slots and G P done flags, then (16-byte aligned) a word per
+    wavefront: parts of rows, G P for the reduce-scatter and (n - 1) G P for
+    the all-gather; a workgroup per row, tiles x wavefronts per workgroup for
+    the reduce-scatter and n - 1 times that for the all-gather."""
+    V, G = s.vecs(), s.rows // s.n
+    P = -(-V // 64)
+    if s.twoshot_parts():
+        rs = G * P
+    else:
+        tile = -(-G // 1024)
+        vpt = 1 if V <= 1024 else (2 if V <= 2048 else 4)
+        rs = -(-G // tile) * -(-(-(-V // vpt)) // 64)
+    off = -(-(32 * G * V + 12 * G * P) // 16) * 16
+    w = s.segs[r][off: off + 4 * s.n * rs].view(torch.int32).cpu().numpy()
+    return w[:rs], w[rs:]
+
+
+def check_epochs(s: Setup, calls):
+    # every reduce-scatter word advanced once per step; only rank 0's all-gather ran
+    for r in range(s.n):
+        rs, ag = epoch_words(s, r)
+        assert (rs == calls).all(), f"rank {r}: reduce-scatter epochs {set(rs.tolist())}, want {calls}"
+        assert (ag == (calls if r == 0 else 0)).all(), f"rank {r}: all-gather epochs {set(ag.tolist())}"
+
+
+def check_share(s: Setup, me, what):
+    want_ro, y = s.want()
+    assert np.array_equal(bits(s.ros[me]), oracle_bits(want_ro)), f"{what}: residual_out"
+    check_out(host_values(s.outs[me], s.dt), y, s.dt, what)
+
+
+def new_data(s: Setup, config):
+    s.host = synth.rank_inputs(s.n, s.rows * s.hidden, s.dt, "normal", config=config)
+    for t, a in zip(s.ins, s.host):
+        t.copy_(to_dev(a))
+
+
+# parts of rows (8 and 2 rows per rank), a workgroup per row (300 rows per rank; light rows)
+AUTO_CASES = [(8, 64, 8192), (16, 32, 16384), (8, 8 * 300, 8192), (4, 32, 64)]
+
+
+@pytest.mark.parametrize("n, rows, hidden", AUTO_CASES)
+def test_auto_step_ids_in_a_row(n, rows, hidden):
+    s = Setup(n, "bf16", rows, hidden, config=460)
+    for it in range(4):
+        new_data(s, 461 + it)
+        car.ar_twoshot_rmsnorm(s.ins, s.residuals, s.weight, s.segs, s.flags, 0, r0=1, r1=n, eps=s.eps)
+        s.share(0, 0)
+        torch.cuda.synchronize()
+        car.raise_on_status(s.flags, f"auto step {it}")
+        check_share(s, 0, f"n={n} rows={rows} hidden={hidden} auto step {it}")
+    check_epochs(s, 4)
+
+
+@pytest.mark.parametrize("n, rows, hidden", [AUTO_CASES[0], AUTO_CASES[2]])
+def test_auto_step_ids_replayed_in_a_graph(n, rows, hidden):
+    # the peers' reduce-scatters and rank 0's share captured once; each replay
+    # takes the next id, with eager calls on the same segments in between
+    s = Setup(n, "bf16", rows, hidden, config=470)
+    only0 = (lambda ts: [ts[0]] + [None] * (n - 1))
+    peers = car.prepare_twoshot_rmsnorm(s.ins, s.residuals, s.weight, s.segs, s.flags, 1, n, eps=s.eps)
+    share = car.prepare_twoshot_rmsnorm(s.ins, s.residuals, s.weight, s.segs, s.flags, 0, 1, only0(s.ros),
+                                        only0(s.outs), eps=s.eps)
+
+    def step():
+        peers(0)
+        share(0)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()  # warm-up outside the capture
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    calls = 1
+    for rep in range(6):
+        new_data(s, 471 + rep)
+        if rep % 2:
+            step()  # eager, between replays
+            calls += 1
+            torch.cuda.synchronize()
+        g.replay()
+        calls += 1
+        torch.cuda.synchronize()
+        car.raise_on_status(s.flags, f"replay {rep}")
+        check_share(s, 0, f"n={n} rows={rows} replay {rep}")
+    check_epochs(s, calls)
