@@ -492,7 +492,14 @@ def add_rmsnorm_calls(torch, car, rig):
             tr = car.prepare_twoshot_rmsnorm(b.ins, resid, w, segs, fl, ME, ME + 1,
                                              only_me(b, b.outs[2:3] * n), only_me(b, b.outs[3:4] * n))
             c["twoshot_rmsnorm"] = lambda s, f=tr: f(s)
-            keep[i] = segs
+            # the same share with auto step ids, on segments of its own (explicit
+            # and auto ids do not mix); its peers published at PEER_STEP too
+            segs_a = car.new_rmsnorm_segments(n, rows, RMS_ROW // es, rig.dt)
+            car.ar_twoshot_rmsnorm(b.ins, resid, w, segs_a, fl, PEER_STEP, r0=1, r1=n)
+            ta = car.prepare_twoshot_rmsnorm(b.ins, resid, w, segs_a, fl, ME, ME + 1,
+                                             only_me(b, b.outs[2:3] * n), only_me(b, b.outs[3:4] * n))
+            c["twoshot_rmsnorm_auto"] = lambda s, f=ta: f(0)
+            keep[i] = (segs, segs_a)
     torch.cuda.synchronize()
     car.raise_on_status(fl, "publishing the peers' fused reduce-scatters")
     keep["flags"], keep["weight"], keep["workspace"] = fl, w, ws
@@ -562,7 +569,8 @@ def sweep(args, torch, car, np, out_path):
                     ("push", acc.push(S, n)), ("stage", acc.push(S, 1)), ("ag_copy", acc.twoshot_ag(n, S, 1)),
                     ("twoshot_auto", acc.twoshot(n, S, 1)),
                     ("oneshot_rmsnorm", acc.oneshot_rmsnorm(n, S, RMS_ROW)),
-                    *([("twoshot_rmsnorm", acc.twoshot_rmsnorm(n, S, RMS_ROW))] if rms_ts else []),
+                    *([("twoshot_rmsnorm", acc.twoshot_rmsnorm(n, S, RMS_ROW)),
+                       ("twoshot_rmsnorm_auto", acc.twoshot_rmsnorm(n, S, RMS_ROW))] if rms_ts else []),
                     # the all-rank launches last: they rewrite every rank's segments
                     ("twoshot_full", acc.twoshot(n, S, n)), ("twoshot_ll_full", acc.twoshot_ll(n, S, n, "ll")),
                     ("twoshot_ll128_full", acc.twoshot_ll(n, S, n, "ll128"))]
