@@ -123,11 +123,11 @@ __device__ __forceinline__ void row_store_coherent(u32x4* row, uint32_t row_byte
 
 // One row: base = the row's first vector in the ranks' inputs, residual =
 // the row's first vector of the residual.
-template <typename T, int NR, int VPT>
+template <typename T, int NR, int VPT, int RBMAX = (VPT == 1 ? kMaxRanks : 8)>
 __device__ __forceinline__ void rmsnorm_row(const RmsParams& p, size_t base, const u32x4* residual, RowDst d,
                                             float (&part)[kMaxWaves], float& factor) {
     constexpr int E = Vec<T>::E;
-    constexpr int RB = VPT == 1 || NR <= 8 ? NR : 8;  // loads in flight per vector
+    constexpr int RB = NR <= RBMAX ? NR : RBMAX;  // loads in flight per vector
     const uint32_t tid = threadIdx.x;
     const uint32_t lane = tid & (kWave - 1);
     const uint32_t wave = tid / kWave;
@@ -433,7 +433,7 @@ __device__ __forceinline__ void twoshot_rmsnorm_rows(const TsRmsParams& q, float
             const size_t base = (size_t(r) * q.group + k) * p.vecs;
             RowDst d{q.do_ag ? q.res_out[r] + base : nullptr, q.do_ag ? q.out[r] + base : nullptr,
                      q.seg[r] + (size_t(q.group) + k) * p.vecs, q.seg[r] + size_t(k) * p.vecs};
-            rmsnorm_row<T, NR, VPT>(p, base, q.residual[r] + base, d, part, factor);
+            rmsnorm_row<T, NR, VPT, (NR > 15 ? 4 : 8)>(p, base, q.residual[r] + base, d, part, factor);
             __syncthreads();  // part and factor are rewritten by the next row
         }
         const uint32_t step = ts_take_step(q, epoch, id);
@@ -481,8 +481,12 @@ __device__ __forceinline__ void twoshot_rmsnorm_rows(const TsRmsParams& q, float
     }
 }
 
+// With one vector per lane and up to 8 ranks the kernel fits 64 VGPRs, so
+// two 1024-lane workgroups share a compute unit (at 66, one did: 57 against
+// 52 us for one rank's share of 64 MiB, n = 8 bf16); above 8 ranks a 64-VGPR
+// bound would spill.
 template <typename T, int NR, int VPT>
-__global__ __launch_bounds__(kMaxBlock) void twoshot_rmsnorm_kernel(TsRmsParams q) {
+__global__ __launch_bounds__(kMaxBlock, VPT == 1 ? 8 : 1) void twoshot_rmsnorm_kernel(TsRmsParams q) {
     __shared__ float part[kMaxWaves];
     __shared__ float factor;
     AutoId id;
