@@ -481,10 +481,11 @@ __device__ __forceinline__ void twoshot_rmsnorm_rows(const TsRmsParams& q, float
     }
 }
 
-// With one vector per lane and up to 8 ranks the kernel fits 64 VGPRs, so
-// two 1024-lane workgroups share a compute unit (at 66, one did: 57 against
-// 52 us for one rank's share of 64 MiB, n = 8 bf16); above 8 ranks a 64-VGPR
-// bound would spill.
+// With one vector per lane the kernel is held to 64 VGPRs (8 waves per
+// SIMD), so two 1024-lane workgroups share a compute unit; the rows' rank
+// loads go out in batches of 8 (4 at 16 ranks) so that this needs no spill.
+// At 66 VGPRs one workgroup did: 57 against 52 us for one rank's share of
+// 64 MiB (n = 8 bf16), 60 against 52 us at n = 16.
 template <typename T, int NR, int VPT>
 __global__ __launch_bounds__(kMaxBlock, VPT == 1 ? 8 : 1) void twoshot_rmsnorm_kernel(TsRmsParams q) {
     __shared__ float part[kMaxWaves];
