@@ -187,9 +187,9 @@ int ar_oneshot_rmsnorm(const void* const* in, int n, const void* residual, const
  *  weight       : hidden elements.
  *  seg          : n device pointers, ar_rmsnorm_segment_bytes(n, rows,
  *                 hidden, dtype) bytes each, zeroed before their first use
- *                 (their slots and flags carry step ids; the last 16 bytes
- *                 hold the rank's epoch for auto ids); seg[r] for r in
- *                 [r0, r1) written, the peers' read when fused.
+ *                 (their slots and flags carry step ids, and they end with
+ *                 the epoch words of auto ids); seg[r] for r in [r0, r1)
+ *                 written, the peers' read when fused.
  *  residual_out, out : NULL (the reduce-scatter of ranks [r0, r1) alone),
  *                 or n device pointers of rows * hidden elements, entries in
  *                 [r0, r1) used, and then r1 = r0 + 1: one rank's share in
@@ -198,12 +198,14 @@ int ar_oneshot_rmsnorm(const void* const* in, int n, const void* residual, const
  *  flags, step  : a flag region of ar_flag_bytes(n) and the step id, >= 1
  *                 and above every earlier call's on these segments and flags
  *                 (the peers' reduce-scatters of this step publish it); or 0
- *                 (auto): rank r's id is its epoch, kept in seg[r], plus
- *                 one, and the launch advances the epochs of ranks [r0, r1)
- *                 once all its wavefronts have finished (they count
- *                 themselves out in seg[r0]).  Every rank's launch of a step
- *                 takes the same id as long as each rank makes one auto call
- *                 per step, so a call captured once into a HIP graph takes a
+ *                 (auto): seg[r] ends with an epoch word per wavefront of
+ *                 rank r's reduce-scatter and of its all-gather; each
+ *                 wavefront uses its word + 1 as the id and stores that back
+ *                 when it ends.  Every rank's launch of a step takes the same
+ *                 id as long as each rank's rows are reduce-scattered once
+ *                 per step (by its share or a reduce-scatter-only call) and
+ *                 each share runs once per step, with the same rows, hidden
+ *                 and dtype, so a call captured once into a HIP graph takes a
  *                 new id on every replay ([CAR] 实现: the graph path keeps
  *                 fixed registered addresses).  Zeroing the segments restarts
  *                 the epochs; do not mix explicit and auto ids between
