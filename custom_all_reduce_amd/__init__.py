@@ -338,7 +338,8 @@ def prepare_oneshot_rmsnorm(ins, residual: torch.Tensor, weight: torch.Tensor, r
 
 def rmsnorm_segment_bytes(n: int, rows: int, hidden: int, dtype) -> int:
     """Bytes of one rank's segment in ar_twoshot_rmsnorm (its rows of out and of
-    residual_out, then the parts' slots and flags); 0 if rows is not a multiple of n."""
+    residual_out, the parts' slots and flags, then the epoch words of auto
+    step ids); 0 if rows is not a multiple of n."""
     return int(_lib.ar_rmsnorm_segment_bytes(int(n), int(rows), int(hidden), _dtype_arg(dtype)))
 
 
