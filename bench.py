@@ -472,7 +472,8 @@ def add_rmsnorm_calls(torch, car, rig):
     residual_out and output in three of the set's other output buffers; where
     the rows split over the ranks, also its two-shot form, rank 0's share, the
     peers' reduce-scatters published once beforehand on a flag region of its
-    own.  Returns (whether the two-shot form was added, the segments to keep
+    own, with explicit step ids and (on segments of its own) auto ones.
+    Returns (whether the two-shot form was added, the buffers to keep
     alive)."""
     n, es, S = rig.n, rig.es, rig.S
     w = torch.ones(RMS_ROW // es, dtype=rig.dt, device="cuda")
