@@ -209,7 +209,11 @@ int ar_oneshot_rmsnorm(const void* const* in, int n, const void* residual, const
  *                 new id on every replay ([CAR] 实现: the graph path keeps
  *                 fixed registered addresses).  Zeroing the segments restarts
  *                 the epochs; do not mix explicit and auto ids between
- *                 zeroings, and zero them before 2^32 - 1 calls.
+ *                 zeroings, and zero them before 2^32 - 1 calls.  A step in
+ *                 which some rank's rows were not reduce-scattered leaves
+ *                 that rank's words a step behind: the shares' all-gathers
+ *                 time out on it until the segments are zeroed (and the flag
+ *                 region reset).
  * A wait that runs out writes AR_ERR_TIMEOUT | phase << 8 | rank << 16 to the
  * flag region's status word: AR_PHASE_TWOSHOT_AG with the peer (all-gather),
  * AR_PHASE_RMSNORM with the rank (a row's parts); detail: the row in the

@@ -260,3 +260,37 @@ def test_auto_step_ids_replayed_in_a_graph(n, rows, hidden):
         car.raise_on_status(s.flags, f"replay {rep}")
         check_share(s, 0, f"n={n} rows={rows} replay {rep}")
     check_epochs(s, calls)
+
+
+@pytest.mark.parametrize("n, rows, hidden", [AUTO_CASES[0], AUTO_CASES[3]])
+def test_auto_step_ids_after_a_missing_peer(n, rows, hidden):
+    # rank 1's reduce-scatter is skipped for a step: rank 0's share times out naming
+    # it, and rank 1's epoch words stay a step behind, so the next step times out
+    # too; zeroing the segments (and resetting the flag region) restarts every epoch
+    s = Setup(n, "bf16", rows, hidden, config=480)
+    old = car.get_poll_timeout_ns()
+    car.set_poll_timeout_ns(1_000_000)
+    try:
+        for it, skip in enumerate((True, False)):
+            new_data(s, 481 + it)
+            car.ar_twoshot_rmsnorm(s.ins, s.residuals, s.weight, s.segs, s.flags, 0, r0=2, r1=n, eps=s.eps)
+            if not skip:
+                car.ar_twoshot_rmsnorm(s.ins, s.residuals, s.weight, s.segs, s.flags, 0, r0=1, r1=2, eps=s.eps)
+            s.share(0, 0)
+            torch.cuda.synchronize()
+            word, _ = car.read_status(s.flags)
+            code, phase, rank = car.decode_status(word)
+            assert (code, phase, rank) == (car.AR_ERR_TIMEOUT, car.PHASE_TWOSHOT_AG, 1), f"step {it}"
+            car.ar_flag_barrier_reset(s.flags, n)
+    finally:
+        car.set_poll_timeout_ns(old)
+    for t in s.segs:
+        t.zero_()
+    for it in range(2):
+        new_data(s, 483 + it)
+        car.ar_twoshot_rmsnorm(s.ins, s.residuals, s.weight, s.segs, s.flags, 0, r0=1, r1=n, eps=s.eps)
+        s.share(0, 0)
+        torch.cuda.synchronize()
+        car.raise_on_status(s.flags, f"after the restart, step {it}")
+        check_share(s, 0, f"n={n} rows={rows} after the restart, step {it}")
+    check_epochs(s, 2)
