@@ -174,7 +174,7 @@ int main(void) {
      * for bit, out within 4e-6 of the oracle's fp64 value (the bound derived for the device's
      * fp32 sum of squares) */
     {
-        const size_t rows = 6, hidden = 4096;
+        const size_t rows = 8, hidden = 4096;
         setup(&c, 8, rows * hidden, AR_F32);
         float* res = malloc(c.bytes);
         float* w = malloc(hidden * 4);
@@ -204,6 +204,42 @@ int main(void) {
         good &= status == 0;
         printf("%-40s n=%2d numel=%8zu f32 : %s\n", "ar_oneshot_rmsnorm", c.n, c.numel, good ? "ok" : "MISMATCH");
         ok &= good;
+
+        /* its two-shot form with auto step ids (step 0): the peers' reduce-scatters, then rank
+         * 0's share into the same outputs, cleared first; the same bounds */
+        const size_t sb = ar_rmsnorm_segment_bytes(c.n, rows, hidden, AR_F32);
+        void* segs[AR_MAX_RANKS];
+        const void* resids[AR_MAX_RANKS];
+        void* ros[AR_MAX_RANKS] = {0};
+        void* outs[AR_MAX_RANKS] = {0};
+        for (int r = 0; r < c.n; ++r) {
+            CHECK_HIP(hipMalloc(&segs[r], sb));
+            CHECK_HIP(hipMemset(segs[r], 0, sb));
+            resids[r] = d_res;
+        }
+        void* fl;
+        CHECK_HIP(hipMalloc(&fl, ar_flag_bytes(c.n)));
+        CHECK_HIP(hipMemset(fl, 0, ar_flag_bytes(c.n)));
+        CHECK_HIP(hipMemset(d_ro, 0xff, c.bytes));
+        CHECK_HIP(hipMemset(d_out, 0xff, c.bytes));
+        ros[0] = d_ro;
+        outs[0] = d_out;
+        ok &= ar_twoshot_rmsnorm((const void* const*)c.dev, c.n, resids, d_w, segs, NULL, NULL, rows, hidden, 1e-6f,
+                                 AR_F32, 1, c.n, (uint32_t*)fl, 0, NULL) == AR_OK;
+        ok &= ar_twoshot_rmsnorm((const void* const*)c.dev, c.n, resids, d_w, segs, ros, outs, rows, hidden, 1e-6f,
+                                 AR_F32, 0, 1, (uint32_t*)fl, 0, NULL) == AR_OK;
+        CHECK_HIP(hipDeviceSynchronize());
+        CHECK_HIP(hipMemcpy(got, d_ro, c.bytes, hipMemcpyDeviceToHost));
+        good = memcmp(got, ro_want, c.bytes) == 0;
+        CHECK_HIP(hipMemcpy(got, d_out, c.bytes, hipMemcpyDeviceToHost));
+        for (size_t i = 0; i < c.numel; ++i) good &= fabs((double)got[i] - y[i]) <= 4e-6 * fabs(y[i]);
+        CHECK_HIP(hipMemcpy(&status, fl, 4, hipMemcpyDeviceToHost));
+        good &= status == 0;
+        printf("%-40s n=%2d numel=%8zu f32 : %s\n", "ar_twoshot_rmsnorm (auto step ids)", c.n, c.numel,
+               good ? "ok" : "MISMATCH");
+        ok &= good;
+        for (int r = 0; r < c.n; ++r) CHECK_HIP(hipFree(segs[r]));
+        CHECK_HIP(hipFree(fl));
         CHECK_HIP(hipFree(d_res));
         CHECK_HIP(hipFree(d_w));
         CHECK_HIP(hipFree(d_ro));
