@@ -207,8 +207,9 @@ def new_data(s: Setup, config):
         t.copy_(to_dev(a))
 
 
-# parts of rows (8 and 2 rows per rank), a workgroup per row (300 rows per rank; light rows)
-AUTO_CASES = [(8, 64, 8192), (16, 32, 16384), (8, 8 * 300, 8192), (4, 32, 64)]
+# parts of rows (8 and 2 rows per rank), a workgroup per row (300 rows per rank; light rows;
+# 1030 rows per rank, two to an arrival slot)
+AUTO_CASES = [(8, 64, 8192), (16, 32, 16384), (8, 8 * 300, 8192), (4, 32, 64), (2, 2 * 1030, 8)]
 
 
 @pytest.mark.parametrize("n, rows, hidden", AUTO_CASES)
