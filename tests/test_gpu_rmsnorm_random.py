@@ -4,7 +4,9 @@ row length (whole 16-byte vectors, up to the 64 KiB row), data type, eps, the
 value distribution (normal, or small integers whose sums are exact), and,
 for the one-shot form, whether residual_out is the residual itself and
 whether a workspace is given; the two-shot form runs every rank's
-reduce-scatter and then every rank's share.  residual_out is compared with
+reduce-scatter and then every rank's share with explicit step ids, or, with
+auto step ids (step 0: ids kept in the segments, one reduce-scatter per rank
+per step), the peers' reduce-scatters and then rank 0's share.  residual_out is compared with
 the oracle bit for bit and out with the oracle's fp64 value within the bound
 derived in test_gpu_rmsnorm.py; where both forms take the same kind of path
 (a workgroup per row, or parts of rows), their outputs must agree bit for
@@ -41,15 +43,16 @@ def draw(i):
     kind = "int" if rng.random() < 0.3 else "normal"
     in_place = bool(rng.random() < 0.3)
     ws = bool(rng.random() < 0.6)
-    return n, dt, rows, hidden, eps, kind, in_place, ws
+    auto = bool(rng.random() < 0.5)
+    return n, dt, rows, hidden, eps, kind, in_place, ws, auto
 
 
 @pytest.mark.parametrize("i", range(CASES))
 def test_random_case(i):
-    n, dt, rows, hidden, eps, kind, in_place, use_ws = draw(i)
+    n, dt, rows, hidden, eps, kind, in_place, use_ws, auto = draw(i)
     numel = rows * hidden
     what = f"case {i}: n={n} {dt} rows={rows} hidden={hidden} eps={eps} {kind}" \
-           f"{' in place' if in_place else ''}{' workspace' if use_ws else ''}"
+           f"{' in place' if in_place else ''}{' workspace' if use_ws else ''}{' auto ids' if auto else ''}"
     print(what, flush=True)
     host = synth.rank_inputs(n, numel, dt, kind, config=9100 + i)
     res = synth.rank_inputs(1, numel, dt, kind, config=9200 + i)[0]
@@ -84,14 +87,19 @@ def test_random_case(i):
     flags = car.new_flags(n)
     outs = [torch.empty(numel, dtype=ins[0].dtype, device="cuda") for _ in range(n)]
     ros = [torch.empty(numel, dtype=ins[0].dtype, device="cuda") for _ in range(n)]
-    car.ar_twoshot_rmsnorm(ins, residuals, d_w, segs, flags, 1, r0=0, r1=n, eps=eps)
-    for me in range(n):
-        car.ar_twoshot_rmsnorm(ins, residuals, d_w, segs, flags, 1, r0=me, r1=me + 1,
+    if auto:
+        car.ar_twoshot_rmsnorm(ins, residuals, d_w, segs, flags, 0, r0=1, r1=n, eps=eps)
+        shares = [0]
+    else:
+        car.ar_twoshot_rmsnorm(ins, residuals, d_w, segs, flags, 1, r0=0, r1=n, eps=eps)
+        shares = range(n)
+    for me in shares:
+        car.ar_twoshot_rmsnorm(ins, residuals, d_w, segs, flags, 0 if auto else 1, r0=me, r1=me + 1,
                                residual_outs=[ros[r] if r == me else None for r in range(n)],
                                outs=[outs[r] if r == me else None for r in range(n)], eps=eps)
     torch.cuda.synchronize()
     car.raise_on_status(flags, what)
-    for me in range(n):
+    for me in shares:
         assert np.array_equal(bits(ros[me]), oracle_bits(want_ro)), f"{what}: two-shot residual_out, rank {me}"
         two = host_values(outs[me], dt)
         check_out(two, y, dt, f"{what} (two-shot, rank {me})")
