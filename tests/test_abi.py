@@ -475,6 +475,68 @@ def test_oneshot_rmsnorm_argument_errors():
     assert f0(ins, n, res, w, ro, out, rows, hidden, 1e-6, 1, w, NUL) == car.AR_ERR_ALIAS
 
 
+def test_twoshot_rmsnorm_argument_errors():
+    # every check happens before anything is enqueued, so fake addresses serve
+    n, rows, hidden = 4, 8, 4096
+    ins = fake_ins(n)
+    res = fake_ins(n, base=A + (64 << 30))
+    segs = fake_ins(n, base=A + (80 << 30))
+    ro = fake_ins(n, base=A + (96 << 30))
+    out = fake_ins(n, base=A + (112 << 30))
+    w, fl = A + (128 << 30), A + (129 << 30)
+
+    def f(ins=ins, n=n, res=res, w=w, segs=segs, ro=ro, out=out, rows=rows, hidden=hidden, eps=1e-6, dt=1, r0=0,
+          r1=1, fl=fl, step=0):
+        return L.ar_twoshot_rmsnorm(ins, n, res, w, segs, ro, out, rows, hidden, eps, dt, r0, r1, fl, step, NUL)
+
+    assert f(n=1) == car.AR_ERR_ARG
+    assert f(rows=0) == car.AR_ERR_ARG
+    assert f(hidden=0) == car.AR_ERR_ARG
+    assert f(dt=2) == car.AR_ERR_ARG
+    assert f(w=None) == car.AR_ERR_ARG
+    assert f(fl=None) == car.AR_ERR_ARG
+    assert f(r0=2, r1=2) == car.AR_ERR_ARG
+    assert f(r0=3, r1=5, ro=None, out=None) == car.AR_ERR_ARG  # past n
+    assert f(r0=0, r1=2) == car.AR_ERR_ARG  # an all-gather for two ranks in one launch
+    assert f(ro=None) == car.AR_ERR_ARG  # out without residual_out
+    for eps in (-1e-6, float("nan"), float("inf")):
+        assert f(eps=eps) == car.AR_ERR_ARG
+    assert f(hidden=32768 + 8) == car.AR_ERR_ARG  # a row of more than 64 KiB
+    assert f(segs=fake_ins(n, base=A + (80 << 30) + 8)) == car.AR_ERR_ALIGN
+    assert f(fl=fl + 4) == car.AR_ERR_ALIGN
+    assert f(w=w + 8) == car.AR_ERR_ALIGN
+    assert f(rows=6) == car.AR_ERR_DIVISIBLE  # rows split over the ranks
+    assert f(hidden=4100) == car.AR_ERR_DIVISIBLE  # whole 16-byte vectors per row
+    # overlaps: an output over an input; residual_out over the residual (no in-place
+    # update in this form); a peer's segment, read by the all-gather, over the output
+    assert f(out=fake_ins(n, base=A + 16)) == car.AR_ERR_ALIAS
+    assert f(ro=res) == car.AR_ERR_ALIAS
+    assert f(segs=arr(*([segs[0]] + [out[0] + 1024] + list(segs)[2:]))) == car.AR_ERR_ALIAS
+    # the flag region over the weight
+    assert f(fl=w) == car.AR_ERR_ALIAS
+
+
+@pytest.mark.parametrize("n, rows, hidden, dt", [(8, 512, 8192, 1), (8, 4096, 8192, 1), (16, 32, 16384, 1),
+                                                 (4, 32, 64, 1), (2, 2060, 8, 1), (8, 64, 4096, 0)])
+def test_rmsnorm_segment_bytes_cover_the_layout(n, rows, hidden, dt):
+    # a rank's segment: G out rows and G residual_out rows, G P 8-byte partial slots and G P
+    # done flags, then (16-byte aligned) the auto ids' epoch words: G P per rank for parts of
+    # rows, tiles x wavefronts per workgroup per rank for a workgroup per row
+    es = 4 if dt == 0 else 2
+    V, G = hidden * es // 16, rows // n
+    P = -(-V // 64)
+    if G < 256 and (n + 1) * V * 16 >= 128 << 10:
+        words = n * G * P
+    else:
+        tile = -(-G // 1024)
+        vpt = 1 if V <= 1024 else (2 if V <= 2048 else 4)
+        words = n * -(-G // tile) * -(-(-(-V // vpt)) // 64)
+    need = -(-(32 * G * V + 12 * G * P) // 16) * 16 + 4 * words
+    got = L.ar_rmsnorm_segment_bytes(n, rows, hidden, dt)
+    assert got % 16 == 0 and need <= got < need + 16
+    assert L.ar_rmsnorm_segment_bytes(n, rows + 1, hidden, dt) == 0  # rows that do not split
+
+
 def test_rmsnorm_workspace_size():
     # 32 status words, 1024 epochs and 1024 8-byte slots
     assert car.rmsnorm_workspace_bytes() == (32 + 1024 + 2 * 1024) * 4
